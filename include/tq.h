@@ -1,0 +1,198 @@
+/*
+ * libtq -- randomized-Hadamard + Lloyd-Max vector codecs for AMD MI355X (gfx950).
+ *
+ * Two codecs share one shape: a randomized Hadamard rotation, a Lloyd-Max
+ * codebook quantiser and bit packing, plus the inverse.
+ *
+ *   TQ3     the 3-bit KV-vector codec of the page "ComfyUI-TurboQuant:
+ *           tq3_core.py" (module docstring, tq3_quantize, tq3_dequantize):
+ *           each 128-float vector becomes a 56-byte record.
+ *   Orbit   the weight codec of the page "zerogpu-sdxlTrainer:
+ *           toolkit/util/orbit_quant.py" (rpbh_forward, _quantize_rows,
+ *           _dequantize_rotated, dequantize): permutation + signs + block
+ *           Hadamard, per-row norms, 2/3/4-bit Gaussian Lloyd-Max codes.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named "device" are HIP device memory owned by the caller; the
+ *     library never allocates, frees or synchronises. Work is enqueued on
+ *     `stream` (a hipStream_t; NULL = the null stream) and runs asynchronously.
+ *   - Pointers named "host" are read during the call only.
+ *   - A count of zero is a successful no-op.
+ *   - Every argument is checked before anything is launched; on a non-zero
+ *     return nothing was enqueued. tq_status_str() names each code.
+ *   - Results are bit-for-bit deterministic: fixed operation order, no atomics.
+ *   - Arithmetic is IEEE fp32, round to nearest even, with the operation order
+ *     fixed by the library (see each function). Inputs holding NaN or Inf are
+ *     outside the contract.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+enum {
+    TQ_OK = 0,
+    TQ_ERR_NULL = 1,    /* a required pointer is NULL                       */
+    TQ_ERR_SHAPE = 2,   /* negative count, bad stride, d not a multiple of h */
+    TQ_ERR_DTYPE = 3,   /* unknown dtype code                               */
+    TQ_ERR_BITS = 4,    /* bits not in {2, 3, 4}                            */
+    TQ_ERR_BLOCK = 5,   /* Hadamard block h = d & -d outside [32, 4096]     */
+    TQ_ERR_ALIGN = 6,   /* pointer or stride breaks the stated alignment    */
+    TQ_ERR_LAUNCH = 7,  /* the HIP runtime refused the launch               */
+    TQ_ERR_ARG = 8      /* other invalid argument (flag value, codebook)    */
+};
+
+/* ---- element types ----------------------------------------------------- */
+enum {
+    TQ_F32 = 0,   /* IEEE binary32                              */
+    TQ_BF16 = 1,  /* bfloat16; widened exactly, narrowed by RNE */
+    TQ_F16 = 2    /* IEEE binary16; widened exactly, narrowed by RNE */
+};
+
+/* ---- bit order of packed OrbitQuant codes --------------------------------- */
+enum {
+    TQ_MSB_FIRST = 0, /* the page's pack_codes layout: code j's most significant
+                         bit at stream bit bits*j, stream bit q = bit 7-(q%8)
+                         of byte q/8                                         */
+    TQ_LSB_FIRST = 1  /* code j's bit t at stream bit bits*j+t, stream bit q =
+                         bit q%8 of byte q/8                                 */
+};
+
+#define TQ3_DIM 128          /* elements per TQ3 vector                      */
+#define TQ3_RECORD_BYTES 56  /* 48 bytes of 3-bit indices + fp32 norm + scale */
+
+/*
+ * tq3_quantize -- "tq3_core.py", tq3_quantize (docstring steps 1-6).
+ *
+ * For each of n_vec vectors v (128 elements at x + v*x_row_stride):
+ *   norm   = max(sqrt(sum of squares), 1e-8); the sum is the pairwise tree
+ *            that adds neighbours (j, j^1), then (j, j^2), ..., (j, j^64);
+ *   u_j    = x_j / norm;  w_j = u_j * s_j  (s_j = -1 where sign bit j is set);
+ *   y      = FWHT_128(w) (stages with half-width 1, 2, ..., 64, each pair
+ *            becoming (a + b, a - b)), then times fp32(1/sqrt(128));
+ *   scale  = max(max_j |y_j|, 1e-8);
+ *   idx_j  = number of TQ3 boundaries b_k (fp32 of -0.7992, -0.4824, -0.2304,
+ *            0, 0.2304, 0.4824, 0.7992) with b_k < y_j / scale.
+ * Record v (56 bytes at records + 56*v): bytes 0..47 hold idx_j at stream
+ * bits 3j..3j+2 (LSB-first; stream bit q = bit q%8 of byte q/8), bytes 48..51
+ * the fp32 norm, 52..55 the fp32 scale, little-endian.
+ *
+ *   x            device, n_vec rows of x_dtype; 16-byte aligned; x_row_stride
+ *                in elements, >= 128, a multiple of 8 (16 bytes).
+ *   x_dtype      TQ_F32, TQ_BF16 or TQ_F16.
+ *   sign_mask    host, 16 bytes: bit j (bit j%8 of byte j/8) set <=> s_j = -1.
+ *                The TQ3 page draws s from a CPU generator seeded with 42.
+ *   records      device, n_vec * 56 bytes, 8-byte aligned.
+ */
+int tq3_quantize(const void* x, int x_dtype, int64_t n_vec, int64_t x_row_stride,
+                 const uint8_t* sign_mask, uint8_t* records, void* stream);
+
+/*
+ * tq3_dequantize -- "tq3_core.py", tq3_dequantize.
+ *
+ * For each record: c_j = C[idx_j] * scale (C = fp32 of the printed centroids
+ * -0.9816, -0.6168, -0.3479, -0.1129, 0.1129, 0.3479, 0.6168, 0.9816), the
+ * same FWHT and 1/sqrt(128) multiply as above (the normalised transform is its
+ * own inverse), times s_j, times norm. fp32 results, narrowed by RNE when
+ * y_dtype is TQ_BF16 or TQ_F16.
+ *
+ *   records      device, n_vec * 56 bytes, 8-byte aligned.
+ *   sign_mask    host, 16 bytes, as for tq3_quantize.
+ *   y            device, n_vec rows of y_dtype, 16-byte aligned; y_row_stride
+ *                in elements, >= 128, a multiple of 8.
+ */
+int tq3_dequantize(const uint8_t* records, int64_t n_vec, const uint8_t* sign_mask,
+                   void* y, int y_dtype, int64_t y_row_stride, void* stream);
+
+/*
+ * orbit_quantize_weight -- "orbit_quant.py", _quantize_rows with the buffers
+ * of OrbitQuantizer.quantize_.
+ *
+ * For each of `rows` rows of the fp32 weight W (d elements each, contiguous):
+ *   y_j     = W[perm_j] * signs_j, then on every block of h = d & -d elements
+ *             the FWHT stages above, then times fp32(h ** -0.5);
+ *   norm    = sqrt(s), s = pairwise-tree sums of y^2 inside each block (as
+ *             for TQ3), added block by block from left to right;
+ *   u_j     = y_j / (norm + fp32(1e-10));
+ *   code_j  = number of edges e_k < u_j, e_k = (codebook[k] + codebook[k+1])/2
+ *             in fp32.
+ * Codes are packed in `bit_order` into rows of d*bits/8 bytes.
+ *
+ *   W            device, rows x d fp32, row-major, 16-byte aligned.
+ *   d            input features; h = d & -d must lie in [32, 4096] (the page
+ *                skips layers with h < 32) and d <= 16384.
+ *   bits         2, 3 or 4.
+ *   perm         device, d int32, a permutation of 0..d-1.
+ *   signs        device, d int8, each +1 or -1.
+ *   codebook     host, 2^bits fp32 values in ascending order (the page's
+ *                Gaussian Lloyd-Max codebook times d ** -0.5; see
+ *                orbit_make_codebook).
+ *   bit_order    TQ_MSB_FIRST (the page's layout) or TQ_LSB_FIRST.
+ *   packed       device, rows * d * bits / 8 bytes, 16-byte aligned.
+ *   row_norms    device, rows fp32.
+ */
+int orbit_quantize_weight(const float* W, int64_t rows, int64_t d, int bits,
+                          const int32_t* perm, const int8_t* signs,
+                          const float* codebook, int bit_order, uint8_t* packed,
+                          float* row_norms, void* stream);
+
+/*
+ * orbit_dequantize -- "orbit_quant.py", _dequantize_rotated and dequantize.
+ *
+ *   rotated_only = 1: W'[r, j] = codebook[code_j] * norm_r (the rotated-basis
+ *                     weight that the page's forward multiplies with P x).
+ *   rotated_only = 0: W' as above, then per block the FWHT and h ** -0.5
+ *                     multiply, times signs_j, then out[r, j] = z[inv_perm_j]
+ *                     (the original-basis weight).
+ *
+ *   packed, row_norms   device, as written by orbit_quantize_weight.
+ *   inv_perm            device, d int32, the inverse of perm (used when
+ *                       rotated_only = 0; may be NULL otherwise).
+ *   signs               device, d int8 (may be NULL when rotated_only = 1).
+ *   codebook            host, 2^bits fp32.
+ *   W_out               device, rows x d of out_dtype (TQ_F32, TQ_BF16 or
+ *                       TQ_F16), 16-byte aligned.
+ */
+int orbit_dequantize(const uint8_t* packed, const float* row_norms, int64_t rows,
+                     int64_t d, int bits, const int32_t* inv_perm,
+                     const int8_t* signs, const float* codebook, int bit_order,
+                     int rotated_only, void* W_out, int out_dtype, void* stream);
+
+/* Bytes per TQ3 record: 48 + 4 + 4 = 56 ("tq3_core.py", tq3_memory_bytes). */
+size_t tq3_record_bytes(void);
+
+/* Largest power of two dividing d ("orbit_quant.py", hadamard_block_size);
+ * returns 0 for d <= 0. */
+int64_t orbit_block_size(int64_t d);
+
+/*
+ * tq_gaussian_lloyd_max -- host-side codebook ("orbit_quant.py",
+ * gaussian_lloyd_max): 2^bits levels for the standard normal, started at the
+ * quantiles of (k + 1/2) / 2^bits, `iters` Lloyd iterations in fp64 (edges at
+ * centroid midpoints, centroids at the conditional means of their cells), no
+ * early stop. Writes 2^bits ascending doubles to `out` (host). bits in [1, 8],
+ * iters >= 0.
+ */
+int tq_gaussian_lloyd_max(int bits, int iters, double* out);
+
+/*
+ * orbit_make_codebook -- host-side: the codebook OrbitQuantizer.quantize_
+ * builds for input dimension d: fp32(LM_k) * fp32(d ** -0.5) in fp32, with
+ * LM from tq_gaussian_lloyd_max(bits, 200). Writes 2^bits floats to `out`.
+ */
+int orbit_make_codebook(int bits, int64_t d, float* out);
+
+/* Human-readable name of a status code (static string). */
+const char* tq_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

@@ -1,0 +1,239 @@
+"""Python binding of libtq: the randomized-Hadamard + Lloyd-Max codecs on MI355X.
+
+Argument marshalling only. Every step of every codec runs in the HIP kernels of
+libtq.so (built in-tree by ``build.py``); torch supplies device memory and the
+current stream. There is no CPU fallback: importing this package without the
+built library, or calling it with CPU tensors, raises.
+
+Entry points (same names as the C ABI in include/tq.h):
+  tq3_quantize(x)                  -> uint8 [..., D/128, 56] records
+  tq3_dequantize(records, dtype)   -> [..., D/128 * 128] tensor
+  orbit_quantize_weight(W, bits)   -> (packed uint8, row_norms fp32)
+  orbit_dequantize(packed, norms, d, bits, rotated_only, dtype)
+plus host helpers tq3_record_bytes, orbit_block_size, tq_gaussian_lloyd_max,
+orbit_make_codebook.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtq.so")
+
+TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
+TQ_MSB_FIRST, TQ_LSB_FIRST = 0, 1
+TQ3_DIM, TQ3_RECORD_BYTES = 128, 56
+
+_DTYPES = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16, torch.float16: TQ_F16}
+_STATUS = {
+    1: ValueError, 2: ValueError, 3: TypeError, 4: ValueError, 5: ValueError,
+    6: ValueError, 7: RuntimeError, 8: ValueError,
+}
+
+_vp, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"libtq.so not built at {LIB_PATH}; run `python -m randomized_hadamard_lloyd_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "tq3_quantize": [_vp, _int, _i64, _i64, _vp, _vp, _vp],
+        "tq3_dequantize": [_vp, _i64, _vp, _vp, _int, _i64, _vp],
+        "orbit_quantize_weight": [_vp, _i64, _i64, _int, _vp, _vp, _vp, _int, _vp, _vp, _vp],
+        "orbit_dequantize": [_vp, _vp, _i64, _i64, _int, _vp, _vp, _vp, _int, _int, _vp,
+                             _int, _vp],
+        "tq_gaussian_lloyd_max": [_int, _int, _vp],
+        "orbit_make_codebook": [_int, _i64, _vp],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = _int
+    lib.tq3_record_bytes.argtypes = []
+    lib.tq3_record_bytes.restype = ctypes.c_size_t
+    lib.orbit_block_size.argtypes = [_i64]
+    lib.orbit_block_size.restype = _i64
+    lib.tq_status_str.argtypes = [_int]
+    lib.tq_status_str.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+# the symbols include/tq.h declares
+EXPORTS = ("tq3_quantize", "tq3_dequantize", "orbit_quantize_weight", "orbit_dequantize",
+           "tq3_record_bytes", "orbit_block_size", "tq_gaussian_lloyd_max",
+           "orbit_make_codebook", "tq_status_str")
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        exc = _STATUS.get(status, RuntimeError)
+        raise exc(f"{what}: {lib.tq_status_str(status).decode()} (status {status})")
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("libtq operates on GPU tensors only (no CPU fallback)")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+# ------------------------------------------------------------------- TQ3 ---
+
+def sign_mask(signs) -> bytes:
+    """16-byte mask of a 128-entry +-1 sign vector: bit j set where s_j < 0."""
+    s = torch.as_tensor(signs).reshape(-1).to("cpu", torch.float32)
+    if s.numel() != TQ3_DIM:
+        raise ValueError("TQ3 sign vector must have 128 entries")
+    bits = (s < 0).to(torch.uint8)
+    weights = torch.tensor([1 << i for i in range(8)], dtype=torch.int32)
+    packed = (bits.view(16, 8).to(torch.int32) * weights).sum(1).to(torch.uint8)
+    return bytes(packed.tolist())
+
+
+def tq3_record_bytes() -> int:
+    return int(lib.tq3_record_bytes())
+
+
+def tq3_quantize(x: torch.Tensor, signs, out: torch.Tensor = None) -> torch.Tensor:
+    """x [..., D] (D a positive multiple of 128; fp32, bf16 or fp16, on the GPU)
+    -> uint8 records [..., D/128, 56] (48 bytes of 3-bit indices, fp32 norm,
+    fp32 scale). `signs` is the 128-entry +-1 vector or its 16-byte mask."""
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("tq3_quantize expects a torch.Tensor input")
+    if x.ndim == 0:
+        raise ValueError("tq3_quantize expects at least one dimension")
+    if x.shape[-1] <= 0 or x.shape[-1] % TQ3_DIM:
+        raise ValueError(f"last dim must be a positive multiple of 128, got {x.shape[-1]}")
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    _need_gpu(x)
+    nb = x.shape[-1] // TQ3_DIM
+    xv = x.reshape(-1, TQ3_DIM) if x.is_contiguous() else x.contiguous().reshape(-1, TQ3_DIM)
+    n = xv.shape[0]
+    if out is None:
+        out = torch.empty((*x.shape[:-1], nb, TQ3_RECORD_BYTES), dtype=torch.uint8,
+                          device=x.device)
+    m = signs if isinstance(signs, (bytes, bytearray)) else sign_mask(signs)
+    _check(lib.tq3_quantize(_ptr(xv), _DTYPES[x.dtype], n, xv.stride(0), m, _ptr(out),
+                            _stream(x)), "tq3_quantize")
+    return out
+
+
+def tq3_dequantize(records: torch.Tensor, signs, dtype=torch.float32,
+                   out: torch.Tensor = None) -> torch.Tensor:
+    """uint8 records [..., nb, 56] -> [..., nb*128] of `dtype` (fp32 values,
+    narrowed by round-to-nearest-even for bf16/fp16)."""
+    if records.dtype != torch.uint8 or records.shape[-1] != TQ3_RECORD_BYTES:
+        raise ValueError("records must be uint8 [..., 56]")
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}")
+    _need_gpu(records)
+    rec = records.contiguous()
+    n = rec.numel() // TQ3_RECORD_BYTES
+    lead = tuple(records.shape[:-2])
+    nb = records.shape[-2] if records.ndim >= 2 else 1
+    if out is None:
+        out = torch.empty((*lead, nb * TQ3_DIM), dtype=dtype, device=records.device)
+    m = signs if isinstance(signs, (bytes, bytearray)) else sign_mask(signs)
+    _check(lib.tq3_dequantize(_ptr(rec), n, m, _ptr(out), _DTYPES[dtype], TQ3_DIM,
+                              _stream(records)), "tq3_dequantize")
+    return out
+
+
+def tq3_memory_bytes(shape):
+    """(compressed bytes, fp16 bytes, ratio) for a tensor shape [..., D]."""
+    if not shape:
+        raise ValueError("shape must be non-empty")
+    if shape[-1] <= 0 or shape[-1] % TQ3_DIM:
+        raise ValueError(f"last dim must be a positive multiple of 128, got {shape[-1]}")
+    if any(d <= 0 for d in shape):
+        raise ValueError(f"all dimensions must be positive, got {shape}")
+    numel = 1
+    for d in shape:
+        numel *= d
+    comp = numel // TQ3_DIM * tq3_record_bytes()
+    return comp, numel * 2, numel * 2 / comp
+
+
+# ------------------------------------------------------------ OrbitQuant ---
+
+def orbit_block_size(d: int) -> int:
+    return int(lib.orbit_block_size(d))
+
+
+def tq_gaussian_lloyd_max(bits: int, iters: int = 200) -> torch.Tensor:
+    out = (ctypes.c_double * (1 << bits))()
+    _check(lib.tq_gaussian_lloyd_max(bits, iters, ctypes.cast(out, _vp)), "tq_gaussian_lloyd_max")
+    return torch.tensor(list(out), dtype=torch.float64)
+
+
+def orbit_make_codebook(bits: int, d: int) -> torch.Tensor:
+    out = (ctypes.c_float * (1 << bits))()
+    _check(lib.orbit_make_codebook(bits, d, ctypes.cast(out, _vp)), "orbit_make_codebook")
+    return torch.tensor(list(out), dtype=torch.float32)
+
+
+def _host_f32(cb) -> ctypes.Array:
+    v = torch.as_tensor(cb).reshape(-1).to("cpu", torch.float32).tolist()
+    return (ctypes.c_float * len(v))(*v)
+
+
+def orbit_quantize_weight(W: torch.Tensor, bits: int, perm: torch.Tensor,
+                          signs: torch.Tensor, codebook, bit_order: int = TQ_MSB_FIRST,
+                          packed: torch.Tensor = None, row_norms: torch.Tensor = None):
+    """fp32 W [rows, d] on the GPU -> (packed uint8 [rows, d*bits/8], row_norms fp32).
+    perm: int32 [d], signs: int8 [d] (GPU); codebook: 2^bits fp32 (host values)."""
+    if W.dtype != torch.float32 or W.ndim != 2:
+        raise ValueError("W must be a 2-D fp32 tensor")
+    _need_gpu(W, perm, signs)
+    W = W.contiguous()
+    rows, d = W.shape
+    perm = perm.to(torch.int32).contiguous()
+    signs = signs.to(torch.int8).contiguous()
+    if packed is None:
+        packed = torch.empty((rows, d * bits // 8), dtype=torch.uint8, device=W.device)
+    if row_norms is None:
+        row_norms = torch.empty((rows,), dtype=torch.float32, device=W.device)
+    cb = _host_f32(codebook)
+    if len(cb) != (1 << bits):
+        raise ValueError("codebook must hold 2**bits values")
+    _check(lib.orbit_quantize_weight(_ptr(W), rows, d, bits, _ptr(perm), _ptr(signs),
+                                     ctypes.cast(cb, _vp), bit_order, _ptr(packed),
+                                     _ptr(row_norms), _stream(W)), "orbit_quantize_weight")
+    return packed, row_norms
+
+
+def orbit_dequantize(packed: torch.Tensor, row_norms: torch.Tensor, d: int, bits: int,
+                     inv_perm: torch.Tensor, signs: torch.Tensor, codebook,
+                     bit_order: int = TQ_MSB_FIRST, rotated_only: bool = False,
+                     dtype=torch.float32, out: torch.Tensor = None) -> torch.Tensor:
+    """-> [rows, d] of `dtype`: the rotated-basis W' (rotated_only) or W."""
+    _need_gpu(packed, row_norms)
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}")
+    packed = packed.contiguous()
+    row_norms = row_norms.to(torch.float32).contiguous()
+    rows = row_norms.numel()
+    if out is None:
+        out = torch.empty((rows, d), dtype=dtype, device=packed.device)
+    ip = inv_perm.to(torch.int32).contiguous() if inv_perm is not None else None
+    sg = signs.to(torch.int8).contiguous() if signs is not None else None
+    cb = _host_f32(codebook)
+    _check(lib.orbit_dequantize(_ptr(packed), _ptr(row_norms), rows, d, bits,
+                                _ptr(ip) if ip is not None else None,
+                                _ptr(sg) if sg is not None else None,
+                                ctypes.cast(cb, _vp), bit_order, int(bool(rotated_only)),
+                                _ptr(out), _DTYPES[dtype], _stream(packed)), "orbit_dequantize")
+    return out

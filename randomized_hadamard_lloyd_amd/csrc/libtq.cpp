@@ -1,0 +1,226 @@
+// C-ABI entry points of libtq: argument checks, launch geometry, and the
+// host-side Gaussian Lloyd-Max codebook. Declarations and contracts are in
+// include/tq.h.
+#include "tq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "tq_kernels.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+int g_cu_count[kMaxDevices];
+std::once_flag g_cu_once[kMaxDevices];
+
+// Compute units of the current device (queried once per device).
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  std::call_once(g_cu_once[dev], [dev] {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    g_cu_count[dev] = n;
+  });
+  return g_cu_count[dev];
+}
+
+// Grid of 256-thread blocks for `units` independent work items handled
+// `per_block` at a time by grid-stride loops: enough blocks to fill every CU
+// several times over, never more than there is work for.
+int grid_for(int64_t units, int64_t per_block, int blocks_per_cu) {
+  const int64_t need = (units + per_block - 1) / per_block;
+  const int64_t cap = (int64_t)cu_count() * blocks_per_cu;
+  return (int)(need < cap ? need : cap);
+}
+
+bool valid_dtype(int dt) { return dt == TQ_F32 || dt == TQ_BF16 || dt == TQ_F16; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int launched(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH; }
+
+constexpr int64_t kMaxVectors = (int64_t)1 << 40;
+
+// ---- Gaussian Lloyd-Max (fp64), the procedure of the OrbitQuant page ----
+
+double std_normal_cdf(double t) { return 0.5 * (1.0 + std::erf(t / std::sqrt(2.0))); }
+
+double std_normal_pdf(double t) {
+  if (std::isinf(t)) return 0.0;
+  return std::exp(-t * t / 2.0) / std::sqrt(2.0 * M_PI);
+}
+
+// Quantile of the standard normal: bisection on the CDF written through erfc
+// (accurate in both tails), run until the bracket stops shrinking.
+double std_normal_quantile(double p) {
+  double lo = -40.0, hi = 40.0;
+  for (int it = 0; it < 2000; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    if (mid <= lo || mid >= hi) break;
+    const double c = 0.5 * std::erfc(-mid / std::sqrt(2.0));
+    if (c < p)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tq3_record_bytes(void) { return TQ3_RECORD_BYTES; }
+
+int64_t orbit_block_size(int64_t d) { return d > 0 ? (d & -d) : 0; }
+
+const char* tq_status_str(int status) {
+  switch (status) {
+    case TQ_OK: return "ok";
+    case TQ_ERR_NULL: return "null pointer";
+    case TQ_ERR_SHAPE: return "invalid shape or stride";
+    case TQ_ERR_DTYPE: return "invalid dtype";
+    case TQ_ERR_BITS: return "bits must be 2, 3 or 4";
+    case TQ_ERR_BLOCK: return "Hadamard block d & -d outside [32, 4096] or d > 16384";
+    case TQ_ERR_ALIGN: return "misaligned pointer or stride";
+    case TQ_ERR_LAUNCH: return "kernel launch failed";
+    case TQ_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+int tq3_quantize(const void* x, int x_dtype, int64_t n_vec, int64_t x_row_stride,
+                 const uint8_t* sign_mask, uint8_t* records, void* stream) {
+  if (!valid_dtype(x_dtype)) return TQ_ERR_DTYPE;
+  if (n_vec < 0 || n_vec > kMaxVectors) return TQ_ERR_SHAPE;
+  if (x_row_stride < TQ3_DIM || x_row_stride % 8 != 0 || x_row_stride > ((int64_t)1 << 24))
+    return TQ_ERR_SHAPE;
+  if (n_vec == 0) return TQ_OK;
+  if (!x || !sign_mask || !records) return TQ_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(records, 8)) return TQ_ERR_ALIGN;
+  tq::SignMask m;
+  std::memcpy(m.w, sign_mask, sizeof(m.w));  // little-endian host
+  const int grid = grid_for(n_vec, 64, 8);
+  return launched(tq::launch_tq3_quantize(x, x_dtype, n_vec, x_row_stride, m, records, grid,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int tq3_dequantize(const uint8_t* records, int64_t n_vec, const uint8_t* sign_mask, void* y,
+                   int y_dtype, int64_t y_row_stride, void* stream) {
+  if (!valid_dtype(y_dtype)) return TQ_ERR_DTYPE;
+  if (n_vec < 0 || n_vec > kMaxVectors) return TQ_ERR_SHAPE;
+  if (y_row_stride < TQ3_DIM || y_row_stride % 8 != 0 || y_row_stride > ((int64_t)1 << 24))
+    return TQ_ERR_SHAPE;
+  if (n_vec == 0) return TQ_OK;
+  if (!records || !sign_mask || !y) return TQ_ERR_NULL;
+  if (!aligned(y, 16) || !aligned(records, 8)) return TQ_ERR_ALIGN;
+  tq::SignMask m;
+  std::memcpy(m.w, sign_mask, sizeof(m.w));
+  const int grid = grid_for(n_vec, 64, 8);
+  return launched(tq::launch_tq3_dequantize(records, n_vec, m, y, y_dtype, y_row_stride, grid,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+// Shared checks of the OrbitQuant entry points; fills the kernel's codebook.
+static int orbit_check(int64_t rows, int64_t d, int bits, const float* codebook, int bit_order,
+                       tq::OrbitCodebook* cb) {
+  if (bits < 2 || bits > 4) return TQ_ERR_BITS;
+  if (rows < 0 || rows > kMaxVectors || d <= 0) return TQ_ERR_SHAPE;
+  const int64_t h = d & -d;
+  if (h < 32 || h > 4096 || d > 16384) return TQ_ERR_BLOCK;
+  if (bit_order != TQ_MSB_FIRST && bit_order != TQ_LSB_FIRST) return TQ_ERR_ARG;
+  if (!codebook) return TQ_ERR_NULL;
+  const int levels = 1 << bits;
+  for (int k = 0; k < levels; ++k) {
+    if (!std::isfinite(codebook[k])) return TQ_ERR_ARG;
+    if (k > 0 && !(codebook[k] > codebook[k - 1])) return TQ_ERR_ARG;
+    cb->cb[k] = codebook[k];
+  }
+  for (int k = levels; k < 16; ++k) cb->cb[k] = codebook[levels - 1];
+  // fp32 midpoints of neighbours, as the page's _quantize_rows forms them
+  for (int k = 0; k < 15; ++k)
+    cb->edge[k] = (k + 1 < levels) ? (codebook[k] + codebook[k + 1]) / 2.0f : INFINITY;
+  return TQ_OK;
+}
+
+int orbit_quantize_weight(const float* W, int64_t rows, int64_t d, int bits,
+                          const int32_t* perm, const int8_t* signs, const float* codebook,
+                          int bit_order, uint8_t* packed, float* row_norms, void* stream) {
+  tq::OrbitCodebook cb;
+  const int st = orbit_check(rows, d, bits, codebook, bit_order, &cb);
+  if (st != TQ_OK) return st;
+  if (rows == 0) return TQ_OK;
+  if (!W || !perm || !signs || !packed || !row_norms) return TQ_ERR_NULL;
+  if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(perm, 4) || !aligned(row_norms, 4))
+    return TQ_ERR_ALIGN;
+  const int grid = grid_for(rows, 4, 8);
+  return launched(tq::launch_orbit_quantize(W, rows, d, bits, perm, signs, cb,
+                                            bit_order == TQ_LSB_FIRST, packed, row_norms, grid,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int orbit_dequantize(const uint8_t* packed, const float* row_norms, int64_t rows, int64_t d,
+                     int bits, const int32_t* inv_perm, const int8_t* signs,
+                     const float* codebook, int bit_order, int rotated_only, void* W_out,
+                     int out_dtype, void* stream) {
+  tq::OrbitCodebook cb;
+  const int st = orbit_check(rows, d, bits, codebook, bit_order, &cb);
+  if (st != TQ_OK) return st;
+  if (!valid_dtype(out_dtype)) return TQ_ERR_DTYPE;
+  if (rotated_only != 0 && rotated_only != 1) return TQ_ERR_ARG;
+  if (rows == 0) return TQ_OK;
+  if (!packed || !row_norms || !W_out) return TQ_ERR_NULL;
+  if (!rotated_only && (!inv_perm || !signs)) return TQ_ERR_NULL;
+  if (!aligned(packed, 16) || !aligned(W_out, 16) || !aligned(row_norms, 4) ||
+      (inv_perm && !aligned(inv_perm, 4)))
+    return TQ_ERR_ALIGN;
+  const int grid = grid_for(rows, 4, 8);
+  return launched(tq::launch_orbit_dequantize(packed, row_norms, rows, d, bits, inv_perm, signs,
+                                              cb, bit_order == TQ_LSB_FIRST, rotated_only,
+                                              W_out, out_dtype, grid,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int tq_gaussian_lloyd_max(int bits, int iters, double* out) {
+  if (bits < 1 || bits > 8) return TQ_ERR_BITS;
+  if (iters < 0) return TQ_ERR_ARG;
+  if (!out) return TQ_ERR_NULL;
+  const int levels = 1 << bits;
+  double c[256], lo[256], hi[256];
+  for (int k = 0; k < levels; ++k) c[k] = std_normal_quantile((k + 0.5) / levels);
+  for (int it = 0; it < iters; ++it) {
+    lo[0] = -INFINITY;
+    hi[levels - 1] = INFINITY;
+    for (int k = 0; k + 1 < levels; ++k) {
+      const double e = (c[k] + c[k + 1]) / 2.0;
+      hi[k] = e;
+      lo[k + 1] = e;
+    }
+    for (int k = 0; k < levels; ++k)
+      c[k] = (std_normal_pdf(lo[k]) - std_normal_pdf(hi[k])) /
+             (std_normal_cdf(hi[k]) - std_normal_cdf(lo[k]));
+  }
+  std::memcpy(out, c, sizeof(double) * levels);
+  return TQ_OK;
+}
+
+int orbit_make_codebook(int bits, int64_t d, float* out) {
+  if (bits < 2 || bits > 4) return TQ_ERR_BITS;
+  if (d <= 0) return TQ_ERR_SHAPE;
+  if (!out) return TQ_ERR_NULL;
+  double lm[16];
+  const int st = tq_gaussian_lloyd_max(bits, 200, lm);
+  if (st != TQ_OK) return st;
+  const float s = (float)std::pow((double)d, -0.5);
+  for (int k = 0; k < (1 << bits); ++k) out[k] = (float)lm[k] * s;
+  return TQ_OK;
+}
+
+}  // extern "C"

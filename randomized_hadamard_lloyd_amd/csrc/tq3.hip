@@ -1,0 +1,435 @@
+// TQ3 codec kernels for gfx950 -- "ComfyUI-TurboQuant: tq3_core.py",
+// tq3_quantize / tq3_dequantize.
+//
+// Work mapping. A 128-vector lives in one 4-lane quad: quad lane q holds the
+// 32 elements j = i + 8q + 32g (i = 0..7, g = 0..3) in registers x[g][i], so a
+// wave of 64 lanes carries 16 vectors and a 256-thread block 64 vectors.
+// Index bits 0-2 (i) and 5-6 (g) are register bits; bits 3-4 are quad-lane
+// bits. The FWHT stages with half-width 1, 2, 4 and 32, 64 are in-register
+// butterflies; the stages with half-width 8 and 16 exchange values between
+// quad lanes with ds_swizzle (LDS crossbar, no VALU slot) and combine them
+// with one fmac. Stages always run in the order 1, 2, 4, ..., 64, and the
+// sum of squares follows the same bit order, so every fp32 operation matches
+// the declared reference order exactly.
+//
+// Lazy lane sign. In a cross-lane stage the lower lane needs a + b and the
+// upper lane a - b. Both lanes evaluate fma(partner, c, own) with c = +-1;
+// the upper lane then holds -(a - b). The sign is tracked per lane (it only
+// depends on the quad lane) and folded into the final multiply by
+// 1/sqrt(128), which is exact because a sign change commutes with rounding.
+#include "tq_common.h"
+#include "tq_kernels.h"
+
+namespace tq {
+
+namespace {
+
+// fp32 of the page's printed centroid table (doubles rounded to float32).
+__device__ __forceinline__ float tq3_centroid(int k) {
+  constexpr float c[8] = {(float)-0.9816, (float)-0.6168, (float)-0.3479, (float)-0.1129,
+                          (float)0.1129,  (float)0.3479,  (float)0.6168,  (float)0.9816};
+  return c[k];
+}
+// Centroid 2q + e for quad lane q (e = 0, 1) without a memory table.
+__device__ __forceinline__ float centroid_of_lane(int q, int e) {
+  float lo = tq3_centroid(e), hi = tq3_centroid(2 + e);
+  float lo2 = tq3_centroid(4 + e), hi2 = tq3_centroid(6 + e);
+  const float a = (q & 1) ? hi : lo;
+  const float b = (q & 1) ? hi2 : lo2;
+  return (q & 2) ? b : a;
+}
+// Twice the bit patterns of the positive boundaries (see the index comment).
+constexpr uint32_t kB1x2 = 2u * __builtin_bit_cast(uint32_t, (float)0.2304);
+constexpr uint32_t kB2x2 = 2u * __builtin_bit_cast(uint32_t, (float)0.4824);
+constexpr uint32_t kB3x2 = 2u * __builtin_bit_cast(uint32_t, (float)0.7992);
+constexpr float kInvSqrt128 = (float)0.08838834764831845;  // fp32(1/sqrt(128))
+constexpr float kFloor = (float)1e-8;                      // clamp of norm and scale
+
+// Sign bit of element (q, g, i) from the 128-bit mask (bit j = element j).
+__device__ __forceinline__ uint32_t sign_bit(const SignMask& m, int q, int g, int i) {
+  return (m.w[g] >> (8 * q + i)) & 1u;
+}
+
+// ------------------------------------------------------------- loading ---
+
+template <int DT>
+struct Loader;
+
+template <>
+struct Loader<DT_F32> {
+  // 32 masks, one per element, each 0 or 0x80000000
+  uint32_t sm[4][8];
+  __device__ __forceinline__ void init(const SignMask& m, int q) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sm[g][i] = sign_bit(m, q, g, i) << 31;
+  }
+  // x: signed input (sign flips applied), used for both the norm and u
+  __device__ __forceinline__ void load(const void* base, int64_t row, int64_t stride, int q,
+                                       float (&x)[4][8]) const {
+    const float* r = static_cast<const float*>(base) + row * stride + 8 * q;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint4 a = *reinterpret_cast<const uint4*>(r + 32 * g);
+      const uint4 b = *reinterpret_cast<const uint4*>(r + 32 * g + 4);
+      const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[g][i] = as_f(w[i] ^ sm[g][i]);
+    }
+  }
+};
+
+// bf16 and f16: eight 16-bit values per 16-byte load; sign flips are applied
+// to the packed pairs (bit 15 low element, bit 31 high element).
+template <int DT>
+struct Loader16 {
+  uint32_t sm[4][4];
+  __device__ __forceinline__ void init(const SignMask& m, int q) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        sm[g][p] = (sign_bit(m, q, g, 2 * p) << 15) | (sign_bit(m, q, g, 2 * p + 1) << 31);
+  }
+  __device__ __forceinline__ void load(const void* base, int64_t row, int64_t stride, int q,
+                                       float (&x)[4][8]) const {
+    const uint16_t* r = static_cast<const uint16_t*>(base) + row * stride + 8 * q;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint4 a = *reinterpret_cast<const uint4*>(r + 32 * g);
+      const uint32_t w[4] = {a.x ^ sm[g][0], a.y ^ sm[g][1], a.z ^ sm[g][2], a.w ^ sm[g][3]};
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        if constexpr (DT == DT_BF16) {
+          x[g][2 * p] = as_f(w[p] << 16);
+          x[g][2 * p + 1] = as_f(w[p] & 0xffff0000u);
+        } else {
+          x[g][2 * p] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[p] & 0xffffu));
+          x[g][2 * p + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[p] >> 16));
+        }
+      }
+    }
+  }
+};
+template <>
+struct Loader<DT_BF16> : Loader16<DT_BF16> {};
+template <>
+struct Loader<DT_F16> : Loader16<DT_F16> {};
+
+// ---------------------------------------------------------------- FWHT ---
+
+// In-register stages over index bits 0..2 of each 8-element chunk.
+__device__ __forceinline__ void fwht_low3(float (&x)[4][8]) {
+#pragma unroll
+  for (int h = 1; h < 8; h *= 2)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if ((i & h) == 0) {
+          const float a = x[g][i], b = x[g][i + h];
+          x[g][i] = a + b;
+          x[g][i + h] = a - b;
+        }
+}
+
+// Stages over index bits 3, 4 (quad lanes) with the lazy lane sign, then bits
+// 5, 6 (chunk index g) in registers.
+__device__ __forceinline__ void fwht_high4(float (&x)[4][8], float c1, float c2) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[g][i] = __builtin_fmaf(swz<QP_XOR1>(x[g][i]), c1, x[g][i]);
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[g][i] = __builtin_fmaf(swz<QP_XOR2>(x[g][i]), c2, x[g][i]);
+#pragma unroll
+  for (int hg = 1; hg < 4; hg *= 2)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      if ((g & hg) == 0)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float a = x[g][i], b = x[g + hg][i];
+          x[g][i] = a + b;
+          x[g + hg][i] = a - b;
+        }
+}
+
+// Lane constants of the lazy-sign scheme (see the file comment).
+struct LaneSigns {
+  float c1, c2, sigma;
+};
+__device__ __forceinline__ LaneSigns lane_signs(int q) {
+  LaneSigns s;
+  s.c1 = (q & 1) ? -1.0f : 1.0f;
+  s.c2 = (q & 2) ? -1.0f : 1.0f;
+  s.sigma = (__builtin_popcount(q) & 1) ? -1.0f : 1.0f;
+  return s;
+}
+
+// ------------------------------------------------------------ quantize ---
+
+template <int DT>
+__global__ __launch_bounds__(256) void tq3_quantize_kernel(const void* __restrict__ x,
+                                                           int64_t n_vec, int64_t stride,
+                                                           SignMask mask,
+                                                           uint8_t* __restrict__ rec) {
+  const int q = threadIdx.x & 3;
+  Loader<DT> ld;
+  ld.init(mask, q);
+  const LaneSigns ls = lane_signs(q);
+  const float kq = ls.sigma * kInvSqrt128;
+
+  const int64_t step = (int64_t)gridDim.x * 64;
+  for (int64_t v = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2); v < n_vec; v += step) {
+    float x_[4][8];
+    ld.load(x, v, stride, q, x_);
+
+    // Sum of squares: bits 0..2 in registers, 3..4 across the quad, 5..6 in
+    // registers -- the reference tree's bit order.
+    float part[4];
+    float amin = __builtin_inff();
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float s[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        s[i] = x_[g][i] * x_[g][i];
+        amin = __builtin_fminf(amin, __builtin_fabsf(x_[g][i]));
+      }
+      const float a0 = s[0] + s[1], a1 = s[2] + s[3], a2 = s[4] + s[5], a3 = s[6] + s[7];
+      const float b0 = a0 + a1, b1 = a2 + a3;
+      part[g] = b0 + b1;
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) part[g] = part[g] + swz<QP_XOR1>(part[g]);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) part[g] = part[g] + swz<QP_XOR2>(part[g]);
+    const float ss = (part[0] + part[1]) + (part[2] + part[3]);
+    amin = __builtin_fminf(amin, swz<QP_XOR1>(amin));
+    amin = __builtin_fminf(amin, swz<QP_XOR2>(amin));
+
+    const float norm = __builtin_fmaxf(__builtin_sqrtf(ss), kFloor);
+
+    // u = x / norm, correctly rounded. The shared-reciprocal path is exact
+    // while every nonzero |x_j| >= norm * 2^-60 and norm <= 2^100; otherwise
+    // the vector takes plain IEEE division.
+    float u[4][8];
+    if (amin >= norm * 0x1p-60f && norm <= 0x1p100f) {
+      const Recip rn = make_recip(norm);
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) u[g][i] = div_rn(x_[g][i], rn);
+    } else {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) u[g][i] = x_[g][i] / norm;
+    }
+
+    fwht_low3(u);
+    fwht_high4(u, ls.c1, ls.c2);
+
+    // y = w * fp32(1/sqrt(128)); kq also undoes the lazy lane sign.
+    float amax = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        u[g][i] = u[g][i] * kq;
+        amax = __builtin_fmaxf(amax, __builtin_fabsf(u[g][i]));
+      }
+    amax = __builtin_fmaxf(amax, swz<QP_XOR1>(amax));
+    amax = __builtin_fmaxf(amax, swz<QP_XOR2>(amax));
+    const float scale = __builtin_fmaxf(amax, kFloor);
+    // |y_j| <= scale, so y_j / scale stays in [-1, 1]; its sign and its
+    // comparisons with the boundaries are all the index needs, and the
+    // shared-reciprocal quotient is exact wherever it can reach a boundary.
+    const Recip rs = make_recip(scale);
+
+    // Index = number of boundaries strictly below t = y / scale. The table is
+    // symmetric, so with a = |t| and P = {0.2304, 0.4824, 0.7992}:
+    //   t > 0:  idx = 4 + #{b in P : b < a}
+    //   t <= 0: idx = 3 - #{b in P : b <= a}
+    // Rotating t's bits left by one puts the sign in bit 0: R = 2*bits(a) + sign.
+    // Then R > 2*bits(b) means bits(a) > bits(b) for t >= 0 and bits(a) >= bits(b)
+    // for t < 0 -- exactly the strict/non-strict split of the tie rule -- and
+    // with c = #{R > 2*bits(b)}, idx = c ^ (t > 0 ? 4 : 3).
+    uint32_t chunk[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float t = div_rn(u[g][i], rs);
+        const uint32_t tb = as_u(t);
+        const uint32_t r = __builtin_amdgcn_alignbit(tb, tb, 31);
+        const bool m1 = r > kB1x2, m2 = r > kB2x2, m3 = r > kB3x2;
+        const bool pos = t > 0.0f;
+        const bool b1 = !(m2 ^ pos);
+        const bool b0 = !((m1 ^ m2 ^ m3) ^ pos);
+        c |= ((b0 ? 1u : 0u) | (b1 ? 2u : 0u) | (pos ? 4u : 0u)) << (3 * i);
+      }
+      chunk[g] = c;
+    }
+
+    // Record: 48 bytes of indices = 4 groups of 3 dwords; in group g quad lane
+    // k < 3 writes dword k, which takes its own 24-bit chunk and the next
+    // lane's: (c_k >> 8k) | (c_{k+1} << (24 - 8k)). Lane 3 writes norm, scale.
+    uint8_t* out = rec + v * 56;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t nb = swz<QP_NEXT>(chunk[g]);
+      const uint32_t dw = (chunk[g] >> (8 * q)) | (nb << (24 - 8 * q));
+      if (q < 3) *reinterpret_cast<uint32_t*>(out + 12 * g + 4 * q) = dw;
+    }
+    if (q == 3) *reinterpret_cast<uint2*>(out + 48) = make_uint2(as_u(norm), as_u(scale));
+  }
+}
+
+// ---------------------------------------------------------- dequantize ---
+
+template <int DT>
+__device__ __forceinline__ void store_row(void* base, int64_t row, int64_t stride, int q,
+                                          const float (&y)[4][8]) {
+  if constexpr (DT == DT_F32) {
+    float* r = static_cast<float*>(base) + row * stride + 8 * q;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      *reinterpret_cast<float4*>(r + 32 * g) = make_float4(y[g][0], y[g][1], y[g][2], y[g][3]);
+      *reinterpret_cast<float4*>(r + 32 * g + 4) =
+          make_float4(y[g][4], y[g][5], y[g][6], y[g][7]);
+    }
+  } else {
+    uint16_t* r = static_cast<uint16_t*>(base) + row * stride + 8 * q;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint32_t w[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        if constexpr (DT == DT_BF16) {
+          typedef float f2 __attribute__((ext_vector_type(2)));
+          typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+          const f2 v = {y[g][2 * p], y[g][2 * p + 1]};
+          w[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
+        } else {
+          typedef float f2 __attribute__((ext_vector_type(2)));
+          typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+          const f2 v = {y[g][2 * p], y[g][2 * p + 1]};
+          w[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));
+        }
+      }
+      *reinterpret_cast<uint4*>(r + 32 * g) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void tq3_dequantize_kernel(const uint8_t* __restrict__ rec,
+                                                             int64_t n_vec, SignMask mask,
+                                                             void* __restrict__ y,
+                                                             int64_t stride) {
+  // Per-quad table of the 8 centroids times the record's scale.
+  __shared__ float tbl[64][8];
+  const int q = threadIdx.x & 3;
+  const int quad = threadIdx.x >> 2;
+  const LaneSigns ls = lane_signs(q);
+  // Final per-element factor: lazy lane sign * fp32(1/sqrt(128)) * s_j.
+  float kf[4][8];
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      kf[g][i] = (sign_bit(mask, q, g, i) ? -ls.sigma : ls.sigma) * kInvSqrt128;
+  // The 24-bit chunk of (q, g) starts at byte 3q + 12g: dword 3g + (3q >> 2),
+  // bit offset 24q mod 32.
+  const float c_even = centroid_of_lane(q, 0), c_odd = centroid_of_lane(q, 1);
+  const uint32_t qbase = 32u * quad;
+  const int dsel = (3 * q) >> 2;
+  const uint32_t shift = (24u * q) & 31u;
+
+  const int64_t step = (int64_t)gridDim.x * 64;
+  for (int64_t v = (int64_t)blockIdx.x * 64 + quad; v < n_vec; v += step) {
+    const uint32_t* r32 = reinterpret_cast<const uint32_t*>(rec + v * 56);
+    uint32_t chunk[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t lo = r32[3 * g + dsel];
+      const uint32_t hi = r32[3 * g + dsel + 1];
+      chunk[g] = (uint32_t)((((uint64_t)hi << 32) | lo) >> shift) & 0xffffffu;
+    }
+    const uint2 ns = *reinterpret_cast<const uint2*>(rec + v * 56 + 48);
+    const float norm = as_f(ns.x), scale = as_f(ns.y);
+
+    tbl[quad][2 * q] = c_even * scale;
+    tbl[quad][2 * q + 1] = c_odd * scale;
+    __builtin_amdgcn_wave_barrier();
+
+    // Byte offset of entry idx in this quad's table: 4*idx | 32*quad (the
+    // table row is 32-byte aligned, so OR places the index bits).
+    float w[4][8];
+    const char* tb = reinterpret_cast<const char*>(&tbl[0][0]);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t c4 = chunk[g] << 2;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t off = ((c4 >> (3 * i)) & 28u) | qbase;
+        w[g][i] = *reinterpret_cast<const float*>(tb + off);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    fwht_low3(w);
+    fwht_high4(w, ls.c1, ls.c2);
+
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[g][i] = (w[g][i] * kf[g][i]) * norm;
+
+    store_row<DT>(y, v, stride, q, w);
+  }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------- launchers ---
+
+hipError_t launch_tq3_quantize(const void* x, int dt, int64_t n_vec, int64_t stride,
+                               const SignMask& m, uint8_t* rec, int grid, hipStream_t s) {
+  switch (dt) {
+    case DT_F32:
+      tq3_quantize_kernel<DT_F32><<<grid, 256, 0, s>>>(x, n_vec, stride, m, rec);
+      break;
+    case DT_BF16:
+      tq3_quantize_kernel<DT_BF16><<<grid, 256, 0, s>>>(x, n_vec, stride, m, rec);
+      break;
+    default:
+      tq3_quantize_kernel<DT_F16><<<grid, 256, 0, s>>>(x, n_vec, stride, m, rec);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_tq3_dequantize(const uint8_t* rec, int64_t n_vec, const SignMask& m,
+                                 void* y, int dt, int64_t stride, int grid, hipStream_t s) {
+  switch (dt) {
+    case DT_F32:
+      tq3_dequantize_kernel<DT_F32><<<grid, 256, 0, s>>>(rec, n_vec, m, y, stride);
+      break;
+    case DT_BF16:
+      tq3_dequantize_kernel<DT_BF16><<<grid, 256, 0, s>>>(rec, n_vec, m, y, stride);
+      break;
+    default:
+      tq3_dequantize_kernel<DT_F16><<<grid, 256, 0, s>>>(rec, n_vec, m, y, stride);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tq

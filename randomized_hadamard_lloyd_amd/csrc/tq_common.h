@@ -1,0 +1,59 @@
+// Shared device helpers for the libtq kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+// ds_swizzle in quad-permute mode: lane i of every 4-lane quad receives the
+// value of quad lane (PERM >> 2i) & 3. It runs on the LDS crossbar and costs
+// no VALU issue slot.
+constexpr int qperm(int a, int b, int c, int d) {
+  return 0x8000 | a | (b << 2) | (c << 4) | (d << 6);
+}
+constexpr int QP_XOR1 = qperm(1, 0, 3, 2);
+constexpr int QP_XOR2 = qperm(2, 3, 0, 1);
+constexpr int QP_NEXT = qperm(1, 2, 3, 3);
+
+template <int P>
+__device__ __forceinline__ float swz(float v) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), P));
+}
+template <int P>
+__device__ __forceinline__ uint32_t swz(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), P));
+}
+
+__device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t as_u(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// Quotient a / d rounded to nearest, for a divisor shared by many numerators.
+// rh = RN(1/d), rl = RN(1 - d*rh) * rh carries the reciprocal's rounding error,
+// so q0 = RN(a*rh + RN(a*rl)) is within one ulp of a/d (faithful). The
+// remainder a - d*q0 is then exact and one correction step gives the correctly
+// rounded quotient (P. Markstein, "Computation of elementary functions on the
+// IBM RISC System/6000 processor", IBM J. Res. Dev. 1990; J.-M. Muller et al.,
+// Handbook of Floating-Point Arithmetic, the section on division with an FMA).
+// Valid while no step leaves the normal range: the callers only use it where
+// |a/d| >= 2^-60 (or a = 0) and 1e-8 <= d <= 2^100.
+struct Recip {
+  float d, rh, rl;
+};
+__device__ __forceinline__ Recip make_recip(float d) {
+  Recip r;
+  r.d = d;
+  r.rh = 1.0f / d;  // correctly rounded (hipcc default)
+  const float e = __builtin_fmaf(-d, r.rh, 1.0f);
+  r.rl = e * r.rh;
+  return r;
+}
+__device__ __forceinline__ float div_rn(float a, const Recip& r) {
+  const float t = a * r.rl;
+  const float q0 = __builtin_fmaf(a, r.rh, t);
+  const float rem = __builtin_fmaf(-q0, r.d, a);
+  return __builtin_fmaf(rem, r.rh, q0);
+}
+
+}  // namespace tq

@@ -1,0 +1,38 @@
+// Launch interface between the C-ABI layer (libtq.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+
+// 128-bit TQ3 sign mask passed by value: bit j of the vector (bit j%32 of
+// w[j/32]) set means element j is negated.
+struct SignMask {
+  uint32_t w[4];
+};
+
+hipError_t launch_tq3_quantize(const void* x, int dt, int64_t n_vec, int64_t stride,
+                               const SignMask& m, uint8_t* rec, int grid, hipStream_t s);
+hipError_t launch_tq3_dequantize(const uint8_t* rec, int64_t n_vec, const SignMask& m,
+                                 void* y, int dt, int64_t stride, int grid, hipStream_t s);
+
+// OrbitQuant weight codec.
+struct OrbitCodebook {
+  float cb[16];     // 2^bits ascending centroids
+  float edge[15];   // fp32 midpoints of neighbours
+};
+
+hipError_t launch_orbit_quantize(const float* W, int64_t rows, int64_t d, int bits,
+                                 const int32_t* perm, const int8_t* signs,
+                                 const OrbitCodebook& cb, int lsb_first, uint8_t* packed,
+                                 float* norms, int grid, hipStream_t s);
+hipError_t launch_orbit_dequantize(const uint8_t* packed, const float* norms, int64_t rows,
+                                   int64_t d, int bits, const int32_t* inv_perm,
+                                   const int8_t* signs, const OrbitCodebook& cb,
+                                   int lsb_first, int rotated_only, void* out, int dt,
+                                   int grid, hipStream_t s);
+
+}  // namespace tq

@@ -1,0 +1,83 @@
+"""The C-ABI library loads and exports every symbol include/tq.h declares, and its
+host-side helpers agree with the oracle (no GPU needed)."""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "randomized_hadamard_lloyd_amd", "libtq.so")
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "tq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def tq():
+    if not os.path.exists(LIB):
+        pytest.skip("libtq.so not built")
+    import randomized_hadamard_lloyd_amd as m
+    return m
+
+
+def test_exports_every_declared_symbol(tq):
+    names = declared_symbols()
+    assert {"tq3_quantize", "tq3_dequantize", "orbit_quantize_weight", "orbit_dequantize"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert set(tq.EXPORTS) == set(names)
+
+
+def test_host_helpers(tq):
+    assert tq.tq3_record_bytes() == 56
+    assert tq.orbit_block_size(3072) == 1024
+    assert tq.orbit_block_size(4096) == 4096
+    assert tq.orbit_block_size(0) == 0
+    comp, orig, ratio = tq.tq3_memory_bytes((2, 64, 64, 2048, 128))
+    assert (comp, orig) == (939_524_096, 4_294_967_296) and ratio > 4.0
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_codebook_matches_oracle(tq, bits):
+    import oracle
+    assert np.array_equal(tq.orbit_make_codebook(bits, 3072).numpy(),
+                          oracle.orbit_codebook(bits, 3072))
+    assert np.array_equal(tq.orbit_make_codebook(bits, 96).numpy(), oracle.orbit_codebook(bits, 96))
+    lm = tq.tq_gaussian_lloyd_max(bits).numpy()
+    assert np.array_equal(lm.astype(np.float32), oracle.gaussian_lloyd_max(bits))
+
+
+def test_sign_mask_matches_golden(tq):
+    import json
+    import datagen
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "tq3_signs.json")))
+    m = tq.sign_mask(datagen.tq3_signs())
+    assert hex(int.from_bytes(m, "little")) == g["mask_hex"]
+
+
+def test_argument_errors_without_gpu(tq):
+    L = tq.lib
+    # argument checks run before any device call
+    assert L.tq3_quantize(None, 9, 4, 128, None, None, None) == 3
+    assert L.tq3_quantize(None, 0, 4, 100, None, None, None) == 2
+    assert L.tq3_quantize(None, 0, 0, 128, None, None, None) == 0
+    cb = tq._host_f32([-1.0, -0.5, 0.5, 1.0])
+    import ctypes
+    p = ctypes.cast(cb, ctypes.c_void_p)
+    assert L.orbit_quantize_weight(None, 4, 3072, 5, None, None, p, 0, None, None, None) == 4
+    assert L.orbit_quantize_weight(None, 4, 48, 2, None, None, p, 0, None, None, None) == 5
+    assert L.orbit_quantize_weight(None, 4, 3072, 2, None, None, p, 3, None, None, None) == 8
+    assert L.orbit_quantize_weight(None, 0, 3072, 2, None, None, p, 0, None, None, None) == 0
+    assert L.orbit_quantize_weight(None, 4, 3072, 2, None, None, p, 0, None, None, None) == 1
+    bad = tq._host_f32([1.0, -0.5, 0.5, 1.0])
+    assert L.orbit_quantize_weight(None, 4, 3072, 2, None, None,
+                                   ctypes.cast(bad, ctypes.c_void_p), 0, None, None, None) == 8
+    assert L.orbit_dequantize(None, None, 4, 3072, 2, None, None, p, 0, 0, None, 7, None) == 3
+    assert tq.lib.tq_status_str(5).decode().startswith("Hadamard")

@@ -1,0 +1,232 @@
+"""GPU parity of the TQ3 codec (libtq through its Python binding) against the oracle.
+
+Workloads follow "ComfyUI-TurboQuant: tq3_core.py" (tq3_quantize /
+tq3_dequantize) and the synthetic inputs of datagen: Gaussian vectors, a
+KV-cache layer with outlier channels, structured blocks, decode records.
+Small cases span several 64-vector blocks and ragged tails; the full-size
+cases run at the sizes the benchmark times.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from parity_util import compare_reconstruction, compare_tq3_records, split_records
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def tq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import randomized_hadamard_lloyd_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def signs():
+    return datagen.tq3_signs()
+
+
+def run_quantize(tq, x_cpu, signs):
+    x = x_cpu.to(DEV)
+    rec = tq.tq3_quantize(x, signs)
+    torch.cuda.synchronize()
+    return rec.cpu().numpy().reshape(-1, 56)
+
+
+def check_quantize(tq, x_cpu, signs):
+    g = run_quantize(tq, x_cpu, signs)
+    x32 = x_cpu.to(torch.float32).reshape(-1, 128).numpy()
+    o = oracle.tq3_quantize(x32, signs)
+    st = compare_tq3_records(g, o, oracle.tq3_scaled_coeffs(x32, signs))
+    assert st["exact"], st
+    return g, o
+
+
+def check_dequantize(tq, rec_np, signs, dtype):
+    rec = torch.from_numpy(np.ascontiguousarray(rec_np)).to(DEV)
+    y = tq.tq3_dequantize(rec, signs, dtype=dtype)
+    torch.cuda.synchronize()
+    o = oracle.tq3_dequantize(rec_np, signs)
+    _, norms, _ = split_records(rec_np)
+    st = compare_reconstruction(y.reshape(-1, 128), o, norms, dtype)
+    assert st["exact"], st
+
+
+# ------------------------------------------------------------- small ---
+
+@pytest.mark.parametrize("n", [1, 3, 4, 15, 16, 17, 63, 64, 65, 1000, 4097])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+def test_quantize_sizes_dtypes(tq, signs, n, dtype):
+    x = datagen.gaussian_vectors(n, seed=100 + n).to(dtype)
+    check_quantize(tq, x, signs)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+def test_round_trip_gaussian(tq, signs, dtype):
+    x = datagen.gaussian_vectors(4096)       # workload 1
+    g, _ = check_quantize(tq, x, signs)
+    check_dequantize(tq, g, signs, dtype)
+
+
+def test_gaussian_quality(tq, signs):
+    x = datagen.gaussian_vectors(4096).to(DEV)
+    y = tq.tq3_dequantize(tq.tq3_quantize(x, signs), signs)
+    cos = torch.nn.functional.cosine_similarity(x, y.reshape(x.shape), dim=-1)
+    assert cos.mean().item() > 0.97
+
+
+def test_structured_blocks(tq, signs):
+    x = datagen.structured_blocks(1 << 14)
+    g, _ = check_quantize(tq, x, signs)
+    check_dequantize(tq, g, signs, torch.float32)
+
+
+def test_kv_cache_small(tq, signs):
+    for which in ("K", "V"):
+        x = datagen.kv_cache(which, tokens=2048)
+        g, _ = check_quantize(tq, x, signs)
+        check_dequantize(tq, g, signs, torch.bfloat16)
+
+
+def test_multi_block_rows_and_shape(tq, signs):
+    # [..., D] with D = 4*128: block b of row r is vector 4r + b
+    x = datagen.gaussian_vectors(4 * 32 * 4, seed=9).reshape(4, 32, 512)
+    rec = tq.tq3_quantize(x.to(DEV), signs)
+    assert tuple(rec.shape) == (4, 32, 4, 56)
+    o = oracle.tq3_quantize(x.reshape(-1, 128).numpy(), signs)
+    assert np.array_equal(rec.cpu().numpy().reshape(-1, 56), o)
+    y = tq.tq3_dequantize(rec, signs)
+    assert tuple(y.shape) == (4, 32, 512)
+    assert np.array_equal(y.cpu().numpy().reshape(-1, 128), oracle.tq3_dequantize(o, signs))
+
+
+def test_strided_rows(tq, signs):
+    # rows of 128 taken from a wider buffer (stride 384 elements)
+    base = datagen.gaussian_vectors(3 * 500, seed=5).reshape(500, 384).to(DEV)
+    view = base[:, 128:256]
+    rec = torch.empty((500, 56), dtype=torch.uint8, device=DEV)
+    st = tq.lib.tq3_quantize(tq._ptr(view), tq.TQ_F32, 500, 384, tq.sign_mask(signs),
+                             tq._ptr(rec), tq._stream(view))
+    assert st == 0
+    o = oracle.tq3_quantize(view.cpu().numpy(), signs)
+    assert np.array_equal(rec.cpu().numpy(), o)
+    out = torch.zeros((500, 384), dtype=torch.float32, device=DEV)
+    ov = out[:, 256:]
+    st = tq.lib.tq3_dequantize(tq._ptr(rec), 500, tq.sign_mask(signs), tq._ptr(ov), tq.TQ_F32,
+                               384, tq._stream(rec))
+    assert st == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(ov.cpu().numpy(), oracle.tq3_dequantize(o, signs))
+    assert torch.count_nonzero(out[:, :256]).item() == 0
+
+
+# -------------------------------------------------------------- edges ---
+
+def test_edge_vectors(tq, signs):
+    rng = np.random.default_rng(3)
+    rows = [np.zeros(128), np.full(128, 2.5), np.full(128, -1e-3), np.eye(128)[5] * 7.0]
+    z = rng.standard_normal(128)
+    z[::3] = 0.0                                  # exact zeros (careful division path)
+    rows.append(z)
+    t = rng.standard_normal(128)
+    t[7] = 1e-30                                  # tiny relative to the norm
+    rows.append(t)
+    rows.append(rng.standard_normal(128) * 1e30)  # huge norm
+    rows.append(rng.standard_normal(128) * 1e-30) # tiny norm, below the clamp
+    w = rng.standard_normal(128) * np.exp2(rng.integers(-60, 60, 128))  # wide range
+    rows.append(w)
+    d = np.zeros(128)
+    d[0] = 1.0
+    rows.append(d)
+    bnd = np.zeros(128)
+    bnd[:4] = [1.0, 0.2304, -0.2304, 0.4824]       # exact-tie style values
+    rows.append(bnd)
+    x = torch.tensor(np.stack(rows), dtype=torch.float32)
+    x = torch.cat([x, datagen.gaussian_vectors(64 - x.shape[0] % 64 + 5, seed=4)])
+    g, _ = check_quantize(tq, x, signs)
+    check_dequantize(tq, g, signs, torch.float32)
+    check_dequantize(tq, g, signs, torch.bfloat16)
+
+
+def test_empty_and_errors(tq, signs):
+    x = torch.zeros((0, 128), device=DEV)
+    assert tq.tq3_quantize(x, signs).shape == (0, 1, 56)
+    m = tq.sign_mask(signs)
+    xb = torch.zeros((8, 128), device=DEV)
+    rec = torch.empty((8, 56), dtype=torch.uint8, device=DEV)
+    L = tq.lib
+    assert L.tq3_quantize(tq._ptr(xb), 7, 8, 128, m, tq._ptr(rec), None) == 3
+    assert L.tq3_quantize(tq._ptr(xb), 0, 8, 120, m, tq._ptr(rec), None) == 2
+    assert L.tq3_quantize(tq._ptr(xb), 0, -1, 128, m, tq._ptr(rec), None) == 2
+    assert L.tq3_quantize(None, 0, 8, 128, m, tq._ptr(rec), None) == 1
+    assert L.tq3_quantize(tq._ptr(xb), 0, 0, 128, None, None, None) == 0
+    assert L.tq3_quantize(xb.data_ptr() + 4, 0, 7, 128, m, tq._ptr(rec), None) == 6
+    assert L.tq3_dequantize(rec.data_ptr() + 4, 7, m, tq._ptr(xb), 0, 128, None) == 6
+    with pytest.raises(ValueError):
+        tq.tq3_quantize(torch.zeros((4, 100), device=DEV), signs)
+    with pytest.raises(ValueError):
+        tq.tq3_quantize(torch.zeros((4, 128)), signs)    # CPU tensor: no fallback
+    with pytest.raises(TypeError):
+        tq.tq3_quantize(torch.zeros((4, 128), dtype=torch.float64, device=DEV), signs)
+
+
+def test_deterministic_across_grids(tq, signs):
+    x = datagen.gaussian_vectors(5000, seed=8).to(DEV)
+    a = tq.tq3_quantize(x, signs)
+    b = tq.tq3_quantize(x, signs)
+    assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------- full size ---
+
+def test_full_kv_layer(tq, signs):
+    """K and V of one layer: 2 x 524288 bf16 vectors, every record checked."""
+    for which in ("K", "V"):
+        x = datagen.kv_cache(which)
+        g = run_quantize(tq, x, signs)
+        x32 = x.to(torch.float32).reshape(-1, 128).numpy()
+        o = oracle.tq3_quantize(x32, signs)
+        if not np.array_equal(g, o):
+            st = compare_tq3_records(g, o, oracle.tq3_scaled_coeffs(x32, signs))
+            pytest.fail(f"{which}: not bit-identical: {st}")
+        # dequantize a sample of records to bf16
+        idx = np.random.default_rng(1).choice(g.shape[0], 8192, replace=False)
+        check_dequantize(tq, g[idx], signs, torch.bfloat16)
+
+
+def test_full_structured(tq, signs):
+    """2^20 structured vectors (four quarters), every record checked."""
+    x = datagen.structured_blocks()
+    g = run_quantize(tq, x, signs)
+    o = oracle.tq3_quantize(x.numpy(), signs)
+    if not np.array_equal(g, o):
+        st = compare_tq3_records(g, o, oracle.tq3_scaled_coeffs(x.numpy(), signs))
+        pytest.fail(f"not bit-identical: {st}")
+    # constant quarter: the sign-before-transform ordering keeps cosine high
+    q = x.shape[0] // 4
+    y = oracle.tq3_dequantize(o[:4096], signs)
+    cos = (y * x[:4096].numpy()).sum(1) / (np.linalg.norm(y, axis=1) *
+                                          np.linalg.norm(x[:4096].numpy(), axis=1))
+    assert cos.mean() > 0.97 and q == 262144
+
+
+def test_full_decode_records(tq, signs):
+    """2^24 random records -> bf16, checked on a sample of rows."""
+    rec = datagen.decode_records()
+    y = tq.tq3_dequantize(rec.to(DEV), signs, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(np.random.default_rng(2).choice(rec.shape[0], 65536, replace=False))
+    sample = rec[idx].numpy()
+    o = oracle.tq3_dequantize(sample, signs)
+    _, norms, _ = split_records(sample)
+    st = compare_reconstruction(y[idx.to(DEV)].reshape(-1, 128), o, norms, torch.bfloat16)
+    assert st["exact"], st
+    assert math.isfinite(st["max_abs_over_norm"])
