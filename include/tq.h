@@ -42,7 +42,7 @@ enum {
     TQ_ERR_SHAPE = 2,   /* negative count, bad stride, d not a multiple of h */
     TQ_ERR_DTYPE = 3,   /* unknown dtype code                               */
     TQ_ERR_BITS = 4,    /* bits not in {2, 3, 4}                            */
-    TQ_ERR_BLOCK = 5,   /* Hadamard block h = d & -d outside [32, 4096]     */
+    TQ_ERR_BLOCK = 5,   /* h = d & -d outside [32, 4096], or d > 4096       */
     TQ_ERR_ALIGN = 6,   /* pointer or stride breaks the stated alignment    */
     TQ_ERR_LAUNCH = 7,  /* the HIP runtime refused the launch               */
     TQ_ERR_ARG = 8      /* other invalid argument (flag value, codebook)    */
@@ -126,10 +126,11 @@ int tq3_dequantize(const uint8_t* records, int64_t n_vec, const uint8_t* sign_ma
  *
  *   W            device, rows x d fp32, row-major, 16-byte aligned.
  *   d            input features; h = d & -d must lie in [32, 4096] (the page
- *                skips layers with h < 32) and d <= 16384.
+ *                skips layers with h < 32) and d <= 4096 (one row is held
+ *                on chip by one wave).
  *   bits         2, 3 or 4.
- *   perm         device, d int32, a permutation of 0..d-1.
- *   signs        device, d int8, each +1 or -1.
+ *   perm         device, d int32, a permutation of 0..d-1; 16-byte aligned.
+ *   signs        device, d int8, each +1 or -1; 16-byte aligned.
  *   codebook     host, 2^bits fp32 values in ascending order (the page's
  *                Gaussian Lloyd-Max codebook times d ** -0.5; see
  *                orbit_make_codebook).
@@ -152,9 +153,10 @@ int orbit_quantize_weight(const float* W, int64_t rows, int64_t d, int bits,
  *                     (the original-basis weight).
  *
  *   packed, row_norms   device, as written by orbit_quantize_weight.
- *   inv_perm            device, d int32, the inverse of perm (used when
- *                       rotated_only = 0; may be NULL otherwise).
- *   signs               device, d int8 (may be NULL when rotated_only = 1).
+ *   inv_perm            device, d int32, the inverse of perm, 16-byte aligned
+ *                       (used when rotated_only = 0; may be NULL otherwise).
+ *   signs               device, d int8, 16-byte aligned (may be NULL when
+ *                       rotated_only = 1).
  *   codebook            host, 2^bits fp32.
  *   W_out               device, rows x d of out_dtype (TQ_F32, TQ_BF16 or
  *                       TQ_F16), 16-byte aligned.

@@ -88,7 +88,7 @@ const char* tq_status_str(int status) {
     case TQ_ERR_SHAPE: return "invalid shape or stride";
     case TQ_ERR_DTYPE: return "invalid dtype";
     case TQ_ERR_BITS: return "bits must be 2, 3 or 4";
-    case TQ_ERR_BLOCK: return "Hadamard block d & -d outside [32, 4096] or d > 16384";
+    case TQ_ERR_BLOCK: return "Hadamard block d & -d outside [32, 4096] or d > 4096";
     case TQ_ERR_ALIGN: return "misaligned pointer or stride";
     case TQ_ERR_LAUNCH: return "kernel launch failed";
     case TQ_ERR_ARG: return "invalid argument";
@@ -134,7 +134,7 @@ static int orbit_check(int64_t rows, int64_t d, int bits, const float* codebook,
   if (bits < 2 || bits > 4) return TQ_ERR_BITS;
   if (rows < 0 || rows > kMaxVectors || d <= 0) return TQ_ERR_SHAPE;
   const int64_t h = d & -d;
-  if (h < 32 || h > 4096 || d > 16384) return TQ_ERR_BLOCK;
+  if (h < 32 || h > 4096 || d > 4096) return TQ_ERR_BLOCK;
   if (bit_order != TQ_MSB_FIRST && bit_order != TQ_LSB_FIRST) return TQ_ERR_ARG;
   if (!codebook) return TQ_ERR_NULL;
   const int levels = 1 << bits;
@@ -158,12 +158,14 @@ int orbit_quantize_weight(const float* W, int64_t rows, int64_t d, int bits,
   if (st != TQ_OK) return st;
   if (rows == 0) return TQ_OK;
   if (!W || !perm || !signs || !packed || !row_norms) return TQ_ERR_NULL;
-  if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(perm, 4) || !aligned(row_norms, 4))
+  if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(perm, 16) || !aligned(signs, 16) ||
+      !aligned(row_norms, 4))
     return TQ_ERR_ALIGN;
-  const int grid = grid_for(rows, 4, 8);
+  const int wpb = tq::orbit_waves_per_block(d);
+  const int grid = grid_for(rows, wpb, 8);
   return launched(tq::launch_orbit_quantize(W, rows, d, bits, perm, signs, cb,
                                             bit_order == TQ_LSB_FIRST, packed, row_norms, grid,
-                                            static_cast<hipStream_t>(stream)));
+                                            wpb, static_cast<hipStream_t>(stream)));
 }
 
 int orbit_dequantize(const uint8_t* packed, const float* row_norms, int64_t rows, int64_t d,
@@ -179,12 +181,13 @@ int orbit_dequantize(const uint8_t* packed, const float* row_norms, int64_t rows
   if (!packed || !row_norms || !W_out) return TQ_ERR_NULL;
   if (!rotated_only && (!inv_perm || !signs)) return TQ_ERR_NULL;
   if (!aligned(packed, 16) || !aligned(W_out, 16) || !aligned(row_norms, 4) ||
-      (inv_perm && !aligned(inv_perm, 4)))
+      (!rotated_only && (!aligned(inv_perm, 16) || !aligned(signs, 16))))
     return TQ_ERR_ALIGN;
-  const int grid = grid_for(rows, 4, 8);
+  const int wpb = tq::orbit_waves_per_block(d);
+  const int grid = grid_for(rows, wpb, 8);
   return launched(tq::launch_orbit_dequantize(packed, row_norms, rows, d, bits, inv_perm, signs,
                                               cb, bit_order == TQ_LSB_FIRST, rotated_only,
-                                              W_out, out_dtype, grid,
+                                              W_out, out_dtype, grid, wpb,
                                               static_cast<hipStream_t>(stream)));
 }
 

@@ -1,14 +1,543 @@
-// placeholder, replaced below
+// OrbitQuant weight-codec kernels for gfx950 -- "zerogpu-sdxlTrainer:
+// toolkit/util/orbit_quant.py": rpbh_forward, _quantize_rows,
+// _dequantize_rotated, dequantize.
+//
+// Work mapping. One wave owns one weight row at a time (a 256-thread block
+// keeps four rows in flight). The row (d <= 4096 fp32) is first copied into
+// LDS with coalesced 16-byte loads, then each lane gathers its elements
+// through the permutation. Lane l holds the 16-element chunks c = l + 64t
+// (t = 0..3), element j = 16c + i: index bits 0-3 are register bits (i),
+// bits 4-9 are lane bits, bits 10-11 are tile bits (t). FWHT stages run in
+// the order 1, 2, 4, ..., h/2: in registers for bits 0-3, across lanes for
+// bits 4-9 (ds_swizzle / ds_bpermute plus one fmac, with the lazy lane sign
+// described in tq3.hip), in registers again for bits 10-11. The row norm's
+// sum of squares follows the same bit order inside each h-block; block sums
+// are then added left to right.
+#include "tq_common.h"
 #include "tq_kernels.h"
+
 namespace tq {
-hipError_t launch_orbit_quantize(const float*, int64_t, int64_t, int, const int32_t*,
-                                 const int8_t*, const OrbitCodebook&, int, uint8_t*, float*,
-                                 int, hipStream_t) {
-  return hipErrorNotSupported;
+
+namespace {
+
+constexpr int kMaxTiles = 4;    // d <= 4096
+constexpr int kMaxBlocks = 128; // d / h <= 4096 / 32
+
+// ds_swizzle bit mode: inside each 32-lane half, lane i reads lane i ^ m.
+constexpr int bit_xor(int m) { return (m << 10) | 0x1F; }
+
+// Value of the lane whose index differs in lane bit S.
+template <int S>
+__device__ __forceinline__ float xlane(float v) {
+  if constexpr (S == 0) {
+    return swz<QP_XOR1>(v);
+  } else if constexpr (S == 1) {
+    return swz<QP_XOR2>(v);
+  } else if constexpr (S < 5) {
+    return swz<bit_xor(1 << S)>(v);
+  } else {
+    const int src = ((threadIdx.x & 63) ^ 32) << 2;
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, v)));
+  }
 }
-hipError_t launch_orbit_dequantize(const uint8_t*, const float*, int64_t, int64_t, int,
-                                   const int32_t*, const int8_t*, const OrbitCodebook&, int,
-                                   int, void*, int, int, hipStream_t) {
-  return hipErrorNotSupported;
+
+// One cross-lane butterfly stage on lane bit S (lower lane: a + b; upper
+// lane: the negation of a - b, tracked by the lazy lane sign).
+template <int S>
+__device__ __forceinline__ void lane_stage(float (&y)[kMaxTiles][16], int ntile) {
+  const float c = ((threadIdx.x >> S) & 1) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int t = 0; t < kMaxTiles; ++t)
+    if (t < ntile)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[t][i] = __builtin_fmaf(xlane<S>(y[t][i]), c, y[t][i]);
 }
+
+template <int S>
+__device__ __forceinline__ float lane_sum(float v) {
+  return v + xlane<S>(v);
+}
+
+// Full FWHT stage sequence for blocks of h = 2^log2h (32 <= h <= 4096);
+// without the final scaling.
+__device__ __forceinline__ void fwht_rows(float (&y)[kMaxTiles][16], int ntile, int log2h) {
+#pragma unroll
+  for (int t = 0; t < kMaxTiles; ++t)
+    if (t < ntile)
+#pragma unroll
+      for (int h = 1; h < 16; h *= 2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if ((i & h) == 0) {
+            const float a = y[t][i], b = y[t][i + h];
+            y[t][i] = a + b;
+            y[t][i + h] = a - b;
+          }
+  const int lb = log2h - 4;  // lane bits inside a block (capped at 6 below)
+  if (lb > 0) lane_stage<0>(y, ntile);
+  if (lb > 1) lane_stage<1>(y, ntile);
+  if (lb > 2) lane_stage<2>(y, ntile);
+  if (lb > 3) lane_stage<3>(y, ntile);
+  if (lb > 4) lane_stage<4>(y, ntile);
+  if (lb > 5) lane_stage<5>(y, ntile);
+#pragma unroll
+  for (int ht = 1; ht < kMaxTiles; ht *= 2)
+    if (log2h > 9 + ht)  // ht = 1: bit 10, ht = 2: bit 11
+#pragma unroll
+      for (int t = 0; t < kMaxTiles; ++t)
+        if ((t & ht) == 0 && t + ht < ntile)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float a = y[t][i], b = y[t + ht][i];
+            y[t][i] = a + b;
+            y[t + ht][i] = a - b;
+          }
+}
+
+// Lazy lane sign left by the cross-lane stages of a block of 2^log2h.
+__device__ __forceinline__ float lane_sigma(int log2h) {
+  const int lb = log2h - 4 < 6 ? log2h - 4 : 6;
+  const int bits = (threadIdx.x & 63) & ((1 << lb) - 1);
+  return (__builtin_popcount(bits) & 1) ? -1.0f : 1.0f;
+}
+
+// --------------------------------------------------------------- packing ---
+
+// 16 codes of BITS bits -> 2*BITS bytes of the stream, as a little-endian
+// 64-bit value (byte k of the result = stream byte k of this chunk).
+template <int BITS, bool LSB>
+__device__ __forceinline__ uint64_t pack16(const uint32_t (&code)[16]) {
+  uint64_t acc = 0;
+  if constexpr (LSB) {
+    // code i at stream bits BITS*i .. BITS*i + BITS - 1, bit t at BITS*i + t
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc |= (uint64_t)code[i] << (BITS * i);
+  } else if constexpr (BITS == 3) {
+    // most significant bit first: each 8 codes form a big-endian 24-bit word
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w |= code[8 * g + i] << (21 - 3 * i);
+      const uint32_t le = (w >> 16) | (w & 0xff00u) | ((w & 0xffu) << 16);
+      acc |= (uint64_t)le << (24 * g);
+    }
+  } else {
+    // BITS 2 or 4: a code never crosses a byte; within its byte the earlier
+    // code takes the more significant bits
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int q = BITS * i;
+      const int shift = 8 * (q >> 3) + 8 - (q & 7) - BITS;
+      acc |= (uint64_t)code[i] << shift;
+    }
+  }
+  return acc;
+}
+
+template <int BITS, bool LSB>
+__device__ __forceinline__ void unpack16(uint64_t acc, uint32_t (&code)[16]) {
+  constexpr uint32_t mask = (1u << BITS) - 1;
+  if constexpr (LSB) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) code[i] = (uint32_t)(acc >> (BITS * i)) & mask;
+  } else if constexpr (BITS == 3) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const uint32_t le = (uint32_t)(acc >> (24 * g)) & 0xffffffu;
+      const uint32_t w = (le >> 16) | (le & 0xff00u) | ((le & 0xffu) << 16);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) code[8 * g + i] = (w >> (21 - 3 * i)) & 7u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int q = BITS * i;
+      const int shift = 8 * (q >> 3) + 8 - (q & 7) - BITS;
+      code[i] = (uint32_t)(acc >> shift) & mask;
+    }
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ void store_codes(uint8_t* p, uint64_t acc) {
+  if constexpr (BITS == 2) {
+    *reinterpret_cast<uint32_t*>(p) = (uint32_t)acc;
+  } else if constexpr (BITS == 4) {
+    *reinterpret_cast<uint2*>(p) = make_uint2((uint32_t)acc, (uint32_t)(acc >> 32));
+  } else {
+    uint16_t* q = reinterpret_cast<uint16_t*>(p);
+    q[0] = (uint16_t)acc;
+    q[1] = (uint16_t)(acc >> 16);
+    q[2] = (uint16_t)(acc >> 32);
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ uint64_t load_codes(const uint8_t* p) {
+  if constexpr (BITS == 2) {
+    return *reinterpret_cast<const uint32_t*>(p);
+  } else if constexpr (BITS == 4) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    return (uint64_t)v.x | ((uint64_t)v.y << 32);
+  } else {
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
+    return (uint64_t)q[0] | ((uint64_t)q[1] << 16) | ((uint64_t)q[2] << 32);
+  }
+}
+
+// Sign bit (bit 31) of the int8 +-1 value k of a little-endian word.
+__device__ __forceinline__ uint32_t sign_of(uint32_t w, int k) {
+  return (w << (24 - 8 * k)) & 0x80000000u;
+}
+
+// ------------------------------------------------------------- quantize ---
+
+template <int BITS, bool LSB>
+__global__ __launch_bounds__(256) void orbit_quantize_kernel(
+    const float* __restrict__ W, int64_t rows, int d, int log2h, float kh,
+    const int32_t* __restrict__ perm, const int8_t* __restrict__ signs, OrbitCodebook cb,
+    uint8_t* __restrict__ packed, float* __restrict__ norms) {
+  extern __shared__ float lds[];
+  const int wpb = blockDim.x >> 6;  // rows in flight per block
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  float* rowbuf = lds + wave * (d + kMaxBlocks);
+  float* bsum = rowbuf + d;
+  const int nchunk = d >> 4;
+  const int ntile = (nchunk + 63) >> 6;
+  const int nblk = d >> log2h;
+  const int lb = log2h - 4 < 6 ? log2h - 4 : 6;
+  const float ksig = kh * lane_sigma(log2h);
+  const int64_t row_bytes = (int64_t)d * BITS / 8;
+  constexpr int L = 1 << BITS;
+  const float eps = (float)1e-10;
+
+  for (int64_t r = (int64_t)blockIdx.x * wpb + wave; r < rows;
+       r += (int64_t)gridDim.x * wpb) {
+    // Row into LDS, coalesced.
+    const float4* src = reinterpret_cast<const float4*>(W + r * d);
+    for (int f = lane; f < (d >> 2); f += 64) reinterpret_cast<float4*>(rowbuf)[f] = src[f];
+
+    // y_j = W[perm_j] * signs_j.
+    float y[kMaxTiles][16];
+#pragma unroll
+    for (int t = 0; t < kMaxTiles; ++t) {
+      const int c = lane + 64 * t;
+      if (t < ntile && c < nchunk) {
+        const int4* pp = reinterpret_cast<const int4*>(perm + 16 * c);
+        const uint4 sv = *reinterpret_cast<const uint4*>(signs + 16 * c);
+        const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int4 p = pp[k];
+          const int pi[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            y[t][4 * k + e] = as_f(as_u(rowbuf[pi[e]]) ^ sign_of(sw[k], e));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) y[t][i] = 0.0f;
+      }
+    }
+
+    fwht_rows(y, ntile, log2h);
+#pragma unroll
+    for (int t = 0; t < kMaxTiles; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[t][i] = y[t][i] * ksig;
+
+    // Sum of squares per block: bits 0-3 in registers, then the lane bits,
+    // then the tile bits.
+    float part[kMaxTiles];
+    float amin = __builtin_inff();
+#pragma unroll
+    for (int t = 0; t < kMaxTiles; ++t) {
+      float s[16];
+      const bool act = t < ntile && lane + 64 * t < nchunk;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[i] = y[t][i] * y[t][i];
+        if (act) amin = __builtin_fminf(amin, __builtin_fabsf(y[t][i]));
+      }
+#pragma unroll
+      for (int w = 1; w < 16; w *= 2)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2 * w) s[i] = s[i] + s[i + w];
+      part[t] = s[0];
+    }
+#pragma unroll
+    for (int t = 0; t < kMaxTiles; ++t) {
+      if (lb > 0) part[t] = lane_sum<0>(part[t]);
+      if (lb > 1) part[t] = lane_sum<1>(part[t]);
+      if (lb > 2) part[t] = lane_sum<2>(part[t]);
+      if (lb > 3) part[t] = lane_sum<3>(part[t]);
+      if (lb > 4) part[t] = lane_sum<4>(part[t]);
+      if (lb > 5) part[t] = lane_sum<5>(part[t]);
+    }
+    if (log2h > 10) {
+      part[0] = part[0] + part[1];
+      part[2] = part[2] + part[3];
+    }
+    if (log2h > 11) part[0] = part[0] + part[2];
+    // Block sums to LDS (first lane of each block), then added left to right.
+    if (log2h <= 10) {
+#pragma unroll
+      for (int t = 0; t < kMaxTiles; ++t) {
+        const int c = lane + 64 * t;
+        if (t < ntile && c < nchunk && (c & ((1 << lb) - 1)) == 0) bsum[c >> lb] = part[t];
+      }
+    } else if (lane == 0) {
+      const int per = 1 << (log2h - 10);  // tiles per block
+#pragma unroll
+      for (int t = 0; t < kMaxTiles; t += 2)
+        if (t < ntile && (t % per) == 0) bsum[t / per] = part[t];
+    }
+    float total = bsum[0];
+    for (int b = 1; b < nblk; ++b) total = total + bsum[b];
+    const float norm = __builtin_sqrtf(total);
+    const float denom = norm + eps;
+
+    // u = y / denom, correctly rounded: shared reciprocal while every nonzero
+    // |y| >= denom * 2^-60 (denom >= 1e-10 always), plain division otherwise.
+    if (amin >= denom * 0x1p-60f && denom <= 0x1p100f) {
+      const Recip rd = make_recip(denom);
+#pragma unroll
+      for (int t = 0; t < kMaxTiles; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) y[t][i] = div_rn(y[t][i], rd);
+    } else {
+#pragma unroll
+      for (int t = 0; t < kMaxTiles; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) y[t][i] = y[t][i] / denom;
+    }
+
+    // Codes: number of edges below u.
+#pragma unroll
+    for (int t = 0; t < kMaxTiles; ++t) {
+      const int c = lane + 64 * t;
+      if (t < ntile && c < nchunk) {
+        uint32_t code[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float u = y[t][i];
+          uint32_t n = 0;
+#pragma unroll
+          for (int k = 0; k + 1 < L; ++k) n += (cb.edge[k] < u) ? 1u : 0u;
+          code[i] = n;
+        }
+        store_codes<BITS>(packed + r * row_bytes + 2 * BITS * c, pack16<BITS, LSB>(code));
+      }
+    }
+    if (lane == 0) norms[r] = norm;
+  }
+}
+
+// ----------------------------------------------------------- dequantize ---
+
+template <int DT>
+__device__ __forceinline__ void store16(void* out, int64_t off, const float (&v)[16]) {
+  if constexpr (DT == DT_F32) {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + off);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) p[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+  } else {
+    uint4* p = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + off);
+    uint32_t w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      typedef float f2 __attribute__((ext_vector_type(2)));
+      const f2 pr = {v[2 * k], v[2 * k + 1]};
+      if constexpr (DT == DT_BF16) {
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, b2));
+      } else {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, h2));
+      }
+    }
+    p[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    p[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+}
+
+template <int BITS, bool LSB, int DT>
+__global__ __launch_bounds__(256) void orbit_dequantize_kernel(
+    const uint8_t* __restrict__ packed, const float* __restrict__ norms, int64_t rows, int d,
+    int log2h, float kh, const int32_t* __restrict__ inv_perm,
+    const int8_t* __restrict__ signs, OrbitCodebook cb, int rotated_only,
+    void* __restrict__ out) {
+  extern __shared__ float lds[];
+  const int wpb = blockDim.x >> 6;  // rows in flight per block
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  float* rowbuf = lds + wave * (d + kMaxBlocks);
+  float* tab = rowbuf + d;  // 2^BITS codebook entries times the row norm
+  const int nchunk = d >> 4;
+  const int ntile = (nchunk + 63) >> 6;
+  const float ksig = kh * lane_sigma(log2h);
+  const int64_t row_bytes = (int64_t)d * BITS / 8;
+  constexpr int L = 1 << BITS;
+
+  for (int64_t r = (int64_t)blockIdx.x * wpb + wave; r < rows;
+       r += (int64_t)gridDim.x * wpb) {
+    const float norm = norms[r];
+    if (lane < L) tab[lane] = cb.cb[lane] * norm;
+
+    float w[kMaxTiles][16];
+#pragma unroll
+    for (int t = 0; t < kMaxTiles; ++t) {
+      const int c = lane + 64 * t;
+      if (t < ntile && c < nchunk) {
+        uint32_t code[16];
+        unpack16<BITS, LSB>(load_codes<BITS>(packed + r * row_bytes + 2 * BITS * c), code);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) w[t][i] = tab[code[i]];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) w[t][i] = 0.0f;
+      }
+    }
+
+    if (rotated_only) {
+#pragma unroll
+      for (int t = 0; t < kMaxTiles; ++t) {
+        const int c = lane + 64 * t;
+        if (t < ntile && c < nchunk) store16<DT>(out, r * d + 16 * c, w[t]);
+      }
+      continue;
+    }
+
+    // Inverse rotation: FWHT per block times h^-1/2, times signs_j, then
+    // out[i] = z[inv_perm_i] through LDS.
+    fwht_rows(w, ntile, log2h);
+#pragma unroll
+    for (int t = 0; t < kMaxTiles; ++t) {
+      const int c = lane + 64 * t;
+      if (t < ntile && c < nchunk) {
+        const uint4 sv = *reinterpret_cast<const uint4*>(signs + 16 * c);
+        const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+        float z[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) z[i] = as_f(as_u(w[t][i] * ksig) ^ sign_of(sw[i >> 2], i & 3));
+        float4* dst = reinterpret_cast<float4*>(rowbuf + 16 * c);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dst[k] = make_float4(z[4 * k], z[4 * k + 1], z[4 * k + 2], z[4 * k + 3]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kMaxTiles; ++t) {
+      const int c = lane + 64 * t;
+      if (t < ntile && c < nchunk) {
+        const int4* pp = reinterpret_cast<const int4*>(inv_perm + 16 * c);
+        float o[16];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int4 p = pp[k];
+          o[4 * k] = rowbuf[p.x];
+          o[4 * k + 1] = rowbuf[p.y];
+          o[4 * k + 2] = rowbuf[p.z];
+          o[4 * k + 3] = rowbuf[p.w];
+        }
+        store16<DT>(out, r * d + 16 * c, o);
+      }
+    }
+  }
+}
+
+template <int BITS, bool LSB>
+hipError_t launch_q(const float* W, int64_t rows, int d, int log2h, float kh,
+                    const int32_t* perm, const int8_t* signs, const OrbitCodebook& cb,
+                    uint8_t* packed, float* norms, int grid, int wpb, hipStream_t s) {
+  const size_t shm = (size_t)wpb * (d + kMaxBlocks) * sizeof(float);
+  orbit_quantize_kernel<BITS, LSB><<<grid, 64 * wpb, shm, s>>>(W, rows, d, log2h, kh, perm, signs,
+                                                          cb, packed, norms);
+  return hipGetLastError();
+}
+
+template <int BITS, bool LSB, int DT>
+hipError_t launch_dq(const uint8_t* packed, const float* norms, int64_t rows, int d, int log2h,
+                     float kh, const int32_t* inv_perm, const int8_t* signs,
+                     const OrbitCodebook& cb, int rotated_only, void* out, int grid, int wpb,
+                     hipStream_t s) {
+  const size_t shm = (size_t)wpb * (d + kMaxBlocks) * sizeof(float);
+  orbit_dequantize_kernel<BITS, LSB, DT><<<grid, 64 * wpb, shm, s>>>(
+      packed, norms, rows, d, log2h, kh, inv_perm, signs, cb, rotated_only, out);
+  return hipGetLastError();
+}
+
+template <int BITS, bool LSB>
+hipError_t launch_dq_dt(int dt, const uint8_t* packed, const float* norms, int64_t rows, int d,
+                        int log2h, float kh, const int32_t* inv_perm, const int8_t* signs,
+                        const OrbitCodebook& cb, int rotated_only, void* out, int grid,
+                        int wpb, hipStream_t s) {
+  switch (dt) {
+    case DT_F32:
+      return launch_dq<BITS, LSB, DT_F32>(packed, norms, rows, d, log2h, kh, inv_perm, signs, cb,
+                                          rotated_only, out, grid, wpb, s);
+    case DT_BF16:
+      return launch_dq<BITS, LSB, DT_BF16>(packed, norms, rows, d, log2h, kh, inv_perm, signs,
+                                           cb, rotated_only, out, grid, wpb, s);
+    default:
+      return launch_dq<BITS, LSB, DT_F16>(packed, norms, rows, d, log2h, kh, inv_perm, signs, cb,
+                                          rotated_only, out, grid, wpb, s);
+  }
+}
+
+int ilog2(int64_t v) {
+  int l = 0;
+  while ((int64_t(1) << (l + 1)) <= v) ++l;
+  return l;
+}
+
+}  // namespace
+
+int orbit_waves_per_block(int64_t d) {
+  return 4 * (d + kMaxBlocks) * (int64_t)sizeof(float) <= 65536 ? 4 : 2;
+}
+
+hipError_t launch_orbit_quantize(const float* W, int64_t rows, int64_t d, int bits,
+                                 const int32_t* perm, const int8_t* signs,
+                                 const OrbitCodebook& cb, int lsb_first, uint8_t* packed,
+                                 float* norms, int grid, int wpb, hipStream_t s) {
+  const int64_t h = d & -d;
+  const int log2h = ilog2(h);
+  const float kh = (float)pow((double)h, -0.5);
+  const int di = (int)d;
+#define TQ_Q(B, O) launch_q<B, O>(W, rows, di, log2h, kh, perm, signs, cb, packed, norms, grid, wpb, s)
+  if (lsb_first) {
+    if (bits == 2) return TQ_Q(2, true);
+    if (bits == 3) return TQ_Q(3, true);
+    return TQ_Q(4, true);
+  }
+  if (bits == 2) return TQ_Q(2, false);
+  if (bits == 3) return TQ_Q(3, false);
+  return TQ_Q(4, false);
+#undef TQ_Q
+}
+
+hipError_t launch_orbit_dequantize(const uint8_t* packed, const float* norms, int64_t rows,
+                                   int64_t d, int bits, const int32_t* inv_perm,
+                                   const int8_t* signs, const OrbitCodebook& cb, int lsb_first,
+                                   int rotated_only, void* out, int dt, int grid, int wpb,
+                                   hipStream_t s) {
+  const int64_t h = d & -d;
+  const int log2h = ilog2(h);
+  const float kh = (float)pow((double)h, -0.5);
+  const int di = (int)d;
+#define TQ_DQ(B, O) \
+  launch_dq_dt<B, O>(dt, packed, norms, rows, di, log2h, kh, inv_perm, signs, cb, rotated_only, out, grid, wpb, s)
+  if (lsb_first) {
+    if (bits == 2) return TQ_DQ(2, true);
+    if (bits == 3) return TQ_DQ(3, true);
+    return TQ_DQ(4, true);
+  }
+  if (bits == 2) return TQ_DQ(2, false);
+  if (bits == 3) return TQ_DQ(3, false);
+  return TQ_DQ(4, false);
+#undef TQ_DQ
+}
+
 }  // namespace tq

@@ -28,11 +28,14 @@ struct OrbitCodebook {
 hipError_t launch_orbit_quantize(const float* W, int64_t rows, int64_t d, int bits,
                                  const int32_t* perm, const int8_t* signs,
                                  const OrbitCodebook& cb, int lsb_first, uint8_t* packed,
-                                 float* norms, int grid, hipStream_t s);
+                                 float* norms, int grid, int wpb, hipStream_t s);
 hipError_t launch_orbit_dequantize(const uint8_t* packed, const float* norms, int64_t rows,
                                    int64_t d, int bits, const int32_t* inv_perm,
                                    const int8_t* signs, const OrbitCodebook& cb,
                                    int lsb_first, int rotated_only, void* out, int dt,
-                                   int grid, hipStream_t s);
+                                   int grid, int wpb, hipStream_t s);
+// Rows in flight per block (one per wave) for input dimension d: four, or
+// two when four rows' LDS staging would exceed 64 KB.
+int orbit_waves_per_block(int64_t d);
 
 }  // namespace tq

@@ -1,0 +1,138 @@
+"""GPU parity of the OrbitQuant weight codec against the oracle.
+
+Source: "zerogpu-sdxlTrainer: toolkit/util/orbit_quant.py" (_quantize_rows,
+_dequantize_rotated, dequantize). Weights ~ N(0, 0.02^2); rotations from the
+page's seed rule (datagen.rpbh_params); codebooks from orbit_make_codebook,
+which the CPU tests pin to the oracle's Lloyd-Max procedure.
+"""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from parity_util import compare_reconstruction
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def tq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import randomized_hadamard_lloyd_amd as m
+    return m
+
+
+def edges_of(cb):
+    c = np.asarray(cb, dtype=np.float32)
+    return ((c[:-1] + c[1:]) / np.float32(2)).astype(np.float64)
+
+
+def check(tq, w, d, bits, msb=True, dtype=torch.float32, full_check=True):
+    perm, sg = datagen.rpbh_params(d)
+    inv = torch.argsort(perm)
+    cb = tq.orbit_make_codebook(bits, d)
+    order = tq.TQ_MSB_FIRST if msb else tq.TQ_LSB_FIRST
+    packed, norms = tq.orbit_quantize_weight(w.to(DEV), bits, perm.to(DEV), sg.to(DEV), cb,
+                                             bit_order=order)
+    torch.cuda.synchronize()
+    o_packed, o_norms = oracle.orbit_quantize(w.numpy(), bits, perm, sg, cb.numpy(),
+                                              msb_first=msb)
+    g_norms = norms.cpu().numpy()
+    assert np.max(np.abs(g_norms - o_norms) / np.maximum(o_norms, 1e-30)) <= 1e-6
+    g_packed = packed.cpu().numpy()
+    if not np.array_equal(g_packed, o_packed):
+        rows = w.shape[0]
+        gc = oracle.unpack(g_packed, rows * d, bits, msb_first=msb).reshape(rows, d)
+        oc = oracle.unpack(o_packed, rows * d, bits, msb_first=msb).reshape(rows, d)
+        unit, _ = oracle.orbit_unit(w.numpy(), perm, sg)
+        diff = gc != oc
+        dist = np.min(np.abs(unit[..., None].astype(np.float64) - edges_of(cb)), axis=-1)
+        assert not (diff & (dist >= 1e-5 * np.abs(unit).max())).any(), "flips away from edges"
+        assert diff.sum() <= 1e-6 * rows * d
+        pytest.fail(f"codes not bit-identical: {int(diff.sum())} near-edge flips")
+    assert np.array_equal(g_norms, o_norms)
+    if not full_check:
+        return packed, norms
+    for rotated in (True, False):
+        out = tq.orbit_dequantize(packed, norms, d, bits, inv.to(DEV), sg.to(DEV), cb,
+                                  bit_order=order, rotated_only=rotated, dtype=dtype)
+        torch.cuda.synchronize()
+        ref = oracle.orbit_dequantize(o_packed, o_norms, d, bits, inv, sg, cb.numpy(),
+                                      msb_first=msb, rotated_only=rotated)
+        st = compare_reconstruction(out, ref, o_norms, dtype)
+        assert st["exact"], (rotated, st)
+    return packed, norms
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("msb", [True, False])
+def test_orbit_3072(tq, bits, msb):
+    w = datagen.orbit_weight(rows=257, d=3072, seed=60 + bits)
+    check(tq, w, 3072, bits, msb)
+
+
+@pytest.mark.parametrize("d", [32, 96, 160, 256, 512, 768, 1024, 1536, 2048, 2560, 4096])
+def test_orbit_dims(tq, d):
+    # every Hadamard block size from 32 to 4096, partial and multi-tile rows
+    w = datagen.orbit_weight(rows=67, d=d, seed=d)
+    check(tq, w, d, 3)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_orbit_narrow_outputs(tq, dtype):
+    w = datagen.orbit_weight(rows=64, d=3072, seed=7)
+    check(tq, w, 3072, 4, True, dtype)
+
+
+def test_orbit_edge_rows(tq):
+    d = 3072
+    w = datagen.orbit_weight(rows=8, d=d, seed=3)
+    w[0] = 0.0                       # zero row: norm 0, every code from u = 0
+    w[1] = 1.0                       # constant row
+    w[2, ::7] = 0.0                  # exact zeros in a row
+    w[3] = w[3] * 1e-20              # tiny row
+    w[4] = w[4] * 1e15               # large row
+    w[5, 100] = 50.0                 # outlier
+    check(tq, w, d, 3)
+    check(tq, w, d, 2, msb=False)
+
+
+def test_orbit_errors(tq):
+    d = 3072
+    w = torch.zeros((4, d), device=DEV)
+    perm, sg = datagen.rpbh_params(d)
+    cb = tq.orbit_make_codebook(3, d)
+    with pytest.raises(ValueError):
+        tq.orbit_quantize_weight(w, 5, perm.to(DEV), sg.to(DEV), cb)       # bits
+    with pytest.raises(ValueError):
+        tq.orbit_quantize_weight(torch.zeros((4, 48), device=DEV), 3,      # h = 16
+                                 perm[:48].to(DEV), sg[:48].to(DEV), cb)
+    packed, norms = tq.orbit_quantize_weight(torch.zeros((0, d), device=DEV), 3,
+                                             perm.to(DEV), sg.to(DEV), cb)
+    assert packed.shape == (0, d * 3 // 8) and norms.shape == (0,)
+
+
+def test_orbit_full_weight(tq):
+    """The 12288 x 3072 weight at 2, 3 and 4 bits; every code and norm checked,
+    reconstructions checked on a sample of rows."""
+    d = 3072
+    w = datagen.orbit_weight()
+    perm, sg = datagen.rpbh_params(d)
+    inv = torch.argsort(perm)
+    rows = torch.from_numpy(np.random.default_rng(5).choice(w.shape[0], 512, replace=False))
+    for bits in (2, 3, 4):
+        cb = tq.orbit_make_codebook(bits, d)
+        packed, norms = tq.orbit_quantize_weight(w.to(DEV), bits, perm.to(DEV), sg.to(DEV), cb)
+        full = tq.orbit_dequantize(packed, norms, d, bits, inv.to(DEV), sg.to(DEV), cb)
+        torch.cuda.synchronize()
+        o_packed, o_norms = oracle.orbit_quantize(w.numpy(), bits, perm, sg, cb.numpy())
+        assert np.array_equal(norms.cpu().numpy(), o_norms), bits
+        assert np.array_equal(packed.cpu().numpy(), o_packed), bits
+        ref = oracle.orbit_dequantize(o_packed[rows.numpy()], o_norms[rows.numpy()], d, bits,
+                                      inv, sg, cb.numpy())
+        st = compare_reconstruction(full[rows.to(DEV)], ref, o_norms[rows.numpy()])
+        assert st["exact"], (bits, st)

@@ -139,7 +139,8 @@ def test_edge_vectors(tq, signs):
     t = rng.standard_normal(128)
     t[7] = 1e-30                                  # tiny relative to the norm
     rows.append(t)
-    rows.append(rng.standard_normal(128) * 1e30)  # huge norm
+    rows.append(rng.standard_normal(128) * 1e30)  # sum of squares overflows: norm inf
+    rows.append(rng.standard_normal(128) * 1e18)  # large finite norm
     rows.append(rng.standard_normal(128) * 1e-30) # tiny norm, below the clamp
     w = rng.standard_normal(128) * np.exp2(rng.integers(-60, 60, 128))  # wide range
     rows.append(w)
@@ -221,12 +222,13 @@ def test_full_structured(tq, signs):
 def test_full_decode_records(tq, signs):
     """2^24 random records -> bf16, checked on a sample of rows."""
     rec = datagen.decode_records()
-    y = tq.tq3_dequantize(rec.to(DEV), signs, dtype=torch.bfloat16)
+    # records [N, 56] are N blocks of one row: the output is [N * 128]
+    y = tq.tq3_dequantize(rec.to(DEV), signs, dtype=torch.bfloat16).reshape(-1, 128)
     torch.cuda.synchronize()
     idx = torch.from_numpy(np.random.default_rng(2).choice(rec.shape[0], 65536, replace=False))
     sample = rec[idx].numpy()
     o = oracle.tq3_dequantize(sample, signs)
     _, norms, _ = split_records(sample)
-    st = compare_reconstruction(y[idx.to(DEV)].reshape(-1, 128), o, norms, torch.bfloat16)
+    st = compare_reconstruction(y[idx.to(DEV)], o, norms, torch.bfloat16)
     assert st["exact"], st
     assert math.isfinite(st["max_abs_over_norm"])
