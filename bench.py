@@ -1,18 +1,29 @@
-"""Throughput of the TQ3 codec on one MI355X.
+"""Throughput of the randomized-Hadamard + Lloyd-Max codecs on one MI355X.
 
-A step is one pass of the TQ3 hot path over one layer of KV cache: quantize K
-and V ([32768 tokens, 8 heads, 128] bf16 each, 2 x 524288 vectors) to 56-byte
-records, then dequantize both back to bf16. `value` counts vectors taken
-through the round trip per second (1,048,576 per step). Inputs are resident in
-HBM before timing; the step rotates over several buffer sets whose total size
-exceeds the 256 MB last-level cache, so every launch streams from HBM.
+Headline (`value`): the TQ3 hot path on one layer of KV cache. A step
+quantizes K and V ([32768 tokens, 8 heads, 128] bf16 each, 262144 vectors
+per tensor) to 56-byte records and dequantizes both back to bf16; `value`
+counts vectors taken through that round trip per second (524288 per step).
+Inputs are resident in HBM before timing; steps rotate over buffer sets whose
+total size exceeds the 256 MB last-level cache, so every launch streams from
+HBM. The timed region is bracketed by device synchronisation and measured
+with HIP events on the launch stream.
 
-Prints one JSON line. Extra fields: per-kernel times and effective bandwidth,
-the roofline of the dominant kernel (algorithmic bytes / average launch time,
-HIP events on the launch stream), and the oracle's CPU throughput on a bounded
-sample (the CPU baseline).
+Also reported, each timed with HIP events over repeated launches:
+  * kernels: per-kernel average duration and effective bandwidth
+    (algorithmic bytes read + written) of the headline step;
+  * roofline: the dominant kernel of the step against peak HBM bandwidth,
+    with traffic from the committed rocprofv3 counter summary when it matches
+    the current kernel source;
+  * valu: the same kernel's vector-ALU issue rate (instructions per vector
+    from its code object) against the chip's non-packed VALU peak;
+  * secondary: steady-state rates on larger inputs -- 2^20 structured fp32
+    vectors quantized, 2^24 records dequantized to bf16, the 12288 x 3072
+    OrbitQuant weight at 2/3/4 bits -- and a device-to-device copy;
+  * cpu_baseline: the oracle on the host cores, on a bounded sample.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -25,7 +36,24 @@ sys.path.insert(0, ROOT)
 
 METRIC = "TQ3 quantize+dequantize vectors/s and effective HBM GB/s (% of peak)"
 PEAK_HBM_GBS = 8000.0
+# 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz: one non-packed 32-bit VALU operation
+# per lane per cycle (the 157.3 TFLOP/s fp32 figure counts packed FMA as 4).
+PEAK_VALU_LANE_OPS = 256 * 64 * 2.4e9
 REC = 56
+PROFILES = os.path.join(ROOT, "profiles")
+
+# Arithmetic of the method per 128-vector, one op per fp32 multiply, add,
+# divide, square root, max or compare ("tq3_core.py", tq3_quantize and
+# tq3_dequantize). Quantize: 128 squares + 127 adds + sqrt + clamp (norm),
+# 128 divisions (x / norm), 128 sign multiplies, 7 x 128 butterfly adds,
+# 128 multiplies by 1/sqrt(128), 128 abs-max steps (scale), 128 divisions
+# (y / scale), and per element 3 compares against the positive boundaries plus
+# a sign test (the table is symmetric). Dequantize: 128 centroid x scale,
+# 7 x 128 butterfly adds, 128 x 1/sqrt(128), 128 sign and 128 norm multiplies.
+ALG_OPS_PER_VECTOR = {
+    "quantize": 128 + 127 + 1 + 1 + 128 + 128 + 7 * 128 + 128 + 128 + 128 + 4 * 128,
+    "dequantize": 128 + 7 * 128 + 128 + 128 + 128,
+}
 
 
 def parse():
@@ -36,7 +64,72 @@ def parse():
     p.add_argument("--sets", type=int, default=4, help="rotating buffer sets")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    return p.parse_args()
+    p.add_argument("--no-secondary", action="store_true")
+    p.add_argument("--profile", action="store_true",
+                   help="short run for counter collection: one 256 MiB device copy "
+                        "(calibration), 1 warmup + 3 steps, nothing else")
+    args = p.parse_args()
+    if args.profile:
+        args.steps, args.warmup = 3, 1
+        args.no_secondary = args.no_cpu_baseline = True
+    return args
+
+
+class Timer:
+    """Average duration of repeated launches, HIP events on one stream."""
+
+    def __init__(self, stream):
+        self.stream = stream
+
+    def run(self, fn, iters, warmup=2):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(iters):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+            fn()
+            e1.record(self.stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in evs]
+        return sum(ms) / len(ms), min(ms)
+
+
+def rate(bytes_, ms):
+    return bytes_ / (ms * 1e-3) / 1e9
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in ("tq3.hip", "orbit.hip", "tq_common.h", "tq_kernels.h", "libtq.cpp"):
+        with open(os.path.join(ROOT, "randomized_hadamard_lloyd_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source; otherwise None."""
+    path = os.path.join(PROFILES, "tq3_kv_layer_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash():
+        return None
+    return t.get("kernels", {}).get(kernel)
+
+
+def valu_per_vector():
+    path = os.path.join(PROFILES, "tq3_valu_counts.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    return t if t.get("source_hash") == source_hash() else None
 
 
 def cpu_baseline(k_cpu, signs, seconds):
@@ -55,15 +148,94 @@ def cpu_baseline(k_cpu, signs, seconds):
         if el >= seconds:
             break
     return {"value": n_done / el, "unit": "vectors/s", "cores": threads, "kind": "oracle",
-            "sample": f"first 65536 K vectors (bf16 widened to fp32), quantize+dequantize, "
-                      f"{n_done // 65536} passes in {el:.1f} s"}
+            "sample": f"first 65536 K vectors of the KV layer (bf16 widened to fp32), "
+                      f"quantize + dequantize, {n_done // 65536} passes in {el:.1f} s"}
+
+
+def secondary(tq, timer, dev, signs, mask):
+    import datagen
+    out = {}
+    L = tq.lib
+    sp = tq._stream(torch.empty(1, device=dev))
+
+    # device copy ceiling at the size of one KV tensor's quantize traffic
+    nbytes = 256 << 20
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    ms, _ = timer.run(lambda: b.copy_(a), 20)
+    out["device_copy_256MiB"] = {"avg_ms": ms, "GBps": rate(2 * nbytes, ms)}
+    del a, b
+
+    # 2^20 structured fp32 vectors: quantize, and dequantize back to fp32
+    x = datagen.structured_blocks().to(dev)
+    n = x.shape[0]
+    rec = torch.empty((n, REC), dtype=torch.uint8, device=dev)
+    y = torch.empty((n, 128), dtype=torch.float32, device=dev)
+    ms_q, _ = timer.run(lambda: L.tq3_quantize(tq._ptr(x), tq.TQ_F32, n, 128, mask,
+                                               tq._ptr(rec), sp), 20)
+    ms_d, _ = timer.run(lambda: L.tq3_dequantize(tq._ptr(rec), n, mask, tq._ptr(y),
+                                                 tq.TQ_F32, 128, sp), 20)
+    out["tq3_structured_1M_f32"] = {
+        "vectors": n,
+        "quantize": {"avg_ms": ms_q, "vectors_per_s": n / (ms_q * 1e-3),
+                     "GBps": rate(n * (512 + REC), ms_q)},
+        "dequantize": {"avg_ms": ms_d, "vectors_per_s": n / (ms_d * 1e-3),
+                       "GBps": rate(n * (REC + 512), ms_d)}}
+    del x, rec, y
+
+    # 2^24 decode records to bf16
+    rec = datagen.decode_records().to(dev)
+    n = rec.shape[0]
+    y = torch.empty((n, 128), dtype=torch.bfloat16, device=dev)
+    ms_d, _ = timer.run(lambda: L.tq3_dequantize(tq._ptr(rec), n, mask, tq._ptr(y),
+                                                 tq.TQ_BF16, 128, sp), 10)
+    out["tq3_decode_16M_bf16"] = {"vectors": n, "avg_ms": ms_d,
+                                  "vectors_per_s": n / (ms_d * 1e-3),
+                                  "GBps": rate(n * (REC + 256), ms_d)}
+    del rec, y
+
+    # OrbitQuant weight 12288 x 3072 at 2, 3, 4 bits
+    d = 3072
+    w = datagen.orbit_weight().to(dev)
+    rows = w.shape[0]
+    perm, sg = datagen.rpbh_params(d)
+    perm_d = perm.to(torch.int32).to(dev)
+    inv_d = torch.argsort(perm).to(torch.int32).to(dev)
+    sg_d = sg.to(dev)
+    norms = torch.empty(rows, dtype=torch.float32, device=dev)
+    wout = torch.empty_like(w)
+    orb = {}
+    import ctypes
+    for bits in (2, 3, 4):
+        cb = tq.orbit_make_codebook(bits, d)
+        cbh = (ctypes.c_float * len(cb))(*cb.tolist())
+        cbp = ctypes.cast(cbh, ctypes.c_void_p)
+        packed = torch.empty((rows, d * bits // 8), dtype=torch.uint8, device=dev)
+        ms_q, _ = timer.run(lambda: L.orbit_quantize_weight(
+            tq._ptr(w), rows, d, bits, tq._ptr(perm_d), tq._ptr(sg_d), cbp, tq.TQ_MSB_FIRST,
+            tq._ptr(packed), tq._ptr(norms), sp), 10)
+        ms_r, _ = timer.run(lambda: L.orbit_dequantize(
+            tq._ptr(packed), tq._ptr(norms), rows, d, bits, tq._ptr(inv_d), tq._ptr(sg_d), cbp,
+            tq.TQ_MSB_FIRST, 1, tq._ptr(wout), tq.TQ_F32, sp), 10)
+        ms_f, _ = timer.run(lambda: L.orbit_dequantize(
+            tq._ptr(packed), tq._ptr(norms), rows, d, bits, tq._ptr(inv_d), tq._ptr(sg_d), cbp,
+            tq.TQ_MSB_FIRST, 0, tq._ptr(wout), tq.TQ_F32, sp), 10)
+        row_bytes = 4 * d + d * bits // 8 + 4
+        orb[f"{bits}bit"] = {
+            "quantize": {"avg_ms": ms_q, "rows_per_s": rows / (ms_q * 1e-3),
+                         "GBps": rate(rows * row_bytes, ms_q)},
+            "dequantize_rotated": {"avg_ms": ms_r, "GBps": rate(rows * row_bytes, ms_r)},
+            "dequantize_full": {"avg_ms": ms_f, "GBps": rate(rows * row_bytes, ms_f)}}
+    out["orbit_12288x3072"] = orb
+    return out
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); "
-              "the codec is data-parallel per vector and needs no collective", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the codecs are "
+              "data-parallel per vector or row and this build measures one GPU's share",
+              file=sys.stderr)
         sys.exit(2)
     import datagen
     import randomized_hadamard_lloyd_amd as tq
@@ -100,35 +272,48 @@ def main():
     def step(i, evs=None):
         b = sets[i % len(sets)]
         seq = [(launch_q, b["k"], b["rk"], "quantize"), (launch_q, b["v"], b["rv"], "quantize"),
-               (launch_dq, b["rk"], b["ok"], "dequantize"), (launch_dq, b["rv"], b["ov"], "dequantize")]
+               (launch_dq, b["rk"], b["ok"], "dequantize"),
+               (launch_dq, b["rv"], b["ov"], "dequantize")]
         for fn, a, o, name in seq:
-            if evs is not None:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
+            if evs is None:
                 fn(a, o)
-                e1.record(stream)
-                evs.append((name, e0, e1))
-            else:
-                fn(a, o)
+                continue
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn(a, o)
+            e1.record(stream)
+            evs.append((name, e0, e1))
+
+    if args.profile:
+        # reference kernel for scaling the HBM byte counters: copies 256 MiB
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: K steps, wall time by events around the whole region
-    evs = []
+    # timed region: exactly `steps` steps
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
-        step(i, evs)
+        step(i)
     t_end.record(stream)
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_step = total_ms / args.steps
+    ms_step = t_start.elapsed_time(t_end) / args.steps
 
+    # per-kernel durations: the same steps again with events around each launch
+    evs = []
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs)
+    torch.cuda.synchronize()
     per = {}
     for name, e0, e1 in evs:
         per.setdefault(name, []).append(e0.elapsed_time(e1))
@@ -136,16 +321,41 @@ def main():
     kernels = {}
     for name, times in per.items():
         avg = sum(times) / len(times)
-        gbs = bytes_per_vec[name] * n / (avg * 1e-3) / 1e9
-        kernels[name] = {"avg_ms": avg, "launches": len(times), "bytes_per_vector": bytes_per_vec[name],
+        gbs = rate(bytes_per_vec[name] * n, avg)
+        kernels[name] = {"kernel": f"tq3_{name}_kernel<bf16>", "avg_ms": avg,
+                         "launches": len(times), "bytes_per_vector": bytes_per_vec[name],
                          "vectors_per_launch": n, "GBps": gbs, "frac_peak_hbm": gbs / PEAK_HBM_GBS}
-    dom = max(kernels, key=lambda k: kernels[k]["avg_ms"] * kernels[k]["launches"])
+    dom = max(kernels, key=lambda k: kernels[k]["avg_ms"])
     vec_per_step = 2 * n
     value = vec_per_step / (ms_step * 1e-3)
     step_bytes = 2 * n * (bytes_per_vec["quantize"] + bytes_per_vec["dequantize"])
-    eff_gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    eff_gbs = rate(step_bytes, ms_step)
 
-    # correctness spot check of the last set against the oracle (outside timing)
+    for name, k in kernels.items():
+        k["alg_ops_per_vector"] = ALG_OPS_PER_VECTOR[name]
+        k["alg_TOPs"] = ALG_OPS_PER_VECTOR[name] * n / (k["avg_ms"] * 1e-3) / 1e12
+    # The quantize kernel issues ~32 VALU lane-ops per element against 2.4
+    # bytes of HBM traffic: the vector ALU, not HBM, bounds it. Its roofline is
+    # the method's arithmetic against the chip's non-packed fp32 VALU peak.
+    traffic = measured_traffic(kernels[dom]["kernel"])
+    ach = kernels[dom]["alg_TOPs"]
+    peak = PEAK_VALU_LANE_OPS / 1e12
+    roofline = {"bound": "alu", "kernel": kernels[dom]["kernel"], "achieved": ach,
+                "peak": peak, "unit": "TOP/s", "frac": ach / peak, "traffic": traffic,
+                "alg_ops_per_launch": ALG_OPS_PER_VECTOR[dom] * n,
+                "alg_bytes_per_launch": bytes_per_vec[dom] * n,
+                "hbm": {"achieved": kernels[dom]["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": kernels[dom]["frac_peak_hbm"]}}
+    valu = None
+    vc = valu_per_vector()
+    if vc is not None and kernels[dom]["kernel"] in vc.get("kernels", {}):
+        ops = vc["kernels"][kernels[dom]["kernel"]]["valu_lane_ops_per_vector"]
+        issued = ops * n / (kernels[dom]["avg_ms"] * 1e-3)
+        valu = {"kernel": kernels[dom]["kernel"], "issued_lane_ops_per_vector": ops,
+                "achieved": issued / 1e12, "peak": peak, "unit": "TOP/s",
+                "frac": issued / PEAK_VALU_LANE_OPS}
+
+    # correctness spot check of one set against the oracle (outside timing)
     import oracle
     b = sets[(args.steps - 1) % len(sets)]
     k32 = k_cpu.reshape(-1, 128)[:4096].to(torch.float32).numpy()
@@ -157,15 +367,17 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "TQ3 round trip of one KV-cache layer: K and V, 32768 tokens x "
-                               "8 heads x 128, bf16 in, 56-byte records, bf16 out",
+                               "8 heads x 128 (262144 vectors each), bf16 in, 56-byte records, "
+                               "bf16 out",
                    "vectors_per_step": vec_per_step, "buffer_sets": args.sets},
         "effective_GBps": eff_gbs, "pct_of_peak_hbm": 100.0 * eff_gbs / PEAK_HBM_GBS,
         "kernels": kernels,
-        "roofline": {"bound": "hbm", "kernel": f"tq3_{dom}_kernel<bf16>",
-                     "achieved": kernels[dom]["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": kernels[dom]["frac_peak_hbm"], "traffic": None},
+        "roofline": roofline,
+        "valu": valu,
         "parity_spot_check": ok,
     }
+    if not args.no_secondary:
+        result["secondary"] = secondary(tq, Timer(stream), dev, signs, mask)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(k_cpu, signs, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -107,7 +107,7 @@ int tq3_quantize(const void* x, int x_dtype, int64_t n_vec, int64_t x_row_stride
   if (!aligned(x, 16) || !aligned(records, 8)) return TQ_ERR_ALIGN;
   tq::SignMask m;
   std::memcpy(m.w, sign_mask, sizeof(m.w));  // little-endian host
-  const int grid = grid_for(n_vec, 64, 8);
+  const int grid = grid_for(n_vec, tq::kTq3VecPerBlock, 8);
   return launched(tq::launch_tq3_quantize(x, x_dtype, n_vec, x_row_stride, m, records, grid,
                                           static_cast<hipStream_t>(stream)));
 }
@@ -123,7 +123,7 @@ int tq3_dequantize(const uint8_t* records, int64_t n_vec, const uint8_t* sign_ma
   if (!aligned(y, 16) || !aligned(records, 8)) return TQ_ERR_ALIGN;
   tq::SignMask m;
   std::memcpy(m.w, sign_mask, sizeof(m.w));
-  const int grid = grid_for(n_vec, 64, 8);
+  const int grid = grid_for(n_vec, tq::kTq3VecPerBlock, 8);
   return launched(tq::launch_tq3_dequantize(records, n_vec, m, y, y_dtype, y_row_stride, grid,
                                             static_cast<hipStream_t>(stream)));
 }

@@ -24,6 +24,8 @@ namespace tq {
 
 namespace {
 
+static_assert(kTq3VecPerBlock == 64, "a 256-thread block carries 64 vectors, one per quad");
+
 // fp32 of the page's printed centroid table (doubles rounded to float32).
 __device__ __forceinline__ float tq3_centroid(int k) {
   constexpr float c[8] = {(float)-0.9816, (float)-0.6168, (float)-0.3479, (float)-0.1129,
@@ -183,8 +185,9 @@ __global__ __launch_bounds__(256) void tq3_quantize_kernel(const void* __restric
   const LaneSigns ls = lane_signs(q);
   const float kq = ls.sigma * kInvSqrt128;
 
-  const int64_t step = (int64_t)gridDim.x * 64;
-  for (int64_t v = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2); v < n_vec; v += step) {
+  const int64_t step = (int64_t)gridDim.x * kTq3VecPerBlock;
+  for (int64_t v = (int64_t)blockIdx.x * kTq3VecPerBlock + (threadIdx.x >> 2); v < n_vec;
+       v += step) {
     float x_[4][8];
     ld.load(x, v, stride, q, x_);
 
@@ -352,8 +355,8 @@ __global__ __launch_bounds__(256) void tq3_dequantize_kernel(const uint8_t* __re
   const int dsel = (3 * q) >> 2;
   const uint32_t shift = (24u * q) & 31u;
 
-  const int64_t step = (int64_t)gridDim.x * 64;
-  for (int64_t v = (int64_t)blockIdx.x * 64 + quad; v < n_vec; v += step) {
+  const int64_t step = (int64_t)gridDim.x * kTq3VecPerBlock;
+  for (int64_t v = (int64_t)blockIdx.x * kTq3VecPerBlock + quad; v < n_vec; v += step) {
     const uint32_t* r32 = reinterpret_cast<const uint32_t*>(rec + v * 56);
     uint32_t chunk[4];
 #pragma unroll

@@ -14,6 +14,10 @@ struct SignMask {
   uint32_t w[4];
 };
 
+// Vectors one 256-thread TQ3 block handles per grid-stride iteration
+// (a 4-lane quad owns one vector).
+constexpr int kTq3VecPerBlock = 64;
+
 hipError_t launch_tq3_quantize(const void* x, int dt, int64_t n_vec, int64_t stride,
                                const SignMask& m, uint8_t* rec, int grid, hipStream_t s);
 hipError_t launch_tq3_dequantize(const uint8_t* rec, int64_t n_vec, const SignMask& m,
