@@ -47,6 +47,14 @@ constexpr uint32_t kB3x2 = 2u * __builtin_bit_cast(uint32_t, (float)0.7992);
 constexpr float kInvSqrt128 = (float)0.08838834764831845;  // fp32(1/sqrt(128))
 constexpr float kFloor = (float)1e-8;                      // clamp of norm and scale
 
+// acc * 2 + (this lane's bit of the wave mask `bits`): one add with carry-in.
+__device__ __forceinline__ uint32_t shift_in(uint32_t acc, uint64_t bits) {
+  uint32_t r;
+  uint64_t carry_out;
+  asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(acc), "s"(bits));
+  return r;
+}
+
 // Sign bit of element (q, g, i) from the 128-bit mask (bit j = element j).
 __device__ __forceinline__ uint32_t sign_bit(const SignMask& m, int q, int g, int i) {
   return (m.w[g] >> (8 * q + i)) & 1u;
@@ -254,28 +262,34 @@ __global__ __launch_bounds__(256) void tq3_quantize_kernel(const void* __restric
     // shared-reciprocal quotient is exact wherever it can reach a boundary.
     const Recip rs = make_recip(scale);
 
-    // Index = number of boundaries strictly below t = y / scale. The table is
-    // symmetric, so with a = |t| and P = {0.2304, 0.4824, 0.7992}:
+    // Index = number of boundaries strictly below t. The table is symmetric,
+    // so with a = |t| and P = {0.2304, 0.4824, 0.7992}:
     //   t > 0:  idx = 4 + #{b in P : b < a}
     //   t <= 0: idx = 3 - #{b in P : b <= a}
     // Rotating t's bits left by one puts the sign in bit 0: R = 2*bits(a) + sign.
     // Then R > 2*bits(b) means bits(a) > bits(b) for t >= 0 and bits(a) >= bits(b)
     // for t < 0 -- exactly the strict/non-strict split of the tie rule -- and
-    // with c = #{R > 2*bits(b)}, idx = c ^ (t > 0 ? 4 : 3).
+    // with c = #{R > 2*bits(b)} (a thermometer code m1 >= m2 >= m3),
+    // idx = c ^ (t > 0 ? 4 : 3): bit 2 = (t > 0), bit 1 = m2 xnor (t > 0),
+    // bit 0 = (m1 ^ m2 ^ m3) xnor (t > 0). The compares leave wave-wide lane
+    // masks; the bit logic runs on the scalar unit and each bit enters the
+    // lane's chunk through one add-with-carry.
     uint32_t chunk[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       uint32_t c = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 7; i >= 0; --i) {
         const float t = div_rn(u[g][i], rs);
         const uint32_t tb = as_u(t);
         const uint32_t r = __builtin_amdgcn_alignbit(tb, tb, 31);
-        const bool m1 = r > kB1x2, m2 = r > kB2x2, m3 = r > kB3x2;
-        const bool pos = t > 0.0f;
-        const bool b1 = !(m2 ^ pos);
-        const bool b0 = !((m1 ^ m2 ^ m3) ^ pos);
-        c |= ((b0 ? 1u : 0u) | (b1 ? 2u : 0u) | (pos ? 4u : 0u)) << (3 * i);
+        const uint64_t m1 = __builtin_amdgcn_ballot_w64(r > kB1x2);
+        const uint64_t m2 = __builtin_amdgcn_ballot_w64(r > kB2x2);
+        const uint64_t m3 = __builtin_amdgcn_ballot_w64(r > kB3x2);
+        const uint64_t pos = __builtin_amdgcn_ballot_w64(t > 0.0f);
+        c = shift_in(c, pos);
+        c = shift_in(c, ~(m2 ^ pos));
+        c = shift_in(c, ~(m1 ^ m2 ^ m3 ^ pos));
       }
       chunk[g] = c;
     }
