@@ -65,6 +65,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
+    p.add_argument("--only-secondary", action="store_true",
+                   help="run only the secondary measurements and print them as one JSON line")
     p.add_argument("--profile", action="store_true",
                    help="short run for counter collection: one 256 MiB device copy "
                         "(calibration), 1 warmup + 3 steps, nothing else")
@@ -111,8 +113,9 @@ def source_hash():
 
 
 def measured_traffic(kernel):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel source; otherwise None."""
+    """HBM bytes per launch (FETCH_SIZE and WRITE_SIZE, each scaled by what the
+    counter reads for a 256 MiB device copy) from the committed counter
+    summary, if it was taken on the current kernel source; otherwise None."""
     path = os.path.join(PROFILES, "tq3_kv_layer_traffic.json")
     if not os.path.exists(path):
         return None
@@ -120,7 +123,8 @@ def measured_traffic(kernel):
         t = json.load(f)
     if t.get("source_hash") != source_hash():
         return None
-    return t.get("kernels", {}).get(kernel)
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k["hbm_bytes"]
 
 
 def valu_per_vector():
@@ -244,6 +248,10 @@ def main():
     torch.cuda.set_device(dev)
     signs = datagen.tq3_signs()
     mask = tq.sign_mask(signs)
+    if args.only_secondary:
+        stream = torch.cuda.current_stream(dev)
+        print(json.dumps({"secondary": secondary(tq, Timer(stream), dev, signs, mask)}), flush=True)
+        return
     k_cpu = datagen.kv_cache("K")
     v_cpu = datagen.kv_cache("V")
     n = k_cpu.numel() // 128                       # vectors per tensor
