@@ -147,6 +147,17 @@ static int orbit_check(int64_t rows, int64_t d, int bits, const float* codebook,
   // fp32 midpoints of neighbours, as the page's _quantize_rows forms them
   for (int k = 0; k < 15; ++k)
     cb->edge[k] = (k + 1 < levels) ? (codebook[k] + codebook[k + 1]) / 2.0f : INFINITY;
+  // Exactly symmetric codebooks (the Gaussian Lloyd-Max ones are) let the
+  // kernels compare |u| against the positive edges only.
+  bool sym = true;
+  for (int k = 0; k < levels; ++k) sym = sym && codebook[k] == -codebook[levels - 1 - k];
+  cb->sym = sym && cb->edge[levels / 2 - 1] == 0.0f;
+  for (int i = 0; i < 7; ++i) {
+    const int k = levels / 2 + i;
+    uint32_t b = 0;
+    if (k < levels - 1) std::memcpy(&b, &cb->edge[k], 4);
+    cb->th[i] = 2u * b;
+  }
   return TQ_OK;
 }
 

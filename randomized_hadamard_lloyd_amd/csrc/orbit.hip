@@ -20,7 +20,6 @@ namespace tq {
 
 namespace {
 
-constexpr int kMaxTiles = 4;    // d <= 4096
 constexpr int kMaxBlocks = 128; // d / h <= 4096 / 32
 
 // ds_swizzle bit mode: inside each 32-lane half, lane i reads lane i ^ m.
@@ -43,14 +42,13 @@ __device__ __forceinline__ float xlane(float v) {
 
 // One cross-lane butterfly stage on lane bit S (lower lane: a + b; upper
 // lane: the negation of a - b, tracked by the lazy lane sign).
-template <int S>
-__device__ __forceinline__ void lane_stage(float (&y)[kMaxTiles][16], int ntile) {
+template <int S, int NT>
+__device__ __forceinline__ void lane_stage(float (&y)[NT][16]) {
   const float c = ((threadIdx.x >> S) & 1) ? -1.0f : 1.0f;
 #pragma unroll
-  for (int t = 0; t < kMaxTiles; ++t)
-    if (t < ntile)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) y[t][i] = __builtin_fmaf(xlane<S>(y[t][i]), c, y[t][i]);
+    for (int i = 0; i < 16; ++i) y[t][i] = __builtin_fmaf(xlane<S>(y[t][i]), c, y[t][i]);
 }
 
 template <int S>
@@ -58,34 +56,34 @@ __device__ __forceinline__ float lane_sum(float v) {
   return v + xlane<S>(v);
 }
 
-// Full FWHT stage sequence for blocks of h = 2^log2h (32 <= h <= 4096);
-// without the final scaling.
-__device__ __forceinline__ void fwht_rows(float (&y)[kMaxTiles][16], int ntile, int log2h) {
+// Full FWHT stage sequence for blocks of h = 2^log2h (32 <= h <= 4096) over
+// NT tiles of 64 x 16 elements; without the final scaling.
+template <int NT>
+__device__ __forceinline__ void fwht_rows(float (&y)[NT][16], int log2h) {
 #pragma unroll
-  for (int t = 0; t < kMaxTiles; ++t)
-    if (t < ntile)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int h = 1; h < 16; h *= 2)
+    for (int h = 1; h < 16; h *= 2)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if ((i & h) == 0) {
-            const float a = y[t][i], b = y[t][i + h];
-            y[t][i] = a + b;
-            y[t][i + h] = a - b;
-          }
+      for (int i = 0; i < 16; ++i)
+        if ((i & h) == 0) {
+          const float a = y[t][i], b = y[t][i + h];
+          y[t][i] = a + b;
+          y[t][i + h] = a - b;
+        }
   const int lb = log2h - 4;  // lane bits inside a block (capped at 6 below)
-  if (lb > 0) lane_stage<0>(y, ntile);
-  if (lb > 1) lane_stage<1>(y, ntile);
-  if (lb > 2) lane_stage<2>(y, ntile);
-  if (lb > 3) lane_stage<3>(y, ntile);
-  if (lb > 4) lane_stage<4>(y, ntile);
-  if (lb > 5) lane_stage<5>(y, ntile);
+  if (lb > 0) lane_stage<0>(y);
+  if (lb > 1) lane_stage<1>(y);
+  if (lb > 2) lane_stage<2>(y);
+  if (lb > 3) lane_stage<3>(y);
+  if (lb > 4) lane_stage<4>(y);
+  if (lb > 5) lane_stage<5>(y);
 #pragma unroll
-  for (int ht = 1; ht < kMaxTiles; ht *= 2)
+  for (int ht = 1; ht < NT; ht *= 2)
     if (log2h > 9 + ht)  // ht = 1: bit 10, ht = 2: bit 11
 #pragma unroll
-      for (int t = 0; t < kMaxTiles; ++t)
-        if ((t & ht) == 0 && t + ht < ntile)
+      for (int t = 0; t < NT; ++t)
+        if ((t & ht) == 0 && t + ht < NT)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const float a = y[t][i], b = y[t + ht][i];
@@ -103,36 +101,90 @@ __device__ __forceinline__ float lane_sigma(int log2h) {
 
 // --------------------------------------------------------------- packing ---
 
-// 16 codes of BITS bits -> 2*BITS bytes of the stream, as a little-endian
-// 64-bit value (byte k of the result = stream byte k of this chunk).
-template <int BITS, bool LSB>
-__device__ __forceinline__ uint64_t pack16(const uint32_t (&code)[16]) {
-  uint64_t acc = 0;
-  if constexpr (LSB) {
-    // code i at stream bits BITS*i .. BITS*i + BITS - 1, bit t at BITS*i + t
+// Code of u = number of codebook edges strictly below u, as BITS wave masks,
+// most significant bit first.
+//
+// Any codebook: T_k = (e_k < u) for the 2^BITS - 1 ascending edges is a
+// thermometer code, so bit j of the count is the XOR of T_k over the k that
+// are multiples of 2^j (k = 1, 2, ...).
+// Symmetric codebook (edges -e_H .. -e_1, 0, e_1 .. e_H, H = 2^(BITS-1) - 1):
+// as for the TQ3 index, R = bits(u) rotated left by one compares with
+// 2 * bits(e_i) as "|u| > e_i" for u >= 0 and "|u| >= e_i" for u < 0; with
+// c = #{R > 2 bits(e_i)} the code is c ^ (u > 0 ? H + 1 : H): the top bit is
+// (u > 0) and bit j below it is c_j xor (u <= 0).
+template <int BITS, bool SYM>
+__device__ __forceinline__ void code_masks(float u, const OrbitCodebook& cb,
+                                           uint64_t (&m)[BITS]) {
+  constexpr int L = 1 << BITS;
+  if constexpr (SYM) {
+    constexpr int H = L / 2 - 1;
+    const uint32_t ub = as_u(u);
+    const uint32_t r = __builtin_amdgcn_alignbit(ub, ub, 31);
+    uint64_t T[H + 1];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc |= (uint64_t)code[i] << (BITS * i);
-  } else if constexpr (BITS == 3) {
-    // most significant bit first: each 8 codes form a big-endian 24-bit word
+    for (int i = 1; i <= H; ++i) T[i] = __builtin_amdgcn_ballot_w64(r > cb.th[i - 1]);
+    const uint64_t pos = __builtin_amdgcn_ballot_w64(u > 0.0f);
+    m[0] = pos;
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      uint32_t w = 0;
+    for (int j = 0; j < BITS - 1; ++j) {
+      uint64_t x = ~pos;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) w |= code[8 * g + i] << (21 - 3 * i);
-      const uint32_t le = (w >> 16) | (w & 0xff00u) | ((w & 0xffu) << 16);
-      acc |= (uint64_t)le << (24 * g);
+      for (int i = 1 << j; i <= H; i += 1 << j) x ^= T[i];
+      m[BITS - 1 - j] = x;
     }
   } else {
-    // BITS 2 or 4: a code never crosses a byte; within its byte the earlier
-    // code takes the more significant bits
+    uint64_t T[L];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int q = BITS * i;
-      const int shift = 8 * (q >> 3) + 8 - (q & 7) - BITS;
-      acc |= (uint64_t)code[i] << shift;
+    for (int k = 1; k < L; ++k) T[k] = __builtin_amdgcn_ballot_w64(cb.edge[k - 1] < u);
+#pragma unroll
+    for (int j = 0; j < BITS; ++j) {
+      uint64_t x = 0;
+#pragma unroll
+      for (int k = 1 << j; k < L; k += 1 << j) x ^= T[k];
+      m[BITS - 1 - j] = x;
     }
   }
-  return acc;
+}
+
+__device__ __forceinline__ uint32_t bswap24(uint32_t w) {
+  return (w >> 16) | (w & 0xff00u) | ((w & 0xffu) << 16);
+}
+
+// Codes of 16 consecutive elements -> their 2*BITS bytes of the packed row,
+// as a little-endian 64-bit value (byte k of the result = stream byte k of
+// this chunk). Bits enter 32-bit words through add-with-carry in stream order
+// for MSB-first words and in reverse for LSB-first ones.
+template <int BITS, bool LSB, bool SYM>
+__device__ __forceinline__ uint64_t pack16(const float (&u)[16], const OrbitCodebook& cb) {
+  constexpr int NW = BITS == 2 ? 1 : 2;  // 32-bit words (3 bits: 24-bit words)
+  constexpr int PER = 16 / NW;           // codes per word
+  uint32_t word[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    uint32_t acc = 0;
+#pragma unroll
+    for (int s = 0; s < PER; ++s) {
+      const int i = LSB ? w * PER + (PER - 1 - s) : w * PER + s;
+      uint64_t m[BITS];
+      code_masks<BITS, SYM>(u[i], cb, m);
+#pragma unroll
+      for (int b = 0; b < BITS; ++b) acc = shift_in(acc, m[b]);
+    }
+    word[w] = acc;
+  }
+  if constexpr (LSB) {
+    // code i's bit t is stream bit BITS*i + t: the words are already in order
+    if constexpr (BITS == 2) return word[0];
+    else if constexpr (BITS == 3) return (uint64_t)word[0] | ((uint64_t)word[1] << 24);
+    else return (uint64_t)word[0] | ((uint64_t)word[1] << 32);
+  } else {
+    // each word is big-endian: code 0 in its most significant bits
+    if constexpr (BITS == 2) return __builtin_bswap32(word[0]);
+    else if constexpr (BITS == 3)
+      return (uint64_t)bswap24(word[0]) | ((uint64_t)bswap24(word[1]) << 24);
+    else
+      return (uint64_t)__builtin_bswap32(word[0]) | ((uint64_t)__builtin_bswap32(word[1]) << 32);
+  }
 }
 
 template <int BITS, bool LSB>
@@ -193,7 +245,7 @@ __device__ __forceinline__ uint32_t sign_of(uint32_t w, int k) {
 
 // ------------------------------------------------------------- quantize ---
 
-template <int BITS, bool LSB>
+template <int BITS, bool LSB, int NT>
 __global__ __launch_bounds__(256) void orbit_quantize_kernel(
     const float* __restrict__ W, int64_t rows, int d, int log2h, float kh,
     const int32_t* __restrict__ perm, const int8_t* __restrict__ signs, OrbitCodebook cb,
@@ -205,12 +257,10 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
   float* rowbuf = lds + wave * (d + kMaxBlocks);
   float* bsum = rowbuf + d;
   const int nchunk = d >> 4;
-  const int ntile = (nchunk + 63) >> 6;
   const int nblk = d >> log2h;
   const int lb = log2h - 4 < 6 ? log2h - 4 : 6;
   const float ksig = kh * lane_sigma(log2h);
   const int64_t row_bytes = (int64_t)d * BITS / 8;
-  constexpr int L = 1 << BITS;
   const float eps = (float)1e-10;
 
   for (int64_t r = (int64_t)blockIdx.x * wpb + wave; r < rows;
@@ -220,11 +270,11 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
     for (int f = lane; f < (d >> 2); f += 64) reinterpret_cast<float4*>(rowbuf)[f] = src[f];
 
     // y_j = W[perm_j] * signs_j.
-    float y[kMaxTiles][16];
+    float y[NT][16];
 #pragma unroll
-    for (int t = 0; t < kMaxTiles; ++t) {
+    for (int t = 0; t < NT; ++t) {
       const int c = lane + 64 * t;
-      if (t < ntile && c < nchunk) {
+      if (c < nchunk) {
         const int4* pp = reinterpret_cast<const int4*>(perm + 16 * c);
         const uint4 sv = *reinterpret_cast<const uint4*>(signs + 16 * c);
         const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
@@ -242,25 +292,26 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
       }
     }
 
-    fwht_rows(y, ntile, log2h);
+    fwht_rows<NT>(y, log2h);
 #pragma unroll
-    for (int t = 0; t < kMaxTiles; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) y[t][i] = y[t][i] * ksig;
 
     // Sum of squares per block: bits 0-3 in registers, then the lane bits,
     // then the tile bits.
-    float part[kMaxTiles];
+    float part[NT];
     float amin = __builtin_inff();
 #pragma unroll
-    for (int t = 0; t < kMaxTiles; ++t) {
+    for (int t = 0; t < NT; ++t) {
       float s[16];
-      const bool act = t < ntile && lane + 64 * t < nchunk;
+      float tmin = __builtin_fabsf(y[t][0]);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         s[i] = y[t][i] * y[t][i];
-        if (act) amin = __builtin_fminf(amin, __builtin_fabsf(y[t][i]));
+        if (i > 0) tmin = __builtin_fminf(tmin, __builtin_fabsf(y[t][i]));
       }
+      if (lane + 64 * t < nchunk) amin = __builtin_fminf(amin, tmin);
 #pragma unroll
       for (int w = 1; w < 16; w *= 2)
 #pragma unroll
@@ -268,7 +319,7 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
       part[t] = s[0];
     }
 #pragma unroll
-    for (int t = 0; t < kMaxTiles; ++t) {
+    for (int t = 0; t < NT; ++t) {
       if (lb > 0) part[t] = lane_sum<0>(part[t]);
       if (lb > 1) part[t] = lane_sum<1>(part[t]);
       if (lb > 2) part[t] = lane_sum<2>(part[t]);
@@ -276,23 +327,27 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
       if (lb > 4) part[t] = lane_sum<4>(part[t]);
       if (lb > 5) part[t] = lane_sum<5>(part[t]);
     }
-    if (log2h > 10) {
-      part[0] = part[0] + part[1];
-      part[2] = part[2] + part[3];
+    if constexpr (NT >= 2) {
+      if (log2h > 10) {
+        part[0] = part[0] + part[1];
+        if constexpr (NT == 4) part[2] = part[2] + part[3];
+      }
     }
-    if (log2h > 11) part[0] = part[0] + part[2];
+    if constexpr (NT == 4) {
+      if (log2h > 11) part[0] = part[0] + part[2];
+    }
     // Block sums to LDS (first lane of each block), then added left to right.
     if (log2h <= 10) {
 #pragma unroll
-      for (int t = 0; t < kMaxTiles; ++t) {
+      for (int t = 0; t < NT; ++t) {
         const int c = lane + 64 * t;
-        if (t < ntile && c < nchunk && (c & ((1 << lb) - 1)) == 0) bsum[c >> lb] = part[t];
+        if (c < nchunk && (c & ((1 << lb) - 1)) == 0) bsum[c >> lb] = part[t];
       }
     } else if (lane == 0) {
       const int per = 1 << (log2h - 10);  // tiles per block
 #pragma unroll
-      for (int t = 0; t < kMaxTiles; t += 2)
-        if (t < ntile && (t % per) == 0) bsum[t / per] = part[t];
+      for (int t = 0; t < NT; t += 2)
+        if ((t % per) == 0) bsum[t / per] = part[t];
     }
     float total = bsum[0];
     for (int b = 1; b < nblk; ++b) total = total + bsum[b];
@@ -304,32 +359,29 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
     if (amin >= denom * 0x1p-60f && denom <= 0x1p100f) {
       const Recip rd = make_recip(denom);
 #pragma unroll
-      for (int t = 0; t < kMaxTiles; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) y[t][i] = div_rn(y[t][i], rd);
     } else {
 #pragma unroll
-      for (int t = 0; t < kMaxTiles; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) y[t][i] = y[t][i] / denom;
     }
 
-    // Codes: number of edges below u.
+    // Codes and packing (the codebook test is uniform: one branch per row).
+    uint64_t bytes[NT];
+    if (cb.sym) {
 #pragma unroll
-    for (int t = 0; t < kMaxTiles; ++t) {
+      for (int t = 0; t < NT; ++t) bytes[t] = pack16<BITS, LSB, true>(y[t], cb);
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) bytes[t] = pack16<BITS, LSB, false>(y[t], cb);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
       const int c = lane + 64 * t;
-      if (t < ntile && c < nchunk) {
-        uint32_t code[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float u = y[t][i];
-          uint32_t n = 0;
-#pragma unroll
-          for (int k = 0; k + 1 < L; ++k) n += (cb.edge[k] < u) ? 1u : 0u;
-          code[i] = n;
-        }
-        store_codes<BITS>(packed + r * row_bytes + 2 * BITS * c, pack16<BITS, LSB>(code));
-      }
+      if (c < nchunk) store_codes<BITS>(packed + r * row_bytes + 2 * BITS * c, bytes[t]);
     }
     if (lane == 0) norms[r] = norm;
   }
@@ -363,7 +415,7 @@ __device__ __forceinline__ void store16(void* out, int64_t off, const float (&v)
   }
 }
 
-template <int BITS, bool LSB, int DT>
+template <int BITS, bool LSB, int DT, int NT>
 __global__ __launch_bounds__(256) void orbit_dequantize_kernel(
     const uint8_t* __restrict__ packed, const float* __restrict__ norms, int64_t rows, int d,
     int log2h, float kh, const int32_t* __restrict__ inv_perm,
@@ -376,7 +428,6 @@ __global__ __launch_bounds__(256) void orbit_dequantize_kernel(
   float* rowbuf = lds + wave * (d + kMaxBlocks);
   float* tab = rowbuf + d;  // 2^BITS codebook entries times the row norm
   const int nchunk = d >> 4;
-  const int ntile = (nchunk + 63) >> 6;
   const float ksig = kh * lane_sigma(log2h);
   const int64_t row_bytes = (int64_t)d * BITS / 8;
   constexpr int L = 1 << BITS;
@@ -386,11 +437,11 @@ __global__ __launch_bounds__(256) void orbit_dequantize_kernel(
     const float norm = norms[r];
     if (lane < L) tab[lane] = cb.cb[lane] * norm;
 
-    float w[kMaxTiles][16];
+    float w[NT][16];
 #pragma unroll
-    for (int t = 0; t < kMaxTiles; ++t) {
+    for (int t = 0; t < NT; ++t) {
       const int c = lane + 64 * t;
-      if (t < ntile && c < nchunk) {
+      if (c < nchunk) {
         uint32_t code[16];
         unpack16<BITS, LSB>(load_codes<BITS>(packed + r * row_bytes + 2 * BITS * c), code);
 #pragma unroll
@@ -403,20 +454,20 @@ __global__ __launch_bounds__(256) void orbit_dequantize_kernel(
 
     if (rotated_only) {
 #pragma unroll
-      for (int t = 0; t < kMaxTiles; ++t) {
+      for (int t = 0; t < NT; ++t) {
         const int c = lane + 64 * t;
-        if (t < ntile && c < nchunk) store16<DT>(out, r * d + 16 * c, w[t]);
+        if (c < nchunk) store16<DT>(out, r * d + 16 * c, w[t]);
       }
       continue;
     }
 
     // Inverse rotation: FWHT per block times h^-1/2, times signs_j, then
     // out[i] = z[inv_perm_i] through LDS.
-    fwht_rows(w, ntile, log2h);
+    fwht_rows<NT>(w, log2h);
 #pragma unroll
-    for (int t = 0; t < kMaxTiles; ++t) {
+    for (int t = 0; t < NT; ++t) {
       const int c = lane + 64 * t;
-      if (t < ntile && c < nchunk) {
+      if (c < nchunk) {
         const uint4 sv = *reinterpret_cast<const uint4*>(signs + 16 * c);
         const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
         float z[16];
@@ -428,9 +479,9 @@ __global__ __launch_bounds__(256) void orbit_dequantize_kernel(
       }
     }
 #pragma unroll
-    for (int t = 0; t < kMaxTiles; ++t) {
+    for (int t = 0; t < NT; ++t) {
       const int c = lane + 64 * t;
-      if (t < ntile && c < nchunk) {
+      if (c < nchunk) {
         const int4* pp = reinterpret_cast<const int4*>(inv_perm + 16 * c);
         float o[16];
 #pragma unroll
@@ -447,42 +498,70 @@ __global__ __launch_bounds__(256) void orbit_dequantize_kernel(
   }
 }
 
-template <int BITS, bool LSB>
+template <int BITS, bool LSB, int NT>
 hipError_t launch_q(const float* W, int64_t rows, int d, int log2h, float kh,
                     const int32_t* perm, const int8_t* signs, const OrbitCodebook& cb,
                     uint8_t* packed, float* norms, int grid, int wpb, hipStream_t s) {
   const size_t shm = (size_t)wpb * (d + kMaxBlocks) * sizeof(float);
-  orbit_quantize_kernel<BITS, LSB><<<grid, 64 * wpb, shm, s>>>(W, rows, d, log2h, kh, perm, signs,
-                                                          cb, packed, norms);
+  orbit_quantize_kernel<BITS, LSB, NT><<<grid, 64 * wpb, shm, s>>>(W, rows, d, log2h, kh, perm,
+                                                                  signs, cb, packed, norms);
   return hipGetLastError();
 }
 
-template <int BITS, bool LSB, int DT>
+template <int BITS, bool LSB>
+hipError_t launch_q_nt(int nt, const float* W, int64_t rows, int d, int log2h, float kh,
+                       const int32_t* perm, const int8_t* signs, const OrbitCodebook& cb,
+                       uint8_t* packed, float* norms, int grid, int wpb, hipStream_t s) {
+  switch (nt) {
+    case 1: return launch_q<BITS, LSB, 1>(W, rows, d, log2h, kh, perm, signs, cb, packed, norms, grid, wpb, s);
+    case 2: return launch_q<BITS, LSB, 2>(W, rows, d, log2h, kh, perm, signs, cb, packed, norms, grid, wpb, s);
+    case 3: return launch_q<BITS, LSB, 3>(W, rows, d, log2h, kh, perm, signs, cb, packed, norms, grid, wpb, s);
+    default: return launch_q<BITS, LSB, 4>(W, rows, d, log2h, kh, perm, signs, cb, packed, norms, grid, wpb, s);
+  }
+}
+
+template <int BITS, bool LSB, int DT, int NT>
 hipError_t launch_dq(const uint8_t* packed, const float* norms, int64_t rows, int d, int log2h,
                      float kh, const int32_t* inv_perm, const int8_t* signs,
                      const OrbitCodebook& cb, int rotated_only, void* out, int grid, int wpb,
                      hipStream_t s) {
   const size_t shm = (size_t)wpb * (d + kMaxBlocks) * sizeof(float);
-  orbit_dequantize_kernel<BITS, LSB, DT><<<grid, 64 * wpb, shm, s>>>(
+  orbit_dequantize_kernel<BITS, LSB, DT, NT><<<grid, 64 * wpb, shm, s>>>(
       packed, norms, rows, d, log2h, kh, inv_perm, signs, cb, rotated_only, out);
   return hipGetLastError();
 }
 
-template <int BITS, bool LSB>
-hipError_t launch_dq_dt(int dt, const uint8_t* packed, const float* norms, int64_t rows, int d,
+template <int BITS, bool LSB, int DT>
+hipError_t launch_dq_nt(int nt, const uint8_t* packed, const float* norms, int64_t rows, int d,
                         int log2h, float kh, const int32_t* inv_perm, const int8_t* signs,
+                        const OrbitCodebook& cb, int rotated_only, void* out, int grid,
+                        int wpb, hipStream_t s) {
+#define TQ_DQN(N) launch_dq<BITS, LSB, DT, N>(packed, norms, rows, d, log2h, kh, inv_perm, signs, \
+                                              cb, rotated_only, out, grid, wpb, s)
+  switch (nt) {
+    case 1: return TQ_DQN(1);
+    case 2: return TQ_DQN(2);
+    case 3: return TQ_DQN(3);
+    default: return TQ_DQN(4);
+  }
+#undef TQ_DQN
+}
+
+template <int BITS, bool LSB>
+hipError_t launch_dq_dt(int dt, int nt, const uint8_t* packed, const float* norms, int64_t rows,
+                        int d, int log2h, float kh, const int32_t* inv_perm, const int8_t* signs,
                         const OrbitCodebook& cb, int rotated_only, void* out, int grid,
                         int wpb, hipStream_t s) {
   switch (dt) {
     case DT_F32:
-      return launch_dq<BITS, LSB, DT_F32>(packed, norms, rows, d, log2h, kh, inv_perm, signs, cb,
-                                          rotated_only, out, grid, wpb, s);
+      return launch_dq_nt<BITS, LSB, DT_F32>(nt, packed, norms, rows, d, log2h, kh, inv_perm,
+                                             signs, cb, rotated_only, out, grid, wpb, s);
     case DT_BF16:
-      return launch_dq<BITS, LSB, DT_BF16>(packed, norms, rows, d, log2h, kh, inv_perm, signs,
-                                           cb, rotated_only, out, grid, wpb, s);
+      return launch_dq_nt<BITS, LSB, DT_BF16>(nt, packed, norms, rows, d, log2h, kh, inv_perm,
+                                              signs, cb, rotated_only, out, grid, wpb, s);
     default:
-      return launch_dq<BITS, LSB, DT_F16>(packed, norms, rows, d, log2h, kh, inv_perm, signs, cb,
-                                          rotated_only, out, grid, wpb, s);
+      return launch_dq_nt<BITS, LSB, DT_F16>(nt, packed, norms, rows, d, log2h, kh, inv_perm,
+                                             signs, cb, rotated_only, out, grid, wpb, s);
   }
 }
 
@@ -506,7 +585,8 @@ hipError_t launch_orbit_quantize(const float* W, int64_t rows, int64_t d, int bi
   const int log2h = ilog2(h);
   const float kh = (float)pow((double)h, -0.5);
   const int di = (int)d;
-#define TQ_Q(B, O) launch_q<B, O>(W, rows, di, log2h, kh, perm, signs, cb, packed, norms, grid, wpb, s)
+  const int nt = (di + 1023) >> 10;  // tiles of 64 lanes x 16 elements
+#define TQ_Q(B, O) launch_q_nt<B, O>(nt, W, rows, di, log2h, kh, perm, signs, cb, packed, norms, grid, wpb, s)
   if (lsb_first) {
     if (bits == 2) return TQ_Q(2, true);
     if (bits == 3) return TQ_Q(3, true);
@@ -527,8 +607,9 @@ hipError_t launch_orbit_dequantize(const uint8_t* packed, const float* norms, in
   const int log2h = ilog2(h);
   const float kh = (float)pow((double)h, -0.5);
   const int di = (int)d;
+  const int nt = (di + 1023) >> 10;
 #define TQ_DQ(B, O) \
-  launch_dq_dt<B, O>(dt, packed, norms, rows, di, log2h, kh, inv_perm, signs, cb, rotated_only, out, grid, wpb, s)
+  launch_dq_dt<B, O>(dt, nt, packed, norms, rows, di, log2h, kh, inv_perm, signs, cb, rotated_only, out, grid, wpb, s)
   if (lsb_first) {
     if (bits == 2) return TQ_DQ(2, true);
     if (bits == 3) return TQ_DQ(3, true);

@@ -47,14 +47,6 @@ constexpr uint32_t kB3x2 = 2u * __builtin_bit_cast(uint32_t, (float)0.7992);
 constexpr float kInvSqrt128 = (float)0.08838834764831845;  // fp32(1/sqrt(128))
 constexpr float kFloor = (float)1e-8;                      // clamp of norm and scale
 
-// acc * 2 + (this lane's bit of the wave mask `bits`): one add with carry-in.
-__device__ __forceinline__ uint32_t shift_in(uint32_t acc, uint64_t bits) {
-  uint32_t r;
-  uint64_t carry_out;
-  asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(acc), "s"(bits));
-  return r;
-}
-
 // Sign bit of element (q, g, i) from the 128-bit mask (bit j = element j).
 __device__ __forceinline__ uint32_t sign_bit(const SignMask& m, int q, int g, int i) {
   return (m.w[g] >> (8 * q + i)) & 1u;

@@ -56,4 +56,13 @@ __device__ __forceinline__ float div_rn(float a, const Recip& r) {
   return __builtin_fmaf(rem, r.rh, q0);
 }
 
+// acc * 2 + (this lane's bit of the wave mask `bits`): one add with carry-in,
+// so a wave-wide compare result enters a lane's bit field at one VALU op.
+__device__ __forceinline__ uint32_t shift_in(uint32_t acc, uint64_t bits) {
+  uint32_t r;
+  uint64_t carry_out;
+  asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(acc), "s"(bits));
+  return r;
+}
+
 }  // namespace tq

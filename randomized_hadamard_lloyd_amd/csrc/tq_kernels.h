@@ -27,6 +27,11 @@ hipError_t launch_tq3_dequantize(const uint8_t* rec, int64_t n_vec, const SignMa
 struct OrbitCodebook {
   float cb[16];     // 2^bits ascending centroids
   float edge[15];   // fp32 midpoints of neighbours
+  // Set when cb[k] == -cb[2^bits - 1 - k] for every k: the edges are then
+  // symmetric with the middle one exactly 0, and th[i] = 2 * bits(e) for the
+  // positive edges e in ascending order (see the bucketize comment).
+  int sym;
+  uint32_t th[7];
 };
 
 hipError_t launch_orbit_quantize(const float* W, int64_t rows, int64_t d, int bits,
