@@ -1,25 +1,27 @@
 """Throughput of the randomized-Hadamard + Lloyd-Max codecs on one MI355X.
 
-Headline (`value`): the TQ3 hot path on one layer of KV cache. A step
-quantizes K and V ([32768 tokens, 8 heads, 128] bf16 each, 262144 vectors
-per tensor) to 56-byte records and dequantizes both back to bf16; `value`
-counts vectors taken through that round trip per second (524288 per step).
-Inputs are resident in HBM before timing; steps rotate over buffer sets whose
-total size exceeds the 256 MB last-level cache, so every launch streams from
-HBM. The timed region is bracketed by device synchronisation and measured
-with HIP events on the launch stream.
+Headline (`value`): the TQ3 hot path on one layer of KV cache. K and V
+([32768 tokens, 8 heads, 128] bf16 each, 262144 vectors per tensor) sit in one
+[2, 32768, 8, 128] buffer, the layout paged KV caches use; a step quantizes
+the 524288 vectors to 56-byte records with one launch and dequantizes them
+back to bf16 with another. `value` counts vectors taken through that round
+trip per second. Inputs are resident in HBM before timing; steps rotate over
+buffer sets whose total size exceeds the 256 MB last-level cache, so every
+launch streams from HBM. The timed region is bracketed by device
+synchronisation and measured with HIP events on the launch stream.
 
 Also reported, each timed with HIP events over repeated launches:
   * kernels: per-kernel average duration and effective bandwidth
     (algorithmic bytes read + written) of the headline step;
-  * roofline: the dominant kernel of the step against peak HBM bandwidth,
-    with traffic from the committed rocprofv3 counter summary when it matches
-    the current kernel source;
-  * valu: the same kernel's vector-ALU issue rate (instructions per vector
-    from its code object) against the chip's non-packed VALU peak;
-  * secondary: steady-state rates on larger inputs -- 2^20 structured fp32
-    vectors quantized, 2^24 records dequantized to bf16, the 12288 x 3072
-    OrbitQuant weight at 2/3/4 bits -- and a device-to-device copy;
+  * roofline: the dominant kernel of the step against the vector-ALU peak
+    (it is issue-bound), with its HBM figures beside, and traffic from the
+    committed rocprofv3 counter summary when it matches the kernel source;
+  * valu: the same kernel's issued VALU lane-ops (from the committed
+    SQ_INSTS_VALU summary) against the same peak;
+  * secondary: the same layer with K and V as separate tensors (four
+    launches per step); 2^20 structured fp32 vectors; 2^24 records
+    dequantized to bf16; the 12288 x 3072 OrbitQuant weight at 2/3/4 bits;
+    a device-to-device copy;
   * cpu_baseline: the oracle on the host cores, on a bounded sample.
 """
 import argparse
@@ -59,8 +61,10 @@ ALG_OPS_PER_VECTOR = {
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    # The GPU idles at a low clock and takes some 20 ms of load to reach its
+    # sustained one: 300 warmup steps (~25 ms) come before the timed region.
+    p.add_argument("--steps", type=int, default=500)
+    p.add_argument("--warmup", type=int, default=300)
     p.add_argument("--sets", type=int, default=4, help="rotating buffer sets")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -83,7 +87,7 @@ class Timer:
     def __init__(self, stream):
         self.stream = stream
 
-    def run(self, fn, iters, warmup=2):
+    def run(self, fn, iters, warmup=5):
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
@@ -161,6 +165,32 @@ def secondary(tq, timer, dev, signs, mask):
     out = {}
     L = tq.lib
     sp = tq._stream(torch.empty(1, device=dev))
+
+    # the KV layer with K and V as separate tensors: four launches per step
+    kc, vc = datagen.kv_cache("K"), datagen.kv_cache("V")
+    n = kc.numel() // 128
+    bufs = [dict(k=kc.to(dev), v=vc.to(dev),
+                 rk=torch.empty((n, REC), dtype=torch.uint8, device=dev),
+                 rv=torch.empty((n, REC), dtype=torch.uint8, device=dev),
+                 ok=torch.empty((n, 128), dtype=torch.bfloat16, device=dev),
+                 ov=torch.empty((n, 128), dtype=torch.bfloat16, device=dev)) for _ in range(4)]
+    calls = []
+    for b in bufs:
+        calls.append([(L.tq3_quantize, (tq._ptr(b["k"]), tq.TQ_BF16, n, 128, mask, tq._ptr(b["rk"]), sp)),
+                      (L.tq3_quantize, (tq._ptr(b["v"]), tq.TQ_BF16, n, 128, mask, tq._ptr(b["rv"]), sp)),
+                      (L.tq3_dequantize, (tq._ptr(b["rk"]), n, mask, tq._ptr(b["ok"]), tq.TQ_BF16, 128, sp)),
+                      (L.tq3_dequantize, (tq._ptr(b["rv"]), n, mask, tq._ptr(b["ov"]), tq.TQ_BF16, 128, sp))])
+    it = [0]
+
+    def sep_step():
+        for f, a in calls[it[0] % 4]:
+            f(*a)
+        it[0] += 1
+    ms, _ = timer.run(sep_step, 40, warmup=8)
+    out["tq3_kv_layer_separate_tensors"] = {
+        "launches_per_step": 4, "vectors_per_step": 2 * n, "ms_per_step": ms,
+        "vectors_per_s": 2 * n / (ms * 1e-3), "GBps": rate(2 * n * 2 * (256 + REC), ms)}
+    del bufs, calls
 
     # device copy ceiling at the size of one KV tensor's quantize traffic
     nbytes = 256 << 20
@@ -254,44 +284,31 @@ def main():
         return
     k_cpu = datagen.kv_cache("K")
     v_cpu = datagen.kv_cache("V")
-    n = k_cpu.numel() // 128                       # vectors per tensor
+    # The layer's K and V live in one [2, tokens, heads, 128] buffer (the
+    # layout paged KV caches use), so one launch covers both tensors.
+    kv_cpu = torch.stack([k_cpu, v_cpu])
+    n = kv_cpu.numel() // 128                      # vectors per step (K and V)
 
     sets = []
     for _ in range(args.sets):
         sets.append({
-            "k": k_cpu.to(dev), "v": v_cpu.to(dev),
-            "rk": torch.empty((n, REC), dtype=torch.uint8, device=dev),
-            "rv": torch.empty((n, REC), dtype=torch.uint8, device=dev),
-            "ok": torch.empty((n, 128), dtype=torch.bfloat16, device=dev),
-            "ov": torch.empty((n, 128), dtype=torch.bfloat16, device=dev),
+            "kv": kv_cpu.to(dev),
+            "rec": torch.empty((n, REC), dtype=torch.uint8, device=dev),
+            "out": torch.empty(kv_cpu.shape, dtype=torch.bfloat16, device=dev),
         })
     stream = torch.cuda.current_stream(dev)
-    sp = tq._stream(sets[0]["k"])
+    sp = tq._stream(sets[0]["kv"])
     L = tq.lib
+    # launch arguments bound once per buffer set, so the timed loop does no
+    # more host work than two library calls per step
+    q_args = [(tq._ptr(b["kv"]), tq.TQ_BF16, n, 128, mask, tq._ptr(b["rec"]), sp) for b in sets]
+    d_args = [(tq._ptr(b["rec"]), n, mask, tq._ptr(b["out"]), tq.TQ_BF16, 128, sp) for b in sets]
+    fq, fd = L.tq3_quantize, L.tq3_dequantize
+    assert fq(*q_args[0]) == 0 and fd(*d_args[0]) == 0
 
-    def launch_q(x, r):
-        st = L.tq3_quantize(tq._ptr(x), tq.TQ_BF16, n, 128, mask, tq._ptr(r), sp)
-        assert st == 0, st
-
-    def launch_dq(r, y):
-        st = L.tq3_dequantize(tq._ptr(r), n, mask, tq._ptr(y), tq.TQ_BF16, 128, sp)
-        assert st == 0, st
-
-    def step(i, evs=None):
-        b = sets[i % len(sets)]
-        seq = [(launch_q, b["k"], b["rk"], "quantize"), (launch_q, b["v"], b["rv"], "quantize"),
-               (launch_dq, b["rk"], b["ok"], "dequantize"),
-               (launch_dq, b["rv"], b["ov"], "dequantize")]
-        for fn, a, o, name in seq:
-            if evs is None:
-                fn(a, o)
-                continue
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fn(a, o)
-            e1.record(stream)
-            evs.append((name, e0, e1))
+    def step(i):
+        fq(*q_args[i % len(sets)])
+        fd(*d_args[i % len(sets)])
 
     if args.profile:
         # reference kernel for scaling the HBM byte counters: copies 256 MiB
@@ -316,27 +333,52 @@ def main():
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
 
-    # per-kernel durations: the same steps again with events around each launch
+    # Per-kernel durations, two ways. In the step: the same steps again with an
+    # event before, between and after the two launches (each event costs a
+    # little). Alone: `steps` back-to-back launches of one kernel over the same
+    # rotating buffer sets, bracketed by one pair of events -- the figure the
+    # roofline uses. (Dequantize alone runs slower than in the step, where it
+    # reads records the quantize launch has just left in the last-level cache
+    # and its writes drain while the next quantize computes.)
+    in_step = {"quantize": [], "dequantize": []}
+    torch.cuda.synchronize()
     evs = []
-    torch.cuda.synchronize()
     for i in range(args.steps):
-        step(i, evs)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        fq(*q_args[i % len(sets)])
+        e[1].record(stream)
+        fd(*d_args[i % len(sets)])
+        e[2].record(stream)
+        evs.append(e)
     torch.cuda.synchronize()
+    for e in evs:
+        in_step["quantize"].append(e[0].elapsed_time(e[1]))
+        in_step["dequantize"].append(e[1].elapsed_time(e[2]))
     per = {}
-    for name, e0, e1 in evs:
-        per.setdefault(name, []).append(e0.elapsed_time(e1))
+    for name, f, a in (("quantize", fq, q_args), ("dequantize", fd, d_args)):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            f(*a[i % len(sets)])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per[name] = (e0.elapsed_time(e1) / args.steps, args.steps)
     bytes_per_vec = {"quantize": 128 * 2 + REC, "dequantize": REC + 128 * 2}
     kernels = {}
-    for name, times in per.items():
-        avg = sum(times) / len(times)
+    for name, (avg, count) in per.items():
         gbs = rate(bytes_per_vec[name] * n, avg)
+        st = sum(in_step[name]) / len(in_step[name])
         kernels[name] = {"kernel": f"tq3_{name}_kernel<bf16>", "avg_ms": avg,
-                         "launches": len(times), "bytes_per_vector": bytes_per_vec[name],
-                         "vectors_per_launch": n, "GBps": gbs, "frac_peak_hbm": gbs / PEAK_HBM_GBS}
+                         "launches": count, "bytes_per_vector": bytes_per_vec[name],
+                         "vectors_per_launch": n, "GBps": gbs, "frac_peak_hbm": gbs / PEAK_HBM_GBS,
+                         "in_step_avg_ms": st, "in_step_GBps": rate(bytes_per_vec[name] * n, st)}
     dom = max(kernels, key=lambda k: kernels[k]["avg_ms"])
-    vec_per_step = 2 * n
+    vec_per_step = n
     value = vec_per_step / (ms_step * 1e-3)
-    step_bytes = 2 * n * (bytes_per_vec["quantize"] + bytes_per_vec["dequantize"])
+    step_bytes = n * (bytes_per_vec["quantize"] + bytes_per_vec["dequantize"])
     eff_gbs = rate(step_bytes, ms_step)
 
     for name, k in kernels.items():
@@ -367,7 +409,9 @@ def main():
     import oracle
     b = sets[(args.steps - 1) % len(sets)]
     k32 = k_cpu.reshape(-1, 128)[:4096].to(torch.float32).numpy()
-    ok = bool((b["rk"][:4096].cpu().numpy() == oracle.tq3_quantize(k32, signs.numpy())).all())
+    v32 = v_cpu.reshape(-1, 128)[-4096:].to(torch.float32).numpy()
+    ok = bool((b["rec"][:4096].cpu().numpy() == oracle.tq3_quantize(k32, signs.numpy())).all()
+              and (b["rec"][-4096:].cpu().numpy() == oracle.tq3_quantize(v32, signs.numpy())).all())
 
     result = {
         "metric": METRIC, "value": value, "unit": "vectors/s", "n_gpus": 1,
@@ -375,8 +419,9 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "TQ3 round trip of one KV-cache layer: K and V, 32768 tokens x "
-                               "8 heads x 128 (262144 vectors each), bf16 in, 56-byte records, "
-                               "bf16 out",
+                               "8 heads x 128 (262144 vectors each) in one [2, 32768, 8, 128] "
+                               "bf16 buffer; one quantize launch to 56-byte records and one "
+                               "dequantize launch back to bf16 per step",
                    "vectors_per_step": vec_per_step, "buffer_sets": args.sets},
         "effective_GBps": eff_gbs, "pct_of_peak_hbm": 100.0 * eff_gbs / PEAK_HBM_GBS,
         "kernels": kernels,

@@ -31,15 +31,6 @@ int cu_count() {
   return g_cu_count[dev];
 }
 
-// Grid of 256-thread blocks for `units` independent work items handled
-// `per_block` at a time by grid-stride loops: enough blocks to fill every CU
-// several times over, never more than there is work for.
-int grid_for(int64_t units, int64_t per_block, int blocks_per_cu) {
-  const int64_t need = (units + per_block - 1) / per_block;
-  const int64_t cap = (int64_t)cu_count() * blocks_per_cu;
-  return (int)(need < cap ? need : cap);
-}
-
 bool valid_dtype(int dt) { return dt == TQ_F32 || dt == TQ_BF16 || dt == TQ_F16; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -107,8 +98,7 @@ int tq3_quantize(const void* x, int x_dtype, int64_t n_vec, int64_t x_row_stride
   if (!aligned(x, 16) || !aligned(records, 8)) return TQ_ERR_ALIGN;
   tq::SignMask m;
   std::memcpy(m.w, sign_mask, sizeof(m.w));  // little-endian host
-  const int grid = grid_for(n_vec, tq::kTq3VecPerBlock, 8);
-  return launched(tq::launch_tq3_quantize(x, x_dtype, n_vec, x_row_stride, m, records, grid,
+  return launched(tq::launch_tq3_quantize(x, x_dtype, n_vec, x_row_stride, m, records, cu_count(),
                                           static_cast<hipStream_t>(stream)));
 }
 
@@ -123,8 +113,7 @@ int tq3_dequantize(const uint8_t* records, int64_t n_vec, const uint8_t* sign_ma
   if (!aligned(y, 16) || !aligned(records, 8)) return TQ_ERR_ALIGN;
   tq::SignMask m;
   std::memcpy(m.w, sign_mask, sizeof(m.w));
-  const int grid = grid_for(n_vec, tq::kTq3VecPerBlock, 8);
-  return launched(tq::launch_tq3_dequantize(records, n_vec, m, y, y_dtype, y_row_stride, grid,
+  return launched(tq::launch_tq3_dequantize(records, n_vec, m, y, y_dtype, y_row_stride, cu_count(),
                                             static_cast<hipStream_t>(stream)));
 }
 
@@ -173,9 +162,8 @@ int orbit_quantize_weight(const float* W, int64_t rows, int64_t d, int bits,
       !aligned(row_norms, 4))
     return TQ_ERR_ALIGN;
   const int wpb = tq::orbit_waves_per_block(d);
-  const int grid = grid_for(rows, wpb, 8);
   return launched(tq::launch_orbit_quantize(W, rows, d, bits, perm, signs, cb,
-                                            bit_order == TQ_LSB_FIRST, packed, row_norms, grid,
+                                            bit_order == TQ_LSB_FIRST, packed, row_norms, cu_count(),
                                             wpb, static_cast<hipStream_t>(stream)));
 }
 
@@ -195,10 +183,9 @@ int orbit_dequantize(const uint8_t* packed, const float* row_norms, int64_t rows
       (!rotated_only && (!aligned(inv_perm, 16) || !aligned(signs, 16))))
     return TQ_ERR_ALIGN;
   const int wpb = tq::orbit_waves_per_block(d);
-  const int grid = grid_for(rows, wpb, 8);
   return launched(tq::launch_orbit_dequantize(packed, row_norms, rows, d, bits, inv_perm, signs,
                                               cb, bit_order == TQ_LSB_FIRST, rotated_only,
-                                              W_out, out_dtype, grid, wpb,
+                                              W_out, out_dtype, cu_count(), wpb,
                                               static_cast<hipStream_t>(stream)));
 }
 

@@ -501,8 +501,10 @@ __global__ __launch_bounds__(256) void orbit_dequantize_kernel(
 template <int BITS, bool LSB, int NT>
 hipError_t launch_q(const float* W, int64_t rows, int d, int log2h, float kh,
                     const int32_t* perm, const int8_t* signs, const OrbitCodebook& cb,
-                    uint8_t* packed, float* norms, int grid, int wpb, hipStream_t s) {
+                    uint8_t* packed, float* norms, int cus, int wpb, hipStream_t s) {
   const size_t shm = (size_t)wpb * (d + kMaxBlocks) * sizeof(float);
+  const int per_cu = resident_blocks_per_cu(orbit_quantize_kernel<BITS, LSB, NT>, 64 * wpb, shm);
+  const int grid = grid_size((rows + wpb - 1) / wpb, cus, per_cu);
   orbit_quantize_kernel<BITS, LSB, NT><<<grid, 64 * wpb, shm, s>>>(W, rows, d, log2h, kh, perm,
                                                                   signs, cb, packed, norms);
   return hipGetLastError();
@@ -511,21 +513,24 @@ hipError_t launch_q(const float* W, int64_t rows, int d, int log2h, float kh,
 template <int BITS, bool LSB>
 hipError_t launch_q_nt(int nt, const float* W, int64_t rows, int d, int log2h, float kh,
                        const int32_t* perm, const int8_t* signs, const OrbitCodebook& cb,
-                       uint8_t* packed, float* norms, int grid, int wpb, hipStream_t s) {
+                       uint8_t* packed, float* norms, int cus, int wpb, hipStream_t s) {
   switch (nt) {
-    case 1: return launch_q<BITS, LSB, 1>(W, rows, d, log2h, kh, perm, signs, cb, packed, norms, grid, wpb, s);
-    case 2: return launch_q<BITS, LSB, 2>(W, rows, d, log2h, kh, perm, signs, cb, packed, norms, grid, wpb, s);
-    case 3: return launch_q<BITS, LSB, 3>(W, rows, d, log2h, kh, perm, signs, cb, packed, norms, grid, wpb, s);
-    default: return launch_q<BITS, LSB, 4>(W, rows, d, log2h, kh, perm, signs, cb, packed, norms, grid, wpb, s);
+    case 1: return launch_q<BITS, LSB, 1>(W, rows, d, log2h, kh, perm, signs, cb, packed, norms, cus, wpb, s);
+    case 2: return launch_q<BITS, LSB, 2>(W, rows, d, log2h, kh, perm, signs, cb, packed, norms, cus, wpb, s);
+    case 3: return launch_q<BITS, LSB, 3>(W, rows, d, log2h, kh, perm, signs, cb, packed, norms, cus, wpb, s);
+    default: return launch_q<BITS, LSB, 4>(W, rows, d, log2h, kh, perm, signs, cb, packed, norms, cus, wpb, s);
   }
 }
 
 template <int BITS, bool LSB, int DT, int NT>
 hipError_t launch_dq(const uint8_t* packed, const float* norms, int64_t rows, int d, int log2h,
                      float kh, const int32_t* inv_perm, const int8_t* signs,
-                     const OrbitCodebook& cb, int rotated_only, void* out, int grid, int wpb,
+                     const OrbitCodebook& cb, int rotated_only, void* out, int cus, int wpb,
                      hipStream_t s) {
   const size_t shm = (size_t)wpb * (d + kMaxBlocks) * sizeof(float);
+  const int per_cu =
+      resident_blocks_per_cu(orbit_dequantize_kernel<BITS, LSB, DT, NT>, 64 * wpb, shm);
+  const int grid = grid_size((rows + wpb - 1) / wpb, cus, per_cu);
   orbit_dequantize_kernel<BITS, LSB, DT, NT><<<grid, 64 * wpb, shm, s>>>(
       packed, norms, rows, d, log2h, kh, inv_perm, signs, cb, rotated_only, out);
   return hipGetLastError();
@@ -534,10 +539,10 @@ hipError_t launch_dq(const uint8_t* packed, const float* norms, int64_t rows, in
 template <int BITS, bool LSB, int DT>
 hipError_t launch_dq_nt(int nt, const uint8_t* packed, const float* norms, int64_t rows, int d,
                         int log2h, float kh, const int32_t* inv_perm, const int8_t* signs,
-                        const OrbitCodebook& cb, int rotated_only, void* out, int grid,
+                        const OrbitCodebook& cb, int rotated_only, void* out, int cus,
                         int wpb, hipStream_t s) {
 #define TQ_DQN(N) launch_dq<BITS, LSB, DT, N>(packed, norms, rows, d, log2h, kh, inv_perm, signs, \
-                                              cb, rotated_only, out, grid, wpb, s)
+                                              cb, rotated_only, out, cus, wpb, s)
   switch (nt) {
     case 1: return TQ_DQN(1);
     case 2: return TQ_DQN(2);
@@ -550,18 +555,18 @@ hipError_t launch_dq_nt(int nt, const uint8_t* packed, const float* norms, int64
 template <int BITS, bool LSB>
 hipError_t launch_dq_dt(int dt, int nt, const uint8_t* packed, const float* norms, int64_t rows,
                         int d, int log2h, float kh, const int32_t* inv_perm, const int8_t* signs,
-                        const OrbitCodebook& cb, int rotated_only, void* out, int grid,
+                        const OrbitCodebook& cb, int rotated_only, void* out, int cus,
                         int wpb, hipStream_t s) {
   switch (dt) {
     case DT_F32:
       return launch_dq_nt<BITS, LSB, DT_F32>(nt, packed, norms, rows, d, log2h, kh, inv_perm,
-                                             signs, cb, rotated_only, out, grid, wpb, s);
+                                             signs, cb, rotated_only, out, cus, wpb, s);
     case DT_BF16:
       return launch_dq_nt<BITS, LSB, DT_BF16>(nt, packed, norms, rows, d, log2h, kh, inv_perm,
-                                              signs, cb, rotated_only, out, grid, wpb, s);
+                                              signs, cb, rotated_only, out, cus, wpb, s);
     default:
       return launch_dq_nt<BITS, LSB, DT_F16>(nt, packed, norms, rows, d, log2h, kh, inv_perm,
-                                             signs, cb, rotated_only, out, grid, wpb, s);
+                                             signs, cb, rotated_only, out, cus, wpb, s);
   }
 }
 
@@ -580,13 +585,13 @@ int orbit_waves_per_block(int64_t d) {
 hipError_t launch_orbit_quantize(const float* W, int64_t rows, int64_t d, int bits,
                                  const int32_t* perm, const int8_t* signs,
                                  const OrbitCodebook& cb, int lsb_first, uint8_t* packed,
-                                 float* norms, int grid, int wpb, hipStream_t s) {
+                                 float* norms, int cus, int wpb, hipStream_t s) {
   const int64_t h = d & -d;
   const int log2h = ilog2(h);
   const float kh = (float)pow((double)h, -0.5);
   const int di = (int)d;
   const int nt = (di + 1023) >> 10;  // tiles of 64 lanes x 16 elements
-#define TQ_Q(B, O) launch_q_nt<B, O>(nt, W, rows, di, log2h, kh, perm, signs, cb, packed, norms, grid, wpb, s)
+#define TQ_Q(B, O) launch_q_nt<B, O>(nt, W, rows, di, log2h, kh, perm, signs, cb, packed, norms, cus, wpb, s)
   if (lsb_first) {
     if (bits == 2) return TQ_Q(2, true);
     if (bits == 3) return TQ_Q(3, true);
@@ -601,7 +606,7 @@ hipError_t launch_orbit_quantize(const float* W, int64_t rows, int64_t d, int bi
 hipError_t launch_orbit_dequantize(const uint8_t* packed, const float* norms, int64_t rows,
                                    int64_t d, int bits, const int32_t* inv_perm,
                                    const int8_t* signs, const OrbitCodebook& cb, int lsb_first,
-                                   int rotated_only, void* out, int dt, int grid, int wpb,
+                                   int rotated_only, void* out, int dt, int cus, int wpb,
                                    hipStream_t s) {
   const int64_t h = d & -d;
   const int log2h = ilog2(h);
@@ -609,7 +614,7 @@ hipError_t launch_orbit_dequantize(const uint8_t* packed, const float* norms, in
   const int di = (int)d;
   const int nt = (di + 1023) >> 10;
 #define TQ_DQ(B, O) \
-  launch_dq_dt<B, O>(dt, nt, packed, norms, rows, di, log2h, kh, inv_perm, signs, cb, rotated_only, out, grid, wpb, s)
+  launch_dq_dt<B, O>(dt, nt, packed, norms, rows, di, log2h, kh, inv_perm, signs, cb, rotated_only, out, cus, wpb, s)
   if (lsb_first) {
     if (bits == 2) return TQ_DQ(2, true);
     if (bits == 3) return TQ_DQ(3, true);

@@ -26,6 +26,8 @@ namespace {
 
 static_assert(kTq3VecPerBlock == 64, "a 256-thread block carries 64 vectors, one per quad");
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // fp32 of the page's printed centroid table (doubles rounded to float32).
 __device__ __forceinline__ float tq3_centroid(int k) {
   constexpr float c[8] = {(float)-0.9816, (float)-0.6168, (float)-0.3479, (float)-0.1129,
@@ -67,18 +69,27 @@ struct Loader<DT_F32> {
 #pragma unroll
       for (int i = 0; i < 8; ++i) sm[g][i] = sign_bit(m, q, g, i) << 31;
   }
-  // x: signed input (sign flips applied), used for both the norm and u
-  __device__ __forceinline__ void load(const void* base, int64_t row, int64_t stride, int q,
-                                       float (&x)[4][8]) const {
+  // Raw 16-byte chunks of this lane's 32 elements of one row.
+  struct Raw {
+    u32x4 c[8];
+  };
+  __device__ __forceinline__ Raw fetch(const void* base, int64_t row, int64_t stride,
+                                       int q) const {
     const float* r = static_cast<const float*>(base) + row * stride + 8 * q;
+    Raw raw;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const uint4 a = *reinterpret_cast<const uint4*>(r + 32 * g);
-      const uint4 b = *reinterpret_cast<const uint4*>(r + 32 * g + 4);
-      const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[g][i] = as_f(w[i] ^ sm[g][i]);
+      raw.c[2 * g] = *reinterpret_cast<const u32x4*>(r + 32 * g);
+      raw.c[2 * g + 1] = *reinterpret_cast<const u32x4*>(r + 32 * g + 4);
     }
+    return raw;
+  }
+  // x: signed input (sign flips applied), used for both the norm and u
+  __device__ __forceinline__ void convert(const Raw& raw, float (&x)[4][8]) const {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[g][i] = as_f(raw.c[2 * g + (i >> 2)][i & 3] ^ sm[g][i]);
   }
 };
 
@@ -94,12 +105,21 @@ struct Loader16 {
       for (int p = 0; p < 4; ++p)
         sm[g][p] = (sign_bit(m, q, g, 2 * p) << 15) | (sign_bit(m, q, g, 2 * p + 1) << 31);
   }
-  __device__ __forceinline__ void load(const void* base, int64_t row, int64_t stride, int q,
-                                       float (&x)[4][8]) const {
+  struct Raw {
+    u32x4 c[4];
+  };
+  __device__ __forceinline__ Raw fetch(const void* base, int64_t row, int64_t stride,
+                                       int q) const {
     const uint16_t* r = static_cast<const uint16_t*>(base) + row * stride + 8 * q;
+    Raw raw;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) raw.c[g] = *reinterpret_cast<const u32x4*>(r + 32 * g);
+    return raw;
+  }
+  __device__ __forceinline__ void convert(const Raw& raw, float (&x)[4][8]) const {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const uint4 a = *reinterpret_cast<const uint4*>(r + 32 * g);
+      const u32x4 a = raw.c[g];
       const uint32_t w[4] = {a.x ^ sm[g][0], a.y ^ sm[g][1], a.z ^ sm[g][2], a.w ^ sm[g][3]};
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
@@ -174,7 +194,10 @@ __device__ __forceinline__ LaneSigns lane_signs(int q) {
 
 // ------------------------------------------------------------ quantize ---
 
-template <int DT>
+// PF: software-pipelined loop -- the next vector's loads are issued before
+// the current one is processed (worth it once every wave runs many
+// iterations; the clamped fetch past the end re-reads the current row).
+template <int DT, bool PF>
 __global__ __launch_bounds__(256) void tq3_quantize_kernel(const void* __restrict__ x,
                                                            int64_t n_vec, int64_t stride,
                                                            SignMask mask,
@@ -186,10 +209,18 @@ __global__ __launch_bounds__(256) void tq3_quantize_kernel(const void* __restric
   const float kq = ls.sigma * kInvSqrt128;
 
   const int64_t step = (int64_t)gridDim.x * kTq3VecPerBlock;
-  for (int64_t v = (int64_t)blockIdx.x * kTq3VecPerBlock + (threadIdx.x >> 2); v < n_vec;
-       v += step) {
+  int64_t v = (int64_t)blockIdx.x * kTq3VecPerBlock + (threadIdx.x >> 2);
+  typename Loader<DT>::Raw nxt;
+  if (PF && v < n_vec) nxt = ld.fetch(x, v, stride, q);
+  for (; v < n_vec; v += step) {
     float x_[4][8];
-    ld.load(x, v, stride, q, x_);
+    if constexpr (PF) {
+      const typename Loader<DT>::Raw cur = nxt;
+      nxt = ld.fetch(x, v + step < n_vec ? v + step : v, stride, q);
+      ld.convert(cur, x_);
+    } else {
+      ld.convert(ld.fetch(x, v, stride, q), x_);
+    }
 
     // Sum of squares: bits 0..2 in registers, 3..4 across the quad, 5..6 in
     // registers -- the reference tree's bit order.
@@ -337,7 +368,7 @@ __device__ __forceinline__ void store_row(void* base, int64_t row, int64_t strid
   }
 }
 
-template <int DT>
+template <int DT, bool PF>
 __global__ __launch_bounds__(256) void tq3_dequantize_kernel(const uint8_t* __restrict__ rec,
                                                              int64_t n_vec, SignMask mask,
                                                              void* __restrict__ y,
@@ -362,16 +393,38 @@ __global__ __launch_bounds__(256) void tq3_dequantize_kernel(const uint8_t* __re
   const uint32_t shift = (24u * q) & 31u;
 
   const int64_t step = (int64_t)gridDim.x * kTq3VecPerBlock;
-  for (int64_t v = (int64_t)blockIdx.x * kTq3VecPerBlock + quad; v < n_vec; v += step) {
-    const uint32_t* r32 = reinterpret_cast<const uint32_t*>(rec + v * 56);
-    uint32_t chunk[4];
+  // This lane's words of a record: two dwords per 24-bit group, norm/scale.
+  struct RecRaw {
+    uint32_t lo[4], hi[4];
+    uint2 ns;
+  };
+  auto fetch = [&](int64_t vv) {
+    RecRaw rr;
+    const uint32_t* r32 = reinterpret_cast<const uint32_t*>(rec + vv * 56);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const uint32_t lo = r32[3 * g + dsel];
-      const uint32_t hi = r32[3 * g + dsel + 1];
-      chunk[g] = (uint32_t)((((uint64_t)hi << 32) | lo) >> shift) & 0xffffffu;
+      rr.lo[g] = r32[3 * g + dsel];
+      rr.hi[g] = r32[3 * g + dsel + 1];
     }
-    const uint2 ns = *reinterpret_cast<const uint2*>(rec + v * 56 + 48);
+    rr.ns = *reinterpret_cast<const uint2*>(rec + vv * 56 + 48);
+    return rr;
+  };
+  int64_t v = (int64_t)blockIdx.x * kTq3VecPerBlock + quad;
+  RecRaw nxt;
+  if (PF && v < n_vec) nxt = fetch(v);
+  for (; v < n_vec; v += step) {
+    RecRaw cur;
+    if constexpr (PF) {
+      cur = nxt;
+      nxt = fetch(v + step < n_vec ? v + step : v);
+    } else {
+      cur = fetch(v);
+    }
+    uint32_t chunk[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      chunk[g] = (uint32_t)((((uint64_t)cur.hi[g] << 32) | cur.lo[g]) >> shift) & 0xffffffu;
+    const uint2 ns = cur.ns;
     const float norm = as_f(ns.x), scale = as_f(ns.y);
 
     tbl[quad][2 * q] = c_even * scale;
@@ -409,36 +462,59 @@ __global__ __launch_bounds__(256) void tq3_dequantize_kernel(const uint8_t* __re
 
 // ------------------------------------------------------------- launchers ---
 
-hipError_t launch_tq3_quantize(const void* x, int dt, int64_t n_vec, int64_t stride,
-                               const SignMask& m, uint8_t* rec, int grid, hipStream_t s) {
-  switch (dt) {
-    case DT_F32:
-      tq3_quantize_kernel<DT_F32><<<grid, 256, 0, s>>>(x, n_vec, stride, m, rec);
-      break;
-    case DT_BF16:
-      tq3_quantize_kernel<DT_BF16><<<grid, 256, 0, s>>>(x, n_vec, stride, m, rec);
-      break;
-    default:
-      tq3_quantize_kernel<DT_F16><<<grid, 256, 0, s>>>(x, n_vec, stride, m, rec);
-      break;
+// Iterations per wave from which the software-pipelined kernels pay off.
+#ifndef TQ3_PIPELINE_MIN_ITERS
+#define TQ3_PIPELINE_MIN_ITERS 16
+#endif
+
+template <int DT>
+hipError_t tq3_q(const void* x, int64_t n_vec, int64_t stride, const SignMask& m, uint8_t* rec,
+                 int cus, hipStream_t s) {
+  static const int per_cu = resident_blocks_per_cu(tq3_quantize_kernel<DT, false>, 256, 0);
+  static const int per_cu_pf = resident_blocks_per_cu(tq3_quantize_kernel<DT, true>, 256, 0);
+  const int64_t need = (n_vec + kTq3VecPerBlock - 1) / kTq3VecPerBlock;
+  const int grid_pf = grid_size(need, cus, per_cu_pf);
+  if (need >= (int64_t)grid_pf * TQ3_PIPELINE_MIN_ITERS) {
+    tq3_quantize_kernel<DT, true><<<grid_pf, 256, 0, s>>>(x, n_vec, stride, m, rec);
+  } else {
+    tq3_quantize_kernel<DT, false><<<grid_size(need, cus, per_cu), 256, 0, s>>>(x, n_vec, stride,
+                                                                                m, rec);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_tq3_dequantize(const uint8_t* rec, int64_t n_vec, const SignMask& m,
-                                 void* y, int dt, int64_t stride, int grid, hipStream_t s) {
-  switch (dt) {
-    case DT_F32:
-      tq3_dequantize_kernel<DT_F32><<<grid, 256, 0, s>>>(rec, n_vec, m, y, stride);
-      break;
-    case DT_BF16:
-      tq3_dequantize_kernel<DT_BF16><<<grid, 256, 0, s>>>(rec, n_vec, m, y, stride);
-      break;
-    default:
-      tq3_dequantize_kernel<DT_F16><<<grid, 256, 0, s>>>(rec, n_vec, m, y, stride);
-      break;
+template <int DT>
+hipError_t tq3_dq(const uint8_t* rec, int64_t n_vec, const SignMask& m, void* y, int64_t stride,
+                  int cus, hipStream_t s) {
+  static const int per_cu = resident_blocks_per_cu(tq3_dequantize_kernel<DT, false>, 256, 0);
+  static const int per_cu_pf = resident_blocks_per_cu(tq3_dequantize_kernel<DT, true>, 256, 0);
+  const int64_t need = (n_vec + kTq3VecPerBlock - 1) / kTq3VecPerBlock;
+  const int grid_pf = grid_size(need, cus, per_cu_pf);
+  if (need >= (int64_t)grid_pf * TQ3_PIPELINE_MIN_ITERS) {
+    tq3_dequantize_kernel<DT, true><<<grid_pf, 256, 0, s>>>(rec, n_vec, m, y, stride);
+  } else {
+    tq3_dequantize_kernel<DT, false><<<grid_size(need, cus, per_cu), 256, 0, s>>>(rec, n_vec, m,
+                                                                                  y, stride);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_tq3_quantize(const void* x, int dt, int64_t n_vec, int64_t stride,
+                               const SignMask& m, uint8_t* rec, int cus, hipStream_t s) {
+  switch (dt) {
+    case DT_F32: return tq3_q<DT_F32>(x, n_vec, stride, m, rec, cus, s);
+    case DT_BF16: return tq3_q<DT_BF16>(x, n_vec, stride, m, rec, cus, s);
+    default: return tq3_q<DT_F16>(x, n_vec, stride, m, rec, cus, s);
+  }
+}
+
+hipError_t launch_tq3_dequantize(const uint8_t* rec, int64_t n_vec, const SignMask& m, void* y,
+                                 int dt, int64_t stride, int cus, hipStream_t s) {
+  switch (dt) {
+    case DT_F32: return tq3_dq<DT_F32>(rec, n_vec, m, y, stride, cus, s);
+    case DT_BF16: return tq3_dq<DT_BF16>(rec, n_vec, m, y, stride, cus, s);
+    default: return tq3_dq<DT_F16>(rec, n_vec, m, y, stride, cus, s);
+  }
 }
 
 }  // namespace tq

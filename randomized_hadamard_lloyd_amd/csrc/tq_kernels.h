@@ -18,10 +18,14 @@ struct SignMask {
 // (a 4-lane quad owns one vector).
 constexpr int kTq3VecPerBlock = 64;
 
+// Launchers take the device's compute-unit count `cus`: grids hold as many
+// blocks as the CUs keep resident at once (from the occupancy of the exact
+// kernel instantiation), never more than there is work for, and the kernels'
+// grid-stride loops spread the rest evenly.
 hipError_t launch_tq3_quantize(const void* x, int dt, int64_t n_vec, int64_t stride,
-                               const SignMask& m, uint8_t* rec, int grid, hipStream_t s);
+                               const SignMask& m, uint8_t* rec, int cus, hipStream_t s);
 hipError_t launch_tq3_dequantize(const uint8_t* rec, int64_t n_vec, const SignMask& m,
-                                 void* y, int dt, int64_t stride, int grid, hipStream_t s);
+                                 void* y, int dt, int64_t stride, int cus, hipStream_t s);
 
 // OrbitQuant weight codec.
 struct OrbitCodebook {
@@ -37,12 +41,26 @@ struct OrbitCodebook {
 hipError_t launch_orbit_quantize(const float* W, int64_t rows, int64_t d, int bits,
                                  const int32_t* perm, const int8_t* signs,
                                  const OrbitCodebook& cb, int lsb_first, uint8_t* packed,
-                                 float* norms, int grid, int wpb, hipStream_t s);
+                                 float* norms, int cus, int wpb, hipStream_t s);
 hipError_t launch_orbit_dequantize(const uint8_t* packed, const float* norms, int64_t rows,
                                    int64_t d, int bits, const int32_t* inv_perm,
                                    const int8_t* signs, const OrbitCodebook& cb,
                                    int lsb_first, int rotated_only, void* out, int dt,
-                                   int grid, int wpb, hipStream_t s);
+                                   int cus, int wpb, hipStream_t s);
+// Blocks of `kernel` that one CU keeps resident with `block` threads and
+// `shm` bytes of dynamic LDS (at least 1).
+template <typename K>
+inline int resident_blocks_per_cu(K kernel, int block, size_t shm) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, block, shm) != hipSuccess || n < 1)
+    n = 1;
+  return n;
+}
+inline int grid_size(int64_t need_blocks, int cus, int per_cu) {
+  const int64_t cap = (int64_t)(cus > 0 ? cus : 1) * per_cu;
+  return (int)(need_blocks < cap ? need_blocks : cap);
+}
+
 // Rows in flight per block (one per wave) for input dimension d: four, or
 // two when four rows' LDS staging would exceed 64 KB.
 int orbit_waves_per_block(int64_t d);

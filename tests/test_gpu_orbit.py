@@ -31,10 +31,11 @@ def edges_of(cb):
     return ((c[:-1] + c[1:]) / np.float32(2)).astype(np.float64)
 
 
-def check(tq, w, d, bits, msb=True, dtype=torch.float32, full_check=True):
+def check(tq, w, d, bits, msb=True, dtype=torch.float32, full_check=True, cb=None):
     perm, sg = datagen.rpbh_params(d)
     inv = torch.argsort(perm)
-    cb = tq.orbit_make_codebook(bits, d)
+    if cb is None:
+        cb = tq.orbit_make_codebook(bits, d)
     order = tq.TQ_MSB_FIRST if msb else tq.TQ_LSB_FIRST
     packed, norms = tq.orbit_quantize_weight(w.to(DEV), bits, perm.to(DEV), sg.to(DEV), cb,
                                              bit_order=order)
@@ -99,6 +100,39 @@ def test_orbit_edge_rows(tq):
     w[5, 100] = 50.0                 # outlier
     check(tq, w, d, 3)
     check(tq, w, d, 2, msb=False)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("msb", [True, False])
+def test_orbit_asymmetric_codebook(tq, bits, msb):
+    """Codebooks that are not mirror-symmetric take the general edge count (the
+    Gaussian ones take the symmetric compare): a shifted Gaussian codebook and
+    an uneven random ascending one."""
+    d = 3072
+    w = datagen.orbit_weight(rows=129, d=d, seed=20 + bits)
+    base = tq.orbit_make_codebook(bits, d)
+    shifted = base + np.float32(0.37) * (base[1] - base[0])
+    rng = np.random.default_rng(bits)
+    rand = torch.from_numpy(np.sort(rng.normal(0.0, 1.5 / np.sqrt(d), 1 << bits))
+                            .astype(np.float32))
+    for cb in (shifted, rand):
+        assert not all(cb[k] == -cb[len(cb) - 1 - k] for k in range(len(cb)))
+        check(tq, w, d, bits, msb, cb=cb)
+
+
+def test_orbit_exact_zero_coefficients(tq):
+    """Rows whose permuted, sign-flipped values are constant: every block's
+    transform is zero except its first coefficient, so most u are exactly 0
+    (the middle edge of a symmetric codebook; a tie that goes down) and the
+    division takes its plain IEEE path."""
+    d = 3072
+    perm, sg = datagen.rpbh_params(d)
+    inv = torch.argsort(perm)
+    c = torch.tensor([1.0, -2.0, 0.5, 3.0, -0.25, 1e-3])[:, None]
+    w = (c * sg[inv].to(torch.float32)[None, :]).contiguous()
+    for bits in (2, 3, 4):
+        check(tq, w, d, bits, True)
+        check(tq, w, d, bits, False)
 
 
 def test_orbit_errors(tq):
