@@ -245,112 +245,149 @@ __device__ __forceinline__ uint32_t sign_of(uint32_t w, int k) {
 
 // ------------------------------------------------------------- quantize ---
 
+// One block of NT waves per row (NT = ceil(d / 1024)): wave w holds the row's
+// elements [1024 w, 1024 w + 1024), lane l the 16 consecutive ones from
+// 16 (l + 64 w). The row is staged in LDS once per block and gathered through
+// the permutation, whose byte offsets (and the signs) each lane keeps in
+// registers for the whole kernel; the next row's loads are in flight while
+// the current one is processed.
 template <int BITS, bool LSB, int NT>
 __global__ __launch_bounds__(256) void orbit_quantize_kernel(
     const float* __restrict__ W, int64_t rows, int d, int log2h, float kh,
     const int32_t* __restrict__ perm, const int8_t* __restrict__ signs, OrbitCodebook cb,
     uint8_t* __restrict__ packed, float* __restrict__ norms) {
   extern __shared__ float lds[];
-  const int wpb = blockDim.x >> 6;  // rows in flight per block
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  float* rowbuf = lds + wave * (d + kMaxBlocks);
-  float* bsum = rowbuf + d;
-  const int nchunk = d >> 4;
+  float* rowbuf = lds;     // the row; later the cross-wave butterfly exchange
+  float* bsum = lds + d;   // block (or, for h > 1024, tile) sums of squares
+  constexpr int NTHR = 64 * NT;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c = lane + 64 * wave;  // this lane's chunk of 16 elements
+  const bool act = c < (d >> 4);
   const int nblk = d >> log2h;
   const int lb = log2h - 4 < 6 ? log2h - 4 : 6;
   const float ksig = kh * lane_sigma(log2h);
   const int64_t row_bytes = (int64_t)d * BITS / 8;
   const float eps = (float)1e-10;
+  const int nf4 = d >> 2;
 
-  for (int64_t r = (int64_t)blockIdx.x * wpb + wave; r < rows;
-       r += (int64_t)gridDim.x * wpb) {
-    // Row into LDS, coalesced.
-    const float4* src = reinterpret_cast<const float4*>(W + r * d);
-    for (int f = lane; f < (d >> 2); f += 64) reinterpret_cast<float4*>(rowbuf)[f] = src[f];
+  // Byte offsets into the staged row and sign masks of this lane's elements.
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  uint32_t poff[16], smask[16];
+  {
+    const int cc = act ? c : 0;  // inactive lanes read chunk 0 and never use it
+    const u32x4* pp = reinterpret_cast<const u32x4*>(perm + 16 * cc);
+    const u32x4 sv = *reinterpret_cast<const u32x4*>(signs + 16 * cc);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const u32x4 p = pp[k];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        poff[4 * k + e] = 4u * p[e];
+        smask[4 * k + e] = sign_of(sv[k], e);
+      }
+    }
+  }
+
+  // The next row, <= 4 x 16 bytes per thread (d <= 1024 NT). Loads past the
+  // row's end re-read its last 16 bytes (kept unconditional so the values
+  // stay in registers); only those below the end reach LDS.
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  f32x4 pre[4];
+  int fidx[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int f = tid + NTHR * k;
+    fidx[k] = f < nf4 ? f : nf4 - 1;
+  }
+  int64_t r = blockIdx.x;
+  {
+    const f32x4* src = reinterpret_cast<const f32x4*>(W + (r < rows ? r : 0) * d);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pre[k] = src[fidx[k]];
+  }
+  for (; r < rows; r += gridDim.x) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (tid + NTHR * k < nf4) reinterpret_cast<f32x4*>(rowbuf)[tid + NTHR * k] = pre[k];
+    __syncthreads();
+    {
+      const int64_t rn = r + gridDim.x < rows ? r + gridDim.x : r;
+      const f32x4* src = reinterpret_cast<const f32x4*>(W + rn * d);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) pre[k] = src[fidx[k]];
+    }
 
     // y_j = W[perm_j] * signs_j.
-    float y[NT][16];
+    float y[1][16];
+    const char* rb = reinterpret_cast<const char*>(rowbuf);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int c = lane + 64 * t;
-      if (c < nchunk) {
-        const int4* pp = reinterpret_cast<const int4*>(perm + 16 * c);
-        const uint4 sv = *reinterpret_cast<const uint4*>(signs + 16 * c);
-        const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+    for (int i = 0; i < 16; ++i)
+      y[0][i] = act ? as_f(*reinterpret_cast<const uint32_t*>(rb + poff[i]) ^ smask[i]) : 0.0f;
+
+    // Butterflies inside the wave (index bits 0..9), then across waves
+    // through LDS for blocks longer than 1024 (bits 10, 11): the lower tile
+    // takes a + b, the upper b' - a' = a - b with the same lazy lane sign.
+    fwht_rows<1>(y, log2h);
+    if (log2h > 10) {
+      float4* mine = reinterpret_cast<float4*>(rowbuf + 16 * c);
+#pragma unroll
+      for (int ht = 1; ht < NT; ht *= 2) {
+        if (log2h <= 9 + ht) break;
+        __syncthreads();  // everyone is done reading the row buffer
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          mine[k] = make_float4(y[0][4 * k], y[0][4 * k + 1], y[0][4 * k + 2], y[0][4 * k + 3]);
+        __syncthreads();
+        const float4* other = reinterpret_cast<const float4*>(rowbuf + 16 * (c ^ (64 * ht)));
+        const bool upper = (wave & ht) != 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const int4 p = pp[k];
-          const int pi[4] = {p.x, p.y, p.z, p.w};
+          const float4 o = other[k];
+          const float ov[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            y[t][4 * k + e] = as_f(as_u(rowbuf[pi[e]]) ^ sign_of(sw[k], e));
+          for (int e = 0; e < 4; ++e) {
+            const float a = y[0][4 * k + e];
+            y[0][4 * k + e] = upper ? ov[e] - a : a + ov[e];
+          }
         }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) y[t][i] = 0.0f;
       }
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) y[0][i] = y[0][i] * ksig;
 
-    fwht_rows<NT>(y, log2h);
+    // Sum of squares: bits 0-3 in registers, then the lane bits inside the
+    // block; block (h <= 1024) or tile (h > 1024) sums meet in LDS.
+    float s[16];
+    float amin = __builtin_fabsf(y[0][0]);
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) y[t][i] = y[t][i] * ksig;
-
-    // Sum of squares per block: bits 0-3 in registers, then the lane bits,
-    // then the tile bits.
-    float part[NT];
-    float amin = __builtin_inff();
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      float s[16];
-      float tmin = __builtin_fabsf(y[t][0]);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[i] = y[t][i] * y[t][i];
-        if (i > 0) tmin = __builtin_fminf(tmin, __builtin_fabsf(y[t][i]));
-      }
-      if (lane + 64 * t < nchunk) amin = __builtin_fminf(amin, tmin);
-#pragma unroll
-      for (int w = 1; w < 16; w *= 2)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2 * w) s[i] = s[i] + s[i + w];
-      part[t] = s[0];
+    for (int i = 0; i < 16; ++i) {
+      s[i] = y[0][i] * y[0][i];
+      if (i > 0) amin = __builtin_fminf(amin, __builtin_fabsf(y[0][i]));
     }
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (lb > 0) part[t] = lane_sum<0>(part[t]);
-      if (lb > 1) part[t] = lane_sum<1>(part[t]);
-      if (lb > 2) part[t] = lane_sum<2>(part[t]);
-      if (lb > 3) part[t] = lane_sum<3>(part[t]);
-      if (lb > 4) part[t] = lane_sum<4>(part[t]);
-      if (lb > 5) part[t] = lane_sum<5>(part[t]);
-    }
-    if constexpr (NT >= 2) {
-      if (log2h > 10) {
-        part[0] = part[0] + part[1];
-        if constexpr (NT == 4) part[2] = part[2] + part[3];
-      }
-    }
-    if constexpr (NT == 4) {
-      if (log2h > 11) part[0] = part[0] + part[2];
-    }
-    // Block sums to LDS (first lane of each block), then added left to right.
+    for (int w = 1; w < 16; w *= 2)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2 * w) s[i] = s[i] + s[i + w];
+    float part = s[0];
+    if (lb > 0) part = lane_sum<0>(part);
+    if (lb > 1) part = lane_sum<1>(part);
+    if (lb > 2) part = lane_sum<2>(part);
+    if (lb > 3) part = lane_sum<3>(part);
+    if (lb > 4) part = lane_sum<4>(part);
+    if (lb > 5) part = lane_sum<5>(part);
+    if (act && (c & ((1 << lb) - 1)) == 0) bsum[c >> lb] = part;  // one writer per block/tile
+    __syncthreads();
+    float total;
     if (log2h <= 10) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int c = lane + 64 * t;
-        if (c < nchunk && (c & ((1 << lb) - 1)) == 0) bsum[c >> lb] = part[t];
-      }
-    } else if (lane == 0) {
-      const int per = 1 << (log2h - 10);  // tiles per block
-#pragma unroll
-      for (int t = 0; t < NT; t += 2)
-        if ((t % per) == 0) bsum[t / per] = part[t];
+      total = bsum[0];
+      for (int bi = 1; bi < nblk; ++bi) total = total + bsum[bi];
+    } else if (log2h == 11) {
+      total = bsum[0] + bsum[1];
+    } else {
+      total = (bsum[0] + bsum[1]) + (bsum[2] + bsum[3]);
     }
-    float total = bsum[0];
-    for (int b = 1; b < nblk; ++b) total = total + bsum[b];
     const float norm = __builtin_sqrtf(total);
     const float denom = norm + eps;
 
@@ -359,31 +396,17 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
     if (amin >= denom * 0x1p-60f && denom <= 0x1p100f) {
       const Recip rd = make_recip(denom);
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) y[t][i] = div_rn(y[t][i], rd);
+      for (int i = 0; i < 16; ++i) y[0][i] = div_rn(y[0][i], rd);
     } else {
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) y[t][i] = y[t][i] / denom;
+      for (int i = 0; i < 16; ++i) y[0][i] = y[0][i] / denom;
     }
 
-    // Codes and packing (the codebook test is uniform: one branch per row).
-    uint64_t bytes[NT];
-    if (cb.sym) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) bytes[t] = pack16<BITS, LSB, true>(y[t], cb);
-    } else {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) bytes[t] = pack16<BITS, LSB, false>(y[t], cb);
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int c = lane + 64 * t;
-      if (c < nchunk) store_codes<BITS>(packed + r * row_bytes + 2 * BITS * c, bytes[t]);
-    }
-    if (lane == 0) norms[r] = norm;
+    // Codes and packing (the codebook test is uniform).
+    const uint64_t bytes =
+        cb.sym ? pack16<BITS, LSB, true>(y[0], cb) : pack16<BITS, LSB, false>(y[0], cb);
+    if (act) store_codes<BITS>(packed + r * row_bytes + 2 * BITS * c, bytes);
+    if (tid == 0) norms[r] = norm;
   }
 }
 
@@ -502,11 +525,12 @@ template <int BITS, bool LSB, int NT>
 hipError_t launch_q(const float* W, int64_t rows, int d, int log2h, float kh,
                     const int32_t* perm, const int8_t* signs, const OrbitCodebook& cb,
                     uint8_t* packed, float* norms, int cus, int wpb, hipStream_t s) {
-  const size_t shm = (size_t)wpb * (d + kMaxBlocks) * sizeof(float);
-  const int per_cu = resident_blocks_per_cu(orbit_quantize_kernel<BITS, LSB, NT>, 64 * wpb, shm);
-  const int grid = grid_size((rows + wpb - 1) / wpb, cus, per_cu);
-  orbit_quantize_kernel<BITS, LSB, NT><<<grid, 64 * wpb, shm, s>>>(W, rows, d, log2h, kh, perm,
-                                                                  signs, cb, packed, norms);
+  (void)wpb;
+  const size_t shm = (size_t)(d + kMaxBlocks) * sizeof(float);
+  const int per_cu = resident_blocks_per_cu(orbit_quantize_kernel<BITS, LSB, NT>, 64 * NT, shm);
+  const int grid = grid_size(rows, cus, per_cu);
+  orbit_quantize_kernel<BITS, LSB, NT><<<grid, 64 * NT, shm, s>>>(W, rows, d, log2h, kh, perm,
+                                                                 signs, cb, packed, norms);
   return hipGetLastError();
 }
 
