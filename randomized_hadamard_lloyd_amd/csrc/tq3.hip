@@ -361,6 +361,32 @@ __global__ __launch_bounds__(256) void tq3_quantize_kernel(const void* __restric
 
 // ---------------------------------------------------------- dequantize ---
 
+constexpr int kStageRow = 320;  // padded bytes per staged 16-bit output row
+
+// Two output values -> one dword of bf16 / fp16 (round to nearest even).
+template <int DT>
+__device__ __forceinline__ uint32_t narrow2(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 v = {a, b};
+  if constexpr (DT == DT_BF16) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
+  } else {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));
+  }
+}
+
+// Quad lane q's 32 narrowed values of one row into its padded staging row.
+template <int DT>
+__device__ __forceinline__ void stage_row16(uint8_t* row, int q, const float (&y)[4][8]) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    *reinterpret_cast<u32x4*>(row + g * 64 + q * 16) =
+        u32x4{narrow2<DT>(y[g][0], y[g][1]), narrow2<DT>(y[g][2], y[g][3]),
+              narrow2<DT>(y[g][4], y[g][5]), narrow2<DT>(y[g][6], y[g][7])};
+}
+
 template <int DT>
 __device__ __forceinline__ void store_row(void* base, int64_t row, int64_t stride, int q,
                                           const float (&y)[4][8]) {
@@ -403,6 +429,13 @@ __global__ __launch_bounds__(256) void tq3_dequantize_kernel(const uint8_t* __re
                                                              int64_t stride) {
   // Per-quad table of the 8 centroids times the record's scale.
   __shared__ float tbl[64][8];
+  // Per-wave staging of 16-bit outputs: 16 rows, each padded from 256 to 320
+  // bytes so that both the quad-ordered writes and the row-ordered reads are
+  // free of bank conflicts.
+  __shared__ __attribute__((aligned(16))) uint8_t ostage[4][16 * kStageRow];
+  uint8_t* ost = ostage[threadIdx.x >> 6];
+  const int olane = threadIdx.x & 63;
+  const int oqv = (threadIdx.x >> 2) & 15;
   const int q = threadIdx.x & 3;
   const int quad = threadIdx.x >> 2;
   const LaneSigns ls = lane_signs(q);
@@ -482,7 +515,22 @@ __global__ __launch_bounds__(256) void tq3_dequantize_kernel(const uint8_t* __re
 #pragma unroll
       for (int i = 0; i < 8; ++i) w[g][i] = (w[g][i] * kf[g][i]) * norm;
 
-    store_row<DT>(y, v, stride, q, w);
+    if (DT != DT_F32 && stride == 128 && (v - oqv) + 16 <= n_vec) {
+      // The wave's 16 consecutive contiguous rows (4 KB) leave as four fully
+      // coalesced 1 KB stores instead of sixteen 64-byte pieces per store.
+      stage_row16<DT>(ost + oqv * kStageRow, q, w);
+      __builtin_amdgcn_wave_barrier();
+      uint8_t* dst = static_cast<uint8_t*>(y) + (v - oqv) * 256;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int o = olane * 16 + k * 1024;
+        *reinterpret_cast<u32x4*>(dst + o) =
+            *reinterpret_cast<const u32x4*>(ost + (o >> 8) * kStageRow + (o & 255));
+      }
+      __builtin_amdgcn_wave_barrier();
+    } else {
+      store_row<DT>(y, v, stride, q, w);
+    }
   }
 }
 
