@@ -21,6 +21,7 @@ namespace tq {
 namespace {
 
 constexpr int kMaxBlocks = 128; // d / h <= 4096 / 32
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // ds_swizzle bit mode: inside each 32-lane half, lane i reads lane i ^ m.
 constexpr int bit_xor(int m) { return (m << 10) | 0x1F; }
@@ -412,17 +413,17 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
 
 // ----------------------------------------------------------- dequantize ---
 
+// 16 bytes of outputs (EPS = 4 fp32 or 8 bf16/fp16 values) at element j0.
 template <int DT>
-__device__ __forceinline__ void store16(void* out, int64_t off, const float (&v)[16]) {
+__device__ __forceinline__ void store_group(void* out, int64_t j0, const float* v) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   if constexpr (DT == DT_F32) {
-    float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + off);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) p[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+    *reinterpret_cast<u32x4*>(static_cast<float*>(out) + j0) =
+        u32x4{as_u(v[0]), as_u(v[1]), as_u(v[2]), as_u(v[3])};
   } else {
-    uint4* p = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + off);
-    uint32_t w[8];
+    uint32_t w[4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < 4; ++k) {
       typedef float f2 __attribute__((ext_vector_type(2)));
       const f2 pr = {v[2 * k], v[2 * k + 1]};
       if constexpr (DT == DT_BF16) {
@@ -433,11 +434,17 @@ __device__ __forceinline__ void store16(void* out, int64_t off, const float (&v)
         w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, h2));
       }
     }
-    p[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    p[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + j0) = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
+// One block of NT waves per row, wave w owning the row's elements
+// [1024 w, 1024 w + 1024). Codes are read in stream order (lane l: the 16
+// from 16 (l + 64 w)); outputs leave in coalesced 16-byte groups (lane l:
+// elements 1024 w + EPS l + 64 EPS k .. + EPS - 1, EPS values per 16 bytes),
+// re-read from LDS in that order -- through the inverse permutation when
+// the rotation is undone. The next row's codes and norm are loaded while the
+// current row is processed.
 template <int BITS, bool LSB, int DT, int NT>
 __global__ __launch_bounds__(256) void orbit_dequantize_kernel(
     const uint8_t* __restrict__ packed, const float* __restrict__ norms, int64_t rows, int d,
@@ -445,78 +452,134 @@ __global__ __launch_bounds__(256) void orbit_dequantize_kernel(
     const int8_t* __restrict__ signs, OrbitCodebook cb, int rotated_only,
     void* __restrict__ out) {
   extern __shared__ float lds[];
-  const int wpb = blockDim.x >> 6;  // rows in flight per block
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  float* rowbuf = lds + wave * (d + kMaxBlocks);
-  float* tab = rowbuf + d;  // 2^BITS codebook entries times the row norm
-  const int nchunk = d >> 4;
+  float* rowbuf = lds;  // d floats
+  constexpr int EPS = DT == DT_F32 ? 4 : 8;
+  constexpr int NG = 16 / EPS;  // 16-byte output groups per lane per tile
+  constexpr int L = 1 << BITS;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  float* tab = lds + d + 16 * wave;  // this wave's codebook x row norm
+  const int c = lane + 64 * wave;
+  const bool act = c < (d >> 4);
   const float ksig = kh * lane_sigma(log2h);
   const int64_t row_bytes = (int64_t)d * BITS / 8;
-  constexpr int L = 1 << BITS;
 
-  for (int64_t r = (int64_t)blockIdx.x * wpb + wave; r < rows;
-       r += (int64_t)gridDim.x * wpb) {
-    const float norm = norms[r];
-    if (lane < L) tab[lane] = cb.cb[lane] * norm;
-
-    float w[NT][16];
+  // Output groups of this lane and, when the rotation is undone, the byte
+  // offsets of their sources in the staged row and the signs of its chunk.
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  int j0[NG];
+  bool gact[NG];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int c = lane + 64 * t;
-      if (c < nchunk) {
-        uint32_t code[16];
-        unpack16<BITS, LSB>(load_codes<BITS>(packed + r * row_bytes + 2 * BITS * c), code);
+  for (int k = 0; k < NG; ++k) {
+    j0[k] = 1024 * wave + EPS * lane + 64 * EPS * k;
+    gact[k] = j0[k] < d;
+  }
+  uint32_t ioff[16], smask[16];
+  if (!rotated_only) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) w[t][i] = tab[code[i]];
-      } else {
+    for (int k = 0; k < NG; ++k) {
+      const u32x4* ip = reinterpret_cast<const u32x4*>(inv_perm + (gact[k] ? j0[k] : 0));
 #pragma unroll
-        for (int i = 0; i < 16; ++i) w[t][i] = 0.0f;
+      for (int e4 = 0; e4 < EPS / 4; ++e4) {
+        const u32x4 p = ip[e4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ioff[EPS * k + 4 * e4 + e] = 4u * p[e];
       }
     }
+    const u32x4 sv = *reinterpret_cast<const u32x4*>(signs + 16 * (act ? c : 0));
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) smask[4 * k + e] = sign_of(sv[k], e);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ioff[i] = smask[i] = 0;
+  }
+
+  int64_t r = blockIdx.x;
+  const int cc = act ? c : 0;
+  uint64_t ncodes = load_codes<BITS>(packed + (r < rows ? r : 0) * row_bytes + 2 * BITS * cc);
+  float nnorm = norms[r < rows ? r : 0];
+  for (; r < rows; r += gridDim.x) {
+    const uint64_t codes = ncodes;
+    const float norm = nnorm;
+    {
+      const int64_t rn = r + gridDim.x < rows ? r + gridDim.x : r;
+      ncodes = load_codes<BITS>(packed + rn * row_bytes + 2 * BITS * cc);
+      nnorm = norms[rn];
+    }
+    if (lane < L) tab[lane] = cb.cb[lane] * norm;
+    __builtin_amdgcn_wave_barrier();
+    uint32_t code[16];
+    unpack16<BITS, LSB>(codes, code);
+    float w[1][16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[0][i] = tab[code[i]];
 
     if (rotated_only) {
+      // Stage this wave's tile in element order, re-read it in store order.
+      if (act) {
+        f32x4_t* mine = reinterpret_cast<f32x4_t*>(rowbuf + 16 * c);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int c = lane + 64 * t;
-        if (c < nchunk) store16<DT>(out, r * d + 16 * c, w[t]);
+        for (int k = 0; k < 4; ++k)
+          mine[k] = f32x4_t{w[0][4 * k], w[0][4 * k + 1], w[0][4 * k + 2], w[0][4 * k + 3]};
       }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int k = 0; k < NG; ++k)
+        if (gact[k]) store_group<DT>(out, r * d + j0[k], rowbuf + j0[k]);
+      __builtin_amdgcn_wave_barrier();
       continue;
     }
 
-    // Inverse rotation: FWHT per block times h^-1/2, times signs_j, then
-    // out[i] = z[inv_perm_i] through LDS.
-    fwht_rows<NT>(w, log2h);
+    // Inverse rotation: FWHT per block (across waves through LDS beyond
+    // 1024), times h^-1/2 and the lazy lane sign, times signs_j.
+    fwht_rows<1>(w, log2h);
+    if (log2h > 10) {
+      f32x4_t* mine = reinterpret_cast<f32x4_t*>(rowbuf + 16 * c);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int c = lane + 64 * t;
-      if (c < nchunk) {
-        const uint4 sv = *reinterpret_cast<const uint4*>(signs + 16 * c);
-        const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
-        float z[16];
+      for (int ht = 1; ht < NT; ht *= 2) {
+        if (log2h <= 9 + ht) break;
+        __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 16; ++i) z[i] = as_f(as_u(w[t][i] * ksig) ^ sign_of(sw[i >> 2], i & 3));
-        float4* dst = reinterpret_cast<float4*>(rowbuf + 16 * c);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) dst[k] = make_float4(z[4 * k], z[4 * k + 1], z[4 * k + 2], z[4 * k + 3]);
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int c = lane + 64 * t;
-      if (c < nchunk) {
-        const int4* pp = reinterpret_cast<const int4*>(inv_perm + 16 * c);
-        float o[16];
+        for (int k = 0; k < 4; ++k)
+          mine[k] = f32x4_t{w[0][4 * k], w[0][4 * k + 1], w[0][4 * k + 2], w[0][4 * k + 3]};
+        __syncthreads();
+        const f32x4_t* other = reinterpret_cast<const f32x4_t*>(rowbuf + 16 * (c ^ (64 * ht)));
+        const bool upper = (wave & ht) != 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const int4 p = pp[k];
-          o[4 * k] = rowbuf[p.x];
-          o[4 * k + 1] = rowbuf[p.y];
-          o[4 * k + 2] = rowbuf[p.z];
-          o[4 * k + 3] = rowbuf[p.w];
+          const f32x4_t o = other[k];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float a = w[0][4 * k + e];
+            w[0][4 * k + e] = upper ? o[e] - a : a + o[e];
+          }
         }
-        store16<DT>(out, r * d + 16 * c, o);
       }
+    }
+    __syncthreads();  // the row buffer is free
+    if (act) {
+      f32x4_t* mine = reinterpret_cast<f32x4_t*>(rowbuf + 16 * c);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float z[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[e] = as_f(as_u(w[0][4 * k + e] * ksig) ^ smask[4 * k + e]);
+        mine[k] = f32x4_t{z[0], z[1], z[2], z[3]};
+      }
+    }
+    __syncthreads();
+    // out[j] = z[inv_perm_j], gathered from the staged row.
+    const char* rb = reinterpret_cast<const char*>(rowbuf);
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+      if (!gact[k]) continue;
+      float o[EPS];
+#pragma unroll
+      for (int e = 0; e < EPS; ++e) o[e] = *reinterpret_cast<const float*>(rb + ioff[EPS * k + e]);
+      store_group<DT>(out, r * d + j0[k], o);
     }
   }
 }
@@ -551,11 +614,12 @@ hipError_t launch_dq(const uint8_t* packed, const float* norms, int64_t rows, in
                      float kh, const int32_t* inv_perm, const int8_t* signs,
                      const OrbitCodebook& cb, int rotated_only, void* out, int cus, int wpb,
                      hipStream_t s) {
-  const size_t shm = (size_t)wpb * (d + kMaxBlocks) * sizeof(float);
+  (void)wpb;
+  const size_t shm = (size_t)(d + kMaxBlocks) * sizeof(float);
   const int per_cu =
-      resident_blocks_per_cu(orbit_dequantize_kernel<BITS, LSB, DT, NT>, 64 * wpb, shm);
-  const int grid = grid_size((rows + wpb - 1) / wpb, cus, per_cu);
-  orbit_dequantize_kernel<BITS, LSB, DT, NT><<<grid, 64 * wpb, shm, s>>>(
+      resident_blocks_per_cu(orbit_dequantize_kernel<BITS, LSB, DT, NT>, 64 * NT, shm);
+  const int grid = grid_size(rows, cus, per_cu);
+  orbit_dequantize_kernel<BITS, LSB, DT, NT><<<grid, 64 * NT, shm, s>>>(
       packed, norms, rows, d, log2h, kh, inv_perm, signs, cb, rotated_only, out);
   return hipGetLastError();
 }
