@@ -361,7 +361,17 @@ __global__ __launch_bounds__(256) void tq3_quantize_kernel(const void* __restric
 
 // ---------------------------------------------------------- dequantize ---
 
-constexpr int kStageRow = 320;  // padded bytes per staged 16-bit output row
+constexpr int kStageRow = 320;     // padded bytes per staged 16-bit output row
+constexpr int kStageRowF32 = 512;  // bytes per staged fp32 output row (XOR-swizzled)
+
+// Byte offset of byte o of staged fp32 row v: the 16-byte slot index is XORed
+// with the row's low two bits placed at slot bits 0 and 3, so that the 16
+// lanes of a quarter-wave hit 16 distinct 4-bank groups both when quads write
+// their 32-byte pieces and when lanes read consecutive 16-byte slots.
+__device__ __forceinline__ int f32_stage_off(int v, int o) {
+  const int sw = ((v & 1) | ((v & 2) << 2)) << 4;
+  return v * kStageRowF32 + (o ^ sw);
+}
 
 // Two output values -> one dword of bf16 / fp16 (round to nearest even).
 template <int DT>
@@ -432,7 +442,8 @@ __global__ __launch_bounds__(256) void tq3_dequantize_kernel(const uint8_t* __re
   // Per-wave staging of 16-bit outputs: 16 rows, each padded from 256 to 320
   // bytes so that both the quad-ordered writes and the row-ordered reads are
   // free of bank conflicts.
-  __shared__ __attribute__((aligned(16))) uint8_t ostage[4][16 * kStageRow];
+  __shared__ __attribute__((aligned(16)))
+  uint8_t ostage[4][16 * (DT == DT_F32 ? kStageRowF32 : kStageRow)];
   uint8_t* ost = ostage[threadIdx.x >> 6];
   const int olane = threadIdx.x & 63;
   const int oqv = (threadIdx.x >> 2) & 15;
@@ -515,7 +526,25 @@ __global__ __launch_bounds__(256) void tq3_dequantize_kernel(const uint8_t* __re
 #pragma unroll
       for (int i = 0; i < 8; ++i) w[g][i] = (w[g][i] * kf[g][i]) * norm;
 
-    if (DT != DT_F32 && stride == 128 && (v - oqv) + 16 <= n_vec) {
+    if (DT == DT_F32 && stride == 128 && (v - oqv) + 16 <= n_vec) {
+      // fp32 rows: the wave's 8 KB leave as eight coalesced 1 KB stores.
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          *reinterpret_cast<u32x4*>(ost + f32_stage_off(oqv, g * 128 + q * 32 + h * 16)) =
+              u32x4{as_u(w[g][4 * h]), as_u(w[g][4 * h + 1]), as_u(w[g][4 * h + 2]),
+                    as_u(w[g][4 * h + 3])};
+      __builtin_amdgcn_wave_barrier();
+      uint8_t* dst = static_cast<uint8_t*>(y) + (v - oqv) * 512;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int o = olane * 16 + k * 1024;
+        *reinterpret_cast<u32x4*>(dst + o) =
+            *reinterpret_cast<const u32x4*>(ost + f32_stage_off(o >> 9, o & 511));
+      }
+      __builtin_amdgcn_wave_barrier();
+    } else if (DT != DT_F32 && stride == 128 && (v - oqv) + 16 <= n_vec) {
       // The wave's 16 consecutive contiguous rows (4 KB) leave as four fully
       // coalesced 1 KB stores instead of sixteen 64-byte pieces per store.
       stage_row16<DT>(ost + oqv * kStageRow, q, w);

@@ -157,6 +157,55 @@ def test_edge_vectors(tq, signs):
     check_dequantize(tq, g, signs, torch.bfloat16)
 
 
+def near_boundary_vectors(n, signs, seed):
+    """Vectors whose scaled coefficients land on or within a few ulps of the
+    decision boundaries: target coefficients t (max |t| = 1) are chosen
+    there, and the input is the fp64 inverse of the transform applied to
+    t / |t|, rounded to fp32 (the fp32 forward pass then moves each
+    coefficient by a few ulps around its target)."""
+    from scipy.linalg import hadamard
+    rng = np.random.default_rng(seed)
+    b = np.array([0.2304, 0.4824, 0.7992], dtype=np.float32)
+    cand = [np.float32(0.0)]
+    for v in b:
+        x = v
+        for _ in range(4):
+            cand.append(x)
+            x = np.nextafter(x, np.float32(1))
+        x = np.nextafter(v, np.float32(0))
+        for _ in range(3):
+            cand.append(x)
+            x = np.nextafter(x, np.float32(0))
+    cand = np.array(cand, dtype=np.float64)
+    h = hadamard(128).astype(np.float64) / np.sqrt(128.0)
+    s = np.asarray(signs, dtype=np.float64).reshape(128)
+    out = np.empty((n, 128), dtype=np.float32)
+    for r in range(n):
+        t = rng.choice(cand, 128) * rng.choice([-1.0, 1.0], 128)
+        k = rng.integers(0, 128, 8)
+        t[k] = rng.uniform(-1, 1, 8)                # some unconstrained values
+        t[rng.integers(0, 128)] = rng.choice([-1.0, 1.0])
+        y = t / np.linalg.norm(t)
+        out[r] = (h @ y) * s * rng.uniform(0.5, 4.0)
+    return torch.from_numpy(out)
+
+
+def test_near_boundary_stress(tq, signs):
+    """Thousands of coefficients on or next to a boundary (ties included):
+    the index decision must match the oracle's IEEE division exactly."""
+    x = near_boundary_vectors(4096 + 37, signs.numpy(), seed=12)
+    xs = oracle.tq3_scaled_coeffs(x.numpy(), signs)
+    b = np.array([0.2304, 0.4824, 0.7992], dtype=np.float32)
+    a = np.abs(xs)
+    near = np.zeros(a.shape, dtype=bool)
+    for v in b:
+        near |= np.abs(a - v) <= 4 * np.spacing(v)
+    ties = np.isin(a, b)
+    assert near.mean() > 0.2 and ties.sum() > 1000, (near.mean(), ties.sum())
+    g, _ = check_quantize(tq, x, signs)
+    check_dequantize(tq, g, signs, torch.float32)
+
+
 def test_empty_and_errors(tq, signs):
     x = torch.zeros((0, 128), device=DEV)
     assert tq.tq3_quantize(x, signs).shape == (0, 1, 56)
