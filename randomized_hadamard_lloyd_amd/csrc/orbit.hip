@@ -2,17 +2,16 @@
 // toolkit/util/orbit_quant.py": rpbh_forward, _quantize_rows,
 // _dequantize_rotated, dequantize.
 //
-// Work mapping. One wave owns one weight row at a time (a 256-thread block
-// keeps four rows in flight). The row (d <= 4096 fp32) is first copied into
-// LDS with coalesced 16-byte loads, then each lane gathers its elements
-// through the permutation. Lane l holds the 16-element chunks c = l + 64t
-// (t = 0..3), element j = 16c + i: index bits 0-3 are register bits (i),
-// bits 4-9 are lane bits, bits 10-11 are tile bits (t). FWHT stages run in
-// the order 1, 2, 4, ..., h/2: in registers for bits 0-3, across lanes for
-// bits 4-9 (ds_swizzle / ds_bpermute plus one fmac, with the lazy lane sign
-// described in tq3.hip), in registers again for bits 10-11. The row norm's
-// sum of squares follows the same bit order inside each h-block; block sums
-// are then added left to right.
+// Work mapping. One block of NT = ceil(d / 1024) waves owns one weight row
+// at a time; wave w holds the row's elements [1024 w, 1024 w + 1024) as 64
+// chunks of 16, one chunk per lane (see lane_chunk for which lane holds
+// which). Element j = 16 c + i of chunk c: index bits 0-3 are register bits,
+// bits 4-9 chunk bits inside the wave, bits 10-11 the wave. FWHT stages run
+// in the order 1, 2, 4, ..., h/2: in registers for bits 0-3; across lanes
+// without LDS for bits 4-9 (DPP fmac with the lazy lane sign described in
+// tq3.hip for bits 4-7, permlane16/32 swaps for bits 8 and 9); across waves
+// through LDS for bits 10-11. The row norm's sum of squares follows the same
+// bit order inside each h-block; block sums are then added left to right.
 #include "tq_common.h"
 #include "tq_kernels.h"
 
@@ -23,81 +22,98 @@ namespace {
 constexpr int kMaxBlocks = 128; // d / h <= 4096 / 32
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// ds_swizzle bit mode: inside each 32-lane half, lane i reads lane i ^ m.
-constexpr int bit_xor(int m) { return (m << 10) | 0x1F; }
+// Chunk position (within its wave's 64 chunks) held by physical lane l.
+// The register-only cross-lane exchanges pair lane l with l ^ 1 and l ^ 2
+// (DPP quad_perm), l ^ 7 (row_half_mirror), l ^ 15 (row_mirror), l ^ 16 and
+// l ^ 32 (permlane16/32 swap). Lane l holds chunk L(l) for the GF(2)-linear
+// L that maps 1, 2, 7, 15, 16, 32 to 1, 2, 4, 8, 16, 32, so each of those
+// exchanges pairs exactly the chunks whose indices differ in one bit.
+__device__ __forceinline__ int lane_chunk(int l) {
+  return (l & 0x33) ^ ((l & 4) ? 7 : 0) ^ ((l & 8) ? 12 : 0);
+}
 
-// Value of the lane whose index differs in lane bit S.
+// DPP controls of the exchanges on chunk bits 0..3.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror: lane ^ 7
+constexpr int kDppMirror = 0x140;      // row_mirror: lane ^ 15
+
+// v + (the value of the lane holding the chunk that differs in bit S):
+// DPP for bits 0..3, ds_swizzle (lane ^ 16 inside 32) and ds_bpermute
+// (lane ^ 32) for bits 4 and 5. (A permlane swap of a value with itself is
+// not used here: hipcc folds the pair of results into one.)
 template <int S>
-__device__ __forceinline__ float xlane(float v) {
-  if constexpr (S == 0) {
-    return swz<QP_XOR1>(v);
-  } else if constexpr (S == 1) {
-    return swz<QP_XOR2>(v);
-  } else if constexpr (S < 5) {
-    return swz<bit_xor(1 << S)>(v);
+__device__ __forceinline__ float lane_sum(float v) {
+  const int iv = __builtin_bit_cast(int, v);
+  int o;
+  if constexpr (S < 4) {
+    constexpr int ctrl = S == 0 ? kDppXor1 : S == 1 ? kDppXor2 : S == 2 ? kDppHalfMirror : kDppMirror;
+    o = __builtin_amdgcn_mov_dpp(iv, ctrl, 0xF, 0xF, false);
+  } else if constexpr (S == 4) {
+    o = __builtin_amdgcn_ds_swizzle(iv, (16 << 10) | 0x1F);
   } else {
-    const int src = ((threadIdx.x & 63) ^ 32) << 2;
-    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, v)));
+    o = __builtin_amdgcn_ds_bpermute(((threadIdx.x & 63) ^ 32) << 2, iv);
+  }
+  return v + __builtin_bit_cast(float, o);
+}
+
+// Butterflies on chunk bit 4 or 5 for 16 registers, exact signs: a swap
+// gives a lower-row lane (own, partner) of register a and an upper-row lane
+// (partner, own) of register b; sum and difference are then the lower
+// result of a / upper result of b where they are, and a second swap returns
+// the other two to the lanes that own them.
+template <int S>
+__device__ __forceinline__ void swap_stage(float (&y)[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    const uint32_t a = as_u(y[i]), b = as_u(y[i + 1]);
+    const auto p = S == 4 ? __builtin_amdgcn_permlane16_swap(a, b, false, false)
+                          : __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    const float lo = as_f(p[0]), hi = as_f(p[1]);
+    const uint32_t sm = as_u(lo + hi), df = as_u(lo - hi);
+    const auto r = S == 4 ? __builtin_amdgcn_permlane16_swap(sm, df, false, false)
+                          : __builtin_amdgcn_permlane32_swap(sm, df, false, false);
+    y[i] = as_f(r[0]);
+    y[i + 1] = as_f(r[1]);
   }
 }
 
-// One cross-lane butterfly stage on lane bit S (lower lane: a + b; upper
-// lane: the negation of a - b, tracked by the lazy lane sign).
-template <int S, int NT>
-__device__ __forceinline__ void lane_stage(float (&y)[NT][16]) {
-  const float c = ((threadIdx.x >> S) & 1) ? -1.0f : 1.0f;
+// Per-lane constants of the cross-lane stages: on chunk bits 0..3 the lane
+// holding the upper chunk of a pair computes own - partner = -(a - b), and
+// the sign is applied once at the end (sigma); bits 4, 5 use exact signs.
+struct LaneCx {
+  float c[4];
+  float sigma;
+};
+__device__ __forceinline__ LaneCx lane_cx(int lc, int log2h) {
+  LaneCx x;
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) y[t][i] = __builtin_fmaf(xlane<S>(y[t][i]), c, y[t][i]);
+  for (int k = 0; k < 4; ++k) x.c[k] = ((lc >> k) & 1) ? -1.0f : 1.0f;
+  const int lazy = log2h - 4 < 4 ? log2h - 4 : 4;  // chunk bits inside a block, up to 4
+  x.sigma = (__builtin_popcount(lc & ((1 << lazy) - 1)) & 1) ? -1.0f : 1.0f;
+  return x;
 }
 
-template <int S>
-__device__ __forceinline__ float lane_sum(float v) {
-  return v + xlane<S>(v);
-}
-
-// Full FWHT stage sequence for blocks of h = 2^log2h (32 <= h <= 4096) over
-// NT tiles of 64 x 16 elements; without the final scaling.
-template <int NT>
-__device__ __forceinline__ void fwht_rows(float (&y)[NT][16], int log2h) {
+// Full FWHT stage sequence for one wave's 64 x 16 elements in blocks of
+// h = 2^log2h (32 <= h <= 1024 inside the wave), without the final scaling
+// and with the lazy sign sigma still to apply.
+__device__ __forceinline__ void fwht_rows(float (&y)[16], int log2h, const LaneCx& cx) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+  for (int h = 1; h < 16; h *= 2)
 #pragma unroll
-    for (int h = 1; h < 16; h *= 2)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if ((i & h) == 0) {
-          const float a = y[t][i], b = y[t][i + h];
-          y[t][i] = a + b;
-          y[t][i + h] = a - b;
-        }
-  const int lb = log2h - 4;  // lane bits inside a block (capped at 6 below)
-  if (lb > 0) lane_stage<0>(y);
-  if (lb > 1) lane_stage<1>(y);
-  if (lb > 2) lane_stage<2>(y);
-  if (lb > 3) lane_stage<3>(y);
-  if (lb > 4) lane_stage<4>(y);
-  if (lb > 5) lane_stage<5>(y);
-#pragma unroll
-  for (int ht = 1; ht < NT; ht *= 2)
-    if (log2h > 9 + ht)  // ht = 1: bit 10, ht = 2: bit 11
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        if ((t & ht) == 0 && t + ht < NT)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float a = y[t][i], b = y[t + ht][i];
-            y[t][i] = a + b;
-            y[t + ht][i] = a - b;
-          }
-}
-
-// Lazy lane sign left by the cross-lane stages of a block of 2^log2h.
-__device__ __forceinline__ float lane_sigma(int log2h) {
-  const int lb = log2h - 4 < 6 ? log2h - 4 : 6;
-  const int bits = (threadIdx.x & 63) & ((1 << lb) - 1);
-  return (__builtin_popcount(bits) & 1) ? -1.0f : 1.0f;
+    for (int i = 0; i < 16; ++i)
+      if ((i & h) == 0) {
+        const float a = y[i], b = y[i + h];
+        y[i] = a + b;
+        y[i + h] = a - b;
+      }
+  const int lb = log2h - 4;  // chunk bits inside a block
+  if (lb > 0) TQ_DPP_FMAC16("quad_perm:[1,0,3,2]", cx.c[0], y);
+  if (lb > 1) TQ_DPP_FMAC16("quad_perm:[2,3,0,1]", cx.c[1], y);
+  if (lb > 2) TQ_DPP_FMAC16("row_half_mirror", cx.c[2], y);
+  if (lb > 3) TQ_DPP_FMAC16("row_mirror", cx.c[3], y);
+  if (lb > 4) swap_stage<4>(y);
+  if (lb > 5) swap_stage<5>(y);
 }
 
 // --------------------------------------------------------------- packing ---
@@ -264,11 +280,13 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int c = lane + 64 * wave;  // this lane's chunk of 16 elements
+  const int lc = lane_chunk(lane);
+  const int c = lc + 64 * wave;  // this lane's chunk of 16 elements
   const bool act = c < (d >> 4);
   const int nblk = d >> log2h;
   const int lb = log2h - 4 < 6 ? log2h - 4 : 6;
-  const float ksig = kh * lane_sigma(log2h);
+  const LaneCx cx = lane_cx(lc, log2h);
+  const float ksig = kh * cx.sigma;
   const int64_t row_bytes = (int64_t)d * BITS / 8;
   const float eps = (float)1e-10;
   const int nf4 = d >> 2;
@@ -321,16 +339,16 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
     }
 
     // y_j = W[perm_j] * signs_j.
-    float y[1][16];
+    float y[16];
     const char* rb = reinterpret_cast<const char*>(rowbuf);
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      y[0][i] = act ? as_f(*reinterpret_cast<const uint32_t*>(rb + poff[i]) ^ smask[i]) : 0.0f;
+      y[i] = act ? as_f(*reinterpret_cast<const uint32_t*>(rb + poff[i]) ^ smask[i]) : 0.0f;
 
     // Butterflies inside the wave (index bits 0..9), then across waves
     // through LDS for blocks longer than 1024 (bits 10, 11): the lower tile
     // takes a + b, the upper b' - a' = a - b with the same lazy lane sign.
-    fwht_rows<1>(y, log2h);
+    fwht_rows(y, log2h, cx);
     if (log2h > 10) {
       float4* mine = reinterpret_cast<float4*>(rowbuf + 16 * c);
 #pragma unroll
@@ -339,7 +357,7 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
         __syncthreads();  // everyone is done reading the row buffer
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          mine[k] = make_float4(y[0][4 * k], y[0][4 * k + 1], y[0][4 * k + 2], y[0][4 * k + 3]);
+          mine[k] = make_float4(y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3]);
         __syncthreads();
         const float4* other = reinterpret_cast<const float4*>(rowbuf + 16 * (c ^ (64 * ht)));
         const bool upper = (wave & ht) != 0;
@@ -349,23 +367,23 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
           const float ov[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float a = y[0][4 * k + e];
-            y[0][4 * k + e] = upper ? ov[e] - a : a + ov[e];
+            const float a = y[4 * k + e];
+            y[4 * k + e] = upper ? ov[e] - a : a + ov[e];
           }
         }
       }
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) y[0][i] = y[0][i] * ksig;
+    for (int i = 0; i < 16; ++i) y[i] = y[i] * ksig;
 
     // Sum of squares: bits 0-3 in registers, then the lane bits inside the
     // block; block (h <= 1024) or tile (h > 1024) sums meet in LDS.
     float s[16];
-    float amin = __builtin_fabsf(y[0][0]);
+    float amin = __builtin_fabsf(y[0]);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      s[i] = y[0][i] * y[0][i];
-      if (i > 0) amin = __builtin_fminf(amin, __builtin_fabsf(y[0][i]));
+      s[i] = y[i] * y[i];
+      if (i > 0) amin = __builtin_fminf(amin, __builtin_fabsf(y[i]));
     }
 #pragma unroll
     for (int w = 1; w < 16; w *= 2)
@@ -397,15 +415,15 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
     if (amin >= denom * 0x1p-60f && denom <= 0x1p100f) {
       const Recip rd = make_recip(denom);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) y[0][i] = div_rn(y[0][i], rd);
+      for (int i = 0; i < 16; ++i) y[i] = div_rn(y[i], rd);
     } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) y[0][i] = y[0][i] / denom;
+      for (int i = 0; i < 16; ++i) y[i] = y[i] / denom;
     }
 
     // Codes and packing (the codebook test is uniform).
     const uint64_t bytes =
-        cb.sym ? pack16<BITS, LSB, true>(y[0], cb) : pack16<BITS, LSB, false>(y[0], cb);
+        cb.sym ? pack16<BITS, LSB, true>(y, cb) : pack16<BITS, LSB, false>(y, cb);
     if (act) store_codes<BITS>(packed + r * row_bytes + 2 * BITS * c, bytes);
     if (tid == 0) norms[r] = norm;
   }
@@ -460,9 +478,11 @@ __global__ __launch_bounds__(256) void orbit_dequantize_kernel(
   const int lane = tid & 63;
   const int wave = tid >> 6;
   float* tab = lds + d + 16 * wave;  // this wave's codebook x row norm
-  const int c = lane + 64 * wave;
+  const int lc = lane_chunk(lane);
+  const int c = lc + 64 * wave;
   const bool act = c < (d >> 4);
-  const float ksig = kh * lane_sigma(log2h);
+  const LaneCx cx = lane_cx(lc, log2h);
+  const float ksig = kh * cx.sigma;
   const int64_t row_bytes = (int64_t)d * BITS / 8;
 
   // Output groups of this lane and, when the rotation is undone, the byte
@@ -513,9 +533,9 @@ __global__ __launch_bounds__(256) void orbit_dequantize_kernel(
     __builtin_amdgcn_wave_barrier();
     uint32_t code[16];
     unpack16<BITS, LSB>(codes, code);
-    float w[1][16];
+    float w[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) w[0][i] = tab[code[i]];
+    for (int i = 0; i < 16; ++i) w[i] = tab[code[i]];
 
     if (rotated_only) {
       // Stage this wave's tile in element order, re-read it in store order.
@@ -523,7 +543,7 @@ __global__ __launch_bounds__(256) void orbit_dequantize_kernel(
         f32x4_t* mine = reinterpret_cast<f32x4_t*>(rowbuf + 16 * c);
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          mine[k] = f32x4_t{w[0][4 * k], w[0][4 * k + 1], w[0][4 * k + 2], w[0][4 * k + 3]};
+          mine[k] = f32x4_t{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
       }
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -535,7 +555,7 @@ __global__ __launch_bounds__(256) void orbit_dequantize_kernel(
 
     // Inverse rotation: FWHT per block (across waves through LDS beyond
     // 1024), times h^-1/2 and the lazy lane sign, times signs_j.
-    fwht_rows<1>(w, log2h);
+    fwht_rows(w, log2h, cx);
     if (log2h > 10) {
       f32x4_t* mine = reinterpret_cast<f32x4_t*>(rowbuf + 16 * c);
 #pragma unroll
@@ -544,7 +564,7 @@ __global__ __launch_bounds__(256) void orbit_dequantize_kernel(
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          mine[k] = f32x4_t{w[0][4 * k], w[0][4 * k + 1], w[0][4 * k + 2], w[0][4 * k + 3]};
+          mine[k] = f32x4_t{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
         __syncthreads();
         const f32x4_t* other = reinterpret_cast<const f32x4_t*>(rowbuf + 16 * (c ^ (64 * ht)));
         const bool upper = (wave & ht) != 0;
@@ -553,8 +573,8 @@ __global__ __launch_bounds__(256) void orbit_dequantize_kernel(
           const f32x4_t o = other[k];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float a = w[0][4 * k + e];
-            w[0][4 * k + e] = upper ? o[e] - a : a + o[e];
+            const float a = w[4 * k + e];
+            w[4 * k + e] = upper ? o[e] - a : a + o[e];
           }
         }
       }
@@ -566,7 +586,7 @@ __global__ __launch_bounds__(256) void orbit_dequantize_kernel(
       for (int k = 0; k < 4; ++k) {
         float z[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) z[e] = as_f(as_u(w[0][4 * k + e] * ksig) ^ smask[4 * k + e]);
+        for (int e = 0; e < 4; ++e) z[e] = as_f(as_u(w[4 * k + e] * ksig) ^ smask[4 * k + e]);
         mine[k] = f32x4_t{z[0], z[1], z[2], z[3]};
       }
     }

@@ -49,36 +49,6 @@ constexpr uint32_t kB3x2 = 2u * __builtin_bit_cast(uint32_t, (float)0.7992);
 constexpr float kInvSqrt128 = (float)0.08838834764831845;  // fp32(1/sqrt(128))
 constexpr float kFloor = (float)1e-8;                      // clamp of norm and scale
 
-// 16 butterflies across quad lanes, one VALU instruction each: x += c *
-// x(partner), the partner's value read through a DPP quad permute (no LDS
-// crossbar trip). gfx9 needs two wait states between a VALU write of a
-// register and a DPP read of it, and five after a VALU write of EXEC; the
-// leading s_nop 4 covers both for whatever the compiler placed before the
-// block, and no instruction inside it reads another one's result.
-#define TQ_DPP_FMAC16(PERM, c, a)                                                  \
-  asm volatile("s_nop 4\n"                                                         \
-               "v_fmac_f32_dpp %0, %0, %16 " PERM " row_mask:0xf bank_mask:0xf\n"   \
-               "v_fmac_f32_dpp %1, %1, %16 " PERM " row_mask:0xf bank_mask:0xf\n"   \
-               "v_fmac_f32_dpp %2, %2, %16 " PERM " row_mask:0xf bank_mask:0xf\n"   \
-               "v_fmac_f32_dpp %3, %3, %16 " PERM " row_mask:0xf bank_mask:0xf\n"   \
-               "v_fmac_f32_dpp %4, %4, %16 " PERM " row_mask:0xf bank_mask:0xf\n"   \
-               "v_fmac_f32_dpp %5, %5, %16 " PERM " row_mask:0xf bank_mask:0xf\n"   \
-               "v_fmac_f32_dpp %6, %6, %16 " PERM " row_mask:0xf bank_mask:0xf\n"   \
-               "v_fmac_f32_dpp %7, %7, %16 " PERM " row_mask:0xf bank_mask:0xf\n"   \
-               "v_fmac_f32_dpp %8, %8, %16 " PERM " row_mask:0xf bank_mask:0xf\n"   \
-               "v_fmac_f32_dpp %9, %9, %16 " PERM " row_mask:0xf bank_mask:0xf\n"   \
-               "v_fmac_f32_dpp %10, %10, %16 " PERM " row_mask:0xf bank_mask:0xf\n" \
-               "v_fmac_f32_dpp %11, %11, %16 " PERM " row_mask:0xf bank_mask:0xf\n" \
-               "v_fmac_f32_dpp %12, %12, %16 " PERM " row_mask:0xf bank_mask:0xf\n" \
-               "v_fmac_f32_dpp %13, %13, %16 " PERM " row_mask:0xf bank_mask:0xf\n" \
-               "v_fmac_f32_dpp %14, %14, %16 " PERM " row_mask:0xf bank_mask:0xf\n" \
-               "v_fmac_f32_dpp %15, %15, %16 " PERM " row_mask:0xf bank_mask:0xf\n" \
-               : "+v"(a[0][0]), "+v"(a[0][1]), "+v"(a[0][2]), "+v"(a[0][3]),            \
-                 "+v"(a[0][4]), "+v"(a[0][5]), "+v"(a[0][6]), "+v"(a[0][7]),            \
-                 "+v"(a[1][0]), "+v"(a[1][1]), "+v"(a[1][2]), "+v"(a[1][3]),            \
-                 "+v"(a[1][4]), "+v"(a[1][5]), "+v"(a[1][6]), "+v"(a[1][7])             \
-               : "v"(c))
-
 // Sign bit of element (q, g, i) from the 128-bit mask (bit j = element j).
 __device__ __forceinline__ uint32_t sign_bit(const SignMask& m, int q, int g, int i) {
   return (m.w[g] >> (8 * q + i)) & 1u;
@@ -189,8 +159,8 @@ __device__ __forceinline__ void fwht_low3(float (&x)[4][8]) {
 // Stages over index bits 3, 4 (quad lanes) with the lazy lane sign, then bits
 // 5, 6 (chunk index g) in registers.
 __device__ __forceinline__ void fwht_high4(float (&x)[4][8], float c1, float c2) {
-  float (&lo)[2][8] = *reinterpret_cast<float (*)[2][8]>(&x[0][0]);
-  float (&hi)[2][8] = *reinterpret_cast<float (*)[2][8]>(&x[2][0]);
+  float (&lo)[16] = *reinterpret_cast<float (*)[16]>(&x[0][0]);
+  float (&hi)[16] = *reinterpret_cast<float (*)[16]>(&x[2][0]);
   TQ_DPP_FMAC16("quad_perm:[1,0,3,2]", c1, lo);
   TQ_DPP_FMAC16("quad_perm:[1,0,3,2]", c1, hi);
   TQ_DPP_FMAC16("quad_perm:[2,3,0,1]", c2, lo);

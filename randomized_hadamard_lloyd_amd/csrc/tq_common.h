@@ -26,6 +26,36 @@ __device__ __forceinline__ uint32_t swz(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), P));
 }
 
+// 16 butterflies across lanes, one VALU instruction each: v[k] += c *
+// v[k](partner), the partner's value read through DPP (CTRL: a quad_perm,
+// row_mirror or row_half_mirror control; no LDS crossbar trip). gfx9 needs
+// two wait states between a VALU write of a register and a DPP read of it,
+// and five after a VALU write of EXEC; the leading s_nop 4 covers both for
+// whatever the compiler placed before the block, and no instruction inside
+// it reads another one's result.
+#define TQ_DPP_FMAC16(CTRL, c, v)                                                \
+  asm volatile("s_nop 4\n"                                                       \
+               "v_fmac_f32_dpp %0, %0, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"   \
+               "v_fmac_f32_dpp %1, %1, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"   \
+               "v_fmac_f32_dpp %2, %2, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"   \
+               "v_fmac_f32_dpp %3, %3, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"   \
+               "v_fmac_f32_dpp %4, %4, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"   \
+               "v_fmac_f32_dpp %5, %5, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"   \
+               "v_fmac_f32_dpp %6, %6, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"   \
+               "v_fmac_f32_dpp %7, %7, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"   \
+               "v_fmac_f32_dpp %8, %8, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"   \
+               "v_fmac_f32_dpp %9, %9, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"   \
+               "v_fmac_f32_dpp %10, %10, %16 " CTRL " row_mask:0xf bank_mask:0xf\n" \
+               "v_fmac_f32_dpp %11, %11, %16 " CTRL " row_mask:0xf bank_mask:0xf\n" \
+               "v_fmac_f32_dpp %12, %12, %16 " CTRL " row_mask:0xf bank_mask:0xf\n" \
+               "v_fmac_f32_dpp %13, %13, %16 " CTRL " row_mask:0xf bank_mask:0xf\n" \
+               "v_fmac_f32_dpp %14, %14, %16 " CTRL " row_mask:0xf bank_mask:0xf\n" \
+               "v_fmac_f32_dpp %15, %15, %16 " CTRL " row_mask:0xf bank_mask:0xf\n" \
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), \
+                 "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), \
+                 "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15])                     \
+               : "v"(c))
+
 __device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t as_u(float f) { return __builtin_bit_cast(uint32_t, f); }
 
