@@ -15,7 +15,7 @@ LIB = os.path.join(HERE, "libtq.so")
 SOURCES = ["tq3.hip", "orbit.hip", "libtq.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
@@ -24,19 +24,36 @@ def sources():
     return [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *sources(), "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+
+
+def _finish(proc, what):
+    out, _ = proc.communicate()
     # hipcc's host pass does not know the packed-fp32 feature name; drop that note
-    out = "\n".join(l for l in res.stdout.splitlines()
+    out = "\n".join(l for l in out.splitlines()
                     if "packed-fp32-ops" not in l and "warning generated" not in l)
     if out.strip():
         print(out, file=sys.stderr)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode})")
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {what} ({proc.returncode})")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object in parallel, then link libtq.so."""
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs, procs = [], []
+    for src in sources():
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        objs.append(obj)
+        procs.append((_run([HIPCC, *FLAGS, "-c", src, "-o", obj], verbose), src))
+    for proc, src in procs:
+        _finish(proc, os.path.basename(src))
+    tmp = LIB + ".tmp"
+    _finish(_run([HIPCC, *FLAGS, "-shared", *objs, "-o", tmp], verbose), "link")
     os.replace(tmp, LIB)
     return LIB
 

@@ -96,7 +96,9 @@ __device__ __forceinline__ LaneCx lane_cx(int lc, int log2h) {
 
 // Full FWHT stage sequence for one wave's 64 x 16 elements in blocks of
 // h = 2^log2h (32 <= h <= 1024 inside the wave), without the final scaling
-// and with the lazy sign sigma still to apply.
+// and with the lazy sign sigma still to apply. FULL: h >= 1024, every
+// in-wave stage runs (known at compile time, so no stage is a branch).
+template <bool FULL>
 __device__ __forceinline__ void fwht_rows(float (&y)[16], int log2h, const LaneCx& cx) {
 #pragma unroll
   for (int h = 1; h < 16; h *= 2)
@@ -107,7 +109,7 @@ __device__ __forceinline__ void fwht_rows(float (&y)[16], int log2h, const LaneC
         y[i] = a + b;
         y[i + h] = a - b;
       }
-  const int lb = log2h - 4;  // chunk bits inside a block
+  const int lb = FULL ? 6 : log2h - 4;  // chunk bits inside a block
   if (lb > 0) TQ_DPP_FMAC16("quad_perm:[1,0,3,2]", cx.c[0], y);
   if (lb > 1) TQ_DPP_FMAC16("quad_perm:[2,3,0,1]", cx.c[1], y);
   if (lb > 2) TQ_DPP_FMAC16("row_half_mirror", cx.c[2], y);
@@ -268,7 +270,7 @@ __device__ __forceinline__ uint32_t sign_of(uint32_t w, int k) {
 // the permutation, whose byte offsets (and the signs) each lane keeps in
 // registers for the whole kernel; the next row's loads are in flight while
 // the current one is processed.
-template <int BITS, bool LSB, int NT>
+template <int BITS, bool LSB, int NT, bool FULL>
 __global__ __launch_bounds__(256) void orbit_quantize_kernel(
     const float* __restrict__ W, int64_t rows, int d, int log2h, float kh,
     const int32_t* __restrict__ perm, const int8_t* __restrict__ signs, OrbitCodebook cb,
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
   const int c = lc + 64 * wave;  // this lane's chunk of 16 elements
   const bool act = c < (d >> 4);
   const int nblk = d >> log2h;
-  const int lb = log2h - 4 < 6 ? log2h - 4 : 6;
+  const int lb = FULL ? 6 : (log2h - 4 < 6 ? log2h - 4 : 6);
   const LaneCx cx = lane_cx(lc, log2h);
   const float ksig = kh * cx.sigma;
   const int64_t row_bytes = (int64_t)d * BITS / 8;
@@ -293,7 +295,7 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
 
   // Byte offsets into the staged row and sign masks of this lane's elements.
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  uint32_t poff[16], smask[16];
+  uint32_t poff[16], sbits = 0;  // sbits: bit i set when signs_j = -1 for element i
   {
     const int cc = act ? c : 0;  // inactive lanes read chunk 0 and never use it
     const u32x4* pp = reinterpret_cast<const u32x4*>(perm + 16 * cc);
@@ -304,7 +306,7 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         poff[4 * k + e] = 4u * p[e];
-        smask[4 * k + e] = sign_of(sv[k], e);
+        sbits |= (sign_of(sv[k], e) >> 31) << (4 * k + e);
       }
     }
   }
@@ -343,12 +345,14 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
     const char* rb = reinterpret_cast<const char*>(rowbuf);
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      y[i] = act ? as_f(*reinterpret_cast<const uint32_t*>(rb + poff[i]) ^ smask[i]) : 0.0f;
+      y[i] = act ? as_f(*reinterpret_cast<const uint32_t*>(rb + poff[i]) ^
+                        ((sbits << (31 - i)) & 0x80000000u))
+                 : 0.0f;
 
     // Butterflies inside the wave (index bits 0..9), then across waves
     // through LDS for blocks longer than 1024 (bits 10, 11): the lower tile
     // takes a + b, the upper b' - a' = a - b with the same lazy lane sign.
-    fwht_rows(y, log2h, cx);
+    fwht_rows<FULL>(y, log2h, cx);
     if (log2h > 10) {
       float4* mine = reinterpret_cast<float4*>(rowbuf + 16 * c);
 #pragma unroll
@@ -463,7 +467,7 @@ __device__ __forceinline__ void store_group(void* out, int64_t j0, const float* 
 // re-read from LDS in that order -- through the inverse permutation when
 // the rotation is undone. The next row's codes and norm are loaded while the
 // current row is processed.
-template <int BITS, bool LSB, int DT, int NT>
+template <int BITS, bool LSB, int DT, int NT, bool FULL>
 __global__ __launch_bounds__(256) void orbit_dequantize_kernel(
     const uint8_t* __restrict__ packed, const float* __restrict__ norms, int64_t rows, int d,
     int log2h, float kh, const int32_t* __restrict__ inv_perm,
@@ -555,7 +559,7 @@ __global__ __launch_bounds__(256) void orbit_dequantize_kernel(
 
     // Inverse rotation: FWHT per block (across waves through LDS beyond
     // 1024), times h^-1/2 and the lazy lane sign, times signs_j.
-    fwht_rows(w, log2h, cx);
+    fwht_rows<FULL>(w, log2h, cx);
     if (log2h > 10) {
       f32x4_t* mine = reinterpret_cast<f32x4_t*>(rowbuf + 16 * c);
 #pragma unroll
@@ -604,15 +608,15 @@ __global__ __launch_bounds__(256) void orbit_dequantize_kernel(
   }
 }
 
-template <int BITS, bool LSB, int NT>
+template <int BITS, bool LSB, int NT, bool FULL>
 hipError_t launch_q(const float* W, int64_t rows, int d, int log2h, float kh,
                     const int32_t* perm, const int8_t* signs, const OrbitCodebook& cb,
                     uint8_t* packed, float* norms, int cus, int wpb, hipStream_t s) {
   (void)wpb;
   const size_t shm = (size_t)(d + kMaxBlocks) * sizeof(float);
-  const int per_cu = resident_blocks_per_cu(orbit_quantize_kernel<BITS, LSB, NT>, 64 * NT, shm);
+  const int per_cu = resident_blocks_per_cu(orbit_quantize_kernel<BITS, LSB, NT, FULL>, 64 * NT, shm);
   const int grid = grid_size(rows, cus, per_cu);
-  orbit_quantize_kernel<BITS, LSB, NT><<<grid, 64 * NT, shm, s>>>(W, rows, d, log2h, kh, perm,
+  orbit_quantize_kernel<BITS, LSB, NT, FULL><<<grid, 64 * NT, shm, s>>>(W, rows, d, log2h, kh, perm,
                                                                  signs, cb, packed, norms);
   return hipGetLastError();
 }
@@ -621,15 +625,19 @@ template <int BITS, bool LSB>
 hipError_t launch_q_nt(int nt, const float* W, int64_t rows, int d, int log2h, float kh,
                        const int32_t* perm, const int8_t* signs, const OrbitCodebook& cb,
                        uint8_t* packed, float* norms, int cus, int wpb, hipStream_t s) {
+#define TQ_QN(N, F) \
+  launch_q<BITS, LSB, N, F>(W, rows, d, log2h, kh, perm, signs, cb, packed, norms, cus, wpb, s)
+  const bool full = log2h >= 10;
   switch (nt) {
-    case 1: return launch_q<BITS, LSB, 1>(W, rows, d, log2h, kh, perm, signs, cb, packed, norms, cus, wpb, s);
-    case 2: return launch_q<BITS, LSB, 2>(W, rows, d, log2h, kh, perm, signs, cb, packed, norms, cus, wpb, s);
-    case 3: return launch_q<BITS, LSB, 3>(W, rows, d, log2h, kh, perm, signs, cb, packed, norms, cus, wpb, s);
-    default: return launch_q<BITS, LSB, 4>(W, rows, d, log2h, kh, perm, signs, cb, packed, norms, cus, wpb, s);
+    case 1: return full ? TQ_QN(1, true) : TQ_QN(1, false);
+    case 2: return full ? TQ_QN(2, true) : TQ_QN(2, false);
+    case 3: return full ? TQ_QN(3, true) : TQ_QN(3, false);
+    default: return full ? TQ_QN(4, true) : TQ_QN(4, false);
   }
+#undef TQ_QN
 }
 
-template <int BITS, bool LSB, int DT, int NT>
+template <int BITS, bool LSB, int DT, int NT, bool FULL>
 hipError_t launch_dq(const uint8_t* packed, const float* norms, int64_t rows, int d, int log2h,
                      float kh, const int32_t* inv_perm, const int8_t* signs,
                      const OrbitCodebook& cb, int rotated_only, void* out, int cus, int wpb,
@@ -637,9 +645,9 @@ hipError_t launch_dq(const uint8_t* packed, const float* norms, int64_t rows, in
   (void)wpb;
   const size_t shm = (size_t)(d + kMaxBlocks) * sizeof(float);
   const int per_cu =
-      resident_blocks_per_cu(orbit_dequantize_kernel<BITS, LSB, DT, NT>, 64 * NT, shm);
+      resident_blocks_per_cu(orbit_dequantize_kernel<BITS, LSB, DT, NT, FULL>, 64 * NT, shm);
   const int grid = grid_size(rows, cus, per_cu);
-  orbit_dequantize_kernel<BITS, LSB, DT, NT><<<grid, 64 * NT, shm, s>>>(
+  orbit_dequantize_kernel<BITS, LSB, DT, NT, FULL><<<grid, 64 * NT, shm, s>>>(
       packed, norms, rows, d, log2h, kh, inv_perm, signs, cb, rotated_only, out);
   return hipGetLastError();
 }
@@ -649,13 +657,14 @@ hipError_t launch_dq_nt(int nt, const uint8_t* packed, const float* norms, int64
                         int log2h, float kh, const int32_t* inv_perm, const int8_t* signs,
                         const OrbitCodebook& cb, int rotated_only, void* out, int cus,
                         int wpb, hipStream_t s) {
-#define TQ_DQN(N) launch_dq<BITS, LSB, DT, N>(packed, norms, rows, d, log2h, kh, inv_perm, signs, \
-                                              cb, rotated_only, out, cus, wpb, s)
+#define TQ_DQN(N, F) launch_dq<BITS, LSB, DT, N, F>(packed, norms, rows, d, log2h, kh, inv_perm, \
+                                                 signs, cb, rotated_only, out, cus, wpb, s)
+  const bool full = log2h >= 10;
   switch (nt) {
-    case 1: return TQ_DQN(1);
-    case 2: return TQ_DQN(2);
-    case 3: return TQ_DQN(3);
-    default: return TQ_DQN(4);
+    case 1: return full ? TQ_DQN(1, true) : TQ_DQN(1, false);
+    case 2: return full ? TQ_DQN(2, true) : TQ_DQN(2, false);
+    case 3: return full ? TQ_DQN(3, true) : TQ_DQN(3, false);
+    default: return full ? TQ_DQN(4, true) : TQ_DQN(4, false);
   }
 #undef TQ_DQN
 }
