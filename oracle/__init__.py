@@ -16,6 +16,9 @@ tests/test_oracle_*.py. Parity status per function:
   * OrbitQuant quantize / dequantize: pinned against brute force on small
     rows; reconstruction quality on the config-5 weights is parity unpinned
     (the page prints no figure for it).
+  * Decode attention over TQ3 records (attention.py): pinned by closed forms
+    (one token, zero scale, duplicate keys, a dominant key) and invariants
+    (token order, query-head grouping).
 """
 import ctypes
 import os
