@@ -116,6 +116,12 @@ def orbit_weight(rows: int = 12288, d: int = 3072, seed: int = 5) -> torch.Tenso
     return torch.randn(rows, d, generator=_gen(seed), dtype=torch.float32) * 0.02
 
 
+def attention_queries(n_heads: int = 32, seed: int = 6) -> torch.Tensor:
+    """Decode-step queries for attention over the KV layer: [n_heads, 128]
+    fp32 N(0, 1) (32 query heads over the layer's 8 KV heads)."""
+    return torch.randn(n_heads, HEAD_DIM, generator=_gen(seed), dtype=torch.float32)
+
+
 def sign_mask_bytes(signs) -> bytes:
     """16-byte little-endian mask of a 128-entry sign vector: bit j set means
     sign j is negative. (Pure reformatting of a drawn input.)"""

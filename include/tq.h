@@ -166,6 +166,42 @@ int orbit_dequantize(const uint8_t* packed, const float* row_norms, int64_t rows
                      const int8_t* signs, const float* codebook, int bit_order,
                      int rotated_only, void* W_out, int out_dtype, void* stream);
 
+/*
+ * tq3_decode_attention -- one decode step of attention over a KV cache whose
+ * K and V vectors are TQ3 records ("ComfyUI-TurboQuant: tq3_core.py": TQ3 is
+ * a KV-cache codec; attention reads the vectors tq3_dequantize reconstructs).
+ * For each query head h, with j = h / (n_q_heads / n_kv_heads):
+ *     s_t = softmax_scale * <q_h, Khat_{t,j}>,  p = softmax(s),
+ *     out_h = sum_t p_t Vhat_{t,j},
+ * where Khat, Vhat are the tq3_dequantize reconstructions. The kernels never
+ * reconstruct a vector: they score and accumulate in the rotated domain and
+ * rotate each output back once; results agree with the definition to fp32
+ * rounding, not bit for bit.
+ *   q            device, n_q_heads x 128 of q_dtype (TQ_F32, TQ_BF16, TQ_F16),
+ *                16-byte aligned.
+ *   k_records,   device, n_tokens x n_kv_heads records of 56 bytes, token
+ *   v_records    major (record t * n_kv_heads + j is token t of KV head j),
+ *                8-byte aligned.
+ *   n_tokens     >= 1, <= 2^31.
+ *   n_q_heads / n_kv_heads must be 1, 2, 4 or 8 (n_kv_heads >= 1).
+ *   sign_mask    host, 16 bytes, the mask the records were written with.
+ *   workspace    device, at least tq3_attention_workspace_bytes(n_tokens,
+ *                n_q_heads, n_kv_heads) bytes, 16-byte aligned; scratch for
+ *                the per-chunk partial results, overwritten.
+ *   out          device, n_q_heads x 128 of out_dtype (TQ_F32, TQ_BF16 or
+ *                TQ_F16), 16-byte aligned.
+ * Returns TQ_ERR_SHAPE for bad counts or head ratios, TQ_ERR_ARG for a short
+ * workspace or a non-finite scale.
+ */
+int tq3_decode_attention(const void* q, int q_dtype, int n_q_heads,
+                         const uint8_t* k_records, const uint8_t* v_records,
+                         int64_t n_tokens, int n_kv_heads, const uint8_t* sign_mask,
+                         float softmax_scale, void* workspace, size_t workspace_bytes,
+                         void* out, int out_dtype, void* stream);
+
+/* Workspace bytes tq3_decode_attention needs for these sizes (0 if invalid). */
+size_t tq3_attention_workspace_bytes(int64_t n_tokens, int n_q_heads, int n_kv_heads);
+
 /* Bytes per TQ3 record: 48 + 4 + 4 = 56 ("tq3_core.py", tq3_memory_bytes). */
 size_t tq3_record_bytes(void);
 

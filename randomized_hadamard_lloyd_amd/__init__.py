@@ -10,12 +10,15 @@ Entry points (same names as the C ABI in include/tq.h):
   tq3_dequantize(records, dtype)   -> [..., D/128 * 128] tensor
   orbit_quantize_weight(W, bits)   -> (packed uint8, row_norms fp32)
   orbit_dequantize(packed, norms, d, bits, rotated_only, dtype)
+  tq3_decode_attention(q, k_records, v_records, n_kv_heads, signs, scale)
+                                   -> [Hq, 128] attention output
 plus host helpers tq3_record_bytes, orbit_block_size, tq_gaussian_lloyd_max,
 orbit_make_codebook.
 """
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -47,6 +50,8 @@ def _load():
                              _int, _vp],
         "tq_gaussian_lloyd_max": [_int, _int, _vp],
         "orbit_make_codebook": [_int, _i64, _vp],
+        "tq3_decode_attention": [_vp, _int, _int, _vp, _vp, _i64, _int, _vp, ctypes.c_float,
+                                 _vp, ctypes.c_size_t, _vp, _int, _vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -58,6 +63,8 @@ def _load():
     lib.orbit_block_size.restype = _i64
     lib.tq_status_str.argtypes = [_int]
     lib.tq_status_str.restype = ctypes.c_char_p
+    lib.tq3_attention_workspace_bytes.argtypes = [_i64, _int, _int]
+    lib.tq3_attention_workspace_bytes.restype = ctypes.c_size_t
     return lib
 
 
@@ -66,7 +73,8 @@ lib = _load()
 # the symbols include/tq.h declares
 EXPORTS = ("tq3_quantize", "tq3_dequantize", "orbit_quantize_weight", "orbit_dequantize",
            "tq3_record_bytes", "orbit_block_size", "tq_gaussian_lloyd_max",
-           "orbit_make_codebook", "tq_status_str")
+           "orbit_make_codebook", "tq_status_str", "tq3_decode_attention",
+           "tq3_attention_workspace_bytes")
 
 
 def _check(status: int, what: str):
@@ -93,13 +101,11 @@ def _ptr(t):
 
 def sign_mask(signs) -> bytes:
     """16-byte mask of a 128-entry +-1 sign vector: bit j set where s_j < 0."""
-    s = torch.as_tensor(signs).reshape(-1).to("cpu", torch.float32)
-    if s.numel() != TQ3_DIM:
+    s = np.asarray(signs.detach().cpu() if isinstance(signs, torch.Tensor) else signs,
+                   dtype=np.float32).reshape(-1)
+    if s.size != TQ3_DIM:
         raise ValueError("TQ3 sign vector must have 128 entries")
-    bits = (s < 0).to(torch.uint8)
-    weights = torch.tensor([1 << i for i in range(8)], dtype=torch.int32)
-    packed = (bits.view(16, 8).to(torch.int32) * weights).sum(1).to(torch.uint8)
-    return bytes(packed.tolist())
+    return np.packbits(s < 0, bitorder="little").tobytes()
 
 
 def tq3_record_bytes() -> int:
@@ -149,6 +155,54 @@ def tq3_dequantize(records: torch.Tensor, signs, dtype=torch.float32,
     m = signs if isinstance(signs, (bytes, bytearray)) else sign_mask(signs)
     _check(lib.tq3_dequantize(_ptr(rec), n, m, _ptr(out), _DTYPES[dtype], TQ3_DIM,
                               _stream(records)), "tq3_dequantize")
+    return out
+
+
+def tq3_attention_workspace_bytes(n_tokens: int, n_q_heads: int, n_kv_heads: int) -> int:
+    return int(lib.tq3_attention_workspace_bytes(n_tokens, n_q_heads, n_kv_heads))
+
+
+def tq3_decode_attention(q: torch.Tensor, k_records: torch.Tensor, v_records: torch.Tensor,
+                         n_kv_heads: int, signs, softmax_scale: float = None,
+                         dtype=torch.float32, workspace: torch.Tensor = None,
+                         out: torch.Tensor = None) -> torch.Tensor:
+    """One decode step of attention over a TQ3-compressed KV cache.
+
+    q [Hq, 128] (fp32/bf16/fp16); k_records, v_records uint8 [T, Hkv, 56] or
+    [T * Hkv, 56], token-major; query head h reads KV head h // (Hq / Hkv).
+    softmax_scale defaults to 1/sqrt(128). Returns [Hq, 128] of `dtype`.
+    The workspace (uint8, tq3_attention_workspace_bytes) is allocated here
+    when not given."""
+    if q.dtype not in _DTYPES or dtype not in _DTYPES:
+        raise TypeError("unsupported dtype")
+    if q.ndim != 2 or q.shape[1] != TQ3_DIM:
+        raise ValueError("q must be [n_q_heads, 128]")
+    for r in (k_records, v_records):
+        if r.dtype != torch.uint8 or r.shape[-1] != TQ3_RECORD_BYTES:
+            raise ValueError("records must be uint8 [..., 56]")
+    if k_records.numel() != v_records.numel():
+        raise ValueError("K and V must hold the same number of records")
+    _need_gpu(q, k_records, v_records)
+    hq, hkv = q.shape[0], int(n_kv_heads)
+    nrec = k_records.numel() // TQ3_RECORD_BYTES
+    if hkv < 1 or nrec % hkv:
+        raise ValueError("the records must split evenly over the KV heads")
+    n_tok = nrec // hkv
+    if softmax_scale is None:
+        softmax_scale = TQ3_DIM ** -0.5
+    qc, kc, vc = q.contiguous(), k_records.contiguous(), v_records.contiguous()
+    need = tq3_attention_workspace_bytes(n_tok, hq, hkv)
+    if need == 0:
+        raise ValueError("unsupported sizes (need >= 1 token and Hq/Hkv in {1, 2, 4, 8})")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((hq, TQ3_DIM), dtype=dtype, device=q.device)
+    m = signs if isinstance(signs, (bytes, bytearray)) else sign_mask(signs)
+    _check(lib.tq3_decode_attention(_ptr(qc), _DTYPES[q.dtype], hq, _ptr(kc), _ptr(vc), n_tok,
+                                    hkv, m, float(softmax_scale), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _ptr(out),
+                                    _DTYPES[dtype], _stream(q)), "tq3_decode_attention")
     return out
 
 

@@ -189,6 +189,39 @@ int orbit_dequantize(const uint8_t* packed, const float* row_norms, int64_t rows
                                               static_cast<hipStream_t>(stream)));
 }
 
+static bool attn_shape_ok(int64_t n_tok, int hq, int hkv) {
+  if (n_tok < 1 || n_tok > ((int64_t)1 << 31) || hkv < 1 || hq < hkv || hq % hkv != 0)
+    return false;
+  const int g = hq / hkv;
+  return g == 1 || g == 2 || g == 4 || g == 8;
+}
+
+size_t tq3_attention_workspace_bytes(int64_t n_tokens, int n_q_heads, int n_kv_heads) {
+  if (!attn_shape_ok(n_tokens, n_q_heads, n_kv_heads)) return 0;
+  return tq::tq3_attention_ws_floats(n_tokens, n_q_heads, n_kv_heads) * sizeof(float);
+}
+
+int tq3_decode_attention(const void* q, int q_dtype, int n_q_heads, const uint8_t* k_records,
+                         const uint8_t* v_records, int64_t n_tokens, int n_kv_heads,
+                         const uint8_t* sign_mask, float softmax_scale, void* workspace,
+                         size_t workspace_bytes, void* out, int out_dtype, void* stream) {
+  if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype)) return TQ_ERR_DTYPE;
+  if (!attn_shape_ok(n_tokens, n_q_heads, n_kv_heads)) return TQ_ERR_SHAPE;
+  if (!std::isfinite(softmax_scale)) return TQ_ERR_ARG;
+  if (!q || !k_records || !v_records || !sign_mask || !workspace || !out) return TQ_ERR_NULL;
+  if (workspace_bytes < tq3_attention_workspace_bytes(n_tokens, n_q_heads, n_kv_heads))
+    return TQ_ERR_ARG;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(workspace, 16) || !aligned(k_records, 8) ||
+      !aligned(v_records, 8))
+    return TQ_ERR_ALIGN;
+  tq::SignMask m;
+  std::memcpy(m.w, sign_mask, sizeof(m.w));
+  return launched(tq::launch_tq3_attention(q, q_dtype, n_q_heads, k_records, v_records, n_tokens,
+                                           n_kv_heads, m, softmax_scale,
+                                           static_cast<float*>(workspace), out, out_dtype,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 int tq_gaussian_lloyd_max(int bits, int iters, double* out) {
   if (bits < 1 || bits > 8) return TQ_ERR_BITS;
   if (iters < 0) return TQ_ERR_ARG;

@@ -1,0 +1,502 @@
+// Decode attention over a TQ3-compressed KV cache for gfx950: the consumer of
+// the "ComfyUI-TurboQuant: tq3_core.py" codec (module docstring: TQ3 holds
+// the K and V vectors of a KV cache). One query token per head attends to T
+// cached tokens whose K and V vectors are 56-byte records.
+//
+// Rotated-domain evaluation. tq3_dequantize reconstructs a vector as
+//   v = norm * S (K H (scale * c)),   c_j = C[idx_j],
+// with S the sign flips, H the unnormalised 128-point Hadamard matrix and
+// K = fp32(1/sqrt(128)). S and H are symmetric, so
+//   <q, v> = norm * scale * <K H S q, c>   and
+//   sum_t p_t v_t = S K H (sum_t p_t norm_t scale_t c_t).
+// Each query is rotated once (qr = K H S q, times softmax_scale and log2(e)
+// so that exp2 gives the softmax weights); a score reads only a K record's
+// indices and its two scalars; values are accumulated in the rotated domain;
+// one inverse rotation per head finishes the output. No per-token transform.
+//
+// Work mapping. A group of 16 lanes owns one token at a time: lane r holds
+// elements 8r .. 8r+7, i.e. its 24 bits of each record's indices. A
+// 256-thread block (16 groups) handles one KV head over one chunk of tokens
+// for the G query heads that share that KV head, each group keeping a running
+// (max, sum, accumulator) per head (the online softmax). The block merges its
+// groups and writes one partial per head; a second kernel merges the chunks,
+// normalises, rotates back and stores.
+#include "tq_common.h"
+#include "tq_kernels.h"
+
+namespace tq {
+
+namespace {
+
+constexpr float kInvSqrt128A = (float)0.08838834764831845;  // fp32(1/sqrt(128))
+
+__device__ __forceinline__ float tq3_centroid_a(int k) {
+  constexpr float c[8] = {(float)-0.9816, (float)-0.6168, (float)-0.3479, (float)-0.1129,
+                          (float)0.1129,  (float)0.3479,  (float)0.6168,  (float)0.9816};
+  return c[k];
+}
+
+// Sums over the 16-lane group, all in registers: DPP partners r ^ 1, r ^ 2
+// (quad sums), then r ^ 7 (row_half_mirror: the other quad of the 8-lane
+// half) and r ^ 15 (row_mirror: the other half). Every lane ends with the
+// same bits, because each pairwise sum is commutative. Four values at once,
+// one v_add_f32_dpp per step and value.
+// gfx9 needs two wait states between a VALU write of a register and a DPP
+// read of it (five after a VALU write of EXEC): the leading s_nop 4 covers
+// whatever precedes the block, and inside it each value is read again only
+// three instructions after its last write.
+#define TQ_DPP_STEP4(CTRL)                                                          \
+  "v_add_f32_dpp %0, %0, %0 " CTRL " row_mask:0xf bank_mask:0xf\n"                 \
+  "v_add_f32_dpp %1, %1, %1 " CTRL " row_mask:0xf bank_mask:0xf\n"                 \
+  "v_add_f32_dpp %2, %2, %2 " CTRL " row_mask:0xf bank_mask:0xf\n"                 \
+  "v_add_f32_dpp %3, %3, %3 " CTRL " row_mask:0xf bank_mask:0xf\n"
+__device__ __forceinline__ void group_allreduce4(float& a, float& b, float& c, float& d) {
+  asm volatile("s_nop 4\n" TQ_DPP_STEP4("quad_perm:[1,0,3,2]") TQ_DPP_STEP4("quad_perm:[2,3,0,1]")
+                   TQ_DPP_STEP4("row_half_mirror") TQ_DPP_STEP4("row_mirror")
+               : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+
+// Butterfly with the partner lane r ^ (1 << S): lower lane a + b, upper lane
+// a - b (exact signs: fma(own, -1, partner) = partner - own).
+template <int S>
+__device__ __forceinline__ float lane_butterfly(float own, float c) {
+  const int iv = __builtin_bit_cast(int, own);
+  int o;
+  if constexpr (S == 0) o = __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, false);
+  else if constexpr (S == 1) o = __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, false);
+  else if constexpr (S == 2) o = __builtin_amdgcn_ds_swizzle(iv, (4 << 10) | 0x1F);
+  else o = __builtin_amdgcn_ds_swizzle(iv, (8 << 10) | 0x1F);
+  return __builtin_fmaf(own, c, __builtin_bit_cast(float, o));
+}
+
+// Lane r's 8 elements of a 128-vector, in a 16-lane group: the unnormalised
+// Hadamard transform (in registers for index bits 0-2, across the group's
+// lanes for bits 3-6).
+__device__ __forceinline__ void group_fwht(float (&x)[8], int r) {
+#pragma unroll
+  for (int h = 1; h < 8; h *= 2)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if ((i & h) == 0) {
+        const float a = x[i], b = x[i + h];
+        x[i] = a + b;
+        x[i + h] = a - b;
+      }
+  const float c0 = (r & 1) ? -1.0f : 1.0f, c1 = (r & 2) ? -1.0f : 1.0f;
+  const float c2 = (r & 4) ? -1.0f : 1.0f, c3 = (r & 8) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = lane_butterfly<0>(x[i], c0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = lane_butterfly<1>(x[i], c1);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = lane_butterfly<2>(x[i], c2);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = lane_butterfly<3>(x[i], c3);
+}
+
+// Sign of element j = 8r + i from the 128-bit mask.
+__device__ __forceinline__ bool mask_bit(const SignMask& m, int r, int i) {
+  return (m.w[r >> 2] >> (8 * (r & 3) + i)) & 1u;
+}
+
+// This lane's 24 index bits and the (norm, scale) pair of one record.
+struct RecPart {
+  uint32_t lo, hi;
+  uint2 ns;
+};
+
+// From a record staged in LDS (16 dwords per record).
+__device__ __forceinline__ RecPart lds_part(const uint32_t* rec, int dsel) {
+  RecPart p;
+  p.lo = rec[dsel];
+  p.hi = rec[dsel + 1];
+  p.ns = *reinterpret_cast<const uint2*>(rec + 12);
+  return p;
+}
+
+// Centroid values of this lane's 8 elements: each 6-bit field (two indices)
+// selects one 8-byte entry of the pair table.
+__device__ __forceinline__ void decode8(const RecPart& p, uint32_t shift, const char* tb,
+                                        float (&c)[8]) {
+  const uint32_t c8 = (uint32_t)((((uint64_t)p.hi << 32) | p.lo) >> shift) << 3;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float2 v = *reinterpret_cast<const float2*>(tb + ((c8 >> (6 * k)) & 504u));
+    c[2 * k] = v.x;
+    c[2 * k + 1] = v.y;
+  }
+}
+
+// Floats per (head, chunk) partial: max, sum, 2 pad, 128 accumulators.
+constexpr int kPartFloats = 132;
+constexpr int kAttnGroups = 16;        // 16-lane groups per 256-thread block
+constexpr int kAttnTokPerGroup = 16;   // token slots per group: chunks of up to 256 tokens
+#ifndef ATTN_TB
+#define ATTN_TB(G) ((G) <= 2 ? 4 : 2)
+#endif
+
+template <int QDT, int G>
+__global__ __launch_bounds__(256) void tq3_attn_partial_kernel(
+    const void* __restrict__ q, const uint8_t* __restrict__ krec,
+    const uint8_t* __restrict__ vrec, int64_t n_tok, int hkv, SignMask mask, float qscale,
+    int chunk, float* __restrict__ ws) {
+  __shared__ float2 ctab[64];  // (C[p & 7], C[p >> 3]): two consecutive elements' values
+  __shared__ __attribute__((aligned(16))) float red_m[G][16];
+  __shared__ __attribute__((aligned(16))) float red_l[G][16];
+  // Per wave, its groups' records: [token k][K, V][group in wave][16 dwords]
+  // (14 used). Reused by the final merge of the groups' accumulators.
+  __shared__ __attribute__((aligned(16))) uint32_t stage[4][kAttnTokPerGroup][2][4][16];
+  static_assert(sizeof(stage) >= 16 * 132 * sizeof(float), "merge buffer fits the staging area");
+  float (*red_acc)[132] = reinterpret_cast<float (*)[132]>(&stage[0][0][0][0][0]);
+  const int kv = blockIdx.y;
+  const int nchunk = gridDim.x;
+  const int grp = threadIdx.x >> 4, r = threadIdx.x & 15;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (threadIdx.x < 64)
+    ctab[threadIdx.x] = make_float2(tq3_centroid_a(threadIdx.x & 7), tq3_centroid_a(threadIdx.x >> 3));
+
+  // Copy this wave's records into LDS with direct global-to-LDS dword loads:
+  // one instruction moves the 4 groups' records of one token slot (lane
+  // 16a + d: dword min(d, 13) of group a's record). Slots past the chunk's
+  // end re-read token t0's record, which is never used.
+  const int64_t t0 = (int64_t)blockIdx.x * chunk;
+  const int64_t t1 = t0 + chunk < n_tok ? t0 + chunk : n_tok;
+  const int nk = (int)((t1 - t0 + kAttnGroups - 1) / kAttnGroups);  // token slots per group
+  {
+    const int a = lane >> 4, d = lane & 15;
+    const int dd = d < 14 ? d : 13;
+    for (int k = 0; k < nk; ++k) {
+      const int64_t t = t0 + 4 * wave + a + (int64_t)kAttnGroups * k;
+      const int64_t rec = (t < t1 ? t : t0) * hkv + kv;
+      typedef __attribute__((address_space(3))) void lds_void;
+      typedef __attribute__((address_space(1))) void glb_void;
+      __builtin_amdgcn_global_load_lds((glb_void*)(krec + rec * 56 + 4 * dd),
+                                       (lds_void*)&stage[wave][k][0][0][0], 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((glb_void*)(vrec + rec * 56 + 4 * dd),
+                                       (lds_void*)&stage[wave][k][1][0][0], 4, 0, 0);
+    }
+  }
+
+  // Rotated queries of the G heads: lane r keeps elements 8r .. 8r+7.
+  float qr[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const int64_t off = (int64_t)(kv * G + h) * 128 + 8 * r;
+    if constexpr (QDT == DT_F32) {
+      const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(q) + off);
+      const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(q) + off + 4);
+      qr[h][0] = a.x; qr[h][1] = a.y; qr[h][2] = a.z; qr[h][3] = a.w;
+      qr[h][4] = b.x; qr[h][5] = b.y; qr[h][6] = b.z; qr[h][7] = b.w;
+    } else {
+      const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + off);
+      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        if constexpr (QDT == DT_BF16) {
+          qr[h][2 * p] = as_f(w[p] << 16);
+          qr[h][2 * p + 1] = as_f(w[p] & 0xffff0000u);
+        } else {
+          qr[h][2 * p] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[p] & 0xffffu));
+          qr[h][2 * p + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[p] >> 16));
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (mask_bit(mask, r, i)) qr[h][i] = -qr[h][i];
+    group_fwht(qr[h], r);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qr[h][i] = qr[h][i] * qscale;
+  }
+  __syncthreads();  // ctab
+
+  const int dsel = (3 * r) >> 2;
+  const uint32_t shift = (24u * r) & 31u;
+  float m[G], l[G], acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -__builtin_inff();
+    l[h] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[h][i] = 0.0f;
+  }
+  const char* tb = reinterpret_cast<const char*>(ctab);
+  // The wave's records are in LDS once its loads are done (the queries'
+  // loads above overlapped them); no other wave reads them.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  const uint32_t* my = &stage[wave][0][0][grp & 3][0];
+  // Token slots k = 0, 1, ... of this group (token t0 + grp + 16 k), TB per
+  // iteration; the TB scores of each head share one max update. TB shrinks
+  // with G to keep the registers of G heads in budget.
+  constexpr int TB = ATTN_TB(G);
+  // this group's tokens: the first nkg slots (groups differ by at most one)
+  const int nkg = (int)((t1 - t0 - grp + kAttnGroups - 1) / kAttnGroups);
+  for (int k0 = 0; k0 < nkg; k0 += TB) {
+    const int64_t tb0 = t0 + grp + (int64_t)kAttnGroups * k0;
+    RecPart kp[TB], vp[TB];
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      const int ku = k0 + u < nk ? k0 + u : nk - 1;  // a loaded slot (finite values)
+      kp[u] = lds_part(my + ku * 128, dsel);
+      vp[u] = lds_part(my + ku * 128 + 64, dsel);
+    }
+    // scores (base-2 logits); -inf for the tokens past the end
+    float sc[G][TB];
+    {
+      float ck[TB][8];
+#pragma unroll
+      for (int u = 0; u < TB; ++u) decode8(kp[u], shift, tb, ck[u]);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+          float dot = qr[h][0] * ck[u][0];
+#pragma unroll
+          for (int i = 1; i < 8; ++i) dot = __builtin_fmaf(qr[h][i], ck[u][i], dot);
+          sc[h][u] = dot;
+        }
+      static_assert((G * TB) % 4 == 0, "scores reduce four at a time");
+      float* flat = &sc[0][0];
+#pragma unroll
+      for (int k = 0; k < G * TB; k += 4) group_allreduce4(flat[k], flat[k + 1], flat[k + 2], flat[k + 3]);
+#pragma unroll
+      for (int u = 0; u < TB; ++u) {
+        const bool valid = tb0 + kAttnGroups * u < t1;
+        const float wk = as_f(kp[u].ns.x) * as_f(kp[u].ns.y);
+#pragma unroll
+        for (int h = 0; h < G; ++h) sc[h][u] = valid ? sc[h][u] * wk : -__builtin_inff();
+      }
+    }
+    // online softmax: one max update per head for the four tokens
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float bm = sc[h][0];
+#pragma unroll
+      for (int u = 1; u < TB; ++u) bm = __builtin_fmaxf(bm, sc[h][u]);
+      if (__builtin_amdgcn_ballot_w64(bm > m[h])) {
+        // some group of the wave has a new maximum: rescale (corr = 1 elsewhere)
+        const float mn = __builtin_fmaxf(m[h], bm);
+        const float corr = __builtin_amdgcn_exp2f(m[h] - mn);
+        l[h] = l[h] * corr;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[h][i] = acc[h][i] * corr;
+        m[h] = mn;
+      }
+#pragma unroll
+      for (int u = 0; u < TB; ++u) sc[h][u] = __builtin_amdgcn_exp2f(sc[h][u] - m[h]);  // p (0 past the end)
+    }
+    // values
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      float cv[8];
+      decode8(vp[u], shift, tb, cv);
+      const float wv = as_f(vp[u].ns.x) * as_f(vp[u].ns.y);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        l[h] = l[h] + sc[h][u];
+        const float pw = sc[h][u] * wv;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[h][i] = __builtin_fmaf(pw, cv[i], acc[h][i]);
+      }
+    }
+  }
+
+  // Merge the 16 groups: weights 2^(m_g - M); groups that saw no token have
+  // m = -inf and weigh 0.
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    if (r == 0) {
+      red_m[h][grp] = m[h];
+      red_l[h][grp] = l[h];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float mg[16], lg[16];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float4 a = reinterpret_cast<const float4*>(red_m[h])[k];
+      const float4 b = reinterpret_cast<const float4*>(red_l[h])[k];
+      mg[4 * k] = a.x; mg[4 * k + 1] = a.y; mg[4 * k + 2] = a.z; mg[4 * k + 3] = a.w;
+      lg[4 * k] = b.x; lg[4 * k + 1] = b.y; lg[4 * k + 2] = b.z; lg[4 * k + 3] = b.w;
+    }
+    float mx = mg[0];
+#pragma unroll
+    for (int g = 1; g < 16; ++g) mx = __builtin_fmaxf(mx, mg[g]);
+    const float f = m[h] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m[h] - mx);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red_acc[grp][8 * r + i] = acc[h][i] * f;
+    __syncthreads();
+    float* part = ws + ((int64_t)(kv * G + h) * nchunk + blockIdx.x) * kPartFloats;
+    if (threadIdx.x < 128) {
+      float a = red_acc[0][threadIdx.x];
+#pragma unroll
+      for (int g = 1; g < 16; ++g) a = a + red_acc[g][threadIdx.x];
+      part[4 + threadIdx.x] = a;
+    } else if (threadIdx.x == 128) {
+      float sl = 0.0f;
+#pragma unroll
+      for (int g = 0; g < 16; ++g)
+        sl = sl + (mg[g] == -__builtin_inff() ? 0.0f : lg[g] * __builtin_amdgcn_exp2f(mg[g] - mx));
+      part[0] = mx;
+      part[1] = sl;
+    }
+    __syncthreads();
+  }
+}
+
+// One 512-thread block per query head: merge the chunk partials (four
+// slices of the chunks, 128 elements each), divide by the softmax sum,
+// rotate back (S K H) and store.
+constexpr int kCombineSlices = 4;
+template <int ODT>
+__global__ __launch_bounds__(512) void tq3_attn_combine_kernel(const float* __restrict__ ws,
+                                                               int nchunk, SignMask mask,
+                                                               void* __restrict__ out) {
+  __shared__ float red[kCombineSlices][128];
+  __shared__ float fsum[kCombineSlices][128];
+  __shared__ float buf[128];
+  const int h = blockIdx.x;
+  const int j = threadIdx.x & 127, sl = threadIdx.x >> 7;
+  const float* part = ws + (int64_t)h * nchunk * kPartFloats;
+  // the maximum over all chunks
+  float mx = -__builtin_inff();
+  for (int c = threadIdx.x; c < nchunk; c += 512) mx = __builtin_fmaxf(mx, part[c * kPartFloats]);
+  red[sl][j] = mx;
+  __syncthreads();
+  if (threadIdx.x < 128) {
+    float v = red[0][j];
+#pragma unroll
+    for (int k = 1; k < kCombineSlices; ++k) v = __builtin_fmaxf(v, red[k][j]);
+    fsum[0][j] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    float v = __builtin_fmaxf(fsum[0][threadIdx.x], fsum[0][threadIdx.x + 64]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
+    if (threadIdx.x == 0) buf[0] = v;
+  }
+  __syncthreads();
+  mx = buf[0];
+  __syncthreads();
+  // slice sl sums chunks sl, sl + 4, ...: softmax sum and accumulators
+  float a = 0.0f, ls = 0.0f;
+#pragma unroll 8
+  for (int c = sl; c < nchunk; c += kCombineSlices) {
+    const float* pc = part + c * kPartFloats;
+    const float f = __builtin_amdgcn_exp2f(pc[0] - mx);
+    ls = __builtin_fmaf(pc[1], f, ls);
+    a = __builtin_fmaf(pc[4 + j], f, a);
+  }
+  red[sl][j] = a;
+  fsum[sl][j] = ls;
+  __syncthreads();
+  if (threadIdx.x < 128) {
+    float at = red[0][j], lt = fsum[0][j];
+#pragma unroll
+    for (int k = 1; k < kCombineSlices; ++k) {
+      at = at + red[k][j];
+      lt = lt + fsum[k][j];
+    }
+    buf[j] = at / lt;
+  }
+  __syncthreads();
+  // Unnormalised Hadamard transform in LDS, stage hh pairs (j, j ^ hh).
+#pragma unroll
+  for (int hh = 1; hh < 128; hh *= 2) {
+    float x = 0.0f, y = 0.0f;
+    if (threadIdx.x < 128) {
+      x = buf[j];
+      y = buf[j ^ hh];
+    }
+    __syncthreads();
+    if (threadIdx.x < 128) buf[j] = (j & hh) ? y - x : x + y;
+    __syncthreads();
+  }
+  if (threadIdx.x >= 128) return;
+  float o = buf[j] * kInvSqrt128A;
+  if ((mask.w[j >> 5] >> (j & 31)) & 1u) o = -o;
+  if constexpr (ODT == DT_F32) {
+    static_cast<float*>(out)[(int64_t)h * 128 + j] = o;
+  } else if constexpr (ODT == DT_BF16) {
+    static_cast<__bf16*>(out)[(int64_t)h * 128 + j] = (__bf16)o;
+  } else {
+    static_cast<_Float16*>(out)[(int64_t)h * 128 + j] = (_Float16)o;
+  }
+}
+
+template <int QDT, int G>
+hipError_t launch_partial(const void* q, const uint8_t* k, const uint8_t* v, int64_t n_tok,
+                          int hkv, const SignMask& m, float qscale, int chunk, int nchunk,
+                          float* ws, hipStream_t s) {
+  tq3_attn_partial_kernel<QDT, G><<<dim3(nchunk, hkv), 256, 0, s>>>(q, k, v, n_tok, hkv, m,
+                                                                     qscale, chunk, ws);
+  return hipGetLastError();
+}
+
+template <int QDT>
+hipError_t launch_partial_g(int g, const void* q, const uint8_t* k, const uint8_t* v,
+                            int64_t n_tok, int hkv, const SignMask& m, float qscale, int chunk,
+                            int nchunk, float* ws, hipStream_t s) {
+  switch (g) {
+    case 1: return launch_partial<QDT, 1>(q, k, v, n_tok, hkv, m, qscale, chunk, nchunk, ws, s);
+    case 2: return launch_partial<QDT, 2>(q, k, v, n_tok, hkv, m, qscale, chunk, nchunk, ws, s);
+    case 4: return launch_partial<QDT, 4>(q, k, v, n_tok, hkv, m, qscale, chunk, nchunk, ws, s);
+    default: return launch_partial<QDT, 8>(q, k, v, n_tok, hkv, m, qscale, chunk, nchunk, ws, s);
+  }
+}
+
+}  // namespace
+
+AttnPlan tq3_attention_plan(int64_t n_tok, int hkv) {
+  // About 1024 blocks in total (four per CU of a 256-CU part), at least one
+  // token per group (16 per chunk); chunks are multiples of 16 tokens and
+  // at most 16 token slots per group (256 tokens).
+  AttnPlan p;
+  const int64_t target = 1024;
+  int64_t nch = (target + hkv - 1) / hkv;
+  const int64_t max_ch = (n_tok + 15) / 16;
+  if (nch > max_ch) nch = max_ch;
+  if (nch < 1) nch = 1;
+  int64_t chunk = (n_tok + nch - 1) / nch;
+  chunk = (chunk + 15) / 16 * 16;
+  if (chunk > 16 * kAttnTokPerGroup) chunk = 16 * kAttnTokPerGroup;
+  p.chunk = chunk;
+  p.nchunk = (n_tok + chunk - 1) / chunk;
+  return p;
+}
+
+size_t tq3_attention_ws_floats(int64_t n_tok, int hq, int hkv) {
+  const AttnPlan p = tq3_attention_plan(n_tok, hkv);
+  return (size_t)hq * (size_t)p.nchunk * kPartFloats;
+}
+
+hipError_t launch_tq3_attention(const void* q, int qdt, int hq, const uint8_t* k,
+                                const uint8_t* v, int64_t n_tok, int hkv, const SignMask& m,
+                                float softmax_scale, float* ws, void* out, int odt,
+                                hipStream_t s) {
+  const AttnPlan p = tq3_attention_plan(n_tok, hkv);
+  const int g = hq / hkv;
+  // log2(e) turns the scores into base-2 logits for exp2; K = fp32(1/sqrt(128))
+  // is the forward transform's factor.
+  const float qscale = (float)((double)softmax_scale * 1.4426950408889634) * kInvSqrt128A;
+  hipError_t e;
+  if (qdt == DT_F32)
+    e = launch_partial_g<DT_F32>(g, q, k, v, n_tok, hkv, m, qscale, (int)p.chunk, (int)p.nchunk, ws, s);
+  else if (qdt == DT_BF16)
+    e = launch_partial_g<DT_BF16>(g, q, k, v, n_tok, hkv, m, qscale, (int)p.chunk, (int)p.nchunk, ws, s);
+  else
+    e = launch_partial_g<DT_F16>(g, q, k, v, n_tok, hkv, m, qscale, (int)p.chunk, (int)p.nchunk, ws, s);
+  if (e != hipSuccess) return e;
+  if (odt == DT_F32)
+    tq3_attn_combine_kernel<DT_F32><<<hq, 512, 0, s>>>(ws, (int)p.nchunk, m, out);
+  else if (odt == DT_BF16)
+    tq3_attn_combine_kernel<DT_BF16><<<hq, 512, 0, s>>>(ws, (int)p.nchunk, m, out);
+  else
+    tq3_attn_combine_kernel<DT_F16><<<hq, 512, 0, s>>>(ws, (int)p.nchunk, m, out);
+  return hipGetLastError();
+}
+
+}  // namespace tq

@@ -47,6 +47,19 @@ hipError_t launch_orbit_dequantize(const uint8_t* packed, const float* norms, in
                                    const int8_t* signs, const OrbitCodebook& cb,
                                    int lsb_first, int rotated_only, void* out, int dt,
                                    int cus, int wpb, hipStream_t s);
+// Decode attention over TQ3 records: the token chunk per block and the number
+// of chunks, both fixed by (n_tok, hkv) so that the caller can size the
+// workspace before the call.
+struct AttnPlan {
+  int64_t chunk, nchunk;
+};
+AttnPlan tq3_attention_plan(int64_t n_tok, int hkv);
+size_t tq3_attention_ws_floats(int64_t n_tok, int hq, int hkv);
+hipError_t launch_tq3_attention(const void* q, int qdt, int hq, const uint8_t* k,
+                                const uint8_t* v, int64_t n_tok, int hkv, const SignMask& m,
+                                float softmax_scale, float* ws, void* out, int odt,
+                                hipStream_t s);
+
 // Blocks of `kernel` that one CU keeps resident with `block` threads and
 // `shm` bytes of dynamic LDS (at least 1).
 template <typename K>

@@ -81,3 +81,29 @@ def test_argument_errors_without_gpu(tq):
                                    ctypes.cast(bad, ctypes.c_void_p), 0, None, None, None) == 8
     assert L.orbit_dequantize(None, None, 4, 3072, 2, None, None, p, 0, 0, None, 7, None) == 3
     assert tq.lib.tq_status_str(5).decode().startswith("Hadamard")
+
+
+def test_attention_arguments_without_gpu(tq):
+    L = tq.lib
+    assert tq.tq3_attention_workspace_bytes(0, 8, 8) == 0
+    assert tq.tq3_attention_workspace_bytes(10, 12, 8) == 0   # 12 query heads over 8
+    assert tq.tq3_attention_workspace_bytes(10, 24, 8) == 0   # group of 3
+    assert tq.tq3_attention_workspace_bytes(10, 8, 0) == 0
+    ws = tq.tq3_attention_workspace_bytes(32768, 32, 8)
+    assert ws > 0 and ws % 16 == 0
+    assert tq.tq3_attention_workspace_bytes(1, 8, 1) > 0
+    m = bytes(16)
+    args = lambda **kw: dict(dict(q=1 << 20, qd=0, hq=32, k=1 << 20, v=1 << 20, t=32768, hkv=8,
+                                  m=m, sc=0.088, ws=1 << 20, wsb=ws, o=1 << 20, od=0), **kw)
+    call = lambda a: L.tq3_decode_attention(a["q"], a["qd"], a["hq"], a["k"], a["v"], a["t"],
+                                            a["hkv"], a["m"], a["sc"], a["ws"], a["wsb"], a["o"],
+                                            a["od"], None)
+    assert call(args(qd=7)) == 3
+    assert call(args(od=7)) == 3
+    assert call(args(t=0)) == 2
+    assert call(args(hq=24)) == 2
+    assert call(args(sc=float("nan"))) == 8
+    assert call(args(q=None)) == 1
+    assert call(args(wsb=ws - 1)) == 8
+    assert call(args(q=(1 << 20) + 4)) == 6
+    assert call(args(k=(1 << 20) + 4)) == 6
