@@ -228,6 +228,45 @@ def secondary(tq, timer, dev, signs, mask):
                                   "GBps": rate(n * (REC + 256), ms_d)}
     del rec, y
 
+    # decode attention over the KV layer's records (32768 tokens x 8 KV heads):
+    # one query token per head, 8 or 32 query heads (groups of 1 and 4)
+    import ctypes
+    kv_k = tq.tq3_quantize(datagen.kv_cache("K").to(dev), mask).reshape(-1, REC)
+    kv_v = tq.tq3_quantize(datagen.kv_cache("V").to(dev), mask).reshape(-1, REC)
+    n_tok, hkv = datagen.KV_TOKENS, datagen.KV_HEADS
+    att = {}
+    for group in (1, 4):
+        hq = hkv * group
+        qh = datagen.attention_queries(hq).to(dev)
+        ws = torch.zeros(tq.tq3_attention_workspace_bytes(n_tok, hq, hkv), dtype=torch.uint8,
+                         device=dev)
+        o = torch.empty((hq, 128), dtype=torch.float32, device=dev)
+        ms_a, _ = timer.run(lambda: L.tq3_decode_attention(
+            tq._ptr(qh), tq.TQ_F32, hq, tq._ptr(kv_k), tq._ptr(kv_v), n_tok, hkv, mask,
+            ctypes.c_float(128 ** -0.5), tq._ptr(ws), ws.numel(), tq._ptr(o), tq.TQ_F32, sp), 50,
+            warmup=20)
+        ent = {"query_heads": hq, "kv_heads": hkv, "tokens": n_tok, "avg_ms": ms_a,
+               "records_GBps": rate(2 * n_tok * hkv * REC, ms_a)}
+        if group == 4:
+            # the unfused path: dequantize K and V to fp32, then bmm / softmax / bmm
+            kd = torch.empty((n_tok * hkv, 128), dtype=torch.float32, device=dev)
+            vd = torch.empty_like(kd)
+
+            def unfused():
+                L.tq3_dequantize(tq._ptr(kv_k), n_tok * hkv, mask, tq._ptr(kd), tq.TQ_F32, 128, sp)
+                L.tq3_dequantize(tq._ptr(kv_v), n_tok * hkv, mask, tq._ptr(vd), tq.TQ_F32, 128, sp)
+                k3 = kd.view(n_tok, hkv, 128).permute(1, 0, 2).contiguous()
+                v3 = vd.view(n_tok, hkv, 128).permute(1, 0, 2).contiguous()
+                qg = qh.view(hkv, group, 128).transpose(1, 2).contiguous()
+                p = torch.softmax(torch.bmm(k3, qg) * (128 ** -0.5), dim=1)
+                return torch.bmm(p.transpose(1, 2).contiguous(), v3)
+            ms_u, _ = timer.run(unfused, 10, warmup=3)
+            ent["unfused_fp32_dequantize_bmm_softmax_bmm_ms"] = ms_u
+            del kd, vd
+        att[f"hq{hq}"] = ent
+    out["tq3_decode_attention_kv_layer"] = att
+    del kv_k, kv_v
+
     # OrbitQuant weight 12288 x 3072 at 2, 3, 4 bits
     d = 3072
     w = datagen.orbit_weight().to(dev)

@@ -346,12 +346,12 @@ __global__ __launch_bounds__(256) void tq3_attn_partial_kernel(
   }
 }
 
-// One 512-thread block per query head: merge the chunk partials (four
+// One 1024-thread block per query head: merge the chunk partials (eight
 // slices of the chunks, 128 elements each), divide by the softmax sum,
 // rotate back (S K H) and store.
-constexpr int kCombineSlices = 4;
+constexpr int kCombineSlices = 8;
 template <int ODT>
-__global__ __launch_bounds__(512) void tq3_attn_combine_kernel(const float* __restrict__ ws,
+__global__ __launch_bounds__(1024) void tq3_attn_combine_kernel(const float* __restrict__ ws,
                                                                int nchunk, SignMask mask,
                                                                void* __restrict__ out) {
   __shared__ float red[kCombineSlices][128];
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(512) void tq3_attn_combine_kernel(const float* __re
   const float* part = ws + (int64_t)h * nchunk * kPartFloats;
   // the maximum over all chunks
   float mx = -__builtin_inff();
-  for (int c = threadIdx.x; c < nchunk; c += 512) mx = __builtin_fmaxf(mx, part[c * kPartFloats]);
+  for (int c = threadIdx.x; c < nchunk; c += 1024) mx = __builtin_fmaxf(mx, part[c * kPartFloats]);
   red[sl][j] = mx;
   __syncthreads();
   if (threadIdx.x < 128) {
@@ -381,9 +381,9 @@ __global__ __launch_bounds__(512) void tq3_attn_combine_kernel(const float* __re
   __syncthreads();
   mx = buf[0];
   __syncthreads();
-  // slice sl sums chunks sl, sl + 4, ...: softmax sum and accumulators
+  // slice sl sums chunks sl, sl + kCombineSlices, ...: softmax sum and accumulators
   float a = 0.0f, ls = 0.0f;
-#pragma unroll 8
+#pragma unroll 16
   for (int c = sl; c < nchunk; c += kCombineSlices) {
     const float* pc = part + c * kPartFloats;
     const float f = __builtin_amdgcn_exp2f(pc[0] - mx);
@@ -491,11 +491,11 @@ hipError_t launch_tq3_attention(const void* q, int qdt, int hq, const uint8_t* k
     e = launch_partial_g<DT_F16>(g, q, k, v, n_tok, hkv, m, qscale, (int)p.chunk, (int)p.nchunk, ws, s);
   if (e != hipSuccess) return e;
   if (odt == DT_F32)
-    tq3_attn_combine_kernel<DT_F32><<<hq, 512, 0, s>>>(ws, (int)p.nchunk, m, out);
+    tq3_attn_combine_kernel<DT_F32><<<hq, 1024, 0, s>>>(ws, (int)p.nchunk, m, out);
   else if (odt == DT_BF16)
-    tq3_attn_combine_kernel<DT_BF16><<<hq, 512, 0, s>>>(ws, (int)p.nchunk, m, out);
+    tq3_attn_combine_kernel<DT_BF16><<<hq, 1024, 0, s>>>(ws, (int)p.nchunk, m, out);
   else
-    tq3_attn_combine_kernel<DT_F16><<<hq, 512, 0, s>>>(ws, (int)p.nchunk, m, out);
+    tq3_attn_combine_kernel<DT_F16><<<hq, 1024, 0, s>>>(ws, (int)p.nchunk, m, out);
   return hipGetLastError();
 }
 

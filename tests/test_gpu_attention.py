@@ -136,3 +136,18 @@ def test_argument_errors(tq, signs):
         tq.tq3_decode_attention(q[:8], rec, rec[:4], 8, signs)
     with pytest.raises(ValueError):
         tq.tq3_decode_attention(torch.zeros(24, 128, device=DEV), rec, rec, 8, signs)  # group 3
+
+
+def test_workspace_reuse(tq, signs):
+    """One workspace serves consecutive calls of different sizes."""
+    hkv, hq = 4, 16
+    big = tq.tq3_attention_workspace_bytes(3000, hq, hkv)
+    ws = torch.empty(big, dtype=torch.uint8, device=DEV)
+    for t, seed in ((3000, 30), (3000, 31), (700, 32), (3000, 33)):
+        q = np.random.default_rng(seed).standard_normal((hq, 128)).astype(np.float32)
+        k, v = gaussian_records(t * hkv, seed + 100, signs), gaussian_records(t * hkv, seed + 200, signs)
+        out = tq.tq3_decode_attention(torch.from_numpy(q).to(DEV), torch.from_numpy(k).to(DEV),
+                                      torch.from_numpy(v).to(DEV), hkv, signs, 0.1, workspace=ws)
+        ref = oatt.tq3_decode_attention(q, k, v, hkv, signs, 0.1)
+        vmax = np.abs(oracle.tq3_dequantize(v, signs)).max()
+        assert np.abs(out.cpu().numpy() - ref).max() <= 2e-5 * vmax
