@@ -16,6 +16,9 @@ tests/test_oracle_*.py. Parity status per function:
   * OrbitQuant quantize / dequantize: pinned against brute force on small
     rows; reconstruction quality on the config-5 weights is parity unpinned
     (the page prints no figure for it).
+  * OrbitQuant forward (orbit_forward.py): pinned by the cancellation of the
+    two rotations, the zero input, an independent unpack of the rotated
+    weight, and the distortion against the unquantized layer.
   * Decode attention over TQ3 records (attention.py): pinned by closed forms
     (one token, zero scale, duplicate keys, a dominant key) and invariants
     (token order, query-head grouping).
