@@ -12,6 +12,7 @@
 // tq3.hip for bits 4-7, permlane16/32 swaps for bits 8 and 9); across waves
 // through LDS for bits 10-11. The row norm's sum of squares follows the same
 // bit order inside each h-block; block sums are then added left to right.
+#include "orbit_codes.h"
 #include "tq_common.h"
 #include "tq_kernels.h"
 
@@ -206,30 +207,6 @@ __device__ __forceinline__ uint64_t pack16(const float (&u)[16], const OrbitCode
   }
 }
 
-template <int BITS, bool LSB>
-__device__ __forceinline__ void unpack16(uint64_t acc, uint32_t (&code)[16]) {
-  constexpr uint32_t mask = (1u << BITS) - 1;
-  if constexpr (LSB) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) code[i] = (uint32_t)(acc >> (BITS * i)) & mask;
-  } else if constexpr (BITS == 3) {
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const uint32_t le = (uint32_t)(acc >> (24 * g)) & 0xffffffu;
-      const uint32_t w = (le >> 16) | (le & 0xff00u) | ((le & 0xffu) << 16);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) code[8 * g + i] = (w >> (21 - 3 * i)) & 7u;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int q = BITS * i;
-      const int shift = 8 * (q >> 3) + 8 - (q & 7) - BITS;
-      code[i] = (uint32_t)(acc >> shift) & mask;
-    }
-  }
-}
-
 template <int BITS>
 __device__ __forceinline__ void store_codes(uint8_t* p, uint64_t acc) {
   if constexpr (BITS == 2) {
@@ -241,19 +218,6 @@ __device__ __forceinline__ void store_codes(uint8_t* p, uint64_t acc) {
     q[0] = (uint16_t)acc;
     q[1] = (uint16_t)(acc >> 16);
     q[2] = (uint16_t)(acc >> 32);
-  }
-}
-
-template <int BITS>
-__device__ __forceinline__ uint64_t load_codes(const uint8_t* p) {
-  if constexpr (BITS == 2) {
-    return *reinterpret_cast<const uint32_t*>(p);
-  } else if constexpr (BITS == 4) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    return (uint64_t)v.x | ((uint64_t)v.y << 32);
-  } else {
-    const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
-    return (uint64_t)q[0] | ((uint64_t)q[1] << 16) | ((uint64_t)q[2] << 32);
   }
 }
 
@@ -270,11 +234,14 @@ __device__ __forceinline__ uint32_t sign_of(uint32_t w, int k) {
 // the permutation, whose byte offsets (and the signs) each lane keeps in
 // registers for the whole kernel; the next row's loads are in flight while
 // the current one is processed.
-template <int BITS, bool LSB, int NT, bool FULL>
+//
+// ROT: stop after the rotation and store it (rpbh_forward of activation rows,
+// the forward's first step) to xrot instead of quantizing.
+template <int BITS, bool LSB, int NT, bool FULL, bool ROT = false>
 __global__ __launch_bounds__(256) void orbit_quantize_kernel(
     const float* __restrict__ W, int64_t rows, int d, int log2h, float kh,
     const int32_t* __restrict__ perm, const int8_t* __restrict__ signs, OrbitCodebook cb,
-    uint8_t* __restrict__ packed, float* __restrict__ norms) {
+    uint8_t* __restrict__ packed, float* __restrict__ norms, float* __restrict__ xrot) {
   extern __shared__ float lds[];
   float* rowbuf = lds;     // the row; later the cross-wave butterfly exchange
   float* bsum = lds + d;   // block (or, for h > 1024, tile) sums of squares
@@ -379,6 +346,15 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) y[i] = y[i] * ksig;
+    if constexpr (ROT) {
+      if (act) {
+        f32x4_t* dst = reinterpret_cast<f32x4_t*>(xrot + r * d + 16 * c);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dst[k] = f32x4_t{y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3]};
+      }
+      __syncthreads();  // the row buffer is free for the next row
+      continue;
+    }
 
     // Sum of squares: bits 0-3 in registers, then the lane bits inside the
     // block; block (h <= 1024) or tile (h > 1024) sums meet in LDS.
@@ -617,7 +593,7 @@ hipError_t launch_q(const float* W, int64_t rows, int d, int log2h, float kh,
   const int per_cu = resident_blocks_per_cu(orbit_quantize_kernel<BITS, LSB, NT, FULL>, 64 * NT, shm);
   const int grid = grid_size(rows, cus, per_cu);
   orbit_quantize_kernel<BITS, LSB, NT, FULL><<<grid, 64 * NT, shm, s>>>(W, rows, d, log2h, kh, perm,
-                                                                 signs, cb, packed, norms);
+                                                                 signs, cb, packed, norms, nullptr);
   return hipGetLastError();
 }
 
@@ -687,6 +663,19 @@ hipError_t launch_dq_dt(int dt, int nt, const uint8_t* packed, const float* norm
   }
 }
 
+template <int NT, bool FULL>
+hipError_t launch_rot(const float* x, int64_t rows, int d, int log2h, float kh,
+                      const int32_t* perm, const int8_t* signs, float* xrot, int cus, hipStream_t s) {
+  const size_t shm = (size_t)(d + kMaxBlocks) * sizeof(float);
+  const int per_cu =
+      resident_blocks_per_cu(orbit_quantize_kernel<2, false, NT, FULL, true>, 64 * NT, shm);
+  const int grid = grid_size(rows, cus, per_cu);
+  OrbitCodebook cb{};
+  orbit_quantize_kernel<2, false, NT, FULL, true><<<grid, 64 * NT, shm, s>>>(
+      x, rows, d, log2h, kh, perm, signs, cb, nullptr, nullptr, xrot);
+  return hipGetLastError();
+}
+
 int ilog2(int64_t v) {
   int l = 0;
   while ((int64_t(1) << (l + 1)) <= v) ++l;
@@ -718,6 +707,24 @@ hipError_t launch_orbit_quantize(const float* W, int64_t rows, int64_t d, int bi
   if (bits == 3) return TQ_Q(3, false);
   return TQ_Q(4, false);
 #undef TQ_Q
+}
+
+hipError_t launch_orbit_rotate(const float* x, int64_t rows, int64_t d, const int32_t* perm,
+                               const int8_t* signs, float* xrot, int cus, hipStream_t s) {
+  const int64_t h = d & -d;
+  const int log2h = ilog2(h);
+  const float kh = (float)pow((double)h, -0.5);
+  const int di = (int)d;
+  const int nt = (di + 1023) >> 10;
+  const bool full = log2h >= 10;
+#define TQ_R(N, F) launch_rot<N, F>(x, rows, di, log2h, kh, perm, signs, xrot, cus, s)
+  switch (nt) {
+    case 1: return full ? TQ_R(1, true) : TQ_R(1, false);
+    case 2: return full ? TQ_R(2, true) : TQ_R(2, false);
+    case 3: return full ? TQ_R(3, true) : TQ_R(3, false);
+    default: return full ? TQ_R(4, true) : TQ_R(4, false);
+  }
+#undef TQ_R
 }
 
 hipError_t launch_orbit_dequantize(const uint8_t* packed, const float* norms, int64_t rows,

@@ -42,6 +42,11 @@ hipError_t launch_orbit_quantize(const float* W, int64_t rows, int64_t d, int bi
                                  const int32_t* perm, const int8_t* signs,
                                  const OrbitCodebook& cb, int lsb_first, uint8_t* packed,
                                  float* norms, int cus, int wpb, hipStream_t s);
+hipError_t launch_orbit_linear(const float* x, int64_t M, int64_t K, const uint8_t* packed,
+                               const float* norms, int64_t N, int bits, const OrbitCodebook& cb,
+                               int lsb_first, const float* bias, float* y, hipStream_t s);
+hipError_t launch_orbit_rotate(const float* x, int64_t rows, int64_t d, const int32_t* perm,
+                               const int8_t* signs, float* xrot, int cus, hipStream_t s);
 hipError_t launch_orbit_dequantize(const uint8_t* packed, const float* norms, int64_t rows,
                                    int64_t d, int bits, const int32_t* inv_perm,
                                    const int8_t* signs, const OrbitCodebook& cb,
