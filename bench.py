@@ -300,6 +300,39 @@ def secondary(tq, timer, dev, signs, mask):
             "dequantize_rotated": {"avg_ms": ms_r, "GBps": rate(rows * row_bytes, ms_r)},
             "dequantize_full": {"avg_ms": ms_f, "GBps": rate(rows * row_bytes, ms_f)}}
     out["orbit_12288x3072"] = orb
+
+    # OrbitQuant runtime forward on the same weight at 3 bits: rotate the
+    # activations, then the linear layer with the weight decoded on the fly
+    # (fp32 MFMA); beside it torch's fp32 matmul on the pre-dequantized W'
+    bits = 3
+    cb = tq.orbit_make_codebook(bits, d)
+    cbh = (ctypes.c_float * len(cb))(*cb.tolist())
+    cbp = ctypes.cast(cbh, ctypes.c_void_p)
+    packed = torch.empty((rows, d * bits // 8), dtype=torch.uint8, device=dev)
+    L.orbit_quantize_weight(tq._ptr(w), rows, d, bits, tq._ptr(perm_d), tq._ptr(sg_d), cbp,
+                            tq.TQ_MSB_FIRST, tq._ptr(packed), tq._ptr(norms), sp)
+    L.orbit_dequantize(tq._ptr(packed), tq._ptr(norms), rows, d, bits, tq._ptr(inv_d),
+                       tq._ptr(sg_d), cbp, tq.TQ_MSB_FIRST, 1, tq._ptr(wout), tq.TQ_F32, sp)
+    wrt = wout.t().contiguous()
+    fwd = {}
+    for m in (16, 1024):
+        xa = torch.randn(m, d, generator=torch.Generator().manual_seed(m)).to(dev)
+        xr = torch.empty_like(xa)
+        yo = torch.empty((m, rows), dtype=torch.float32, device=dev)
+        ms_r, _ = timer.run(lambda: L.orbit_rotate(tq._ptr(xa), m, d, tq._ptr(perm_d),
+                                                   tq._ptr(sg_d), tq._ptr(xr), sp), 20)
+        ms_l, _ = timer.run(lambda: L.orbit_linear(tq._ptr(xr), m, d, tq._ptr(packed),
+                                                   tq._ptr(norms), rows, bits, cbp,
+                                                   tq.TQ_MSB_FIRST, None, tq._ptr(yo), sp), 20)
+        ms_t, _ = timer.run(lambda: torch.matmul(xr, wrt), 20)
+        flop = 2.0 * m * rows * d
+        fwd[f"m{m}"] = {"rotate_ms": ms_r, "linear_ms": ms_l,
+                        "linear_TFLOPs": flop / (ms_l * 1e-3) / 1e12,
+                        "linear_frac_fp32_mfma_peak": flop / (ms_l * 1e-3) / 157.3e12,
+                        "codes_GBps": rate(packed.numel() + 4 * m * d + 4 * m * rows, ms_l),
+                        "torch_fp32_matmul_on_dequantized_ms": ms_t}
+    out["orbit_forward_12288x3072_3bit"] = fwd
+    del wrt
     return out
 
 
