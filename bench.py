@@ -192,6 +192,28 @@ def secondary(tq, timer, dev, signs, mask):
         "vectors_per_s": 2 * n / (ms * 1e-3), "GBps": rate(2 * n * 2 * (256 + REC), ms)}
     del bufs, calls
 
+    # the same layer (K and V in one buffer) on the page's three-array layout:
+    # indices, norms and scales in separate tensors, one launch each way
+    kv = torch.stack([kc, vc])
+    n2 = kv.numel() // 128
+    bufs = [dict(x=kv.to(dev), p=torch.empty((n2, 48), dtype=torch.uint8, device=dev),
+                 nr=torch.empty(n2, dtype=torch.float32, device=dev),
+                 sc=torch.empty(n2, dtype=torch.float32, device=dev),
+                 o=torch.empty((n2, 128), dtype=torch.bfloat16, device=dev)) for _ in range(4)]
+    calls = []
+    for b in bufs:
+        calls.append([(L.tq3_quantize_split, (tq._ptr(b["x"]), tq.TQ_BF16, n2, 128, mask,
+                                              tq._ptr(b["p"]), tq._ptr(b["nr"]), tq._ptr(b["sc"]), sp)),
+                      (L.tq3_dequantize_split, (tq._ptr(b["p"]), tq._ptr(b["nr"]), tq._ptr(b["sc"]),
+                                                n2, mask, tq._ptr(b["o"]), tq.TQ_BF16, 128, sp))])
+    it[0] = 0
+    del kv
+    ms, _ = timer.run(sep_step, 40, warmup=8)
+    out["tq3_kv_layer_split_layout"] = {
+        "launches_per_step": 2, "vectors_per_step": n2, "ms_per_step": ms,
+        "vectors_per_s": n2 / (ms * 1e-3), "GBps": rate(n2 * 2 * (256 + REC), ms)}
+    del bufs, calls
+
     # device copy ceiling at the size of one KV tensor's quantize traffic
     nbytes = 256 << 20
     a = torch.empty(nbytes, dtype=torch.uint8, device=dev)

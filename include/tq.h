@@ -111,6 +111,29 @@ int tq3_dequantize(const uint8_t* records, int64_t n_vec, const uint8_t* sign_ma
                    void* y, int y_dtype, int64_t y_row_stride, void* stream);
 
 /*
+ * tq3_quantize_split / tq3_dequantize_split -- "tq3_core.py", tq3_quantize and
+ * tq3_dequantize in the page's own storage layout: the dict it returns keeps
+ * the indices, the norms and the scales as three tensors ("packed" uint8
+ * [..., 48], "norms" and "scales" fp32 [...]) rather than one record.
+ *
+ * Same arithmetic, same index bytes and the same fp32 values as tq3_quantize /
+ * tq3_dequantize; vector v's fields live at packed + 48*v, norms[v] and
+ * scales[v] instead of at records + 56*v.
+ *
+ *   x, x_dtype, x_row_stride, y, y_dtype, y_row_stride, sign_mask
+ *                as for tq3_quantize / tq3_dequantize.
+ *   packed       device, n_vec * 48 bytes, 4-byte aligned.
+ *   norms        device, n_vec fp32, 4-byte aligned.
+ *   scales       device, n_vec fp32, 4-byte aligned.
+ */
+int tq3_quantize_split(const void* x, int x_dtype, int64_t n_vec, int64_t x_row_stride,
+                       const uint8_t* sign_mask, uint8_t* packed, float* norms,
+                       float* scales, void* stream);
+int tq3_dequantize_split(const uint8_t* packed, const float* norms, const float* scales,
+                         int64_t n_vec, const uint8_t* sign_mask, void* y, int y_dtype,
+                         int64_t y_row_stride, void* stream);
+
+/*
  * orbit_quantize_weight -- "orbit_quant.py", _quantize_rows with the buffers
  * of OrbitQuantizer.quantize_.
  *

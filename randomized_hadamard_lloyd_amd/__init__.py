@@ -8,6 +8,11 @@ built library, or calling it with CPU tensors, raises.
 Entry points (same names as the C ABI in include/tq.h):
   tq3_quantize(x)                  -> uint8 [..., D/128, 56] records
   tq3_dequantize(records, dtype)   -> [..., D/128 * 128] tensor
+  tq3_quantize_split(x)            -> (packed [..., D/128, 48], norms, scales)
+  tq3_dequantize_split(packed, norms, scales, dtype)
+                                   -> the same codec on the three-array layout;
+                                      tq3_quantize_dict / tq3_dequantize_dict wrap
+                                      it in the TQ3 page's dict form
   orbit_quantize_weight(W, bits)   -> (packed uint8, row_norms fp32)
   orbit_dequantize(packed, norms, d, bits, rotated_only, dtype)
   tq3_decode_attention(q, k_records, v_records, n_kv_heads, signs, scale)
@@ -50,6 +55,8 @@ def _load():
     sig = {
         "tq3_quantize": [_vp, _int, _i64, _i64, _vp, _vp, _vp],
         "tq3_dequantize": [_vp, _i64, _vp, _vp, _int, _i64, _vp],
+        "tq3_quantize_split": [_vp, _int, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
+        "tq3_dequantize_split": [_vp, _vp, _vp, _i64, _vp, _vp, _int, _i64, _vp],
         "orbit_quantize_weight": [_vp, _i64, _i64, _int, _vp, _vp, _vp, _int, _vp, _vp, _vp],
         "orbit_dequantize": [_vp, _vp, _i64, _i64, _int, _vp, _vp, _vp, _int, _int, _vp,
                              _int, _vp],
@@ -78,8 +85,8 @@ def _load():
 lib = _load()
 
 # the symbols include/tq.h declares
-EXPORTS = ("tq3_quantize", "tq3_dequantize", "orbit_quantize_weight", "orbit_dequantize",
-           "tq3_record_bytes", "orbit_block_size", "tq_gaussian_lloyd_max",
+EXPORTS = ("tq3_quantize", "tq3_dequantize", "tq3_quantize_split", "tq3_dequantize_split",
+           "orbit_quantize_weight", "orbit_dequantize", "tq3_record_bytes", "orbit_block_size", "tq_gaussian_lloyd_max",
            "orbit_make_codebook", "tq_status_str", "tq3_decode_attention",
            "tq3_attention_workspace_bytes", "orbit_rotate", "orbit_linear")
 
@@ -163,6 +170,82 @@ def tq3_dequantize(records: torch.Tensor, signs, dtype=torch.float32,
     _check(lib.tq3_dequantize(_ptr(rec), n, m, _ptr(out), _DTYPES[dtype], TQ3_DIM,
                               _stream(records)), "tq3_dequantize")
     return out
+
+
+def tq3_quantize_split(x: torch.Tensor, signs, packed: torch.Tensor = None,
+                       norms: torch.Tensor = None, scales: torch.Tensor = None):
+    """x [..., D] -> (packed uint8 [..., D/128, 48], norms fp32 [..., D/128],
+    scales fp32 [..., D/128]): tq3_quantize's fields in three arrays."""
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("tq3_quantize expects a torch.Tensor input")
+    if x.ndim == 0:
+        raise ValueError("tq3_quantize expects at least one dimension")
+    if x.shape[-1] <= 0 or x.shape[-1] % TQ3_DIM:
+        raise ValueError(f"last dim must be a positive multiple of 128, got {x.shape[-1]}")
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    _need_gpu(x)
+    nb = x.shape[-1] // TQ3_DIM
+    xv = x.reshape(-1, TQ3_DIM) if x.is_contiguous() else x.contiguous().reshape(-1, TQ3_DIM)
+    n = xv.shape[0]
+    lead = (*x.shape[:-1], nb)
+    if packed is None:
+        packed = torch.empty((*lead, 48), dtype=torch.uint8, device=x.device)
+    if norms is None:
+        norms = torch.empty(lead, dtype=torch.float32, device=x.device)
+    if scales is None:
+        scales = torch.empty(lead, dtype=torch.float32, device=x.device)
+    for t, want, name in ((packed, torch.uint8, "packed"), (norms, torch.float32, "norms"),
+                          (scales, torch.float32, "scales")):
+        if t.dtype != want or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {want} tensor")
+    if packed.numel() != n * 48 or norms.numel() != n or scales.numel() != n:
+        raise ValueError("output sizes do not match the input's vector count")
+    m = signs if isinstance(signs, (bytes, bytearray)) else sign_mask(signs)
+    _check(lib.tq3_quantize_split(_ptr(xv), _DTYPES[x.dtype], n, xv.stride(0), m, _ptr(packed),
+                                  _ptr(norms), _ptr(scales), _stream(x)), "tq3_quantize_split")
+    return packed, norms, scales
+
+
+def tq3_dequantize_split(packed: torch.Tensor, norms: torch.Tensor, scales: torch.Tensor, signs,
+                         dtype=torch.float32, out: torch.Tensor = None) -> torch.Tensor:
+    """(packed uint8 [..., nb, 48], norms [..., nb], scales [..., nb], both fp32)
+    -> [..., nb*128] of `dtype`."""
+    if norms.shape != scales.shape:
+        raise ValueError("TQ3 norms and scales must have identical shapes")
+    if packed.dtype != torch.uint8 or packed.shape[:-1] != norms.shape or packed.shape[-1] != 48:
+        raise ValueError("TQ3 packed must be uint8 with the shape of norms/scales + [48]")
+    if norms.dtype != torch.float32 or scales.dtype != torch.float32:
+        raise TypeError("TQ3 norms and scales must be float32")
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}")
+    _need_gpu(packed, norms, scales)
+    pk, nr, sc = packed.contiguous(), norms.contiguous(), scales.contiguous()
+    n = nr.numel()
+    lead = tuple(norms.shape[:-1])
+    nb = norms.shape[-1] if norms.ndim >= 1 else 1
+    if out is None:
+        out = torch.empty((*lead, nb * TQ3_DIM), dtype=dtype, device=packed.device)
+    m = signs if isinstance(signs, (bytes, bytearray)) else sign_mask(signs)
+    _check(lib.tq3_dequantize_split(_ptr(pk), _ptr(nr), _ptr(sc), n, m, _ptr(out), _DTYPES[dtype],
+                                    TQ3_DIM, _stream(packed)), "tq3_dequantize_split")
+    return out
+
+
+def tq3_quantize_dict(x: torch.Tensor, signs) -> dict:
+    """The TQ3 page's return form: {"norms", "scales", "packed", "orig_shape"}."""
+    packed, norms, scales = tq3_quantize_split(x, signs)
+    return {"norms": norms, "scales": scales, "packed": packed, "orig_shape": x.shape}
+
+
+def tq3_dequantize_dict(tq3: dict, signs, dtype=torch.float32) -> torch.Tensor:
+    """A dict in the TQ3 page's form -> tensor of its orig_shape (fp32 unless
+    `dtype` says otherwise). Missing keys raise KeyError, as on the page."""
+    missing = {"norms", "scales", "packed", "orig_shape"}.difference(tq3)
+    if missing:
+        raise KeyError("TQ3 payload missing required keys: " + ", ".join(sorted(missing)))
+    y = tq3_dequantize_split(tq3["packed"], tq3["norms"], tq3["scales"], signs, dtype)
+    return y.reshape(tq3["orig_shape"])
 
 
 def tq3_attention_workspace_bytes(n_tokens: int, n_q_heads: int, n_kv_heads: int) -> int:
@@ -267,6 +350,13 @@ def orbit_quantize_weight(W: torch.Tensor, bits: int, perm: torch.Tensor,
         packed = torch.empty((rows, d * bits // 8), dtype=torch.uint8, device=W.device)
     if row_norms is None:
         row_norms = torch.empty((rows,), dtype=torch.float32, device=W.device)
+    # caller-given buffers (requantize_ writes into the layer's own) must fit
+    if (packed.dtype != torch.uint8 or not packed.is_contiguous() or not packed.is_cuda
+            or packed.numel() != rows * d * bits // 8):
+        raise ValueError("packed must be a contiguous uint8 GPU tensor of rows*d*bits/8 bytes")
+    if (row_norms.dtype != torch.float32 or not row_norms.is_contiguous() or not row_norms.is_cuda
+            or row_norms.numel() != rows):
+        raise ValueError("row_norms must be a contiguous fp32 GPU tensor of `rows` values")
     cb = _host_f32(codebook)
     if len(cb) != (1 << bits):
         raise ValueError("codebook must hold 2**bits values")

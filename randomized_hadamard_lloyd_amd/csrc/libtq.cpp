@@ -117,6 +117,42 @@ int tq3_dequantize(const uint8_t* records, int64_t n_vec, const uint8_t* sign_ma
                                             static_cast<hipStream_t>(stream)));
 }
 
+int tq3_quantize_split(const void* x, int x_dtype, int64_t n_vec, int64_t x_row_stride,
+                       const uint8_t* sign_mask, uint8_t* packed, float* norms, float* scales,
+                       void* stream) {
+  if (!valid_dtype(x_dtype)) return TQ_ERR_DTYPE;
+  if (n_vec < 0 || n_vec > kMaxVectors) return TQ_ERR_SHAPE;
+  if (x_row_stride < TQ3_DIM || x_row_stride % 8 != 0 || x_row_stride > ((int64_t)1 << 24))
+    return TQ_ERR_SHAPE;
+  if (n_vec == 0) return TQ_OK;
+  if (!x || !sign_mask || !packed || !norms || !scales) return TQ_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(packed, 4) || !aligned(norms, 4) || !aligned(scales, 4))
+    return TQ_ERR_ALIGN;
+  tq::SignMask m;
+  std::memcpy(m.w, sign_mask, sizeof(m.w));
+  return launched(tq::launch_tq3_quantize_split(x, x_dtype, n_vec, x_row_stride, m, packed, norms,
+                                                scales, cu_count(),
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int tq3_dequantize_split(const uint8_t* packed, const float* norms, const float* scales,
+                         int64_t n_vec, const uint8_t* sign_mask, void* y, int y_dtype,
+                         int64_t y_row_stride, void* stream) {
+  if (!valid_dtype(y_dtype)) return TQ_ERR_DTYPE;
+  if (n_vec < 0 || n_vec > kMaxVectors) return TQ_ERR_SHAPE;
+  if (y_row_stride < TQ3_DIM || y_row_stride % 8 != 0 || y_row_stride > ((int64_t)1 << 24))
+    return TQ_ERR_SHAPE;
+  if (n_vec == 0) return TQ_OK;
+  if (!packed || !norms || !scales || !sign_mask || !y) return TQ_ERR_NULL;
+  if (!aligned(y, 16) || !aligned(packed, 4) || !aligned(norms, 4) || !aligned(scales, 4))
+    return TQ_ERR_ALIGN;
+  tq::SignMask m;
+  std::memcpy(m.w, sign_mask, sizeof(m.w));
+  return launched(tq::launch_tq3_dequantize_split(packed, norms, scales, n_vec, m, y, y_dtype,
+                                                  y_row_stride, cu_count(),
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 // Shared checks of the OrbitQuant entry points; fills the kernel's codebook.
 static int orbit_check(int64_t rows, int64_t d, int bits, const float* codebook, int bit_order,
                        tq::OrbitCodebook* cb) {

@@ -195,11 +195,15 @@ __device__ __forceinline__ LaneSigns lane_signs(int q) {
 // PF: software-pipelined loop -- the next vector's loads are issued before
 // the current one is processed (worth it once every wave runs many
 // iterations; the clamped fetch past the end re-reads the current row).
-template <int DT, bool PF>
+// SPLIT: the three fields go to separate arrays (indices [n, 48], norms [n],
+// scales [n]) instead of 56-byte records; `rec` is then the index array.
+template <int DT, bool PF, bool SPLIT>
 __global__ __launch_bounds__(256) void tq3_quantize_kernel(const void* __restrict__ x,
                                                            int64_t n_vec, int64_t stride,
                                                            SignMask mask,
-                                                           uint8_t* __restrict__ rec) {
+                                                           uint8_t* __restrict__ rec,
+                                                           float* __restrict__ norms_out,
+                                                           float* __restrict__ scales_out) {
   const int q = threadIdx.x & 3;
   Loader<DT> ld;
   ld.init(mask, q);
@@ -318,14 +322,21 @@ __global__ __launch_bounds__(256) void tq3_quantize_kernel(const void* __restric
     // Record: 48 bytes of indices = 4 groups of 3 dwords; in group g quad lane
     // k < 3 writes dword k, which takes its own 24-bit chunk and the next
     // lane's: (c_k >> 8k) | (c_{k+1} << (24 - 8k)). Lane 3 writes norm, scale.
-    uint8_t* out = rec + v * 56;
+    uint8_t* out = rec + v * (SPLIT ? 48 : 56);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const uint32_t nb = swz<QP_NEXT>(chunk[g]);
       const uint32_t dw = (chunk[g] >> (8 * q)) | (nb << (24 - 8 * q));
       if (q < 3) *reinterpret_cast<uint32_t*>(out + 12 * g + 4 * q) = dw;
     }
-    if (q == 3) *reinterpret_cast<uint2*>(out + 48) = make_uint2(as_u(norm), as_u(scale));
+    if constexpr (SPLIT) {
+      if (q == 3) {
+        norms_out[v] = norm;
+        scales_out[v] = scale;
+      }
+    } else {
+      if (q == 3) *reinterpret_cast<uint2*>(out + 48) = make_uint2(as_u(norm), as_u(scale));
+    }
   }
 }
 
@@ -402,8 +413,12 @@ __device__ __forceinline__ void store_row(void* base, int64_t row, int64_t strid
   }
 }
 
-template <int DT, bool PF>
+// SPLIT: the fields come from separate arrays (indices [n, 48], norms [n],
+// scales [n]); `rec` is then the index array.
+template <int DT, bool PF, bool SPLIT>
 __global__ __launch_bounds__(256) void tq3_dequantize_kernel(const uint8_t* __restrict__ rec,
+                                                             const float* __restrict__ norms_in,
+                                                             const float* __restrict__ scales_in,
                                                              int64_t n_vec, SignMask mask,
                                                              void* __restrict__ y,
                                                              int64_t stride) {
@@ -428,10 +443,13 @@ __global__ __launch_bounds__(256) void tq3_dequantize_kernel(const uint8_t* __re
     for (int i = 0; i < 8; ++i)
       kf[g][i] = (sign_bit(mask, q, g, i) ? -ls.sigma : ls.sigma) * kInvSqrt128;
   // The 24-bit chunk of (q, g) starts at byte 3q + 12g: dword 3g + (3q >> 2),
-  // bit offset 24q mod 32.
+  // bit offset 24q mod 32. Only lanes 1 and 2 need the following dword. In a
+  // record lane 3's spare read of group 3 lands on the norm; with split arrays
+  // lanes 0 and 3 read their own dword twice, so no read leaves the 48 bytes.
   const float c_even = centroid_of_lane(q, 0), c_odd = centroid_of_lane(q, 1);
   const uint32_t qbase = 32u * quad;
   const int dsel = (3 * q) >> 2;
+  const int dsel_hi = (!SPLIT || q == 1 || q == 2) ? dsel + 1 : dsel;
   const uint32_t shift = (24u * q) & 31u;
 
   const int64_t step = (int64_t)gridDim.x * kTq3VecPerBlock;
@@ -442,13 +460,16 @@ __global__ __launch_bounds__(256) void tq3_dequantize_kernel(const uint8_t* __re
   };
   auto fetch = [&](int64_t vv) {
     RecRaw rr;
-    const uint32_t* r32 = reinterpret_cast<const uint32_t*>(rec + vv * 56);
+    const uint32_t* r32 = reinterpret_cast<const uint32_t*>(rec + vv * (SPLIT ? 48 : 56));
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       rr.lo[g] = r32[3 * g + dsel];
-      rr.hi[g] = r32[3 * g + dsel + 1];
+      rr.hi[g] = r32[3 * g + dsel_hi];
     }
-    rr.ns = *reinterpret_cast<const uint2*>(rec + vv * 56 + 48);
+    if constexpr (SPLIT)
+      rr.ns = make_uint2(as_u(norms_in[vv]), as_u(scales_in[vv]));
+    else
+      rr.ns = *reinterpret_cast<const uint2*>(rec + vv * 56 + 48);
     return rr;
   };
   int64_t v = (int64_t)blockIdx.x * kTq3VecPerBlock + quad;
@@ -542,54 +563,85 @@ __global__ __launch_bounds__(256) void tq3_dequantize_kernel(const uint8_t* __re
 #define TQ3_PIPELINE_MIN_ITERS 16
 #endif
 
-template <int DT>
+template <int DT, bool SPLIT>
 hipError_t tq3_q(const void* x, int64_t n_vec, int64_t stride, const SignMask& m, uint8_t* rec,
-                 int cus, hipStream_t s) {
-  static const int per_cu = resident_blocks_per_cu(tq3_quantize_kernel<DT, false>, 256, 0);
-  static const int per_cu_pf = resident_blocks_per_cu(tq3_quantize_kernel<DT, true>, 256, 0);
+                 float* norms, float* scales, int cus, hipStream_t s) {
+  static const int per_cu =
+      resident_blocks_per_cu(tq3_quantize_kernel<DT, false, SPLIT>, 256, 0);
+  static const int per_cu_pf =
+      resident_blocks_per_cu(tq3_quantize_kernel<DT, true, SPLIT>, 256, 0);
   const int64_t need = (n_vec + kTq3VecPerBlock - 1) / kTq3VecPerBlock;
   const int grid_pf = grid_size(need, cus, per_cu_pf);
   if (need >= (int64_t)grid_pf * TQ3_PIPELINE_MIN_ITERS) {
-    tq3_quantize_kernel<DT, true><<<grid_pf, 256, 0, s>>>(x, n_vec, stride, m, rec);
+    tq3_quantize_kernel<DT, true, SPLIT>
+        <<<grid_pf, 256, 0, s>>>(x, n_vec, stride, m, rec, norms, scales);
   } else {
-    tq3_quantize_kernel<DT, false><<<grid_size(need, cus, per_cu), 256, 0, s>>>(x, n_vec, stride,
-                                                                                m, rec);
+    tq3_quantize_kernel<DT, false, SPLIT>
+        <<<grid_size(need, cus, per_cu), 256, 0, s>>>(x, n_vec, stride, m, rec, norms, scales);
   }
   return hipGetLastError();
 }
 
-template <int DT>
-hipError_t tq3_dq(const uint8_t* rec, int64_t n_vec, const SignMask& m, void* y, int64_t stride,
-                  int cus, hipStream_t s) {
-  static const int per_cu = resident_blocks_per_cu(tq3_dequantize_kernel<DT, false>, 256, 0);
-  static const int per_cu_pf = resident_blocks_per_cu(tq3_dequantize_kernel<DT, true>, 256, 0);
+template <int DT, bool SPLIT>
+hipError_t tq3_dq(const uint8_t* rec, const float* norms, const float* scales, int64_t n_vec,
+                  const SignMask& m, void* y, int64_t stride, int cus, hipStream_t s) {
+  static const int per_cu =
+      resident_blocks_per_cu(tq3_dequantize_kernel<DT, false, SPLIT>, 256, 0);
+  static const int per_cu_pf =
+      resident_blocks_per_cu(tq3_dequantize_kernel<DT, true, SPLIT>, 256, 0);
   const int64_t need = (n_vec + kTq3VecPerBlock - 1) / kTq3VecPerBlock;
   const int grid_pf = grid_size(need, cus, per_cu_pf);
   if (need >= (int64_t)grid_pf * TQ3_PIPELINE_MIN_ITERS) {
-    tq3_dequantize_kernel<DT, true><<<grid_pf, 256, 0, s>>>(rec, n_vec, m, y, stride);
+    tq3_dequantize_kernel<DT, true, SPLIT>
+        <<<grid_pf, 256, 0, s>>>(rec, norms, scales, n_vec, m, y, stride);
   } else {
-    tq3_dequantize_kernel<DT, false><<<grid_size(need, cus, per_cu), 256, 0, s>>>(rec, n_vec, m,
-                                                                                  y, stride);
+    tq3_dequantize_kernel<DT, false, SPLIT>
+        <<<grid_size(need, cus, per_cu), 256, 0, s>>>(rec, norms, scales, n_vec, m, y, stride);
   }
   return hipGetLastError();
+}
+
+template <bool SPLIT>
+hipError_t tq3_q_dt(const void* x, int dt, int64_t n_vec, int64_t stride, const SignMask& m,
+                    uint8_t* rec, float* norms, float* scales, int cus, hipStream_t s) {
+  switch (dt) {
+    case DT_F32: return tq3_q<DT_F32, SPLIT>(x, n_vec, stride, m, rec, norms, scales, cus, s);
+    case DT_BF16: return tq3_q<DT_BF16, SPLIT>(x, n_vec, stride, m, rec, norms, scales, cus, s);
+    default: return tq3_q<DT_F16, SPLIT>(x, n_vec, stride, m, rec, norms, scales, cus, s);
+  }
+}
+
+template <bool SPLIT>
+hipError_t tq3_dq_dt(const uint8_t* rec, const float* norms, const float* scales, int64_t n_vec,
+                     const SignMask& m, void* y, int dt, int64_t stride, int cus,
+                     hipStream_t s) {
+  switch (dt) {
+    case DT_F32: return tq3_dq<DT_F32, SPLIT>(rec, norms, scales, n_vec, m, y, stride, cus, s);
+    case DT_BF16: return tq3_dq<DT_BF16, SPLIT>(rec, norms, scales, n_vec, m, y, stride, cus, s);
+    default: return tq3_dq<DT_F16, SPLIT>(rec, norms, scales, n_vec, m, y, stride, cus, s);
+  }
 }
 
 hipError_t launch_tq3_quantize(const void* x, int dt, int64_t n_vec, int64_t stride,
                                const SignMask& m, uint8_t* rec, int cus, hipStream_t s) {
-  switch (dt) {
-    case DT_F32: return tq3_q<DT_F32>(x, n_vec, stride, m, rec, cus, s);
-    case DT_BF16: return tq3_q<DT_BF16>(x, n_vec, stride, m, rec, cus, s);
-    default: return tq3_q<DT_F16>(x, n_vec, stride, m, rec, cus, s);
-  }
+  return tq3_q_dt<false>(x, dt, n_vec, stride, m, rec, nullptr, nullptr, cus, s);
 }
 
 hipError_t launch_tq3_dequantize(const uint8_t* rec, int64_t n_vec, const SignMask& m, void* y,
                                  int dt, int64_t stride, int cus, hipStream_t s) {
-  switch (dt) {
-    case DT_F32: return tq3_dq<DT_F32>(rec, n_vec, m, y, stride, cus, s);
-    case DT_BF16: return tq3_dq<DT_BF16>(rec, n_vec, m, y, stride, cus, s);
-    default: return tq3_dq<DT_F16>(rec, n_vec, m, y, stride, cus, s);
-  }
+  return tq3_dq_dt<false>(rec, nullptr, nullptr, n_vec, m, y, dt, stride, cus, s);
+}
+
+hipError_t launch_tq3_quantize_split(const void* x, int dt, int64_t n_vec, int64_t stride,
+                                     const SignMask& m, uint8_t* packed, float* norms,
+                                     float* scales, int cus, hipStream_t s) {
+  return tq3_q_dt<true>(x, dt, n_vec, stride, m, packed, norms, scales, cus, s);
+}
+
+hipError_t launch_tq3_dequantize_split(const uint8_t* packed, const float* norms,
+                                       const float* scales, int64_t n_vec, const SignMask& m,
+                                       void* y, int dt, int64_t stride, int cus, hipStream_t s) {
+  return tq3_dq_dt<true>(packed, norms, scales, n_vec, m, y, dt, stride, cus, s);
 }
 
 }  // namespace tq

@@ -26,6 +26,14 @@ hipError_t launch_tq3_quantize(const void* x, int dt, int64_t n_vec, int64_t str
                                const SignMask& m, uint8_t* rec, int cus, hipStream_t s);
 hipError_t launch_tq3_dequantize(const uint8_t* rec, int64_t n_vec, const SignMask& m,
                                  void* y, int dt, int64_t stride, int cus, hipStream_t s);
+// The same codec with the record's fields in three arrays: indices [n, 48],
+// norms [n], scales [n].
+hipError_t launch_tq3_quantize_split(const void* x, int dt, int64_t n_vec, int64_t stride,
+                                     const SignMask& m, uint8_t* packed, float* norms,
+                                     float* scales, int cus, hipStream_t s);
+hipError_t launch_tq3_dequantize_split(const uint8_t* packed, const float* norms,
+                                       const float* scales, int64_t n_vec, const SignMask& m,
+                                       void* y, int dt, int64_t stride, int cus, hipStream_t s);
 
 // OrbitQuant weight codec.
 struct OrbitCodebook {

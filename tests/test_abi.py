@@ -68,6 +68,12 @@ def test_argument_errors_without_gpu(tq):
     assert L.tq3_quantize(None, 9, 4, 128, None, None, None) == 3
     assert L.tq3_quantize(None, 0, 4, 100, None, None, None) == 2
     assert L.tq3_quantize(None, 0, 0, 128, None, None, None) == 0
+    assert L.tq3_quantize_split(None, 9, 4, 128, None, None, None, None, None) == 3
+    assert L.tq3_quantize_split(None, 0, 4, 136, None, None, None, None, None) == 1
+    assert L.tq3_quantize_split(None, 0, 0, 128, None, None, None, None, None) == 0
+    assert L.tq3_dequantize_split(None, None, None, 4, None, None, 0, 64, None) == 2
+    assert L.tq3_dequantize_split(None, None, None, -1, None, None, 0, 128, None) == 2
+    assert L.tq3_dequantize_split(None, None, None, 4, None, None, 1, 128, None) == 1
     cb = tq._host_f32([-1.0, -0.5, 0.5, 1.0])
     import ctypes
     p = ctypes.cast(cb, ctypes.c_void_p)

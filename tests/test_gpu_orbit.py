@@ -170,3 +170,39 @@ def test_orbit_full_weight(tq):
                                       inv, sg, cb.numpy())
         st = compare_reconstruction(full[rows.to(DEV)], ref, o_norms[rows.numpy()])
         assert st["exact"], (bits, st)
+
+
+def test_orbit_requantize_in_place(tq):
+    """requantize_ ("orbit_quant.py", OrbitQuantizer.requantize_): a new fp32
+    weight goes through the layer's stored permutation, signs and codebook into
+    its existing packed / row-norm buffers; the result is the oracle's
+    quantization of the new weight, and the buffers keep their identity."""
+    d, bits, rows = 768, 3, 96
+    perm, sg = datagen.rpbh_params(d)
+    cb = tq.orbit_make_codebook(bits, d)
+    rng = np.random.default_rng(21)
+    w1 = torch.from_numpy((rng.standard_normal((rows, d)) * 0.02).astype(np.float32))
+    w2 = torch.from_numpy((rng.standard_normal((rows, d)) * 0.05).astype(np.float32))
+    p_dev, s_dev = perm.to(DEV), sg.to(DEV)
+    packed, norms = tq.orbit_quantize_weight(w1.to(DEV), bits, p_dev, s_dev, cb)
+    ptrs = (packed.data_ptr(), norms.data_ptr())
+    p2, n2 = tq.orbit_quantize_weight(w2.to(DEV), bits, p_dev, s_dev, cb,
+                                      packed=packed, row_norms=norms)
+    torch.cuda.synchronize()
+    assert (p2.data_ptr(), n2.data_ptr()) == ptrs
+    o_packed, o_norms = oracle.orbit_quantize(w2.numpy(), bits, perm, sg, cb.numpy())
+    assert np.array_equal(packed.cpu().numpy(), o_packed)
+    assert np.array_equal(norms.cpu().numpy(), o_norms)
+
+
+def test_orbit_requantize_rejects_wrong_buffers(tq):
+    d, bits, rows = 256, 2, 8
+    perm, sg = datagen.rpbh_params(d)
+    cb = tq.orbit_make_codebook(bits, d)
+    w = torch.zeros((rows, d), device=DEV)
+    small = torch.empty((rows, d * bits // 8 - 1), dtype=torch.uint8, device=DEV)
+    with pytest.raises(ValueError):
+        tq.orbit_quantize_weight(w, bits, perm.to(DEV), sg.to(DEV), cb, packed=small)
+    with pytest.raises(ValueError):
+        tq.orbit_quantize_weight(w, bits, perm.to(DEV), sg.to(DEV), cb,
+                                 row_norms=torch.empty(rows, dtype=torch.float16, device=DEV))
