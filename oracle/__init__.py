@@ -18,7 +18,10 @@ tests/test_oracle_*.py. Parity status per function:
     (the page prints no figure for it).
   * OrbitQuant forward (orbit_forward.py): pinned by the cancellation of the
     two rotations, the zero input, an independent unpack of the rotated
-    weight, and the distortion against the unquantized layer.
+    weight, and the distortion against the unquantized layer. Its bf16 /
+    fp16 form is pinned by torch's own casts (the rounding), a hand-worked
+    per-stage rounding case, the dense Hadamard product on integer inputs
+    (one rounding), a hand-worked W' product, and the zero input.
   * Decode attention over TQ3 records (attention.py): pinned by closed forms
     (one token, zero scale, duplicate keys, a dominant key) and invariants
     (token order, query-head grouping).
