@@ -341,9 +341,9 @@ def secondary(tq, timer, dev, signs, mask):
         xa = torch.randn(m, d, generator=torch.Generator().manual_seed(m)).to(dev)
         xr = torch.empty_like(xa)
         yo = torch.empty((m, rows), dtype=torch.float32, device=dev)
-        ms_r, _ = timer.run(lambda: L.orbit_rotate(tq._ptr(xa), m, d, tq._ptr(perm_d),
+        ms_r, _ = timer.run(lambda: L.orbit_rotate(tq._ptr(xa), tq.TQ_F32, m, d, tq._ptr(perm_d),
                                                    tq._ptr(sg_d), tq._ptr(xr), sp), 20)
-        ms_l, _ = timer.run(lambda: L.orbit_linear(tq._ptr(xr), m, d, tq._ptr(packed),
+        ms_l, _ = timer.run(lambda: L.orbit_linear(tq._ptr(xr), tq.TQ_F32, m, d, tq._ptr(packed),
                                                    tq._ptr(norms), rows, bits, cbp,
                                                    tq.TQ_MSB_FIRST, None, tq._ptr(yo), sp), 20)
         ms_t, _ = timer.run(lambda: torch.matmul(xr, wrt), 20)
@@ -355,6 +355,30 @@ def secondary(tq, timer, dev, signs, mask):
                         "torch_fp32_matmul_on_dequantized_ms": ms_t}
     out["orbit_forward_12288x3072_3bit"] = fwd
     del wrt
+    # the same forward on bf16 activations (bf16 rotation, W' products and
+    # matrix cores); beside it torch's bf16 matmul on the pre-dequantized
+    # bf16 W' (the weight it reads is 5.3x the codes' size)
+    wrt16 = tq.orbit_dequantize(packed, norms, d, bits, None, None, cb, rotated_only=True,
+                                dtype=torch.float32).to(torch.bfloat16).t().contiguous()
+    fwd16 = {}
+    for m in (16, 1024):
+        xa = torch.randn(m, d, generator=torch.Generator().manual_seed(m)).to(dev).to(torch.bfloat16)
+        xr = torch.empty_like(xa)
+        yo = torch.empty((m, rows), dtype=torch.bfloat16, device=dev)
+        ms_r, _ = timer.run(lambda: L.orbit_rotate(tq._ptr(xa), tq.TQ_BF16, m, d, tq._ptr(perm_d),
+                                                   tq._ptr(sg_d), tq._ptr(xr), sp), 20)
+        ms_l, _ = timer.run(lambda: L.orbit_linear(tq._ptr(xr), tq.TQ_BF16, m, d, tq._ptr(packed),
+                                                   tq._ptr(norms), rows, bits, cbp,
+                                                   tq.TQ_MSB_FIRST, None, tq._ptr(yo), sp), 20)
+        ms_t, _ = timer.run(lambda: torch.matmul(xr, wrt16), 20)
+        flop = 2.0 * m * rows * d
+        fwd16[f"m{m}"] = {"rotate_ms": ms_r, "linear_ms": ms_l,
+                          "linear_TFLOPs": flop / (ms_l * 1e-3) / 1e12,
+                          "linear_frac_bf16_mfma_peak": flop / (ms_l * 1e-3) / 2.5e15,
+                          "codes_GBps": rate(packed.numel() + 2 * m * d + 2 * m * rows, ms_l),
+                          "torch_bf16_matmul_on_dequantized_ms": ms_t}
+    out["orbit_forward_12288x3072_3bit_bf16"] = fwd16
+    del wrt16
     return out
 
 

@@ -193,36 +193,44 @@ int orbit_dequantize(const uint8_t* packed, const float* row_norms, int64_t rows
  * orbit_rotate -- the forward rotation of activation rows ("zerogpu-
  * sdxlTrainer: toolkit/util/orbit_quant.py", rpbh_forward as
  * OrbitQuantizer.forward applies it to x): x_rot[r, j] = FWHT-blocks of
- * (x[r, perm_j] * signs_j), times h^-1/2, h = d & -d, fp32 in the page's
- * stage order (bit-identical to rpbh_forward).
- *   x, x_rot    device, rows x d fp32, row-major, 16-byte aligned.
+ * (x[r, perm_j] * signs_j), times fp32(h^-1/2), h = d & -d, in the page's
+ * stage order, bit-identical to rpbh_forward evaluated on tensors of dtype:
+ * for TQ_BF16 / TQ_F16 every stage's sums and differences and the final
+ * products are computed in fp32 and rounded to that format (nearest even).
+ *   x, x_rot    device, rows x d of dtype (TQ_F32, TQ_BF16, TQ_F16),
+ *               row-major, 16-byte aligned.
  *   perm, signs device, int32 [d] and int8 [d] (+-1), 16-byte aligned.
  * Same limits on d as orbit_quantize_weight (TQ_ERR_BLOCK otherwise).
  */
-int orbit_rotate(const float* x, int64_t rows, int64_t d, const int32_t* perm,
-                 const int8_t* signs, float* x_rot, void* stream);
+int orbit_rotate(const void* x, int dtype, int64_t rows, int64_t d, const int32_t* perm,
+                 const int8_t* signs, void* x_rot, void* stream);
 
 /*
  * orbit_linear -- the forward's matmul ("orbit_quant.py",
  * OrbitQuantizer.forward: F.linear(x_rot, W', bias)) with the rotated-basis
- * weight W'[o, j] = codebook[code_{o,j}] * row_norms[o] (_dequantize_rotated,
- * fp32 products) decoded on the fly from the packed codes:
+ * weight W' of _dequantize_rotated decoded on the fly from the packed codes:
  *     y[i, o] = sum_j x_rot[i, j] W'[o, j] + bias[o].
- * The sum runs on fp32 matrix cores in an order of the library's choosing
- * (the page leaves it to the BLAS): results agree with the definition to
- * fp32 rounding.
- *   x_rot       device, m x d_in fp32 row-major, 16-byte aligned.
+ * dtype TQ_F32: W'[o, j] = codebook[code_{o,j}] * row_norms[o] in fp32, the
+ *   sum on fp32 matrix cores.
+ * dtype TQ_BF16 / TQ_F16 (the page's forward on activations of that dtype):
+ *   W'[o, j] = round(round(codebook[code]) * round(row_norms[o])), each
+ *   round to the dtype (nearest even); the sum on bf16 / fp16 matrix cores
+ *   with fp32 accumulation; y = round(sum + bias).
+ * The summation order is the library's (the page leaves it to the BLAS):
+ * results agree with the definition to fp32 accumulation error (plus the
+ * output's rounding for bf16 / fp16).
+ *   x_rot       device, m x d_in of dtype, row-major, 16-byte aligned.
  *   packed      device, d_out rows of d_in * bits / 8 bytes (the layout
  *               orbit_quantize_weight writes), 16-byte aligned.
  *   row_norms   device, fp32 [d_out].
  *   codebook    host, 2^bits ascending fp32; bit_order as for the codec.
- *   bias        device fp32 [d_out], or NULL.
- *   y           device, m x d_out fp32 row-major.
+ *   bias        device [d_out] of dtype, or NULL.
+ *   y           device, m x d_out of dtype, row-major.
  * d_in must be a positive multiple of 32 (TQ_ERR_SHAPE otherwise).
  */
-int orbit_linear(const float* x_rot, int64_t m, int64_t d_in, const uint8_t* packed,
+int orbit_linear(const void* x_rot, int dtype, int64_t m, int64_t d_in, const uint8_t* packed,
                  const float* row_norms, int64_t d_out, int bits, const float* codebook,
-                 int bit_order, const float* bias, float* y, void* stream);
+                 int bit_order, const void* bias, void* y, void* stream);
 
 /*
  * tq3_decode_attention -- one decode step of attention over a KV cache whose

@@ -17,7 +17,7 @@ Entry points (same names as the C ABI in include/tq.h):
   orbit_dequantize(packed, norms, d, bits, rotated_only, dtype)
   tq3_decode_attention(q, k_records, v_records, n_kv_heads, signs, scale)
                                    -> [Hq, 128] attention output
-  orbit_rotate(x, perm, signs)     -> rpbh_forward of activation rows
+  orbit_rotate(x, perm, signs)     -> rpbh_forward of activation rows (fp32/bf16/fp16)
   orbit_linear(x_rot, packed, norms, bits, codebook, bias)
                                    -> x_rot @ W'^T + bias (W' decoded on the fly)
   orbit_forward(x, packed, norms, perm, signs, bits, codebook, bias)
@@ -62,8 +62,8 @@ def _load():
                              _int, _vp],
         "tq_gaussian_lloyd_max": [_int, _int, _vp],
         "orbit_make_codebook": [_int, _i64, _vp],
-        "orbit_rotate": [_vp, _i64, _i64, _vp, _vp, _vp, _vp],
-        "orbit_linear": [_vp, _i64, _i64, _vp, _vp, _i64, _int, _vp, _int, _vp, _vp, _vp],
+        "orbit_rotate": [_vp, _int, _i64, _i64, _vp, _vp, _vp, _vp],
+        "orbit_linear": [_vp, _int, _i64, _i64, _vp, _vp, _i64, _int, _vp, _int, _vp, _vp, _vp],
         "tq3_decode_attention": [_vp, _int, _int, _vp, _vp, _i64, _int, _vp, ctypes.c_float,
                                  _vp, ctypes.c_size_t, _vp, _int, _vp],
     }
@@ -368,28 +368,32 @@ def orbit_quantize_weight(W: torch.Tensor, bits: int, perm: torch.Tensor,
 
 def orbit_rotate(x: torch.Tensor, perm: torch.Tensor, signs: torch.Tensor,
                  out: torch.Tensor = None) -> torch.Tensor:
-    """rpbh_forward of fp32 activation rows x [..., d] (GPU) -> fp32 [..., d]."""
-    if x.dtype != torch.float32 or x.ndim < 1:
-        raise ValueError("x must be an fp32 tensor")
+    """rpbh_forward of activation rows x [..., d] (fp32, bf16 or fp16, GPU) ->
+    the same shape and dtype; bf16 / fp16 round every stage to their format."""
+    if x.dtype not in _DTYPES or x.ndim < 1:
+        raise ValueError("x must be an fp32, bf16 or fp16 tensor")
     _need_gpu(x, perm, signs)
     d = x.shape[-1]
     xv = x.contiguous().reshape(-1, d)
     perm = perm.to(torch.int32).contiguous()
     signs = signs.to(torch.int8).contiguous()
     if out is None:
-        out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
-    _check(lib.orbit_rotate(_ptr(xv), xv.shape[0], d, _ptr(perm), _ptr(signs), _ptr(out),
-                            _stream(x)), "orbit_rotate")
+        out = torch.empty(x.shape, dtype=x.dtype, device=x.device)
+    if out.dtype != x.dtype or not out.is_contiguous() or out.numel() != x.numel():
+        raise ValueError("out must be a contiguous tensor of x's dtype and size")
+    _check(lib.orbit_rotate(_ptr(xv), _DTYPES[x.dtype], xv.shape[0], d, _ptr(perm), _ptr(signs),
+                            _ptr(out), _stream(x)), "orbit_rotate")
     return out
 
 
 def orbit_linear(x_rot: torch.Tensor, packed: torch.Tensor, row_norms: torch.Tensor, bits: int,
                  codebook, bias: torch.Tensor = None, bit_order: int = TQ_MSB_FIRST,
                  out: torch.Tensor = None) -> torch.Tensor:
-    """x_rot [..., d_in] fp32 times the rotated-basis weight decoded from
-    packed [d_out, d_in*bits/8] and row_norms [d_out], plus bias -> [..., d_out]."""
-    if x_rot.dtype != torch.float32:
-        raise ValueError("x_rot must be fp32")
+    """x_rot [..., d_in] (fp32, bf16 or fp16) times the rotated-basis weight
+    decoded from packed [d_out, d_in*bits/8] and row_norms [d_out], plus bias
+    (same dtype as x_rot) -> [..., d_out] of x_rot's dtype."""
+    if x_rot.dtype not in _DTYPES:
+        raise ValueError("x_rot must be fp32, bf16 or fp16")
     _need_gpu(x_rot, packed, row_norms)
     d_in = x_rot.shape[-1]
     d_out = row_norms.numel()
@@ -400,15 +404,20 @@ def orbit_linear(x_rot: torch.Tensor, packed: torch.Tensor, row_norms: torch.Ten
     pk = packed.contiguous()
     bp = None
     if bias is not None:
-        bias = bias.to(torch.float32).contiguous()
+        if bias.dtype != x_rot.dtype or bias.numel() != d_out:
+            raise ValueError("bias must hold d_out values of x_rot's dtype")
+        bias = bias.contiguous()
         _need_gpu(bias)
         bp = _ptr(bias)
     cb = _host_f32(codebook)
     if len(cb) != (1 << bits):
         raise ValueError("codebook must hold 2**bits values")
     if out is None:
-        out = torch.empty((*x_rot.shape[:-1], d_out), dtype=torch.float32, device=x_rot.device)
-    _check(lib.orbit_linear(_ptr(xv), xv.shape[0], d_in, _ptr(pk), _ptr(nr), d_out, bits,
+        out = torch.empty((*x_rot.shape[:-1], d_out), dtype=x_rot.dtype, device=x_rot.device)
+    if out.dtype != x_rot.dtype or not out.is_contiguous() or out.numel() != xv.shape[0] * d_out:
+        raise ValueError("out must be a contiguous [..., d_out] tensor of x_rot's dtype")
+    _check(lib.orbit_linear(_ptr(xv), _DTYPES[x_rot.dtype], xv.shape[0], d_in, _ptr(pk),
+                            _ptr(nr), d_out, bits,
                             ctypes.cast(cb, _vp), bit_order, bp, _ptr(out), _stream(x_rot)),
            "orbit_linear")
     return out

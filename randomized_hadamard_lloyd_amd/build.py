@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtq.so")
-SOURCES = ["tq3.hip", "tq3_attn.hip", "orbit.hip", "orbit_linear.hip", "libtq.cpp"]
+SOURCES = ["tq3.hip", "tq3_attn.hip", "orbit.hip", "orbit_linear.hip", "orbit_linear_lp.hip", "libtq.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

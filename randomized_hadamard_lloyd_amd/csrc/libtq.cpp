@@ -225,8 +225,9 @@ int orbit_dequantize(const uint8_t* packed, const float* row_norms, int64_t rows
                                               static_cast<hipStream_t>(stream)));
 }
 
-int orbit_rotate(const float* x, int64_t rows, int64_t d, const int32_t* perm,
-                 const int8_t* signs, float* x_rot, void* stream) {
+int orbit_rotate(const void* x, int dtype, int64_t rows, int64_t d, const int32_t* perm,
+                 const int8_t* signs, void* x_rot, void* stream) {
+  if (!valid_dtype(dtype)) return TQ_ERR_DTYPE;
   if (rows < 0 || rows > kMaxVectors || d <= 0) return TQ_ERR_SHAPE;
   const int64_t h = d & -d;
   if (h < 32 || h > 4096 || d > 4096) return TQ_ERR_BLOCK;
@@ -234,13 +235,14 @@ int orbit_rotate(const float* x, int64_t rows, int64_t d, const int32_t* perm,
   if (!x || !perm || !signs || !x_rot) return TQ_ERR_NULL;
   if (!aligned(x, 16) || !aligned(x_rot, 16) || !aligned(perm, 16) || !aligned(signs, 16))
     return TQ_ERR_ALIGN;
-  return launched(tq::launch_orbit_rotate(x, rows, d, perm, signs, x_rot, cu_count(),
+  return launched(tq::launch_orbit_rotate(x, dtype, rows, d, perm, signs, x_rot, cu_count(),
                                           static_cast<hipStream_t>(stream)));
 }
 
-int orbit_linear(const float* x_rot, int64_t m, int64_t d_in, const uint8_t* packed,
+int orbit_linear(const void* x_rot, int dtype, int64_t m, int64_t d_in, const uint8_t* packed,
                  const float* row_norms, int64_t d_out, int bits, const float* codebook,
-                 int bit_order, const float* bias, float* y, void* stream) {
+                 int bit_order, const void* bias, void* y, void* stream) {
+  if (!valid_dtype(dtype)) return TQ_ERR_DTYPE;
   if (bits < 2 || bits > 4) return TQ_ERR_BITS;
   if (m < 0 || m > kMaxVectors || d_in < 32 || d_in % 32 != 0 || d_in > ((int64_t)1 << 24) ||
       d_out < 1 || d_out > ((int64_t)1 << 31))
@@ -252,11 +254,17 @@ int orbit_linear(const float* x_rot, int64_t m, int64_t d_in, const uint8_t* pac
   if (st != TQ_OK) return st;
   if (m == 0) return TQ_OK;
   if (!x_rot || !packed || !row_norms || !y) return TQ_ERR_NULL;
+  const int es = dtype == TQ_F32 ? 4 : 2;
   if (!aligned(x_rot, 16) || !aligned(packed, 16) || !aligned(row_norms, 4) ||
-      !aligned(y, 4) || (bias && !aligned(bias, 4)))
+      !aligned(y, es) || (bias && !aligned(bias, es)))
     return TQ_ERR_ALIGN;
-  return launched(tq::launch_orbit_linear(x_rot, m, d_in, packed, row_norms, d_out, bits, cb,
-                                          bit_order == TQ_LSB_FIRST, bias, y,
+  if (dtype != TQ_F32)
+    return launched(tq::launch_orbit_linear_lp(x_rot, dtype, m, d_in, packed, row_norms, d_out,
+                                               bits, cb, bit_order == TQ_LSB_FIRST, bias, y,
+                                               static_cast<hipStream_t>(stream)));
+  return launched(tq::launch_orbit_linear(static_cast<const float*>(x_rot), m, d_in, packed,
+                                          row_norms, d_out, bits, cb, bit_order == TQ_LSB_FIRST,
+                                          static_cast<const float*>(bias), static_cast<float*>(y),
                                           static_cast<hipStream_t>(stream)));
 }
 

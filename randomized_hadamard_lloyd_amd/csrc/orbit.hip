@@ -58,12 +58,42 @@ __device__ __forceinline__ float lane_sum(float v) {
   return v + __builtin_bit_cast(float, o);
 }
 
+// Rounding of fp32 values to the activation format (RD = DT_BF16 or DT_F16;
+// DT_F32: none), nearest even, back in fp32 registers. Torch evaluates each
+// elementwise operation on bf16 / fp16 tensors in fp32 and rounds the result
+// to the tensor's format; the rotation of such activations repeats that
+// after every butterfly stage and after the scaling. The rounding is odd
+// (round(-v) = -round(v)), so it commutes with the lazy lane sign.
+template <int RD>
+__device__ __forceinline__ void round_pair(float& a, float& b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 v = {a, b};
+  if constexpr (RD == DT_BF16) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
+    a = as_f(w << 16);
+    b = as_f(w & 0xffff0000u);
+  } else if constexpr (RD == DT_F16) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const f2 r = __builtin_convertvector(__builtin_convertvector(v, h2), f2);
+    a = r[0];
+    b = r[1];
+  }
+}
+template <int RD>
+__device__ __forceinline__ void round16(float (&y)[16]) {
+  if constexpr (RD != DT_F32) {
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) round_pair<RD>(y[i], y[i + 1]);
+  }
+}
+
 // Butterflies on chunk bit 4 or 5 for 16 registers, exact signs: a swap
 // gives a lower-row lane (own, partner) of register a and an upper-row lane
 // (partner, own) of register b; sum and difference are then the lower
 // result of a / upper result of b where they are, and a second swap returns
 // the other two to the lanes that own them.
-template <int S>
+template <int S, int RD = DT_F32>
 __device__ __forceinline__ void swap_stage(float (&y)[16]) {
 #pragma unroll
   for (int i = 0; i < 16; i += 2) {
@@ -71,7 +101,9 @@ __device__ __forceinline__ void swap_stage(float (&y)[16]) {
     const auto p = S == 4 ? __builtin_amdgcn_permlane16_swap(a, b, false, false)
                           : __builtin_amdgcn_permlane32_swap(a, b, false, false);
     const float lo = as_f(p[0]), hi = as_f(p[1]);
-    const uint32_t sm = as_u(lo + hi), df = as_u(lo - hi);
+    float fs = lo + hi, fd = lo - hi;
+    round_pair<RD>(fs, fd);
+    const uint32_t sm = as_u(fs), df = as_u(fd);
     const auto r = S == 4 ? __builtin_amdgcn_permlane16_swap(sm, df, false, false)
                           : __builtin_amdgcn_permlane32_swap(sm, df, false, false);
     y[i] = as_f(r[0]);
@@ -99,10 +131,11 @@ __device__ __forceinline__ LaneCx lane_cx(int lc, int log2h) {
 // h = 2^log2h (32 <= h <= 1024 inside the wave), without the final scaling
 // and with the lazy sign sigma still to apply. FULL: h >= 1024, every
 // in-wave stage runs (known at compile time, so no stage is a branch).
-template <bool FULL>
+// RD: the format every stage's results are rounded to (DT_F32: none).
+template <bool FULL, int RD = DT_F32>
 __device__ __forceinline__ void fwht_rows(float (&y)[16], int log2h, const LaneCx& cx) {
 #pragma unroll
-  for (int h = 1; h < 16; h *= 2)
+  for (int h = 1; h < 16; h *= 2) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       if ((i & h) == 0) {
@@ -110,13 +143,15 @@ __device__ __forceinline__ void fwht_rows(float (&y)[16], int log2h, const LaneC
         y[i] = a + b;
         y[i + h] = a - b;
       }
+    round16<RD>(y);
+  }
   const int lb = FULL ? 6 : log2h - 4;  // chunk bits inside a block
-  if (lb > 0) TQ_DPP_FMAC16("quad_perm:[1,0,3,2]", cx.c[0], y);
-  if (lb > 1) TQ_DPP_FMAC16("quad_perm:[2,3,0,1]", cx.c[1], y);
-  if (lb > 2) TQ_DPP_FMAC16("row_half_mirror", cx.c[2], y);
-  if (lb > 3) TQ_DPP_FMAC16("row_mirror", cx.c[3], y);
-  if (lb > 4) swap_stage<4>(y);
-  if (lb > 5) swap_stage<5>(y);
+  if (lb > 0) { TQ_DPP_FMAC16("quad_perm:[1,0,3,2]", cx.c[0], y); round16<RD>(y); }
+  if (lb > 1) { TQ_DPP_FMAC16("quad_perm:[2,3,0,1]", cx.c[1], y); round16<RD>(y); }
+  if (lb > 2) { TQ_DPP_FMAC16("row_half_mirror", cx.c[2], y); round16<RD>(y); }
+  if (lb > 3) { TQ_DPP_FMAC16("row_mirror", cx.c[3], y); round16<RD>(y); }
+  if (lb > 4) swap_stage<4, RD>(y);
+  if (lb > 5) swap_stage<5, RD>(y);
 }
 
 // --------------------------------------------------------------- packing ---
@@ -236,16 +271,20 @@ __device__ __forceinline__ uint32_t sign_of(uint32_t w, int k) {
 // the current one is processed.
 //
 // ROT: stop after the rotation and store it (rpbh_forward of activation rows,
-// the forward's first step) to xrot instead of quantizing.
-template <int BITS, bool LSB, int NT, bool FULL, bool ROT = false>
+// the forward's first step) to xrot instead of quantizing. DT: the format of
+// the rows read and, with ROT, of xrot; for bf16 / fp16 every stage rounds
+// to that format as the page's forward does on such activations.
+template <int BITS, bool LSB, int NT, bool FULL, bool ROT = false, int DT = DT_F32>
 __global__ __launch_bounds__(256) void orbit_quantize_kernel(
-    const float* __restrict__ W, int64_t rows, int d, int log2h, float kh,
+    const void* __restrict__ W, int64_t rows, int d, int log2h, float kh,
     const int32_t* __restrict__ perm, const int8_t* __restrict__ signs, OrbitCodebook cb,
-    uint8_t* __restrict__ packed, float* __restrict__ norms, float* __restrict__ xrot) {
+    uint8_t* __restrict__ packed, float* __restrict__ norms, void* __restrict__ xrot) {
+  static_assert(ROT || DT == DT_F32, "the weight codec reads fp32 rows");
   extern __shared__ float lds[];
   float* rowbuf = lds;     // the row; later the cross-wave butterfly exchange
   float* bsum = lds + d;   // block (or, for h > 1024, tile) sums of squares
   constexpr int NTHR = 64 * NT;
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -258,10 +297,11 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
   const float ksig = kh * cx.sigma;
   const int64_t row_bytes = (int64_t)d * BITS / 8;
   const float eps = (float)1e-10;
-  const int nf4 = d >> 2;
+  constexpr int ES = DT == DT_F32 ? 4 : 2;  // bytes per element of a row
+  constexpr int KL = ES;                     // 16-byte loads per thread (d <= 1024 NT)
+  const int nl = d * ES / 16;               // 16-byte pieces per row
 
   // Byte offsets into the staged row and sign masks of this lane's elements.
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   uint32_t poff[16], sbits = 0;  // sbits: bit i set when signs_j = -1 for element i
   {
     const int cc = act ? c : 0;  // inactive lanes read chunk 0 and never use it
@@ -278,33 +318,59 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
     }
   }
 
-  // The next row, <= 4 x 16 bytes per thread (d <= 1024 NT). Loads past the
+  // The next row, <= KL x 16 bytes per thread (d <= 1024 NT). Loads past the
   // row's end re-read its last 16 bytes (kept unconditional so the values
-  // stay in registers); only those below the end reach LDS.
-  typedef float f32x4 __attribute__((ext_vector_type(4)));
-  f32x4 pre[4];
-  int fidx[4];
+  // stay in registers); only those below the end reach LDS, widened to fp32.
+  const char* Wb = static_cast<const char*>(W);
+  const int64_t row_in = (int64_t)d * ES;
+  u32x4 pre[KL];
+  int fidx[KL];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < KL; ++k) {
     const int f = tid + NTHR * k;
-    fidx[k] = f < nf4 ? f : nf4 - 1;
+    fidx[k] = f < nl ? f : nl - 1;
   }
   int64_t r = blockIdx.x;
   {
-    const f32x4* src = reinterpret_cast<const f32x4*>(W + (r < rows ? r : 0) * d);
+    const u32x4* src = reinterpret_cast<const u32x4*>(Wb + (r < rows ? r : 0) * row_in);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) pre[k] = src[fidx[k]];
+    for (int k = 0; k < KL; ++k) pre[k] = src[fidx[k]];
   }
   for (; r < rows; r += gridDim.x) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (tid + NTHR * k < nf4) reinterpret_cast<f32x4*>(rowbuf)[tid + NTHR * k] = pre[k];
+    for (int k = 0; k < KL; ++k) {
+      const int f = tid + NTHR * k;
+      if (f < nl) {
+        if constexpr (DT == DT_F32) {
+          reinterpret_cast<u32x4*>(rowbuf)[f] = pre[k];
+        } else {
+          u32x4 lo, hi;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const u32x4& src = pre[k];
+            const uint32_t w = src[e];
+            float f0, f1;
+            if constexpr (DT == DT_BF16) {
+              f0 = as_f(w << 16);
+              f1 = as_f(w & 0xffff0000u);
+            } else {
+              f0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+              f1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+            }
+            if (e < 2) { lo[2 * e] = as_u(f0); lo[2 * e + 1] = as_u(f1); }
+            else { hi[2 * e - 4] = as_u(f0); hi[2 * e - 3] = as_u(f1); }
+          }
+          reinterpret_cast<u32x4*>(rowbuf)[2 * f] = lo;
+          reinterpret_cast<u32x4*>(rowbuf)[2 * f + 1] = hi;
+        }
+      }
+    }
     __syncthreads();
     {
       const int64_t rn = r + gridDim.x < rows ? r + gridDim.x : r;
-      const f32x4* src = reinterpret_cast<const f32x4*>(W + rn * d);
+      const u32x4* src = reinterpret_cast<const u32x4*>(Wb + rn * row_in);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) pre[k] = src[fidx[k]];
+      for (int k = 0; k < KL; ++k) pre[k] = src[fidx[k]];
     }
 
     // y_j = W[perm_j] * signs_j.
@@ -319,7 +385,8 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
     // Butterflies inside the wave (index bits 0..9), then across waves
     // through LDS for blocks longer than 1024 (bits 10, 11): the lower tile
     // takes a + b, the upper b' - a' = a - b with the same lazy lane sign.
-    fwht_rows<FULL>(y, log2h, cx);
+    constexpr int RD = ROT ? DT : DT_F32;
+    fwht_rows<FULL, RD>(y, log2h, cx);
     if (log2h > 10) {
       float4* mine = reinterpret_cast<float4*>(rowbuf + 16 * c);
 #pragma unroll
@@ -342,15 +409,41 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
             y[4 * k + e] = upper ? ov[e] - a : a + ov[e];
           }
         }
+        round16<RD>(y);
       }
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) y[i] = y[i] * ksig;
+    round16<RD>(y);
     if constexpr (ROT) {
-      if (act) {
-        f32x4_t* dst = reinterpret_cast<f32x4_t*>(xrot + r * d + 16 * c);
+      // An exact zero here stands for a cancellation a - a or a + (-a), which
+      // IEEE arithmetic returns as +0; the lazy lane sign can leave -0 in its
+      // place. Adding +0 restores +0 (and changes nothing else), so rows
+      // without zero entries match the page's rotation bit for bit.
 #pragma unroll
-        for (int k = 0; k < 4; ++k) dst[k] = f32x4_t{y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3]};
+      for (int i = 0; i < 16; ++i) y[i] = y[i] + 0.0f;
+      if (act) {
+        if constexpr (DT == DT_F32) {
+          f32x4_t* dst = reinterpret_cast<f32x4_t*>(static_cast<float*>(xrot) + r * d + 16 * c);
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            dst[k] = f32x4_t{y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3]};
+        } else {
+          // the values are already in the format: the narrowing is exact
+          uint32_t w[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            if constexpr (DT == DT_BF16) {
+              w[k] = (as_u(y[2 * k]) >> 16) | (as_u(y[2 * k + 1]) & 0xffff0000u);
+            } else {
+              w[k] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[2 * k]) |
+                     ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[2 * k + 1]) << 16);
+            }
+          }
+          u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(xrot) + r * d + 16 * c);
+          dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+          dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+        }
       }
       __syncthreads();  // the row buffer is free for the next row
       continue;
@@ -663,15 +756,15 @@ hipError_t launch_dq_dt(int dt, int nt, const uint8_t* packed, const float* norm
   }
 }
 
-template <int NT, bool FULL>
-hipError_t launch_rot(const float* x, int64_t rows, int d, int log2h, float kh,
-                      const int32_t* perm, const int8_t* signs, float* xrot, int cus, hipStream_t s) {
+template <int NT, bool FULL, int DT>
+hipError_t launch_rot(const void* x, int64_t rows, int d, int log2h, float kh,
+                      const int32_t* perm, const int8_t* signs, void* xrot, int cus, hipStream_t s) {
   const size_t shm = (size_t)(d + kMaxBlocks) * sizeof(float);
   const int per_cu =
-      resident_blocks_per_cu(orbit_quantize_kernel<2, false, NT, FULL, true>, 64 * NT, shm);
+      resident_blocks_per_cu(orbit_quantize_kernel<2, false, NT, FULL, true, DT>, 64 * NT, shm);
   const int grid = grid_size(rows, cus, per_cu);
   OrbitCodebook cb{};
-  orbit_quantize_kernel<2, false, NT, FULL, true><<<grid, 64 * NT, shm, s>>>(
+  orbit_quantize_kernel<2, false, NT, FULL, true, DT><<<grid, 64 * NT, shm, s>>>(
       x, rows, d, log2h, kh, perm, signs, cb, nullptr, nullptr, xrot);
   return hipGetLastError();
 }
@@ -709,15 +802,13 @@ hipError_t launch_orbit_quantize(const float* W, int64_t rows, int64_t d, int bi
 #undef TQ_Q
 }
 
-hipError_t launch_orbit_rotate(const float* x, int64_t rows, int64_t d, const int32_t* perm,
-                               const int8_t* signs, float* xrot, int cus, hipStream_t s) {
-  const int64_t h = d & -d;
-  const int log2h = ilog2(h);
-  const float kh = (float)pow((double)h, -0.5);
-  const int di = (int)d;
+template <int DT>
+hipError_t launch_rot_dt(const void* x, int64_t rows, int di, int log2h, float kh,
+                         const int32_t* perm, const int8_t* signs, void* xrot, int cus,
+                         hipStream_t s) {
   const int nt = (di + 1023) >> 10;
   const bool full = log2h >= 10;
-#define TQ_R(N, F) launch_rot<N, F>(x, rows, di, log2h, kh, perm, signs, xrot, cus, s)
+#define TQ_R(N, F) launch_rot<N, F, DT>(x, rows, di, log2h, kh, perm, signs, xrot, cus, s)
   switch (nt) {
     case 1: return full ? TQ_R(1, true) : TQ_R(1, false);
     case 2: return full ? TQ_R(2, true) : TQ_R(2, false);
@@ -725,6 +816,20 @@ hipError_t launch_orbit_rotate(const float* x, int64_t rows, int64_t d, const in
     default: return full ? TQ_R(4, true) : TQ_R(4, false);
   }
 #undef TQ_R
+}
+
+hipError_t launch_orbit_rotate(const void* x, int dt, int64_t rows, int64_t d,
+                               const int32_t* perm, const int8_t* signs, void* xrot, int cus,
+                               hipStream_t s) {
+  const int64_t h = d & -d;
+  const int log2h = ilog2(h);
+  const float kh = (float)pow((double)h, -0.5);
+  const int di = (int)d;
+  switch (dt) {
+    case DT_F32: return launch_rot_dt<DT_F32>(x, rows, di, log2h, kh, perm, signs, xrot, cus, s);
+    case DT_BF16: return launch_rot_dt<DT_BF16>(x, rows, di, log2h, kh, perm, signs, xrot, cus, s);
+    default: return launch_rot_dt<DT_F16>(x, rows, di, log2h, kh, perm, signs, xrot, cus, s);
+  }
 }
 
 hipError_t launch_orbit_dequantize(const uint8_t* packed, const float* norms, int64_t rows,

@@ -104,11 +104,143 @@ def test_argument_errors(tq):
     cb = tq._host_f32([-1.0, -0.5, 0.5, 1.0])
     import ctypes
     p = ctypes.cast(cb, ctypes.c_void_p)
-    assert L.orbit_linear(None, 4, 100, None, None, 8, 2, p, 0, None, None, None) == 2  # d_in % 32
-    assert L.orbit_linear(None, 4, 96, None, None, 8, 5, p, 0, None, None, None) == 4
-    assert L.orbit_linear(None, 0, 96, None, None, 8, 2, p, 0, None, None, None) == 0
-    assert L.orbit_linear(None, 4, 96, None, None, 8, 2, p, 0, None, None, None) == 1
-    assert L.orbit_rotate(None, 4, 48, None, None, None, None) == 5
+    assert L.orbit_linear(None, 0, 4, 100, None, None, 8, 2, p, 0, None, None, None) == 2  # d_in % 32
+    assert L.orbit_linear(None, 0, 4, 96, None, None, 8, 5, p, 0, None, None, None) == 4
+    assert L.orbit_linear(None, 0, 0, 96, None, None, 8, 2, p, 0, None, None, None) == 0
+    assert L.orbit_linear(None, 0, 4, 96, None, None, 8, 2, p, 0, None, None, None) == 1
+    assert L.orbit_linear(None, 5, 4, 96, None, None, 8, 2, p, 0, None, None, None) == 3
+    assert L.orbit_rotate(None, 0, 4, 48, None, None, None, None) == 5
+    assert L.orbit_rotate(None, 7, 4, 64, None, None, None, None) == 3
     with pytest.raises(ValueError):
         tq.orbit_linear(torch.zeros(3, 96, device=DEV), torch.zeros(10, dtype=torch.uint8, device=DEV),
                         torch.zeros(8, device=DEV), 2, [-1.0, -0.5, 0.5, 1.0])
+
+
+# ----------------------------------------------- bf16 / fp16 activations ---
+# The page's forward in the activation's dtype: the rotation rounds every
+# stage to the format (checked bit for bit against the oracle's form of
+# it); W' = round(round(codebook) * round(norm)); the matmul accumulates in
+# fp32 on the matrix cores (order the library's) and rounds its output once:
+#   |y - y_ref| <= E + ulp_fmt(|y_ref| + E),  E = 2 K u sum|x_rot W'| + u |bias|.
+
+from parity_util import narrow_ulp  # noqa: E402
+
+LP = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def lp_tensor(a, fmt):
+    """fp32 values already in the format -> a tensor of that dtype (exact)."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(LP[fmt])
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [96, 256, 1024, 1536, 2048, 3072, 4096])
+@pytest.mark.parametrize("rows", [1, 7, 300])
+def test_rotate_lowp_bit_exact(tq, fmt, d, rows):
+    x = of.round_to(np.random.default_rng(d + rows).standard_normal((rows, d)).astype(np.float32)
+                    * 3.0, fmt)
+    perm, sg = datagen.rpbh_params(d)
+    got = tq.orbit_rotate(lp_tensor(x, fmt).to(DEV), perm.to(DEV), sg.to(DEV))
+    assert got.dtype == LP[fmt]
+    got = got.float().cpu().numpy()
+    ref = of.rpbh_forward_lowp(x, perm.numpy(), sg.numpy(), fmt)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", ["fp32", "bf16", "f16"])
+def test_rotate_rows_with_zeros(tq, fmt):
+    """Rows that hold exact zeros (half the entries, as after a ReLU) and a
+    row of equal entries: the values match the oracle; an exact zero of the
+    result may carry the other sign where the input held zeros (the page's
+    sign of such a zero follows the signs of the input zeros through every
+    stage), and is +0 where the zero is a cancellation of nonzero inputs."""
+    d = 1536
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((4, d)).astype(np.float32)
+    x[:3] *= rng.random((3, d)) < 0.5
+    x[3] = 1.0
+    perm, sg = datagen.rpbh_params(d)
+    if fmt == "fp32":
+        got = tq.orbit_rotate(torch.from_numpy(x).to(DEV), perm.to(DEV), sg.to(DEV)).cpu().numpy()
+        ref = oracle.rpbh_forward(x, perm, sg)
+    else:
+        x = of.round_to(x, fmt)
+        got = tq.orbit_rotate(lp_tensor(x, fmt).to(DEV), perm.to(DEV), sg.to(DEV))
+        got = got.float().cpu().numpy()
+        ref = of.rpbh_forward_lowp(x, perm.numpy(), sg.numpy(), fmt)
+    assert np.array_equal(got, ref)  # -0 == +0
+    assert np.array_equal(got[3].view(np.uint32), ref[3].view(np.uint32))
+    assert (ref[3] == 0).sum() > 0  # cancellations of nonzero entries
+
+
+def check_linear_lowp(tq, fmt, x_rot, packed, norms, d, bits, cb, bias=None, msb=True):
+    order = tq.TQ_MSB_FIRST if msb else tq.TQ_LSB_FIRST
+    y = tq.orbit_linear(lp_tensor(x_rot, fmt).to(DEV), torch.from_numpy(packed).to(DEV),
+                        torch.from_numpy(norms).to(DEV), bits, cb,
+                        None if bias is None else lp_tensor(bias, fmt).to(DEV), bit_order=order)
+    torch.cuda.synchronize()
+    assert y.dtype == LP[fmt]
+    got = y.float().cpu().numpy().astype(np.float64)
+    w = of.orbit_rotated_weight_lowp(packed, norms, d, bits, cb, fmt, msb).astype(np.float64)
+    ref = x_rot.astype(np.float64) @ w.T
+    E = 2 * d * U * (np.abs(x_rot).astype(np.float64) @ np.abs(w).T)
+    if bias is not None:
+        ref = ref + bias.astype(np.float64)[None, :]
+        E = E + U * np.abs(bias)[None, :]
+    bound = E + narrow_ulp((np.abs(ref) + E).astype(np.float32), LP[fmt])
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), (err.max(), (err / bound).max())
+    return float((err / bound).max())
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+@pytest.mark.parametrize("m", [1, 5, 64, 130, 300])
+@pytest.mark.parametrize("d,n,bits,msb", [(96, 100, 2, True), (1024, 129, 3, True),
+                                          (3072, 384, 4, False), (512, 1, 3, False),
+                                          (2048, 256, 2, True)])
+def test_linear_lowp(tq, fmt, m, d, n, bits, msb):
+    perm, sg, cb, packed, norms = quantized(n, d, bits, d + n + bits, msb)
+    x = of.round_to(np.random.default_rng(m).standard_normal((m, d)).astype(np.float32), fmt)
+    x_rot = of.rpbh_forward_lowp(x, perm.numpy(), sg.numpy(), fmt)
+    bias = (of.round_to(np.random.default_rng(n).standard_normal(n).astype(np.float32), fmt)
+            if m % 2 else None)
+    check_linear_lowp(tq, fmt, x_rot, packed, norms, d, bits, cb, bias, msb)
+
+
+def test_linear_lowp_many_row_tiles(tq):
+    """1024 rows (eight 128-row tiles) at the forward workload's width."""
+    perm, sg, cb, packed, norms = quantized(384, 3072, 3, 77)
+    x = of.round_to(np.random.default_rng(5).standard_normal((1024, 3072)).astype(np.float32),
+                    "bf16")
+    x_rot = of.rpbh_forward_lowp(x, perm.numpy(), sg.numpy(), "bf16")
+    check_linear_lowp(tq, "bf16", x_rot, packed, norms, 3072, 3, cb)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+def test_forward_lowp_config5(tq, fmt):
+    """The 12288 x 3072 weight at 3 bits; 64 activation rows of the format
+    through the whole forward (rotation bit for bit, then the linear layer)."""
+    d, bits = 3072, 3
+    w = datagen.orbit_weight().numpy()
+    perm, sg = datagen.rpbh_params(d)
+    cb = oracle.orbit_codebook(bits, d)
+    packed, norms = oracle.orbit_quantize(w, bits, perm, sg, cb)
+    x = of.round_to(np.random.default_rng(3).standard_normal((64, d)).astype(np.float32), fmt)
+    bias = of.round_to(np.random.default_rng(9).standard_normal(w.shape[0]).astype(np.float32)
+                       * 0.1, fmt)
+    xr = tq.orbit_rotate(lp_tensor(x, fmt).to(DEV), perm.to(DEV), sg.to(DEV))
+    x_rot = of.rpbh_forward_lowp(x, perm.numpy(), sg.numpy(), fmt)
+    assert np.array_equal(xr.float().cpu().numpy().view(np.uint32), x_rot.view(np.uint32))
+    r = check_linear_lowp(tq, fmt, x_rot, packed, norms, d, bits, cb, bias)
+    print(f"{fmt}: max error / bound = {r:.3e}")
+
+
+def test_lowp_argument_errors(tq):
+    x = torch.zeros(3, 96, dtype=torch.bfloat16, device=DEV)
+    pk = torch.zeros(8 * 96 * 2 // 8, dtype=torch.uint8, device=DEV)
+    nr = torch.ones(8, device=DEV)
+    with pytest.raises(ValueError):  # bias of another dtype
+        tq.orbit_linear(x, pk, nr, 2, [-1.0, -0.5, 0.5, 1.0], bias=torch.zeros(8, device=DEV))
+    with pytest.raises(ValueError):  # out of another dtype
+        tq.orbit_linear(x, pk, nr, 2, [-1.0, -0.5, 0.5, 1.0],
+                        out=torch.empty(3, 8, device=DEV))
