@@ -56,8 +56,10 @@ __device__ __forceinline__ f32x4v mfma_lp(u32x4v a, u32x4v b, f32x4v c) {
                                                   __builtin_bit_cast(f16x8v, b), c, 0, 0, 0);
 }
 
-constexpr int kLpBM = 128, kLpBN = 128, kLpBK = 32;
-constexpr int kLpRow = 40;  // padded LDS row (elements)
+constexpr int kLpBM = 128, kLpBN = 128, kLpBK = 64;
+constexpr int kLpRow = 72;  // padded LDS row (elements)
+constexpr int kLpRing = 4;  // K steps whose global loads are in flight
+constexpr size_t kLpSmallLds = 64 * 1024;  // the few-rows kernel's LDS ceiling
 
 template <int DT, int BITS, bool LSB>
 __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t m0 = (int64_t)blockIdx.y * kLpBM, n0 = (int64_t)blockIdx.x * kLpBN;
 
-  // This thread decodes 16 codes of W' row bn per step (half bh of the 32).
+  // This thread decodes 32 codes of W' row bn per step (half bh of the 64).
   const int bn = tid >> 1, bh = tid & 1;
   const bool nvalid = n0 + bn < N;
   const int64_t row_bytes = K * BITS / 8;
@@ -88,37 +90,49 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
     }
   }
 
-  // The next step's operands: two 16-byte pieces of x_rot rows per thread
-  // (piece f: row f / 4, elements 8 (f % 4) .. + 7) and 16 codes. Rows past
-  // M re-read row m0 (unconditional loads) and are zeroed when staged.
-  u32x4v av[2];
-  uint64_t raw;
-  auto fetch = [&](int64_t k0) {
+  // Per step, four 16-byte pieces of x_rot rows per thread (piece f: row
+  // f / 8, elements 8 (f % 8) .. + 7) and 32 codes. Rows past M re-read row
+  // m0 (their outputs are never stored). When K is an odd multiple of 32 the
+  // last step's upper half re-reads the lower half and is zeroed in x_rot.
+  const int64_t steps = (K + kLpBK - 1) / kLpBK;
+  u32x4v av[kLpRing][4];
+  uint64_t raw[kLpRing][2];
+  auto fetch = [&](int u, int64_t st) {
+    const int64_t s = st < steps ? st : steps - 1;
+    const int64_t k0 = s * kLpBK;
+    const bool hv = k0 + 32 < K;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const int f = tid + 256 * i;
-      const int64_t mr = m0 + (f >> 2) < M ? m0 + (f >> 2) : m0;
-      av[i] = *reinterpret_cast<const u32x4v*>(x + mr * K + k0 + 8 * (f & 3));
+      const int64_t mr = m0 + (f >> 3) < M ? m0 + (f >> 3) : m0;
+      const int col = (f & 7) >= 4 && !hv ? 8 * (f & 7) - 32 : 8 * (f & 7);
+      av[u][i] = *reinterpret_cast<const u32x4v*>(x + mr * K + k0 + col);
     }
-    raw = load_codes<BITS>(prow + (k0 / 16 + bh) * (2 * BITS));
+    const int64_t cg = k0 / 16 + (hv ? 2 * bh : 0);  // 16-code group
+#pragma unroll
+    for (int q = 0; q < 2; ++q) raw[u][q] = load_codes<BITS>(prow + (cg + q) * (2 * BITS));
   };
-  auto stage = [&](int buf) {
+  auto stage = [&](int u, int buf, int64_t st) {
+    const bool hv = st * kLpBK + 32 < K;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const int f = tid + 256 * i;
-      const bool mv = m0 + (f >> 2) < M;
       const u32x4v z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4v*>(&As[buf][(f >> 2) * kLpRow + 8 * (f & 3)]) = mv ? av[i] : z;
+      *reinterpret_cast<u32x4v*>(&As[buf][(f >> 3) * kLpRow + 8 * (f & 7)]) =
+          (f & 7) >= 4 && !hv ? z : av[u][i];
     }
-    uint32_t code[16];
-    unpack16<BITS, LSB>(raw, code);
-    uint32_t w[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      w[i] = (uint32_t)tbl[bn][code[2 * i]] | ((uint32_t)tbl[bn][code[2 * i + 1]] << 16);
-    u32x4v* dst = reinterpret_cast<u32x4v*>(&Bs[buf][bn * kLpRow + 16 * bh]);
-    dst[0] = u32x4v{w[0], w[1], w[2], w[3]};
-    dst[1] = u32x4v{w[4], w[5], w[6], w[7]};
+    for (int q = 0; q < 2; ++q) {
+      uint32_t code[16];
+      unpack16<BITS, LSB>(raw[u][q], code);
+      uint32_t w[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        w[e] = (uint32_t)tbl[bn][code[2 * e]] | ((uint32_t)tbl[bn][code[2 * e + 1]] << 16);
+      u32x4v* dst = reinterpret_cast<u32x4v*>(&Bs[buf][bn * kLpRow + 32 * bh + 16 * q]);
+      dst[0] = u32x4v{w[0], w[1], w[2], w[3]};
+      dst[1] = u32x4v{w[4], w[5], w[6], w[7]};
+    }
   };
 
   f32x4v acc[4][4];
@@ -127,31 +141,42 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
 
-  fetch(0);
+#pragma unroll
+  for (int u = 0; u < kLpRing; ++u) fetch(u, u);
   __syncthreads();  // tables
-  stage(0);
+  stage(0, 0, 0);
   __syncthreads();
-  int buf = 0;
-  for (int64_t k0 = 0; k0 < K; k0 += kLpBK) {
-    const bool more = k0 + kLpBK < K;
-    if (more) fetch(k0 + kLpBK);
-    u32x4v a[4], b[4];
-    const int koff = 8 * (lane >> 4);
+  // Step st multiplies LDS buffer st & 1 (staged during step st - 1 from ring
+  // slot st % 4), refills that slot with step st + 4, and stages step st + 1.
+  for (int64_t s0 = 0; s0 < steps; s0 += kLpRing) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[i] = *reinterpret_cast<const u32x4v*>(
-          &As[buf][(wm * 64 + 16 * i + (lane & 15)) * kLpRow + koff]);
+    for (int u = 0; u < kLpRing; ++u) {
+      const int64_t st = s0 + u;
+      if (st < steps) {
+        const int buf = u & 1;
+        const int koff = 8 * (lane >> 4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      b[j] = *reinterpret_cast<const u32x4v*>(
-          &Bs[buf][(wn * 64 + 16 * j + (lane & 15)) * kLpRow + koff]);
+        for (int kk = 0; kk < 2; ++kk) {
+          u32x4v a[4], b[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 4; ++i)
+            a[i] = *reinterpret_cast<const u32x4v*>(
+                &As[buf][(wm * 64 + 16 * i + (lane & 15)) * kLpRow + 32 * kk + koff]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_lp<DT>(a[i], b[j], acc[i][j]);
-    if (more) stage(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
+          for (int j = 0; j < 4; ++j)
+            b[j] = *reinterpret_cast<const u32x4v*>(
+                &Bs[buf][(wn * 64 + 16 * j + (lane & 15)) * kLpRow + 32 * kk + koff]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma_lp<DT>(a[i], b[j], acc[i][j]);
+        }
+        fetch(u, st + kLpRing);
+        asm volatile("" ::: "memory");  // the refill stays a full ring ahead
+        if (st + 1 < steps) stage((u + 1) % kLpRing, buf ^ 1, st + 1);
+        __syncthreads();
+      }
+    }
   }
 
   // y = round(acc + bias)
@@ -170,14 +195,198 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
   }
 }
 
+// Few rows (up to 64): a block owns 16 W' rows (one MFMA column tile) and
+// all MT 16-row tiles of x_rot; its four waves take every fourth K step of
+// 32 and add their partial tiles in LDS at the end, in a fixed order.
+//
+// The block's codes (16 rows, contiguous in memory) are first copied into LDS
+// in one coalesced sweep: read straight from HBM in the MFMA's order, each
+// wave would touch 16 rows 1 row apart per step, a comb of short pieces over
+// the whole weight that reopens every DRAM page many times. In LDS each row
+// is padded by one dword so that the 16 rows a step reads start in 16
+// different banks. x_rot (small,
+// shared by every block, L2-resident) goes straight into registers in the
+// MFMA layout: lane l reads 16 bytes of row 16 t + l % 16 at K offset
+// 8 (l / 16), and the 8 codes of W' row l % 16 at the same offset become its
+// B operand through a per-row table of code pairs: entry (a, b) holds the
+// two rounded products for codes a then b as one packed dword, so one LDS
+// read yields two operand elements. A ring of four K steps keeps the next
+// four steps' loads in flight while one is multiplied.
+template <int DT, int BITS, bool LSB, int MT>
+__global__ __launch_bounds__(256) void orbit_linear_lp_small_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, const uint8_t* __restrict__ packed,
+    const float* __restrict__ norms, int64_t N, OrbitCodebook cb,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y) {
+  constexpr int L = 1 << BITS, P = L * L;
+  constexpr int RING = 4;
+  extern __shared__ __attribute__((aligned(16))) uint32_t lsm[];
+  const int row_bytes = (int)(K * BITS / 8);
+  const int row_dw = row_bytes / 4 + 1;       // padded LDS row, dwords
+  const int code_words = (16 * row_dw + 3) / 4 * 4;
+  uint32_t* codes = lsm;
+  uint32_t* ptab = lsm + code_words;
+  float* red = reinterpret_cast<float*>(ptab + 16 * P);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+
+  // the block's code rows -> LDS (rows past N are left unset: their table
+  // entries are zero)
+  {
+    const int nrows = N - n0 < 16 ? (int)(N - n0) : 16;
+    const int rw = row_bytes / 4;  // dwords per row (a row is a multiple of 4 bytes)
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(packed + n0 * row_bytes);
+    for (int c = tid; c < rw; c += 256) {
+      uint32_t v[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[r] = r < nrows ? src[r * rw + c] : 0u;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) codes[r * row_dw + c] = v[r];
+    }
+  }
+  // Pair tables of the block's 16 rows (zeros past N). Entry index: the
+  // pair's bits as they sit in the stream -- (a << BITS) | b for MSB-first
+  // (code a first), a | (b << BITS) for LSB-first.
+  for (int e = tid; e < 16 * P; e += 256) {
+    const int r = e / P, pr = e % P;
+    const int a = LSB ? pr % L : pr / L, b = LSB ? pr / L : pr % L;
+    const int64_t n = n0 + r;
+    const float nl = n < N ? lp_float<DT>(lp_bits<DT>(norms[n])) : 0.0f;
+    const float wa = lp_float<DT>(lp_bits<DT>(cb.cb[a])) * nl;
+    const float wb = lp_float<DT>(lp_bits<DT>(cb.cb[b])) * nl;
+    ptab[e] = lp_bits<DT>(wa) | (lp_bits<DT>(wb) << 16);
+  }
+
+  const int j = lane >> 4;          // K group of 8 inside a step
+  const int nr = lane & 15;         // W' row inside the block
+  const uint8_t* crow = reinterpret_cast<const uint8_t*>(codes + nr * row_dw);
+  const uint32_t* tb = ptab + nr * P;
+  const uint16_t* xr[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int64_t m = 16 * t + nr < M ? 16 * t + nr : M - 1;
+    xr[t] = x + m * K + 8 * j;
+  }
+  // This lane's group (group j of a step's four) from the staged row: BITS = 3
+  // takes the two dwords its 3 bytes straddle (inside the step's 12 bytes).
+  const int glo = (3 * j) >> 2, ghi = glo + 1 < 3 ? glo + 1 : 2, gsh = 8 * ((3 * j) & 3);
+  auto group = [&](int s) -> uint32_t {
+    const uint8_t* g = crow + s * (4 * BITS);
+    if constexpr (BITS == 4) {
+      return reinterpret_cast<const uint32_t*>(g)[j];
+    } else if constexpr (BITS == 2) {
+      return reinterpret_cast<const uint16_t*>(g)[j];
+    } else {
+      const uint32_t* d = reinterpret_cast<const uint32_t*>(g);
+      return __builtin_amdgcn_alignbit(d[ghi], d[glo], gsh) & 0xffffffu;
+    }
+  };
+  // the group's 4 code pairs in stream order -> 4 packed operand dwords
+  auto decode = [&](uint32_t g, u32x4v& b) {
+    uint32_t w = g;
+    if constexpr (!LSB) {
+      if constexpr (BITS == 4) w = __builtin_bswap32(g);
+      else if constexpr (BITS == 3) w = (g >> 16) | (g & 0xff00u) | ((g & 0xffu) << 16);
+      else w = ((g & 0xffu) << 8) | (g >> 8);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t idx = LSB ? (w >> (2 * BITS * p)) & (P - 1)
+                               : (w >> (BITS * (6 - 2 * p))) & (P - 1);
+      b[p] = tb[idx];
+    }
+  };
+
+  f32x4v acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+  const int steps = (int)(K / 32);
+  // Wave w takes steps w, w + 4, ... (nw of them, possibly none when K has
+  // fewer than four steps); ring slot u holds the x_rot operands of its step
+  // i + u. Loads past the wave's last step re-read that step (step 0 for a
+  // wave without steps) and are never used.
+  const int nw = steps > wave ? (steps - wave + 3) >> 2 : 0;
+  const int s_last = nw > 0 ? wave + 4 * (nw - 1) : 0;
+  u32x4v ar[RING][MT];
+  auto fetch = [&](int u, int i) {
+    const int s = i < nw ? wave + 4 * i : s_last;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) ar[u][t] = *reinterpret_cast<const u32x4v*>(xr[t] + 32 * s);
+  };
+  auto step = [&](int u, int i) {
+    u32x4v b;
+    decode(group(wave + 4 * i), b);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = mfma_lp<DT>(ar[u][t], b, acc[t]);
+  };
+#pragma unroll
+  for (int u = 0; u < RING; ++u) fetch(u, u);
+  __syncthreads();  // codes and pair tables
+  int i = 0;
+  for (; i + RING <= nw; i += RING) {
+#pragma unroll
+    for (int u = 0; u < RING; ++u) {
+      step(u, i + u);
+      fetch(u, i + u + RING);
+      // keep the refill here, a full ring ahead of its use (the scheduler
+      // would otherwise sink every refill to the end of the iteration)
+      asm volatile("" ::: "memory");
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < RING - 1; ++u)
+    if (i + u < nw) step(u, i + u);
+
+  // partial tiles -> LDS; wave-ordered sums; bias; one rounding
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave * MT * 256 + (t * 4 + r) * 64 + lane] = acc[t][r];
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < MT; ++q) {
+    const int v = tid + 256 * q;  // (t * 4 + r) * 64 + lane'
+    const float sum = ((red[v] + red[MT * 256 + v]) + red[2 * MT * 256 + v]) + red[3 * MT * 256 + v];
+    const int ln = v & 63, r = (v >> 6) & 3, t = v >> 8;
+    const int64_t m = 16 * t + 4 * (ln >> 4) + r;
+    const int64_t nn = n0 + (ln & 15);
+    if (m < M && nn < N) {
+      const float bv = bias ? lp_float<DT>(bias[nn]) : 0.0f;
+      y[m * N + nn] = (uint16_t)lp_bits<DT>(sum + bv);
+    }
+  }
+}
+
+// LDS bytes of the small kernel: the block's codes, pair tables, partials.
+inline size_t lp_small_lds(int64_t K, int bits, int mt) {
+  const int64_t row_dw = K * bits / 32 + 1;
+  return (size_t)((16 * row_dw + 3) / 4 * 16) + (size_t)16 * (1 << (2 * bits)) * 4 +
+         (size_t)4 * mt * 256 * 4;
+}
+
 template <int DT, int BITS, bool LSB>
 hipError_t launch_lp(const void* x, int64_t M, int64_t K, const uint8_t* packed,
                      const float* norms, int64_t N, const OrbitCodebook& cb, const void* bias,
                      void* y, hipStream_t s) {
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  const uint16_t* bp = static_cast<const uint16_t*>(bias);
+  uint16_t* yp = static_cast<uint16_t*>(y);
+  const int mt = (int)((M + 15) / 16);
+  if (M <= 64 && lp_small_lds(K, BITS, mt) <= kLpSmallLds) {
+    const dim3 grid((unsigned)((N + 15) / 16));
+    const size_t shm = lp_small_lds(K, BITS, mt);
+#define TQ_SM(T) orbit_linear_lp_small_kernel<DT, BITS, LSB, T><<<grid, 256, shm, s>>>( \
+    xp, M, K, packed, norms, N, cb, bp, yp)
+    if (M <= 16) TQ_SM(1);
+    else if (M <= 32) TQ_SM(2);
+    else if (M <= 48) TQ_SM(3);
+    else TQ_SM(4);
+#undef TQ_SM
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((N + kLpBN - 1) / kLpBN), (unsigned)((M + kLpBM - 1) / kLpBM));
-  orbit_linear_lp_kernel<DT, BITS, LSB><<<grid, 256, 0, s>>>(
-      static_cast<const uint16_t*>(x), M, K, packed, norms, N, cb,
-      static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y));
+  orbit_linear_lp_kernel<DT, BITS, LSB><<<grid, 256, 0, s>>>(xp, M, K, packed, norms, N, cb, bp,
+                                                             yp);
   return hipGetLastError();
 }
 

@@ -194,7 +194,7 @@ def check_linear_lowp(tq, fmt, x_rot, packed, norms, d, bits, cb, bias=None, msb
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
-@pytest.mark.parametrize("m", [1, 5, 64, 130, 300])
+@pytest.mark.parametrize("m", [1, 5, 20, 40, 64, 130, 300])
 @pytest.mark.parametrize("d,n,bits,msb", [(96, 100, 2, True), (1024, 129, 3, True),
                                           (3072, 384, 4, False), (512, 1, 3, False),
                                           (2048, 256, 2, True)])
@@ -244,3 +244,14 @@ def test_lowp_argument_errors(tq):
     with pytest.raises(ValueError):  # out of another dtype
         tq.orbit_linear(x, pk, nr, 2, [-1.0, -0.5, 0.5, 1.0],
                         out=torch.empty(3, 8, device=DEV))
+
+
+@pytest.mark.parametrize("m", [1, 20, 130])
+@pytest.mark.parametrize("d", [32, 64, 96, 160])
+def test_linear_lowp_short_k(tq, m, d):
+    """K of one to five 32-wide steps: fewer steps than the few-rows kernel
+    has waves, and an odd number of 32-column halves for the many-rows one."""
+    perm, sg, cb, packed, norms = quantized(48, d, 3, d + m)
+    x = of.round_to(np.random.default_rng(m + d).standard_normal((m, d)).astype(np.float32), "bf16")
+    x_rot = of.rpbh_forward_lowp(x, perm.numpy(), sg.numpy(), "bf16")
+    check_linear_lowp(tq, "bf16", x_rot, packed, norms, d, 3, cb)
