@@ -61,15 +61,45 @@ constexpr int kLpRow = 72;  // padded LDS row (elements)
 constexpr int kLpRing = 4;  // K steps whose global loads are in flight
 constexpr size_t kLpSmallLds = 64 * 1024;  // the few-rows kernel's LDS ceiling
 
+// Code pairs of a 64-bit chunk of 16 codes (stream order), as table indices:
+// the pair's bits as they sit in the stream, (a << BITS) | b for MSB-first
+// and a | (b << BITS) for LSB-first (a = the earlier code).
+template <int BITS, bool LSB>
+__device__ __forceinline__ void pairs16(uint64_t acc, uint32_t (&pi)[8]) {
+  constexpr uint32_t mask = (1u << (2 * BITS)) - 1;
+  if constexpr (LSB) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) pi[p] = (uint32_t)(acc >> (2 * BITS * p)) & mask;
+  } else if constexpr (BITS == 3) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const uint32_t le = (uint32_t)(acc >> (24 * g)) & 0xffffffu;
+      const uint32_t w = (le >> 16) | (le & 0xff00u) | ((le & 0xffu) << 16);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) pi[4 * g + p] = (w >> (18 - 6 * p)) & mask;
+    }
+  } else {
+    // BITS = 2: each byte holds two pairs, the earlier in its high half
+#pragma unroll
+    for (int p = 0; p < 8; ++p) pi[p] = (uint32_t)(acc >> (8 * (p >> 1) + 4 - 4 * (p & 1))) & mask;
+  }
+}
+
 template <int DT, int BITS, bool LSB>
 __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, const uint8_t* __restrict__ packed,
     const float* __restrict__ norms, int64_t N, OrbitCodebook cb,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y) {
   constexpr int L = 1 << BITS;
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kLpBM * kLpRow];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kLpBN * kLpRow];
-  __shared__ uint16_t tbl[kLpBN][16];
+  // 2- and 3-bit codes decode through a table of code pairs (one dword per
+  // pair, both rounded products); 4-bit codes, whose pair table would not
+  // fit, through a table of single values.
+  constexpr bool PAIRS = BITS <= 3;
+  constexpr int TW = PAIRS ? L * L : L / 2;  // dwords per row's table
+  __shared__ __attribute__((aligned(16))) uint16_t As[1][kLpBM * kLpRow];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[1][kLpBN * kLpRow];
+  __shared__ uint32_t tbw[kLpBN * TW];
+  uint16_t (*tbl)[16] = reinterpret_cast<uint16_t (*)[16]>(tbw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t m0 = (int64_t)blockIdx.y * kLpBM, n0 = (int64_t)blockIdx.x * kLpBN;
@@ -80,13 +110,21 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
   const int64_t row_bytes = K * BITS / 8;
   const uint8_t* prow = packed + (nvalid ? n0 + bn : 0) * row_bytes;
   {
-    // row bn's table: round(round(codebook[c]) * round(norm)); rows past N
-    // get zeros
+    // row bn's table of round(round(codebook[c]) * round(norm)) (zeros for
+    // rows past N), split between the row's two threads
     const float nl = nvalid ? lp_float<DT>(lp_bits<DT>(norms[n0 + bn])) : 0.0f;
+    if constexpr (PAIRS) {
+      for (int e = bh; e < L * L; e += 2) {
+        const int a = LSB ? e % L : e / L, b = LSB ? e / L : e % L;
+        tbw[bn * TW + e] = lp_bits<DT>(lp_float<DT>(lp_bits<DT>(cb.cb[a])) * nl) |
+                           (lp_bits<DT>(lp_float<DT>(lp_bits<DT>(cb.cb[b])) * nl) << 16);
+      }
+    } else {
 #pragma unroll
-    for (int c = 0; c < L; c += 2) {
-      const int cc = c + bh;
-      tbl[bn][cc] = (uint16_t)lp_bits<DT>(lp_float<DT>(lp_bits<DT>(cb.cb[cc])) * nl);
+      for (int c = 0; c < L; c += 2) {
+        const int cc = c + bh;
+        tbl[bn][cc] = (uint16_t)lp_bits<DT>(lp_float<DT>(lp_bits<DT>(cb.cb[cc])) * nl);
+      }
     }
   }
 
@@ -123,12 +161,19 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      uint32_t code[16];
-      unpack16<BITS, LSB>(raw[u][q], code);
       uint32_t w[8];
+      if constexpr (PAIRS) {
+        uint32_t pi[8];
+        pairs16<BITS, LSB>(raw[u][q], pi);
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        w[e] = (uint32_t)tbl[bn][code[2 * e]] | ((uint32_t)tbl[bn][code[2 * e + 1]] << 16);
+        for (int e = 0; e < 8; ++e) w[e] = tbw[bn * TW + pi[e]];
+      } else {
+        uint32_t code[16];
+        unpack16<BITS, LSB>(raw[u][q], code);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          w[e] = (uint32_t)tbl[bn][code[2 * e]] | ((uint32_t)tbl[bn][code[2 * e + 1]] << 16);
+      }
       u32x4v* dst = reinterpret_cast<u32x4v*>(&Bs[buf][bn * kLpRow + 32 * bh + 16 * q]);
       dst[0] = u32x4v{w[0], w[1], w[2], w[3]};
       dst[1] = u32x4v{w[4], w[5], w[6], w[7]};
@@ -144,16 +189,18 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
 #pragma unroll
   for (int u = 0; u < kLpRing; ++u) fetch(u, u);
   __syncthreads();  // tables
-  stage(0, 0, 0);
-  __syncthreads();
-  // Step st multiplies LDS buffer st & 1 (staged during step st - 1 from ring
-  // slot st % 4), refills that slot with step st + 4, and stages step st + 1.
+  // Step st stages ring slot st % 4 into the LDS tiles, refills the slot
+  // with step st + 4 and multiplies; one set of tiles, two barriers a step.
   for (int64_t s0 = 0; s0 < steps; s0 += kLpRing) {
 #pragma unroll
     for (int u = 0; u < kLpRing; ++u) {
       const int64_t st = s0 + u;
       if (st < steps) {
-        const int buf = u & 1;
+        const int buf = 0;
+        stage(u, 0, st);
+        fetch(u, st + kLpRing);
+        asm volatile("" ::: "memory");  // the refill stays a full ring ahead
+        __syncthreads();
         const int koff = 8 * (lane >> 4);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -171,9 +218,6 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = mfma_lp<DT>(a[i], b[j], acc[i][j]);
         }
-        fetch(u, st + kLpRing);
-        asm volatile("" ::: "memory");  // the refill stays a full ring ahead
-        if (st + 1 < steps) stage((u + 1) % kLpRing, buf ^ 1, st + 1);
         __syncthreads();
       }
     }
