@@ -91,6 +91,11 @@ class Timer:
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
+        # A spin kernel first, long enough for the host to enqueue every timed
+        # launch behind it: the launches then run back to back and each event
+        # pair brackets device time only, not the host's launch overhead.
+        with torch.cuda.stream(self.stream):
+            torch.cuda._sleep(int(iters * 100_000))
         evs = []
         for _ in range(iters):
             e0 = torch.cuda.Event(enable_timing=True)
