@@ -94,9 +94,17 @@ __device__ __forceinline__ void group_fwht(float (&x)[8], int r) {
   for (int i = 0; i < 8; ++i) x[i] = lane_butterfly<3>(x[i], c3);
 }
 
-// Sign of element j = 8r + i from the 128-bit mask.
+// Sign of element j = 8r + i from the 128-bit mask (the word is selected
+// from the scalar kernel arguments, not loaded per lane).
 __device__ __forceinline__ bool mask_bit(const SignMask& m, int r, int i) {
-  return (m.w[r >> 2] >> (8 * (r & 3) + i)) & 1u;
+  // readfirstlane keeps the four words in scalar registers (a select on
+  // them is otherwise turned back into a per-lane load)
+  const uint32_t w0 = __builtin_amdgcn_readfirstlane(m.w[0]);
+  const uint32_t w1 = __builtin_amdgcn_readfirstlane(m.w[1]);
+  const uint32_t w2 = __builtin_amdgcn_readfirstlane(m.w[2]);
+  const uint32_t w3 = __builtin_amdgcn_readfirstlane(m.w[3]);
+  const uint32_t w = (r & 8) ? ((r & 4) ? w3 : w2) : ((r & 4) ? w1 : w0);
+  return (w >> (8 * (r & 3) + i)) & 1u;
 }
 
 // This lane's 24 index bits and the (norm, scale) pair of one record.
@@ -154,41 +162,59 @@ __global__ __launch_bounds__(256) void tq3_attn_partial_kernel(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (threadIdx.x < 64)
     ctab[threadIdx.x] = make_float2(tq3_centroid_a(threadIdx.x & 7), tq3_centroid_a(threadIdx.x >> 3));
+  __syncthreads();  // ctab
 
-  // Copy this wave's records into LDS with direct global-to-LDS dword loads:
-  // one instruction moves the 4 groups' records of one token slot (lane
-  // 16a + d: dword min(d, 13) of group a's record). Slots past the chunk's
-  // end re-read token t0's record, which is never used.
-  const int64_t t0 = (int64_t)blockIdx.x * chunk;
-  const int64_t t1 = t0 + chunk < n_tok ? t0 + chunk : n_tok;
-  const int nk = (int)((t1 - t0 + kAttnGroups - 1) / kAttnGroups);  // token slots per group
-  {
-    const int a = lane >> 4, d = lane & 15;
-    const int dd = d < 14 ? d : 13;
-    for (int k = 0; k < nk; ++k) {
-      const int64_t t = t0 + 4 * wave + a + (int64_t)kAttnGroups * k;
-      const int64_t rec = (t < t1 ? t : t0) * hkv + kv;
-      typedef __attribute__((address_space(3))) void lds_void;
-      typedef __attribute__((address_space(1))) void glb_void;
-      __builtin_amdgcn_global_load_lds((glb_void*)(krec + rec * 56 + 4 * dd),
-                                       (lds_void*)&stage[wave][k][0][0][0], 4, 0, 0);
-      __builtin_amdgcn_global_load_lds((glb_void*)(vrec + rec * 56 + 4 * dd),
-                                       (lds_void*)&stage[wave][k][1][0][0], 4, 0, 0);
-    }
-  }
-
-  // Rotated queries of the G heads: lane r keeps elements 8r .. 8r+7.
-  float qr[G][8];
+  // The G heads' query elements 8r .. 8r+7 of lane r, loaded before the
+  // records so that waiting for them never waits for the record copies.
+  uint4 qraw[G][2];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const int64_t off = (int64_t)(kv * G + h) * 128 + 8 * r;
     if constexpr (QDT == DT_F32) {
-      const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(q) + off);
-      const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(q) + off + 4);
-      qr[h][0] = a.x; qr[h][1] = a.y; qr[h][2] = a.z; qr[h][3] = a.w;
-      qr[h][4] = b.x; qr[h][5] = b.y; qr[h][6] = b.z; qr[h][7] = b.w;
+      qraw[h][0] = *reinterpret_cast<const uint4*>(static_cast<const float*>(q) + off);
+      qraw[h][1] = *reinterpret_cast<const uint4*>(static_cast<const float*>(q) + off + 4);
     } else {
-      const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + off);
+      qraw[h][0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + off);
+      qraw[h][1] = qraw[h][0];
+    }
+  }
+
+  // This wave's records, one dword per lane and record (lane 16a + d holds
+  // dword min(d, 13) of group a's record), for all 16 token slots of the
+  // chunk, K and V, in registers: slots past the chunk's end re-read token
+  // t0's record, which is never used. Each slot goes to LDS just before the
+  // loop reads it, so the loop waits only for the loads of the slots it
+  // reaches (the later ones stay in flight). (Copies straight into LDS would
+  // not overlap: the compiler waits for every such copy before any later
+  // LDS read.)
+  const int64_t t0 = (int64_t)blockIdx.x * chunk;
+  const int64_t t1 = t0 + chunk < n_tok ? t0 + chunk : n_tok;
+  const int nk = (int)((t1 - t0 + kAttnGroups - 1) / kAttnGroups);  // token slots per group
+  uint32_t kraw[kAttnTokPerGroup], vraw[kAttnTokPerGroup];
+  {
+    const int a = lane >> 4, d = lane & 15;
+    const int dd = d < 14 ? d : 13;
+#pragma unroll
+    for (int k = 0; k < kAttnTokPerGroup; ++k) {
+      const int64_t t = t0 + 4 * wave + a + (int64_t)kAttnGroups * k;
+      const int64_t rec = (t < t1 ? t : t0) * hkv + kv;
+      kraw[k] = *reinterpret_cast<const uint32_t*>(krec + rec * 56 + 4 * dd);
+      vraw[k] = *reinterpret_cast<const uint32_t*>(vrec + rec * 56 + 4 * dd);
+      // keeps the loads in slot order, as the loop's waits assume
+      asm volatile("" ::: "memory");
+    }
+  }
+
+  // Rotated queries: lane r keeps elements 8r .. 8r+7.
+  float qr[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    if constexpr (QDT == DT_F32) {
+      const uint4 a = qraw[h][0], b = qraw[h][1];
+      qr[h][0] = as_f(a.x); qr[h][1] = as_f(a.y); qr[h][2] = as_f(a.z); qr[h][3] = as_f(a.w);
+      qr[h][4] = as_f(b.x); qr[h][5] = as_f(b.y); qr[h][6] = as_f(b.z); qr[h][7] = as_f(b.w);
+    } else {
+      const uint4 a = qraw[h][0];
       const uint32_t w[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
@@ -208,7 +234,6 @@ __global__ __launch_bounds__(256) void tq3_attn_partial_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) qr[h][i] = qr[h][i] * qscale;
   }
-  __syncthreads();  // ctab
 
   const int dsel = (3 * r) >> 2;
   const uint32_t shift = (24u * r) & 31u;
@@ -221,9 +246,6 @@ __global__ __launch_bounds__(256) void tq3_attn_partial_kernel(
     for (int i = 0; i < 8; ++i) acc[h][i] = 0.0f;
   }
   const char* tb = reinterpret_cast<const char*>(ctab);
-  // The wave's records are in LDS once its loads are done (the queries'
-  // loads above overlapped them); no other wave reads them.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   const uint32_t* my = &stage[wave][0][0][grp & 3][0];
   // Token slots k = 0, 1, ... of this group (token t0 + grp + 16 k), TB per
   // iteration; the TB scores of each head share one max update. TB shrinks
@@ -231,7 +253,16 @@ __global__ __launch_bounds__(256) void tq3_attn_partial_kernel(
   constexpr int TB = ATTN_TB(G);
   // this group's tokens: the first nkg slots (groups differ by at most one)
   const int nkg = (int)((t1 - t0 - grp + kAttnGroups - 1) / kAttnGroups);
-  for (int k0 = 0; k0 < nkg; k0 += TB) {
+#pragma unroll
+  for (int it = 0; it < kAttnTokPerGroup / TB; ++it) {
+    const int k0 = it * TB;
+    if (k0 >= nkg) break;
+    // this iteration's slots -> LDS (only this wave reads them)
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      (&stage[wave][k0 + u][0][0][0])[lane] = kraw[k0 + u];
+      (&stage[wave][k0 + u][1][0][0])[lane] = vraw[k0 + u];
+    }
     const int64_t tb0 = t0 + grp + (int64_t)kAttnGroups * k0;
     RecPart kp[TB], vp[TB];
 #pragma unroll
@@ -299,6 +330,9 @@ __global__ __launch_bounds__(256) void tq3_attn_partial_kernel(
         for (int i = 0; i < 8; ++i) acc[h][i] = __builtin_fmaf(pw, cv[i], acc[h][i]);
       }
     }
+    // keeps the next iteration's slot writes (and so the waits for their
+    // loads) from moving up into this one
+    asm volatile("" ::: "memory");
   }
 
   // Merge the 16 groups: weights 2^(m_g - M); groups that saw no token have
@@ -346,84 +380,82 @@ __global__ __launch_bounds__(256) void tq3_attn_partial_kernel(
   }
 }
 
-// One 1024-thread block per query head: merge the chunk partials (eight
-// slices of the chunks, 128 elements each), divide by the softmax sum,
-// rotate back (S K H) and store.
+// One 1024-thread block per query head. Slice sl (128 threads, one element
+// each) merges chunks sl, sl + 8, ... with the online rule (running maximum,
+// sum and accumulator, rescaled when the maximum grows); after one barrier
+// the first wave merges the eight slices, divides by the softmax sum, runs
+// the inverse rotation (S K H) on its 2 x 64 elements -- the stage on
+// element bit 6 in registers, bits 0..5 across lanes -- and stores.
 constexpr int kCombineSlices = 8;
 template <int ODT>
 __global__ __launch_bounds__(1024) void tq3_attn_combine_kernel(const float* __restrict__ ws,
                                                                int nchunk, SignMask mask,
                                                                void* __restrict__ out) {
-  __shared__ float red[kCombineSlices][128];
-  __shared__ float fsum[kCombineSlices][128];
-  __shared__ float buf[128];
+  __shared__ float sacc[kCombineSlices][128];
+  __shared__ float smax[kCombineSlices], ssum[kCombineSlices];
   const int h = blockIdx.x;
   const int j = threadIdx.x & 127, sl = threadIdx.x >> 7;
   const float* part = ws + (int64_t)h * nchunk * kPartFloats;
-  // the maximum over all chunks
-  float mx = -__builtin_inff();
-  for (int c = threadIdx.x; c < nchunk; c += 1024) mx = __builtin_fmaxf(mx, part[c * kPartFloats]);
-  red[sl][j] = mx;
-  __syncthreads();
-  if (threadIdx.x < 128) {
-    float v = red[0][j];
-#pragma unroll
-    for (int k = 1; k < kCombineSlices; ++k) v = __builtin_fmaxf(v, red[k][j]);
-    fsum[0][j] = v;
-  }
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    float v = __builtin_fmaxf(fsum[0][threadIdx.x], fsum[0][threadIdx.x + 64]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
-    if (threadIdx.x == 0) buf[0] = v;
-  }
-  __syncthreads();
-  mx = buf[0];
-  __syncthreads();
-  // slice sl sums chunks sl, sl + kCombineSlices, ...: softmax sum and accumulators
-  float a = 0.0f, ls = 0.0f;
-#pragma unroll 16
+  float m = -__builtin_inff(), l = 0.0f, a = 0.0f;
+#pragma unroll 8
   for (int c = sl; c < nchunk; c += kCombineSlices) {
-    const float* pc = part + c * kPartFloats;
-    const float f = __builtin_amdgcn_exp2f(pc[0] - mx);
-    ls = __builtin_fmaf(pc[1], f, ls);
-    a = __builtin_fmaf(pc[4 + j], f, a);
+    const float* pc = part + (int64_t)c * kPartFloats;
+    const float mc = pc[0], lc = pc[1], ac = pc[4 + j];
+    const float mn = __builtin_fmaxf(m, mc);
+    // a chunk never has m = -inf (it holds at least one token), so mn is finite
+    const float fo = __builtin_amdgcn_exp2f(m - mn), fc = __builtin_amdgcn_exp2f(mc - mn);
+    l = __builtin_fmaf(l, fo, lc * fc);
+    a = __builtin_fmaf(a, fo, ac * fc);
+    m = mn;
   }
-  red[sl][j] = a;
-  fsum[sl][j] = ls;
-  __syncthreads();
-  if (threadIdx.x < 128) {
-    float at = red[0][j], lt = fsum[0][j];
-#pragma unroll
-    for (int k = 1; k < kCombineSlices; ++k) {
-      at = at + red[k][j];
-      lt = lt + fsum[k][j];
-    }
-    buf[j] = at / lt;
+  sacc[sl][j] = a;
+  if (j == 0) {
+    smax[sl] = m;
+    ssum[sl] = l;
   }
   __syncthreads();
-  // Unnormalised Hadamard transform in LDS, stage hh pairs (j, j ^ hh).
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  float mx = smax[0];
 #pragma unroll
-  for (int hh = 1; hh < 128; hh *= 2) {
-    float x = 0.0f, y = 0.0f;
-    if (threadIdx.x < 128) {
-      x = buf[j];
-      y = buf[j ^ hh];
-    }
-    __syncthreads();
-    if (threadIdx.x < 128) buf[j] = (j & hh) ? y - x : x + y;
-    __syncthreads();
+  for (int k = 1; k < kCombineSlices; ++k) mx = __builtin_fmaxf(mx, smax[k]);
+  float lt = 0.0f, x0 = 0.0f, x1 = 0.0f;  // elements lane and lane + 64
+#pragma unroll
+  for (int k = 0; k < kCombineSlices; ++k) {
+    // a slice without chunks has m = -inf and weighs 0
+    const float f = smax[k] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(smax[k] - mx);
+    lt = __builtin_fmaf(ssum[k], f, lt);
+    x0 = __builtin_fmaf(sacc[k][lane], f, x0);
+    x1 = __builtin_fmaf(sacc[k][lane + 64], f, x1);
   }
-  if (threadIdx.x >= 128) return;
-  float o = buf[j] * kInvSqrt128A;
-  if ((mask.w[j >> 5] >> (j & 31)) & 1u) o = -o;
-  if constexpr (ODT == DT_F32) {
-    static_cast<float*>(out)[(int64_t)h * 128 + j] = o;
-  } else if constexpr (ODT == DT_BF16) {
-    static_cast<__bf16*>(out)[(int64_t)h * 128 + j] = (__bf16)o;
-  } else {
-    static_cast<_Float16*>(out)[(int64_t)h * 128 + j] = (_Float16)o;
+  x0 = x0 / lt;
+  x1 = x1 / lt;
+  // Unnormalised Hadamard transform: element j pairs with j ^ hh, the lower
+  // taking the sum and the upper the lower minus itself.
+  {
+    const float s0 = x0 + x1, d0 = x0 - x1;
+    x0 = s0;
+    x1 = d0;
+  }
+#pragma unroll
+  for (int b = 0; b < 6; ++b) {
+    const float p0 = __shfl_xor(x0, 1 << b, 64), p1 = __shfl_xor(x1, 1 << b, 64);
+    const bool upper = (lane >> b) & 1;
+    x0 = upper ? p0 - x0 : x0 + p0;
+    x1 = upper ? p1 - x1 : x1 + p1;
+  }
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int jj = lane + 64 * e;
+    float o = (e ? x1 : x0) * kInvSqrt128A;
+    if ((mask.w[jj >> 5] >> (jj & 31)) & 1u) o = -o;
+    if constexpr (ODT == DT_F32) {
+      static_cast<float*>(out)[(int64_t)h * 128 + jj] = o;
+    } else if constexpr (ODT == DT_BF16) {
+      static_cast<__bf16*>(out)[(int64_t)h * 128 + jj] = (__bf16)o;
+    } else {
+      static_cast<_Float16*>(out)[(int64_t)h * 128 + jj] = (_Float16)o;
+    }
   }
 }
 
