@@ -3,19 +3,13 @@
 // OrbitQuantizer.forward: with x of dtype bf16 or fp16 the page forms
 // W' = codebook.to(dtype)[code] * row_norms.to(dtype) (each product rounded
 // to the dtype) and F.linear(x_rot, W', bias) in that dtype. Here W' never
-// reaches HBM: each block turns its W' rows into a table of the 2^bits
-// values each row can take (the same rounded products), decodes its tile of
-// codes through that table into LDS, and multiplies on bf16 / fp16 matrix
-// cores (v_mfma_f32_16x16x32_{bf16,f16}) with fp32 accumulation; the bias is
-// added in fp32 and the sum rounded to the dtype once.
-//
-// Tiling. A 256-thread block owns a 128 x 128 tile of y; its four waves sit
-// in a 2 x 2 grid and each owns 64 x 64 outputs as 4 x 4 MFMA tiles. K
-// advances 32 per step through two LDS buffers (one barrier per step): while
-// the matrix cores work on one, the next step's x_rot rows and codes are
-// loaded and written to the other. LDS rows hold 32 elements padded to 40
-// (80 bytes), so the 16-byte operand reads of eight consecutive lanes fall in
-// distinct banks.
+// reaches HBM: each block turns its W' rows into a table of the values each
+// row can take (the same rounded products; for 2- and 3-bit codes a table of
+// code pairs), decodes its codes through that table and multiplies on bf16 /
+// fp16 matrix cores (v_mfma_f32_16x16x32_{bf16,f16}) with fp32
+// accumulation; the bias is added in fp32 and the sum rounded to the dtype
+// once. Two kernels: one for many rows (128 x 128 tiles through LDS) and one
+// for decode-sized batches of up to 64 rows (see each kernel's comment).
 //
 // MFMA operand layout (checked on the device): lane l supplies
 // A[l % 16][8 (l / 16) + e] and B[8 (l / 16) + e][l % 16], e = 0..7, i.e.
@@ -61,6 +55,13 @@ constexpr int kLpRow = 72;  // padded LDS row (elements)
 constexpr int kLpRing = 4;  // K steps whose global loads are in flight
 constexpr size_t kLpSmallLds = 64 * 1024;  // the few-rows kernel's LDS ceiling
 
+// Many rows. A 256-thread block owns a 128 x 128 tile of y; its four waves sit
+// in a 2 x 2 grid and each owns 64 x 64 outputs as 4 x 4 MFMA tiles. K
+// advances 64 per step through one set of LDS tiles (two barriers per step),
+// while the global loads of the next four steps are in flight in a register
+// ring. LDS rows hold 64 elements padded to 72 (144 bytes), so the 16-byte
+// operand reads of eight consecutive lanes fall in distinct banks.
+
 // Code pairs of a 64-bit chunk of 16 codes (stream order), as table indices:
 // the pair's bits as they sit in the stream, (a << BITS) | b for MSB-first
 // and a | (b << BITS) for LSB-first (a = the earlier code).
@@ -96,8 +97,8 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
   // fit, through a table of single values.
   constexpr bool PAIRS = BITS <= 3;
   constexpr int TW = PAIRS ? L * L : L / 2;  // dwords per row's table
-  __shared__ __attribute__((aligned(16))) uint16_t As[1][kLpBM * kLpRow];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[1][kLpBN * kLpRow];
+  __shared__ __attribute__((aligned(16))) uint16_t As[kLpBM * kLpRow];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[kLpBN * kLpRow];
   __shared__ uint32_t tbw[kLpBN * TW];
   uint16_t (*tbl)[16] = reinterpret_cast<uint16_t (*)[16]>(tbw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -150,13 +151,13 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
 #pragma unroll
     for (int q = 0; q < 2; ++q) raw[u][q] = load_codes<BITS>(prow + (cg + q) * (2 * BITS));
   };
-  auto stage = [&](int u, int buf, int64_t st) {
+  auto stage = [&](int u, int64_t st) {
     const bool hv = st * kLpBK + 32 < K;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int f = tid + 256 * i;
       const u32x4v z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4v*>(&As[buf][(f >> 3) * kLpRow + 8 * (f & 7)]) =
+      *reinterpret_cast<u32x4v*>(&As[(f >> 3) * kLpRow + 8 * (f & 7)]) =
           (f & 7) >= 4 && !hv ? z : av[u][i];
     }
 #pragma unroll
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
         for (int e = 0; e < 8; ++e)
           w[e] = (uint32_t)tbl[bn][code[2 * e]] | ((uint32_t)tbl[bn][code[2 * e + 1]] << 16);
       }
-      u32x4v* dst = reinterpret_cast<u32x4v*>(&Bs[buf][bn * kLpRow + 32 * bh + 16 * q]);
+      u32x4v* dst = reinterpret_cast<u32x4v*>(&Bs[bn * kLpRow + 32 * bh + 16 * q]);
       dst[0] = u32x4v{w[0], w[1], w[2], w[3]};
       dst[1] = u32x4v{w[4], w[5], w[6], w[7]};
     }
@@ -196,8 +197,7 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
     for (int u = 0; u < kLpRing; ++u) {
       const int64_t st = s0 + u;
       if (st < steps) {
-        const int buf = 0;
-        stage(u, 0, st);
+        stage(u, st);
         fetch(u, st + kLpRing);
         asm volatile("" ::: "memory");  // the refill stays a full ring ahead
         __syncthreads();
@@ -208,11 +208,11 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             a[i] = *reinterpret_cast<const u32x4v*>(
-                &As[buf][(wm * 64 + 16 * i + (lane & 15)) * kLpRow + 32 * kk + koff]);
+                &As[(wm * 64 + 16 * i + (lane & 15)) * kLpRow + 32 * kk + koff]);
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             b[j] = *reinterpret_cast<const u32x4v*>(
-                &Bs[buf][(wn * 64 + 16 * j + (lane & 15)) * kLpRow + 32 * kk + koff]);
+                &Bs[(wn * 64 + 16 * j + (lane & 15)) * kLpRow + 32 * kk + koff]);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
