@@ -43,7 +43,9 @@ __global__ __launch_bounds__(256) void orbit_linear_kernel(
   __shared__ float cbs[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * kBN;
+  int tx, ty;
+  if (!xcd_tile((int)((N + kBN - 1) / kBN), (int)((M + BM - 1) / BM), tx, ty)) return;
+  const int64_t m0 = (int64_t)ty * BM, n0 = (int64_t)tx * kBN;
   if (tid < 16) cbs[tid] = cb.cb[tid];
 
   // this thread's W' row and half of each K step
@@ -225,7 +227,7 @@ template <int BITS, bool LSB, int BM, int WM>
 hipError_t launch_lin(const float* x, int64_t M, int64_t K, const uint8_t* packed,
                       const float* norms, int64_t N, const OrbitCodebook& cb, const float* bias,
                       float* y, hipStream_t s) {
-  const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + BM - 1) / BM));
+  const unsigned grid = xcd_grid((N + kBN - 1) / kBN, (M + BM - 1) / BM);
   orbit_linear_kernel<BITS, LSB, BM, WM><<<grid, 256, 0, s>>>(x, M, K, packed, norms, N, cb,
                                                                bias, y);
   return hipGetLastError();

@@ -103,7 +103,9 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
   uint16_t (*tbl)[16] = reinterpret_cast<uint16_t (*)[16]>(tbw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * kLpBM, n0 = (int64_t)blockIdx.x * kLpBN;
+  int tx, ty;
+  if (!xcd_tile((int)((N + kLpBN - 1) / kLpBN), (int)((M + kLpBM - 1) / kLpBM), tx, ty)) return;
+  const int64_t m0 = (int64_t)ty * kLpBM, n0 = (int64_t)tx * kLpBN;
 
   // This thread decodes 32 codes of W' row bn per step (half bh of the 64).
   const int bn = tid >> 1, bh = tid & 1;
@@ -428,7 +430,7 @@ hipError_t launch_lp(const void* x, int64_t M, int64_t K, const uint8_t* packed,
 #undef TQ_SM
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)((N + kLpBN - 1) / kLpBN), (unsigned)((M + kLpBM - 1) / kLpBM));
+  const unsigned grid = xcd_grid((N + kLpBN - 1) / kLpBN, (M + kLpBM - 1) / kLpBM);
   orbit_linear_lp_kernel<DT, BITS, LSB><<<grid, 256, 0, s>>>(xp, M, K, packed, norms, N, cb, bp,
                                                              yp);
   return hipGetLastError();

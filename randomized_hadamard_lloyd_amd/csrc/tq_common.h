@@ -86,6 +86,24 @@ __device__ __forceinline__ float div_rn(float a, const Recip& r) {
   return __builtin_fmaf(rem, r.rh, q0);
 }
 
+// Tile (tx, ty) of an nx x ny tiling for block blockIdx.x of a 1-D grid of
+// 8 * ceil(nx * ny / 8) blocks. Blocks go to the 8 XCDs round-robin, so block
+// b runs on XCD b % 8; the tiles are dealt so that each XCD works through a
+// contiguous run of them in row-major order, and the blocks that share a
+// row of tiles (the same rows of the left operand) share that XCD's L2.
+// Returns false for the blocks past the last tile.
+__device__ __forceinline__ bool xcd_tile(int nx, int ny, int& tx, int& ty) {
+  const int tiles = nx * ny;
+  const int per = (tiles + 7) / 8;
+  const int b = (int)blockIdx.x;
+  const int t = (b % 8) * per + b / 8;
+  if (t >= tiles) return false;
+  ty = t / nx;
+  tx = t - ty * nx;
+  return true;
+}
+inline unsigned xcd_grid(int64_t nx, int64_t ny) { return (unsigned)(8 * ((nx * ny + 7) / 8)); }
+
 // acc * 2 + (this lane's bit of the wave mask `bits`): one add with carry-in,
 // so a wave-wide compare result enters a lane's bit field at one VALU op.
 __device__ __forceinline__ uint32_t shift_in(uint32_t acc, uint64_t bits) {
