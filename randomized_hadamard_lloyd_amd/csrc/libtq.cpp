@@ -197,10 +197,9 @@ int orbit_quantize_weight(const float* W, int64_t rows, int64_t d, int bits,
   if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(perm, 16) || !aligned(signs, 16) ||
       !aligned(row_norms, 4))
     return TQ_ERR_ALIGN;
-  const int wpb = tq::orbit_waves_per_block(d);
   return launched(tq::launch_orbit_quantize(W, rows, d, bits, perm, signs, cb,
                                             bit_order == TQ_LSB_FIRST, packed, row_norms, cu_count(),
-                                            wpb, static_cast<hipStream_t>(stream)));
+                                            static_cast<hipStream_t>(stream)));
 }
 
 int orbit_dequantize(const uint8_t* packed, const float* row_norms, int64_t rows, int64_t d,
@@ -218,10 +217,9 @@ int orbit_dequantize(const uint8_t* packed, const float* row_norms, int64_t rows
   if (!aligned(packed, 16) || !aligned(W_out, 16) || !aligned(row_norms, 4) ||
       (!rotated_only && (!aligned(inv_perm, 16) || !aligned(signs, 16))))
     return TQ_ERR_ALIGN;
-  const int wpb = tq::orbit_waves_per_block(d);
   return launched(tq::launch_orbit_dequantize(packed, row_norms, rows, d, bits, inv_perm, signs,
                                               cb, bit_order == TQ_LSB_FIRST, rotated_only,
-                                              W_out, out_dtype, cu_count(), wpb,
+                                              W_out, out_dtype, cu_count(),
                                               static_cast<hipStream_t>(stream)));
 }
 

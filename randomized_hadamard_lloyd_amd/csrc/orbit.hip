@@ -677,13 +677,18 @@ __global__ __launch_bounds__(256) void orbit_dequantize_kernel(
   }
 }
 
+// LDS of a block: the row (d <= 1024 NT floats) and the block sums. The
+// resident-block count is taken once per kernel instantiation at its largest
+// LDS size (at most 17 KB: it never limits below the other resources).
+constexpr size_t orbit_lds(int d) { return (size_t)(d + kMaxBlocks) * sizeof(float); }
+
 template <int BITS, bool LSB, int NT, bool FULL>
 hipError_t launch_q(const float* W, int64_t rows, int d, int log2h, float kh,
                     const int32_t* perm, const int8_t* signs, const OrbitCodebook& cb,
-                    uint8_t* packed, float* norms, int cus, int wpb, hipStream_t s) {
-  (void)wpb;
-  const size_t shm = (size_t)(d + kMaxBlocks) * sizeof(float);
-  const int per_cu = resident_blocks_per_cu(orbit_quantize_kernel<BITS, LSB, NT, FULL>, 64 * NT, shm);
+                    uint8_t* packed, float* norms, int cus, hipStream_t s) {
+  const size_t shm = orbit_lds(d);
+  static const int per_cu = resident_blocks_per_cu(orbit_quantize_kernel<BITS, LSB, NT, FULL>,
+                                                   64 * NT, orbit_lds(1024 * NT));
   const int grid = grid_size(rows, cus, per_cu);
   orbit_quantize_kernel<BITS, LSB, NT, FULL><<<grid, 64 * NT, shm, s>>>(W, rows, d, log2h, kh, perm,
                                                                  signs, cb, packed, norms, nullptr);
@@ -693,9 +698,9 @@ hipError_t launch_q(const float* W, int64_t rows, int d, int log2h, float kh,
 template <int BITS, bool LSB>
 hipError_t launch_q_nt(int nt, const float* W, int64_t rows, int d, int log2h, float kh,
                        const int32_t* perm, const int8_t* signs, const OrbitCodebook& cb,
-                       uint8_t* packed, float* norms, int cus, int wpb, hipStream_t s) {
+                       uint8_t* packed, float* norms, int cus, hipStream_t s) {
 #define TQ_QN(N, F) \
-  launch_q<BITS, LSB, N, F>(W, rows, d, log2h, kh, perm, signs, cb, packed, norms, cus, wpb, s)
+  launch_q<BITS, LSB, N, F>(W, rows, d, log2h, kh, perm, signs, cb, packed, norms, cus, s)
   const bool full = log2h >= 10;
   switch (nt) {
     case 1: return full ? TQ_QN(1, true) : TQ_QN(1, false);
@@ -709,12 +714,11 @@ hipError_t launch_q_nt(int nt, const float* W, int64_t rows, int d, int log2h, f
 template <int BITS, bool LSB, int DT, int NT, bool FULL>
 hipError_t launch_dq(const uint8_t* packed, const float* norms, int64_t rows, int d, int log2h,
                      float kh, const int32_t* inv_perm, const int8_t* signs,
-                     const OrbitCodebook& cb, int rotated_only, void* out, int cus, int wpb,
+                     const OrbitCodebook& cb, int rotated_only, void* out, int cus,
                      hipStream_t s) {
-  (void)wpb;
-  const size_t shm = (size_t)(d + kMaxBlocks) * sizeof(float);
-  const int per_cu =
-      resident_blocks_per_cu(orbit_dequantize_kernel<BITS, LSB, DT, NT, FULL>, 64 * NT, shm);
+  const size_t shm = orbit_lds(d);
+  static const int per_cu = resident_blocks_per_cu(
+      orbit_dequantize_kernel<BITS, LSB, DT, NT, FULL>, 64 * NT, orbit_lds(1024 * NT));
   const int grid = grid_size(rows, cus, per_cu);
   orbit_dequantize_kernel<BITS, LSB, DT, NT, FULL><<<grid, 64 * NT, shm, s>>>(
       packed, norms, rows, d, log2h, kh, inv_perm, signs, cb, rotated_only, out);
@@ -725,9 +729,9 @@ template <int BITS, bool LSB, int DT>
 hipError_t launch_dq_nt(int nt, const uint8_t* packed, const float* norms, int64_t rows, int d,
                         int log2h, float kh, const int32_t* inv_perm, const int8_t* signs,
                         const OrbitCodebook& cb, int rotated_only, void* out, int cus,
-                        int wpb, hipStream_t s) {
+                        hipStream_t s) {
 #define TQ_DQN(N, F) launch_dq<BITS, LSB, DT, N, F>(packed, norms, rows, d, log2h, kh, inv_perm, \
-                                                 signs, cb, rotated_only, out, cus, wpb, s)
+                                                 signs, cb, rotated_only, out, cus, s)
   const bool full = log2h >= 10;
   switch (nt) {
     case 1: return full ? TQ_DQN(1, true) : TQ_DQN(1, false);
@@ -742,26 +746,26 @@ template <int BITS, bool LSB>
 hipError_t launch_dq_dt(int dt, int nt, const uint8_t* packed, const float* norms, int64_t rows,
                         int d, int log2h, float kh, const int32_t* inv_perm, const int8_t* signs,
                         const OrbitCodebook& cb, int rotated_only, void* out, int cus,
-                        int wpb, hipStream_t s) {
+                        hipStream_t s) {
   switch (dt) {
     case DT_F32:
       return launch_dq_nt<BITS, LSB, DT_F32>(nt, packed, norms, rows, d, log2h, kh, inv_perm,
-                                             signs, cb, rotated_only, out, cus, wpb, s);
+                                             signs, cb, rotated_only, out, cus, s);
     case DT_BF16:
       return launch_dq_nt<BITS, LSB, DT_BF16>(nt, packed, norms, rows, d, log2h, kh, inv_perm,
-                                              signs, cb, rotated_only, out, cus, wpb, s);
+                                              signs, cb, rotated_only, out, cus, s);
     default:
       return launch_dq_nt<BITS, LSB, DT_F16>(nt, packed, norms, rows, d, log2h, kh, inv_perm,
-                                             signs, cb, rotated_only, out, cus, wpb, s);
+                                             signs, cb, rotated_only, out, cus, s);
   }
 }
 
 template <int NT, bool FULL, int DT>
 hipError_t launch_rot(const void* x, int64_t rows, int d, int log2h, float kh,
                       const int32_t* perm, const int8_t* signs, void* xrot, int cus, hipStream_t s) {
-  const size_t shm = (size_t)(d + kMaxBlocks) * sizeof(float);
-  const int per_cu =
-      resident_blocks_per_cu(orbit_quantize_kernel<2, false, NT, FULL, true, DT>, 64 * NT, shm);
+  const size_t shm = orbit_lds(d);
+  static const int per_cu = resident_blocks_per_cu(
+      orbit_quantize_kernel<2, false, NT, FULL, true, DT>, 64 * NT, orbit_lds(1024 * NT));
   const int grid = grid_size(rows, cus, per_cu);
   OrbitCodebook cb{};
   orbit_quantize_kernel<2, false, NT, FULL, true, DT><<<grid, 64 * NT, shm, s>>>(
@@ -777,20 +781,16 @@ int ilog2(int64_t v) {
 
 }  // namespace
 
-int orbit_waves_per_block(int64_t d) {
-  return 4 * (d + kMaxBlocks) * (int64_t)sizeof(float) <= 65536 ? 4 : 2;
-}
-
 hipError_t launch_orbit_quantize(const float* W, int64_t rows, int64_t d, int bits,
                                  const int32_t* perm, const int8_t* signs,
                                  const OrbitCodebook& cb, int lsb_first, uint8_t* packed,
-                                 float* norms, int cus, int wpb, hipStream_t s) {
+                                 float* norms, int cus, hipStream_t s) {
   const int64_t h = d & -d;
   const int log2h = ilog2(h);
   const float kh = (float)pow((double)h, -0.5);
   const int di = (int)d;
   const int nt = (di + 1023) >> 10;  // tiles of 64 lanes x 16 elements
-#define TQ_Q(B, O) launch_q_nt<B, O>(nt, W, rows, di, log2h, kh, perm, signs, cb, packed, norms, cus, wpb, s)
+#define TQ_Q(B, O) launch_q_nt<B, O>(nt, W, rows, di, log2h, kh, perm, signs, cb, packed, norms, cus, s)
   if (lsb_first) {
     if (bits == 2) return TQ_Q(2, true);
     if (bits == 3) return TQ_Q(3, true);
@@ -835,7 +835,7 @@ hipError_t launch_orbit_rotate(const void* x, int dt, int64_t rows, int64_t d,
 hipError_t launch_orbit_dequantize(const uint8_t* packed, const float* norms, int64_t rows,
                                    int64_t d, int bits, const int32_t* inv_perm,
                                    const int8_t* signs, const OrbitCodebook& cb, int lsb_first,
-                                   int rotated_only, void* out, int dt, int cus, int wpb,
+                                   int rotated_only, void* out, int dt, int cus,
                                    hipStream_t s) {
   const int64_t h = d & -d;
   const int log2h = ilog2(h);
@@ -843,7 +843,7 @@ hipError_t launch_orbit_dequantize(const uint8_t* packed, const float* norms, in
   const int di = (int)d;
   const int nt = (di + 1023) >> 10;
 #define TQ_DQ(B, O) \
-  launch_dq_dt<B, O>(dt, nt, packed, norms, rows, di, log2h, kh, inv_perm, signs, cb, rotated_only, out, cus, wpb, s)
+  launch_dq_dt<B, O>(dt, nt, packed, norms, rows, di, log2h, kh, inv_perm, signs, cb, rotated_only, out, cus, s)
   if (lsb_first) {
     if (bits == 2) return TQ_DQ(2, true);
     if (bits == 3) return TQ_DQ(3, true);

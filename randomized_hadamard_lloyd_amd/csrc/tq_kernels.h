@@ -49,7 +49,7 @@ struct OrbitCodebook {
 hipError_t launch_orbit_quantize(const float* W, int64_t rows, int64_t d, int bits,
                                  const int32_t* perm, const int8_t* signs,
                                  const OrbitCodebook& cb, int lsb_first, uint8_t* packed,
-                                 float* norms, int cus, int wpb, hipStream_t s);
+                                 float* norms, int cus, hipStream_t s);
 hipError_t launch_orbit_linear(const float* x, int64_t M, int64_t K, const uint8_t* packed,
                                const float* norms, int64_t N, int bits, const OrbitCodebook& cb,
                                int lsb_first, const float* bias, float* y, hipStream_t s);
@@ -66,7 +66,7 @@ hipError_t launch_orbit_dequantize(const uint8_t* packed, const float* norms, in
                                    int64_t d, int bits, const int32_t* inv_perm,
                                    const int8_t* signs, const OrbitCodebook& cb,
                                    int lsb_first, int rotated_only, void* out, int dt,
-                                   int cus, int wpb, hipStream_t s);
+                                   int cus, hipStream_t s);
 // Decode attention over TQ3 records: the token chunk per block and the number
 // of chunks, both fixed by (n_tok, hkv) so that the caller can size the
 // workspace before the call.
@@ -94,8 +94,5 @@ inline int grid_size(int64_t need_blocks, int cus, int per_cu) {
   return (int)(need_blocks < cap ? need_blocks : cap);
 }
 
-// Rows in flight per block (one per wave) for input dimension d: four, or
-// two when four rows' LDS staging would exceed 64 KB.
-int orbit_waves_per_block(int64_t d);
 
 }  // namespace tq
