@@ -142,6 +142,11 @@ constexpr int kAttnTokPerGroup = 16;   // token slots per group: chunks of up to
 #ifndef ATTN_TB
 #define ATTN_TB(G) ((G) <= 2 ? 4 : 2)
 #endif
+#ifndef ATTN_WIN
+// token slots whose record loads are in flight: fewer for many heads, whose
+// scores and accumulators take the registers
+#define ATTN_WIN(G) ((G) <= 4 ? 8 : 4)
+#endif
 
 template <int QDT, int G>
 __global__ __launch_bounds__(256) void tq3_attn_partial_kernel(
@@ -180,30 +185,29 @@ __global__ __launch_bounds__(256) void tq3_attn_partial_kernel(
   }
 
   // This wave's records, one dword per lane and record (lane 16a + d holds
-  // dword min(d, 13) of group a's record), for all 16 token slots of the
-  // chunk, K and V, in registers: slots past the chunk's end re-read token
-  // t0's record, which is never used. Each slot goes to LDS just before the
-  // loop reads it, so the loop waits only for the loads of the slots it
-  // reaches (the later ones stay in flight). (Copies straight into LDS would
-  // not overlap: the compiler waits for every such copy before any later
-  // LDS read.)
+  // dword min(d, 13) of group a's record), K and V, through a window of
+  // kAttnWin token slots in registers: slots past the chunk's end re-read
+  // token t0's record, which is never used. Each slot goes to LDS just before
+  // the loop reads it, and its registers then load the slot kAttnWin later,
+  // so the loop waits only for the loads of the slots it reaches while the
+  // next ones stay in flight. (Copies straight into LDS would not overlap: the
+  // compiler waits for every such copy before any later LDS read.)
   const int64_t t0 = (int64_t)blockIdx.x * chunk;
   const int64_t t1 = t0 + chunk < n_tok ? t0 + chunk : n_tok;
   const int nk = (int)((t1 - t0 + kAttnGroups - 1) / kAttnGroups);  // token slots per group
-  uint32_t kraw[kAttnTokPerGroup], vraw[kAttnTokPerGroup];
-  {
-    const int a = lane >> 4, d = lane & 15;
-    const int dd = d < 14 ? d : 13;
+  constexpr int kAttnWin = ATTN_WIN(G);
+  uint32_t kraw[kAttnWin], vraw[kAttnWin];
+  const int rd = (lane & 15) < 14 ? (lane & 15) : 13;
+  auto load_slot = [&](int k) {
+    const int64_t t = t0 + 4 * wave + (lane >> 4) + (int64_t)kAttnGroups * k;
+    const int64_t rec = (t < t1 ? t : t0) * hkv + kv;
+    kraw[k % kAttnWin] = *reinterpret_cast<const uint32_t*>(krec + rec * 56 + 4 * rd);
+    vraw[k % kAttnWin] = *reinterpret_cast<const uint32_t*>(vrec + rec * 56 + 4 * rd);
+    // keeps the loads in slot order, as the loop's waits assume
+    asm volatile("" ::: "memory");
+  };
 #pragma unroll
-    for (int k = 0; k < kAttnTokPerGroup; ++k) {
-      const int64_t t = t0 + 4 * wave + a + (int64_t)kAttnGroups * k;
-      const int64_t rec = (t < t1 ? t : t0) * hkv + kv;
-      kraw[k] = *reinterpret_cast<const uint32_t*>(krec + rec * 56 + 4 * dd);
-      vraw[k] = *reinterpret_cast<const uint32_t*>(vrec + rec * 56 + 4 * dd);
-      // keeps the loads in slot order, as the loop's waits assume
-      asm volatile("" ::: "memory");
-    }
-  }
+  for (int k = 0; k < kAttnWin; ++k) load_slot(k);
 
   // Rotated queries: lane r keeps elements 8r .. 8r+7.
   float qr[G][8];
@@ -257,11 +261,13 @@ __global__ __launch_bounds__(256) void tq3_attn_partial_kernel(
   for (int it = 0; it < kAttnTokPerGroup / TB; ++it) {
     const int k0 = it * TB;
     if (k0 >= nkg) break;
-    // this iteration's slots -> LDS (only this wave reads them)
+    // this iteration's slots -> LDS (only this wave reads them); their
+    // registers then fetch the slots kAttnWin later
 #pragma unroll
     for (int u = 0; u < TB; ++u) {
-      (&stage[wave][k0 + u][0][0][0])[lane] = kraw[k0 + u];
-      (&stage[wave][k0 + u][1][0][0])[lane] = vraw[k0 + u];
+      (&stage[wave][k0 + u][0][0][0])[lane] = kraw[(k0 + u) % kAttnWin];
+      (&stage[wave][k0 + u][1][0][0])[lane] = vraw[(k0 + u) % kAttnWin];
+      if (k0 + u + kAttnWin < kAttnTokPerGroup) load_slot(k0 + u + kAttnWin);
     }
     const int64_t tb0 = t0 + grp + (int64_t)kAttnGroups * k0;
     RecPart kp[TB], vp[TB];
