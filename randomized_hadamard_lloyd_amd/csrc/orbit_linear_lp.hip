@@ -8,8 +8,10 @@
 // code pairs), decodes its codes through that table and multiplies on bf16 /
 // fp16 matrix cores (v_mfma_f32_16x16x32_{bf16,f16}) with fp32
 // accumulation; the bias is added in fp32 and the sum rounded to the dtype
-// once. Two kernels: one for many rows (128 x 128 tiles through LDS) and one
-// for decode-sized batches of up to 64 rows (see each kernel's comment).
+// once. Three kernels: tall 256 x 64 tiles for batches of more than 64 rows,
+// square 128 x 128 tiles for the shapes the tall ones do not take (K = 32,
+// or rows too long for their 32-bit offsets), and one for decode-sized
+// batches of up to 64 rows (see each kernel's comment).
 //
 // MFMA operand layout (checked on the device): lane l supplies
 // A[l % 16][8 (l / 16) + e] and B[8 (l / 16) + e][l % 16], e = 0..7, i.e.
@@ -27,6 +29,7 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8v __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x2v __attribute__((ext_vector_type(2)));
 
 // fp32 -> the format's bit pattern (nearest even), and back.
 template <int DT>
@@ -55,7 +58,8 @@ constexpr int kLpRow = 72;  // padded LDS row (elements)
 constexpr int kLpRing = 4;  // K steps whose global loads are in flight
 constexpr size_t kLpSmallLds = 64 * 1024;  // the few-rows kernel's LDS ceiling
 
-// Many rows. A 256-thread block owns a 128 x 128 tile of y; its four waves sit
+// Many rows, square tiles (K = 32, or K of 2^22 and more). A 256-thread
+// block owns a 128 x 128 tile of y; its four waves sit
 // in a 2 x 2 grid and each owns 64 x 64 outputs as 4 x 4 MFMA tiles. K
 // advances 64 per step through one set of LDS tiles (two barriers per step),
 // while the global loads of the next four steps are in flight in a register
@@ -96,11 +100,11 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
   // pair, both rounded products); 4-bit codes, whose pair table would not
   // fit, through a table of single values.
   constexpr bool PAIRS = BITS <= 3;
-  constexpr int TW = PAIRS ? L * L : L / 2;  // dwords per row's table
+  // dwords per row's table, padded by one so that rows start in different banks
+  constexpr int TW = (PAIRS ? L * L : L / 2) + 1;
   __shared__ __attribute__((aligned(16))) uint16_t As[kLpBM * kLpRow];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[kLpBN * kLpRow];
   __shared__ uint32_t tbw[kLpBN * TW];
-  uint16_t (*tbl)[16] = reinterpret_cast<uint16_t (*)[16]>(tbw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   int tx, ty;
@@ -112,6 +116,7 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
   const bool nvalid = n0 + bn < N;
   const int64_t row_bytes = K * BITS / 8;
   const uint8_t* prow = packed + (nvalid ? n0 + bn : 0) * row_bytes;
+  uint16_t* t16 = reinterpret_cast<uint16_t*>(tbw) + bn * 2 * TW;
   {
     // row bn's table of round(round(codebook[c]) * round(norm)) (zeros for
     // rows past N), split between the row's two threads
@@ -126,7 +131,7 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
 #pragma unroll
       for (int c = 0; c < L; c += 2) {
         const int cc = c + bh;
-        tbl[bn][cc] = (uint16_t)lp_bits<DT>(lp_float<DT>(lp_bits<DT>(cb.cb[cc])) * nl);
+        t16[cc] = (uint16_t)lp_bits<DT>(lp_float<DT>(lp_bits<DT>(cb.cb[cc])) * nl);
       }
     }
   }
@@ -138,30 +143,37 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
   const int64_t steps = (K + kLpBK - 1) / kLpBK;
   u32x4v av[kLpRing][4];
   uint64_t raw[kLpRing][2];
+  // Piece i of this thread: row tid / 8 + 32 i of the tile, elements
+  // 8 (tid % 8) .. + 7 of the step; `upper` marks the step's second half.
+  const bool upper = (tid & 7) >= 4;
+  const uint16_t* xp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t mr = m0 + (tid >> 3) + 32 * i;
+    xp[i] = x + (mr < M ? mr : m0) * K + 8 * (tid & 7);
+  }
   auto fetch = [&](int u, int64_t st) {
     const int64_t s = st < steps ? st : steps - 1;
     const int64_t k0 = s * kLpBK;
     const bool hv = k0 + 32 < K;
+    const int64_t ka = hv || !upper ? k0 : k0 - 32;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int f = tid + 256 * i;
-      const int64_t mr = m0 + (f >> 3) < M ? m0 + (f >> 3) : m0;
-      const int col = (f & 7) >= 4 && !hv ? 8 * (f & 7) - 32 : 8 * (f & 7);
-      av[u][i] = *reinterpret_cast<const u32x4v*>(x + mr * K + k0 + col);
-    }
+    for (int i = 0; i < 4; ++i) av[u][i] = *reinterpret_cast<const u32x4v*>(xp[i] + ka);
     const int64_t cg = k0 / 16 + (hv ? 2 * bh : 0);  // 16-code group
 #pragma unroll
     for (int q = 0; q < 2; ++q) raw[u][q] = load_codes<BITS>(prow + (cg + q) * (2 * BITS));
   };
   auto stage = [&](int u, int64_t st) {
-    const bool hv = st * kLpBK + 32 < K;
+    if (st * kLpBK + 32 >= K) {
+      // a half step: zeros in the upper half
+      if (upper) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int f = tid + 256 * i;
-      const u32x4v z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4v*>(&As[(f >> 3) * kLpRow + 8 * (f & 7)]) =
-          (f & 7) >= 4 && !hv ? z : av[u][i];
+        for (int i = 0; i < 4; ++i) av[u][i] = u32x4v{0u, 0u, 0u, 0u};
+      }
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4v*>(&As[((tid >> 3) + 32 * i) * kLpRow + 8 * (tid & 7)]) = av[u][i];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       uint32_t w[8];
@@ -175,7 +187,7 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
         unpack16<BITS, LSB>(raw[u][q], code);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          w[e] = (uint32_t)tbl[bn][code[2 * e]] | ((uint32_t)tbl[bn][code[2 * e + 1]] << 16);
+          w[e] = (uint32_t)t16[code[2 * e]] | ((uint32_t)t16[code[2 * e + 1]] << 16);
       }
       u32x4v* dst = reinterpret_cast<u32x4v*>(&Bs[bn * kLpRow + 32 * bh + 16 * q]);
       dst[0] = u32x4v{w[0], w[1], w[2], w[3]};
@@ -236,6 +248,238 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t m = m0 + wm * 64 + 16 * i + 4 * (lane >> 4) + r;
+        if (m < M) y[m * N + n] = (uint16_t)lp_bits<DT>(acc[i][j][r] + bv);
+      }
+  }
+}
+
+// Many rows, tall tiles. A 256-thread block owns a 256 x 64 tile of y and
+// wave w the rows 64 w .. 64 w + 63 of it (4 x 4 MFMA tiles). The block's 64
+// W' rows are decoded once per 64-wide K step into an LDS tile that all four
+// waves read, so each decoded element feeds 256 output rows: the decode's
+// VALU work, which does not overlap the MFMAs, costs half as much per MFMA as
+// in the square tiles. The decoded tile is double-buffered (one barrier per
+// step); codes load two steps ahead. No two waves share an x_rot row: each
+// wave loads its own 64 rows with coalesced 16-byte loads one step ahead and
+// passes them through a private LDS tile into the MFMA layout, without a
+// barrier. Tables of single values (pairs for 2-bit codes) and unpadded,
+// XOR-swizzled tiles keep the block at 52 KB of LDS, so three blocks (twelve
+// waves) share a CU.
+//
+// Tile layout: row r holds 64 elements as eight 16-byte chunks; chunk c sits
+// in slot c ^ ((r / 2) % 8). The MFMA operand reads (16 consecutive rows, one
+// chunk) then cover all 64 banks once per 16 lanes.
+constexpr int kTallBM = 256, kTallBN = 64;
+
+// One v_bfe_u32 per 3-bit field (left to itself the compiler shifts and
+// masks in two instructions to fold the table's element size in).
+__device__ __forceinline__ uint32_t bfe3(uint32_t v, int off) {
+  uint32_t r;
+  asm("v_bfe_u32 %0, %1, %2, 3" : "=v"(r) : "v"(v), "i"(off));
+  return r;
+}
+
+__device__ __forceinline__ int tall_off(int r, int c) {  // byte offset of (row, chunk)
+  return r * 128 + ((c ^ (r >> 1)) & 7) * 16;
+}
+
+template <int DT, int BITS, bool LSB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void
+orbit_linear_lp_tall_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                            const uint8_t* __restrict__ packed, const float* __restrict__ norms,
+                            int64_t N, OrbitCodebook cb, const uint16_t* __restrict__ bias,
+                            uint16_t* __restrict__ y) {
+  constexpr int L = 1 << BITS;
+  constexpr bool PAIRS = BITS == 2;
+  // dwords per row's table, padded by one so that rows start in different banks
+  constexpr int TW = (PAIRS ? L * L : L / 2) + 1;
+  __shared__ __attribute__((aligned(16))) char As[4][64 * 128];
+  __shared__ __attribute__((aligned(16))) char Bs[2][kTallBN * 128];
+  __shared__ uint32_t tbw[kTallBN * TW];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int tx, ty;
+  if (!xcd_tile((int)((N + kTallBN - 1) / kTallBN), (int)((M + kTallBM - 1) / kTallBM), tx, ty))
+    return;
+  const int64_t m0 = (int64_t)ty * kTallBM, n0 = (int64_t)tx * kTallBN;
+
+  // This thread decodes codes 16 bq .. 16 bq + 15 of each step of W' row bn.
+  const int bn = tid >> 2, bq = tid & 3;
+  const bool nvalid = n0 + bn < N;
+  const int64_t row_bytes = K * BITS / 8;
+  const uint8_t* prow = packed + (nvalid ? n0 + bn : 0) * row_bytes;
+  uint16_t* t16 = reinterpret_cast<uint16_t*>(tbw) + bn * 2 * TW;
+  {
+    // row bn's table of round(round(codebook[c]) * round(norm)) (zeros for
+    // rows past N), split between the row's four threads
+    const float nl = nvalid ? lp_float<DT>(lp_bits<DT>(norms[n0 + bn])) : 0.0f;
+    if constexpr (PAIRS) {
+      for (int e = bq; e < L * L; e += 4) {
+        const int a = LSB ? e % L : e / L, b = LSB ? e / L : e % L;
+        tbw[bn * TW + e] = lp_bits<DT>(lp_float<DT>(lp_bits<DT>(cb.cb[a])) * nl) |
+                           (lp_bits<DT>(lp_float<DT>(lp_bits<DT>(cb.cb[b])) * nl) << 16);
+      }
+    } else {
+      for (int c = bq; c < L; c += 4)
+        t16[c] = (uint16_t)lp_bits<DT>(lp_float<DT>(lp_bits<DT>(cb.cb[c])) * nl);
+    }
+  }
+
+  // x_rot: piece p of this lane is row 8 p + lane / 8 of the wave's 64, chunk
+  // lane % 8 of the step (byte offsets from the block's first row at the
+  // step's column; rows past M re-read row m0 and are never stored).
+  const char* xblk = reinterpret_cast<const char*>(x + m0 * K);
+  uint32_t xoff[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int64_t r = 64 * wave + 8 * p + (lane >> 3);
+    xoff[p] = (uint32_t)(((m0 + r < M ? r : 0) * K + 8 * (lane & 7)) * 2);
+  }
+  const int64_t steps = (K + 63) / 64;
+  // K is a multiple of 32 (and at least 64): when it is an odd one, the last
+  // step's window starts 32 columns early, so that its second half holds the
+  // last 32 columns, and the MFMAs skip its first half.
+  const bool half_last = (K & 63) != 0;
+  const int64_t last = steps - 1;
+  auto kbase = [&](int64_t st) { return st * 64 - (half_last && st == last ? 32 : 0); };
+  auto fetch_x = [&](u32x4v (&xv)[8], int64_t st) {
+    const char* b = xblk + kbase(st) * 2;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) xv[p] = *reinterpret_cast<const u32x4v*>(b + xoff[p]);
+  };
+  auto stage_x = [&](const u32x4v (&xv)[8]) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+      *reinterpret_cast<u32x4v*>(&As[wave][tall_off(8 * p + (lane >> 3), lane & 7)]) = xv[p];
+  };
+  auto fetch_c = [&](int64_t st) -> uint64_t {
+    return load_codes<BITS>(prow + (kbase(st) / 16 + bq) * (2 * BITS));
+  };
+  // The 16 decoded elements of one step: chunks 2 bq, 2 bq + 1 of row bn.
+  auto decode = [&](uint64_t raw, int buf) {
+    uint32_t w[8];
+    if constexpr (PAIRS) {
+      uint32_t pi[8];
+      pairs16<BITS, LSB>(raw, pi);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e] = tbw[bn * TW + pi[e]];
+    } else {
+      uint32_t code[16];
+      const uint32_t lo = (uint32_t)raw, hi = (uint32_t)(raw >> 32);
+      if constexpr (BITS == 3 && !LSB) {
+        // the two 24-bit groups of 8 codes, bytes reversed so that the
+        // earliest code sits in the top bits
+        const uint32_t g0 = __builtin_amdgcn_perm(0u, lo, 0x0c000102u);
+        const uint32_t g1 = __builtin_amdgcn_perm(hi, lo, 0x0c030405u);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          code[i] = bfe3(g0, 21 - 3 * i);
+          code[8 + i] = bfe3(g1, 21 - 3 * i);
+        }
+      } else if constexpr (BITS == 4) {
+        // byte b: codes 2 b and 2 b + 1 (the earlier one in the high nibble
+        // for MSB-first)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t wd = i < 8 ? lo : hi;
+          const int sh = 8 * ((i >> 1) & 3) + (LSB ? 4 * (i & 1) : 4 - 4 * (i & 1));
+          code[i] = __builtin_amdgcn_ubfe(wd, sh, 4);
+        }
+      } else {
+        unpack16<BITS, LSB>(raw, code);
+      }
+      // two 16-bit table reads per dword, the second into the upper half
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        u16x2v v;
+        v.x = t16[code[2 * e]];
+        v.y = t16[code[2 * e + 1]];
+        w[e] = __builtin_bit_cast(uint32_t, v);
+      }
+    }
+    *reinterpret_cast<u32x4v*>(&Bs[buf][tall_off(bn, 2 * bq)]) = u32x4v{w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<u32x4v*>(&Bs[buf][tall_off(bn, 2 * bq + 1)]) =
+        u32x4v{w[4], w[5], w[6], w[7]};
+  };
+
+  f32x4v acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+
+  {
+    u32x4v xv[8];
+    fetch_x(xv, 0);
+    stage_x(xv);
+  }
+  const uint64_t craw0 = fetch_c(0);
+  uint64_t cr = fetch_c(steps > 1 ? 1 : 0);
+  __syncthreads();  // tables
+  decode(craw0, 0);
+  __syncthreads();  // the tile of step 0
+  // operand reads: row 16 t + lane % 16 of a tile, chunk 4 kk + lane / 16
+  const int orow = lane & 15, ochk = lane >> 4;
+  // One step: multiply the tile of step st (both halves, or only the second
+  // on a half step) while the next step's x_rot and the codes two steps ahead
+  // load and the next step's tile is decoded into the other buffer.
+  auto step = [&](int64_t st, bool first_half, bool more) {
+    u32x4v xv[8];
+    uint64_t cn = 0;
+    if (more) {
+      fetch_x(xv, st + 1);
+      cn = fetch_c(st + 2 < steps ? st + 2 : last);
+    }
+    // keeps those loads here, a whole step ahead of their use
+    asm volatile("" ::: "memory");
+    const char* at = As[wave];
+    const char* bt = Bs[st & 1];
+    u32x4v a[4], b[4];
+    if (first_half) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a[i] = *reinterpret_cast<const u32x4v*>(&at[tall_off(16 * i + orow, ochk)]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b[j] = *reinterpret_cast<const u32x4v*>(&bt[tall_off(16 * j + orow, ochk)]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_lp<DT>(a[i], b[j], acc[i][j]);
+    }
+    if (more) {
+      decode(cr, (int)((st + 1) & 1));
+      cr = cn;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      a[i] = *reinterpret_cast<const u32x4v*>(&at[tall_off(16 * i + orow, 4 + ochk)]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      b[j] = *reinterpret_cast<const u32x4v*>(&bt[tall_off(16 * j + orow, 4 + ochk)]);
+    // this wave's next x_rot tile, after its last read of this one (a wave's
+    // LDS accesses complete in order)
+    if (more) stage_x(xv);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_lp<DT>(a[i], b[j], acc[i][j]);
+    if (more) __syncthreads();
+  };
+  for (int64_t st = 0; st < last; ++st) step(st, true, true);
+  step(last, !half_last, false);
+
+  // y = round(acc + bias)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = n0 + 16 * j + (lane & 15);
+    if (n >= N) continue;
+    const float bv = bias ? lp_float<DT>(bias[n]) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = m0 + 64 * wave + 16 * i + 4 * (lane >> 4) + r;
         if (m < M) y[m * N + n] = (uint16_t)lp_bits<DT>(acc[i][j][r] + bv);
       }
   }
@@ -428,6 +672,16 @@ hipError_t launch_lp(const void* x, int64_t M, int64_t K, const uint8_t* packed,
     else if (M <= 48) TQ_SM(3);
     else TQ_SM(4);
 #undef TQ_SM
+    return hipGetLastError();
+  }
+  // Tall tiles for every batch above the few-rows range (measured faster
+  // than the square tiles from 65 rows on: even a lone row of tiles fills
+  // twice as many CUs), unless K is a single half step or so large that the
+  // lanes' 32-bit x_rot offsets could overflow.
+  if (K >= 64 && K < ((int64_t)1 << 22)) {
+    const unsigned grid = xcd_grid((N + kTallBN - 1) / kTallBN, (M + kTallBM - 1) / kTallBM);
+    orbit_linear_lp_tall_kernel<DT, BITS, LSB><<<grid, 256, 0, s>>>(xp, M, K, packed, norms, N,
+                                                                    cb, bp, yp);
     return hipGetLastError();
   }
   const unsigned grid = xcd_grid((N + kLpBN - 1) / kLpBN, (M + kLpBM - 1) / kLpBM);

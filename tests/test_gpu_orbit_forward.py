@@ -208,12 +208,29 @@ def test_linear_lowp(tq, fmt, m, d, n, bits, msb):
 
 
 def test_linear_lowp_many_row_tiles(tq):
-    """1024 rows (eight 128-row tiles) at the forward workload's width."""
+    """1024 rows (four 256-row tiles) at the forward workload's width."""
     perm, sg, cb, packed, norms = quantized(384, 3072, 3, 77)
     x = of.round_to(np.random.default_rng(5).standard_normal((1024, 3072)).astype(np.float32),
                     "bf16")
     x_rot = of.rpbh_forward_lowp(x, perm.numpy(), sg.numpy(), "bf16")
     check_linear_lowp(tq, "bf16", x_rot, packed, norms, 3072, 3, cb)
+
+
+@pytest.mark.parametrize("fmt,m,d,n,bits,msb", [
+    ("bf16", 257, 96, 65, 3, True),     # a row tile holding one row, a half step, a lone column
+    ("f16", 520, 160, 130, 4, False),   # three row tiles, two and a half steps
+    ("bf16", 300, 64, 1, 2, True),      # a single step, a single output column
+    ("f16", 65, 3072, 200, 2, False),   # the fewest rows that take 256 x 64 tiles
+    ("bf16", 1000, 1024, 64, 3, False),  # LSB-first 3-bit codes
+])
+def test_linear_lowp_tall_tiles(tq, fmt, m, d, n, bits, msb):
+    """More than 64 rows: 256 x 64 tiles of y, with rows and columns past the
+    ends, K an odd multiple of 32 and a one-step K."""
+    perm, sg, cb, packed, norms = quantized(n, d, bits, d + n + bits + m, msb)
+    x = of.round_to(np.random.default_rng(m + d).standard_normal((m, d)).astype(np.float32), fmt)
+    x_rot = of.rpbh_forward_lowp(x, perm.numpy(), sg.numpy(), fmt)
+    bias = of.round_to(np.random.default_rng(n).standard_normal(n).astype(np.float32), fmt)
+    check_linear_lowp(tq, fmt, x_rot, packed, norms, d, bits, cb, bias, msb)
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
