@@ -246,8 +246,9 @@ int orbit_linear(const void* x_rot, int dtype, int64_t m, int64_t d_in, const ui
       d_out < 1 || d_out > ((int64_t)1 << 31))
     return TQ_ERR_SHAPE;
   if (m > ((int64_t)65535 * 128)) return TQ_ERR_SHAPE;  // grid rows
-  if ((m + 127) / 128 * ((d_out + 127) / 128) > ((int64_t)1 << 30))
-    return TQ_ERR_SHAPE;  // 128 x 128 tiles of a one-dimensional grid
+  if ((m + 127) / 128 * ((d_out + 127) / 128) > ((int64_t)1 << 30) ||
+      (m + 255) / 256 * ((d_out + 63) / 64) > ((int64_t)1 << 30))
+    return TQ_ERR_SHAPE;  // 128 x 128 or 256 x 64 tiles of a one-dimensional grid
   tq::OrbitCodebook cb;
   // the weight codec's codebook checks, at a block size that always passes
   const int st = orbit_check(1, 32, bits, codebook, bit_order, &cb);
