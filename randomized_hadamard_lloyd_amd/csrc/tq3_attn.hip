@@ -138,7 +138,7 @@ __device__ __forceinline__ void decode8(const RecPart& p, uint32_t shift, const 
 // Floats per (head, chunk) partial: max, sum, 2 pad, 128 accumulators.
 constexpr int kPartFloats = 132;
 constexpr int kAttnGroups = 16;        // 16-lane groups per 256-thread block
-constexpr int kAttnTokPerGroup = 16;   // token slots per group: chunks of up to 256 tokens
+constexpr int kAttnTokPerGroup = 16;   // token slots per group: pieces of up to 256 tokens
 #ifndef ATTN_TB
 #define ATTN_TB(G) ((G) <= 2 ? 4 : 2)
 #endif
@@ -184,17 +184,20 @@ __global__ __launch_bounds__(256) void tq3_attn_partial_kernel(
     }
   }
 
-  // This wave's records, one dword per lane and record (lane 16a + d holds
-  // dword min(d, 13) of group a's record), K and V, through a window of
-  // kAttnWin token slots in registers: slots past the chunk's end re-read
-  // token t0's record, which is never used. Each slot goes to LDS just before
-  // the loop reads it, and its registers then load the slot kAttnWin later,
-  // so the loop waits only for the loads of the slots it reaches while the
-  // next ones stay in flight. (Copies straight into LDS would not overlap: the
-  // compiler waits for every such copy before any later LDS read.)
-  const int64_t t0 = (int64_t)blockIdx.x * chunk;
-  const int64_t t1 = t0 + chunk < n_tok ? t0 + chunk : n_tok;
-  const int nk = (int)((t1 - t0 + kAttnGroups - 1) / kAttnGroups);  // token slots per group
+  // The block's chunk [c0, c1) goes by in pieces [t0, t1) of up to 256
+  // tokens (16 slots per group). This wave's records, one dword per lane and
+  // record (lane 16a + d holds dword min(d, 13) of group a's record), K and
+  // V, through a window of kAttnWin token slots in registers: slots past the
+  // piece's end re-read token t0's record, which is never used. Each slot
+  // goes to LDS just before the loop reads it, and its registers then load
+  // the slot kAttnWin later, so the loop waits only for the loads of the
+  // slots it reaches while the next ones stay in flight. (Copies straight
+  // into LDS would not overlap: the compiler waits for every such copy
+  // before any later LDS read.)
+  const int64_t c0 = (int64_t)blockIdx.x * chunk;
+  const int64_t c1 = c0 + chunk < n_tok ? c0 + chunk : n_tok;
+  constexpr int kPiece = kAttnGroups * kAttnTokPerGroup;
+  int64_t t0 = c0, t1 = c0 + kPiece < c1 ? c0 + kPiece : c1;
   constexpr int kAttnWin = ATTN_WIN(G);
   uint32_t kraw[kAttnWin], vraw[kAttnWin];
   const int rd = (lane & 15) < 14 ? (lane & 15) : 13;
@@ -255,90 +258,102 @@ __global__ __launch_bounds__(256) void tq3_attn_partial_kernel(
   // iteration; the TB scores of each head share one max update. TB shrinks
   // with G to keep the registers of G heads in budget.
   constexpr int TB = ATTN_TB(G);
-  // this group's tokens: the first nkg slots (groups differ by at most one)
-  const int nkg = (int)((t1 - t0 - grp + kAttnGroups - 1) / kAttnGroups);
+  for (;;) {
+    const int nk = (int)((t1 - t0 + kAttnGroups - 1) / kAttnGroups);  // token slots per group
+    // this group's tokens: the first nkg slots (groups differ by at most one)
+    const int nkg = (int)((t1 - t0 - grp + kAttnGroups - 1) / kAttnGroups);
 #pragma unroll
-  for (int it = 0; it < kAttnTokPerGroup / TB; ++it) {
-    const int k0 = it * TB;
-    if (k0 >= nkg) break;
-    // this iteration's slots -> LDS (only this wave reads them); their
-    // registers then fetch the slots kAttnWin later
-#pragma unroll
-    for (int u = 0; u < TB; ++u) {
-      (&stage[wave][k0 + u][0][0][0])[lane] = kraw[(k0 + u) % kAttnWin];
-      (&stage[wave][k0 + u][1][0][0])[lane] = vraw[(k0 + u) % kAttnWin];
-      if (k0 + u + kAttnWin < kAttnTokPerGroup) load_slot(k0 + u + kAttnWin);
-    }
-    const int64_t tb0 = t0 + grp + (int64_t)kAttnGroups * k0;
-    RecPart kp[TB], vp[TB];
-#pragma unroll
-    for (int u = 0; u < TB; ++u) {
-      const int ku = k0 + u < nk ? k0 + u : nk - 1;  // a loaded slot (finite values)
-      kp[u] = lds_part(my + ku * 128, dsel);
-      vp[u] = lds_part(my + ku * 128 + 64, dsel);
-    }
-    // scores (base-2 logits); -inf for the tokens past the end
-    float sc[G][TB];
-    {
-      float ck[TB][8];
-#pragma unroll
-      for (int u = 0; u < TB; ++u) decode8(kp[u], shift, tb, ck[u]);
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int u = 0; u < TB; ++u) {
-          float dot = qr[h][0] * ck[u][0];
-#pragma unroll
-          for (int i = 1; i < 8; ++i) dot = __builtin_fmaf(qr[h][i], ck[u][i], dot);
-          sc[h][u] = dot;
-        }
-      static_assert((G * TB) % 4 == 0, "scores reduce four at a time");
-      float* flat = &sc[0][0];
-#pragma unroll
-      for (int k = 0; k < G * TB; k += 4) group_allreduce4(flat[k], flat[k + 1], flat[k + 2], flat[k + 3]);
+    for (int it = 0; it < kAttnTokPerGroup / TB; ++it) {
+      const int k0 = it * TB;
+      if (k0 >= nkg) break;
+      // this iteration's slots -> LDS (only this wave reads them); their
+      // registers then fetch the slots kAttnWin later
 #pragma unroll
       for (int u = 0; u < TB; ++u) {
-        const bool valid = tb0 + kAttnGroups * u < t1;
-        const float wk = as_f(kp[u].ns.x) * as_f(kp[u].ns.y);
-#pragma unroll
-        for (int h = 0; h < G; ++h) sc[h][u] = valid ? sc[h][u] * wk : -__builtin_inff();
+        (&stage[wave][k0 + u][0][0][0])[lane] = kraw[(k0 + u) % kAttnWin];
+        (&stage[wave][k0 + u][1][0][0])[lane] = vraw[(k0 + u) % kAttnWin];
+        if (k0 + u + kAttnWin < kAttnTokPerGroup) load_slot(k0 + u + kAttnWin);
       }
-    }
-    // online softmax: one max update per head for the four tokens
+      const int64_t tb0 = t0 + grp + (int64_t)kAttnGroups * k0;
+      RecPart kp[TB], vp[TB];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float bm = sc[h][0];
-#pragma unroll
-      for (int u = 1; u < TB; ++u) bm = __builtin_fmaxf(bm, sc[h][u]);
-      if (__builtin_amdgcn_ballot_w64(bm > m[h])) {
-        // some group of the wave has a new maximum: rescale (corr = 1 elsewhere)
-        const float mn = __builtin_fmaxf(m[h], bm);
-        const float corr = __builtin_amdgcn_exp2f(m[h] - mn);
-        l[h] = l[h] * corr;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[h][i] = acc[h][i] * corr;
-        m[h] = mn;
+      for (int u = 0; u < TB; ++u) {
+        const int ku = k0 + u < nk ? k0 + u : nk - 1;  // a loaded slot (finite values)
+        kp[u] = lds_part(my + ku * 128, dsel);
+        vp[u] = lds_part(my + ku * 128 + 64, dsel);
       }
+      // scores (base-2 logits); -inf for the tokens past the end
+      float sc[G][TB];
+      {
+        float ck[TB][8];
 #pragma unroll
-      for (int u = 0; u < TB; ++u) sc[h][u] = __builtin_amdgcn_exp2f(sc[h][u] - m[h]);  // p (0 past the end)
-    }
-    // values
+        for (int u = 0; u < TB; ++u) decode8(kp[u], shift, tb, ck[u]);
 #pragma unroll
-    for (int u = 0; u < TB; ++u) {
-      float cv[8];
-      decode8(vp[u], shift, tb, cv);
-      const float wv = as_f(vp[u].ns.x) * as_f(vp[u].ns.y);
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int u = 0; u < TB; ++u) {
+            float dot = qr[h][0] * ck[u][0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) dot = __builtin_fmaf(qr[h][i], ck[u][i], dot);
+            sc[h][u] = dot;
+          }
+        static_assert((G * TB) % 4 == 0, "scores reduce four at a time");
+        float* flat = &sc[0][0];
+#pragma unroll
+        for (int k = 0; k < G * TB; k += 4) group_allreduce4(flat[k], flat[k + 1], flat[k + 2], flat[k + 3]);
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+          const bool valid = tb0 + kAttnGroups * u < t1;
+          const float wk = as_f(kp[u].ns.x) * as_f(kp[u].ns.y);
+#pragma unroll
+          for (int h = 0; h < G; ++h) sc[h][u] = valid ? sc[h][u] * wk : -__builtin_inff();
+        }
+      }
+      // online softmax: one max update per head for the four tokens
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        l[h] = l[h] + sc[h][u];
-        const float pw = sc[h][u] * wv;
+        float bm = sc[h][0];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[h][i] = __builtin_fmaf(pw, cv[i], acc[h][i]);
+        for (int u = 1; u < TB; ++u) bm = __builtin_fmaxf(bm, sc[h][u]);
+        if (__builtin_amdgcn_ballot_w64(bm > m[h])) {
+          // some group of the wave has a new maximum: rescale (corr = 1 elsewhere)
+          const float mn = __builtin_fmaxf(m[h], bm);
+          const float corr = __builtin_amdgcn_exp2f(m[h] - mn);
+          l[h] = l[h] * corr;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[h][i] = acc[h][i] * corr;
+          m[h] = mn;
+        }
+#pragma unroll
+        for (int u = 0; u < TB; ++u) sc[h][u] = __builtin_amdgcn_exp2f(sc[h][u] - m[h]);  // p (0 past the end)
       }
+      // values
+#pragma unroll
+      for (int u = 0; u < TB; ++u) {
+        float cv[8];
+        decode8(vp[u], shift, tb, cv);
+        const float wv = as_f(vp[u].ns.x) * as_f(vp[u].ns.y);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          l[h] = l[h] + sc[h][u];
+          const float pw = sc[h][u] * wv;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[h][i] = __builtin_fmaf(pw, cv[i], acc[h][i]);
+        }
+      }
+      // keeps the next iteration's slot writes (and so the waits for their
+      // loads) from moving up into this one
+      asm volatile("" ::: "memory");
     }
-    // keeps the next iteration's slot writes (and so the waits for their
-    // loads) from moving up into this one
-    asm volatile("" ::: "memory");
+    // the next piece of the chunk (its slots reuse this wave's LDS rows, which
+    // its own reads above have finished with); chunks of up to 4 heads per KV
+    // head are a single piece
+    if constexpr (G <= 4) break;
+    t0 = t1;
+    if (t0 >= c1) break;
+    t1 = t0 + kPiece < c1 ? t0 + kPiece : c1;
+#pragma unroll
+    for (int k = 0; k < kAttnWin; ++k) load_slot(k);
   }
 
   // Merge the 16 groups: weights 2^(m_g - M); groups that saw no token have
@@ -488,26 +503,29 @@ hipError_t launch_partial_g(int g, const void* q, const uint8_t* k, const uint8_
 
 }  // namespace
 
-AttnPlan tq3_attention_plan(int64_t n_tok, int hkv) {
-  // About 1024 blocks in total (four per CU of a 256-CU part), at least one
-  // token per group (16 per chunk); chunks are multiples of 16 tokens and
-  // at most 16 token slots per group (256 tokens).
+AttnPlan tq3_attention_plan(int64_t n_tok, int hkv, int g) {
+  // About four blocks per CU of a 256-CU part up to 4 heads per KV head
+  // (with 2 or 4 heads only three fit at once, but chunks sized for three
+  // measured no faster), chunks of at most 256 tokens (one piece); two
+  // blocks per CU at 8 heads, where the registers allow two and one round of
+  // longer chunks beats two rounds; at least one token per group (16 per
+  // chunk); chunks are multiples of 16 tokens.
   AttnPlan p;
-  const int64_t target = 1024;
-  int64_t nch = (target + hkv - 1) / hkv;
+  const int64_t target = 256 * (g <= 4 ? 4 : 2);
+  int64_t nch = target / hkv;
   const int64_t max_ch = (n_tok + 15) / 16;
   if (nch > max_ch) nch = max_ch;
   if (nch < 1) nch = 1;
   int64_t chunk = (n_tok + nch - 1) / nch;
   chunk = (chunk + 15) / 16 * 16;
-  if (chunk > 16 * kAttnTokPerGroup) chunk = 16 * kAttnTokPerGroup;
+  if (g <= 4 && chunk > kAttnGroups * kAttnTokPerGroup) chunk = kAttnGroups * kAttnTokPerGroup;
   p.chunk = chunk;
   p.nchunk = (n_tok + chunk - 1) / chunk;
   return p;
 }
 
 size_t tq3_attention_ws_floats(int64_t n_tok, int hq, int hkv) {
-  const AttnPlan p = tq3_attention_plan(n_tok, hkv);
+  const AttnPlan p = tq3_attention_plan(n_tok, hkv, hkv > 0 ? hq / hkv : 1);
   return (size_t)hq * (size_t)p.nchunk * kPartFloats;
 }
 
@@ -515,8 +533,8 @@ hipError_t launch_tq3_attention(const void* q, int qdt, int hq, const uint8_t* k
                                 const uint8_t* v, int64_t n_tok, int hkv, const SignMask& m,
                                 float softmax_scale, float* ws, void* out, int odt,
                                 hipStream_t s) {
-  const AttnPlan p = tq3_attention_plan(n_tok, hkv);
   const int g = hq / hkv;
+  const AttnPlan p = tq3_attention_plan(n_tok, hkv, g);
   // log2(e) turns the scores into base-2 logits for exp2; K = fp32(1/sqrt(128))
   // is the forward transform's factor.
   const float qscale = (float)((double)softmax_scale * 1.4426950408889634) * kInvSqrt128A;

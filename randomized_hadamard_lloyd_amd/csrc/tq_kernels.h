@@ -68,12 +68,12 @@ hipError_t launch_orbit_dequantize(const uint8_t* packed, const float* norms, in
                                    int lsb_first, int rotated_only, void* out, int dt,
                                    int cus, hipStream_t s);
 // Decode attention over TQ3 records: the token chunk per block and the number
-// of chunks, both fixed by (n_tok, hkv) so that the caller can size the
-// workspace before the call.
+// of chunks, both fixed by (n_tok, hkv, query heads per KV head) so that the
+// caller can size the workspace before the call.
 struct AttnPlan {
   int64_t chunk, nchunk;
 };
-AttnPlan tq3_attention_plan(int64_t n_tok, int hkv);
+AttnPlan tq3_attention_plan(int64_t n_tok, int hkv, int g);
 size_t tq3_attention_ws_floats(int64_t n_tok, int hq, int hkv);
 hipError_t launch_tq3_attention(const void* q, int qdt, int hq, const uint8_t* k,
                                 const uint8_t* v, int64_t n_tok, int hkv, const SignMask& m,

@@ -87,15 +87,28 @@ def test_dtypes(tq, signs, qdtype, odtype):
           signs, 0.1, qdtype, odtype)
 
 
-def test_kv_layer_full_size(tq, signs):
+@pytest.mark.parametrize("hq", [32, 64])
+def test_kv_layer_full_size(tq, signs, hq):
     """The KV-cache workload: K and V of one layer (32768 tokens x 8 KV heads,
     bf16 with outlier channels and per-token scales), quantized by the
-    oracle, attended by 32 query heads."""
+    oracle, attended by 32 or 64 query heads (64: chunks of 512 tokens, two
+    pieces each)."""
     k = oracle.tq3_quantize(datagen.kv_cache("K").float().numpy().reshape(-1, 128), signs)
     v = oracle.tq3_quantize(datagen.kv_cache("V").float().numpy().reshape(-1, 128), signs)
-    q = datagen.attention_queries(32).numpy()
+    q = datagen.attention_queries(hq).numpy()
     worst = check(tq, q, k, v, 8, signs, 128 ** -0.5)
     print(f"max |o - o_ref| / max|V| = {worst:.3e}")
+
+
+@pytest.mark.parametrize("t,hkv", [(20000, 8), (40000, 4)])
+def test_eight_heads_long_chunks(tq, signs, t, hkv):
+    """Eight query heads per KV head take chunks longer than 256 tokens,
+    processed in pieces of 256: here 320-token chunks (a 64-token last piece)
+    and a shorter last chunk."""
+    q = np.random.default_rng(t).standard_normal((8 * hkv, 128)).astype(np.float32)
+    k = gaussian_records(t * hkv, 300 + hkv, signs)
+    v = gaussian_records(t * hkv, 400 + hkv, signs)
+    check(tq, q, k, v, hkv, signs, 128 ** -0.5)
 
 
 def test_random_records_large(tq, signs):
