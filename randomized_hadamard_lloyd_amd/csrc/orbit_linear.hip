@@ -223,6 +223,158 @@ __global__ __launch_bounds__(64 * kSmallWaves) void orbit_linear_small_kernel(
   }
 }
 
+// One tile of rows (up to 16). A block owns 16 W' rows and the single
+// 16-row tile of x_rot; its four waves take every fourth K step of 32 and add
+// their partial tiles in LDS at the end, in a fixed order. The block's 16
+// code rows (contiguous in memory) are copied to LDS in one coalesced sweep,
+// each row padded by a dword so that the 16 rows a step reads start in
+// different banks, next to a per-row table of code pairs: entry (a, b) holds
+// the two fp32 products codebook[a] * norm and codebook[b] * norm, so one
+// 8-byte LDS read yields two operand values. x_rot (small, shared by every
+// block, L2-resident) goes straight into registers, four steps ahead. The K
+// order inside a step is permuted (the MFMA sums over it): in the step's e-th
+// MFMA, lane l supplies x_rot and W' at column 8 (l / 16) + e, so each lane
+// reads 8 consecutive values of one x_rot row and decodes 8 consecutive
+// codes of one W' row.
+constexpr size_t kFewLds = 64 * 1024;  // LDS ceiling of the one-tile kernel
+
+inline size_t few_lds(int64_t K, int bits) {  // codes, pair tables, partials
+  const int64_t row_dw = K * bits / 32 + 1;
+  return (size_t)((16 * row_dw + 3) / 4 * 16) + (size_t)16 * (1 << (2 * bits)) * 8 +
+         (size_t)4 * 256 * 4;
+}
+
+template <int BITS, bool LSB>
+__global__ __launch_bounds__(256) void orbit_linear_few_kernel(
+    const float* __restrict__ x, int64_t M, int64_t K, const uint8_t* __restrict__ packed,
+    const float* __restrict__ norms, int64_t N, OrbitCodebook cb,
+    const float* __restrict__ bias, float* __restrict__ y) {
+  constexpr int L = 1 << BITS, P = L * L;
+  constexpr int RING = 4;
+  extern __shared__ __attribute__((aligned(16))) uint32_t lsm[];
+  const int row_bytes = (int)(K * BITS / 8);
+  const int row_dw = row_bytes / 4 + 1;       // padded LDS row, dwords
+  const int code_words = (16 * row_dw + 3) / 4 * 4;
+  uint32_t* codes = lsm;
+  float2* ptab = reinterpret_cast<float2*>(lsm + code_words);
+  float* red = reinterpret_cast<float*>(ptab + 16 * P);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+
+  // the block's code rows -> LDS (rows past N are left unset: their table
+  // entries are zero)
+  {
+    const int nrows = N - n0 < 16 ? (int)(N - n0) : 16;
+    const int rw = row_bytes / 4;  // dwords per row (a row is a multiple of 4 bytes)
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(packed + n0 * row_bytes);
+    for (int c = tid; c < rw; c += 256) {
+      uint32_t v[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[r] = r < nrows ? src[r * rw + c] : 0u;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) codes[r * row_dw + c] = v[r];
+    }
+  }
+  // Pair tables of the block's 16 rows (zeros past N). Entry index: the
+  // pair's bits as they sit in the stream -- (a << BITS) | b for MSB-first
+  // (code a first), a | (b << BITS) for LSB-first.
+  for (int e = tid; e < 16 * P; e += 256) {
+    const int r = e / P, pr = e % P;
+    const int a = LSB ? pr % L : pr / L, b = LSB ? pr / L : pr % L;
+    const int64_t n = n0 + r;
+    const float nl = n < N ? norms[n] : 0.0f;
+    ptab[e] = make_float2(cb.cb[a] * nl, cb.cb[b] * nl);
+  }
+
+  const int j = lane >> 4;          // group of 8 columns inside a step
+  const int nr = lane & 15;         // W' row inside the block, and x_rot row
+  const uint8_t* crow = reinterpret_cast<const uint8_t*>(codes + nr * row_dw);
+  const float2* tb = ptab + nr * P;
+  const float* xr = x + (nr < M ? nr : M - 1) * K + 8 * j;  // rows past M: never stored
+  // This lane's group of 8 codes (group j of a step's four) from the staged
+  // row: BITS = 3 takes the two dwords its 3 bytes straddle.
+  const int glo = (3 * j) >> 2, ghi = glo + 1 < 3 ? glo + 1 : 2, gsh = 8 * ((3 * j) & 3);
+  auto group = [&](int s) -> uint32_t {
+    const uint8_t* g = crow + s * (4 * BITS);
+    if constexpr (BITS == 4) {
+      return reinterpret_cast<const uint32_t*>(g)[j];
+    } else if constexpr (BITS == 2) {
+      return reinterpret_cast<const uint16_t*>(g)[j];
+    } else {
+      const uint32_t* d = reinterpret_cast<const uint32_t*>(g);
+      return __builtin_amdgcn_alignbit(d[ghi], d[glo], gsh) & 0xffffffu;
+    }
+  };
+  // the group's 4 code pairs in stream order -> its 8 W' values
+  auto decode = [&](uint32_t g, float (&b)[8]) {
+    uint32_t w = g;
+    if constexpr (!LSB) {
+      if constexpr (BITS == 4) w = __builtin_bswap32(g);
+      else if constexpr (BITS == 3) w = (g >> 16) | (g & 0xff00u) | ((g & 0xffu) << 16);
+      else w = ((g & 0xffu) << 8) | (g >> 8);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t idx = LSB ? (w >> (2 * BITS * p)) & (P - 1)
+                               : (w >> (BITS * (6 - 2 * p))) & (P - 1);
+      const float2 v = tb[idx];
+      b[2 * p] = v.x;
+      b[2 * p + 1] = v.y;
+    }
+  };
+
+  f32x4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int steps = (int)(K / 32);
+  // Wave w takes steps w, w + 4, ... (nw of them, possibly none); ring slot
+  // u holds the x_rot values of its step i + u. Loads past the wave's last
+  // step re-read that step (step 0 for a wave without steps), never used.
+  const int nw = steps > wave ? (steps - wave + 3) >> 2 : 0;
+  const int s_last = nw > 0 ? wave + 4 * (nw - 1) : 0;
+  f32x4v ar[RING][2];
+  auto fetch = [&](int u, int i) {
+    const int s = i < nw ? wave + 4 * i : s_last;
+    ar[u][0] = *reinterpret_cast<const f32x4v*>(xr + 32 * s);
+    ar[u][1] = *reinterpret_cast<const f32x4v*>(xr + 32 * s + 4);
+  };
+  auto step = [&](int u, int i) {
+    float b[8];
+    decode(group(wave + 4 * i), b);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ar[u][e >> 2][e & 3], b[e], acc, 0, 0, 0);
+  };
+#pragma unroll
+  for (int u = 0; u < RING; ++u) fetch(u, u);
+  __syncthreads();  // codes and pair tables
+  int i = 0;
+  for (; i + RING <= nw; i += RING) {
+#pragma unroll
+    for (int u = 0; u < RING; ++u) {
+      step(u, i + u);
+      fetch(u, i + u + RING);
+      // keep the refill here, a full ring ahead of its use
+      asm volatile("" ::: "memory");
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < RING - 1; ++u)
+    if (i + u < nw) step(u, i + u);
+
+  // partial tiles -> LDS; wave-ordered sums; bias
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[wave * 256 + r * 64 + lane] = acc[r];
+  __syncthreads();
+  {
+    const int v = tid;  // r * 64 + lane'
+    const float sum = ((red[v] + red[256 + v]) + red[512 + v]) + red[768 + v];
+    const int ln = v & 63, r = v >> 6;
+    const int64_t m = 4 * (ln >> 4) + r;
+    const int64_t nn = n0 + (ln & 15);
+    if (m < M && nn < N) y[m * N + nn] = sum + (bias ? bias[nn] : 0.0f);
+  }
+}
+
 template <int BITS, bool LSB, int BM, int WM>
 hipError_t launch_lin(const float* x, int64_t M, int64_t K, const uint8_t* packed,
                       const float* norms, int64_t N, const OrbitCodebook& cb, const float* bias,
@@ -237,8 +389,15 @@ template <int BITS, bool LSB>
 hipError_t launch_lin_m(const float* x, int64_t M, int64_t K, const uint8_t* packed,
                         const float* norms, int64_t N, const OrbitCodebook& cb,
                         const float* bias, float* y, hipStream_t s) {
-  // up to 256 rows: 16 x 32 tiles with K split over the waves (enough blocks
-  // to fill the chip); beyond, 128 x 128 tiles
+  // up to 16 rows: one tile of rows per block, codes staged in LDS with pair
+  // tables (while they fit in 64 KB of LDS); up to 256 rows: 16 x 32 tiles
+  // with K split over the waves (enough blocks to fill the chip); beyond,
+  // 128 x 128 tiles
+  if (M <= 16 && few_lds(K, BITS) <= kFewLds) {
+    orbit_linear_few_kernel<BITS, LSB><<<(unsigned)((N + 15) / 16), 256, few_lds(K, BITS), s>>>(
+        x, M, K, packed, norms, N, cb, bias, y);
+    return hipGetLastError();
+  }
   if (M <= 256) {
     const dim3 grid((unsigned)((N + 31) / 32), (unsigned)((M + 15) / 16));
     orbit_linear_small_kernel<BITS, LSB><<<grid, 64 * kSmallWaves, 0, s>>>(x, M, K, packed, norms, N, cb,

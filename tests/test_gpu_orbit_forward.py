@@ -64,7 +64,7 @@ def test_rotate_bit_exact(tq, d, rows):
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
 
 
-@pytest.mark.parametrize("m", [1, 5, 32, 33, 130, 300])
+@pytest.mark.parametrize("m", [1, 5, 16, 17, 32, 33, 130, 300])
 @pytest.mark.parametrize("d,n,bits,msb", [(96, 100, 2, True), (1024, 129, 3, True),
                                           (3072, 384, 4, False), (512, 1, 3, False),
                                           (2048, 256, 2, True)])
@@ -76,16 +76,16 @@ def test_linear(tq, m, d, n, bits, msb):
     check_linear(tq, x_rot, packed, norms, d, bits, cb, bias, msb)
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4])
-def test_forward_config5(tq, bits):
+@pytest.mark.parametrize("bits,rows", [(2, 64), (3, 64), (4, 64), (3, 16), (4, 16)])
+def test_forward_config5(tq, bits, rows):
     """The weight workload (12288 x 3072, N(0, 0.02^2)) quantized by the
-    oracle; 64 activation rows through the whole forward."""
+    oracle; 64 or 16 activation rows through the whole forward."""
     d = 3072
     w = datagen.orbit_weight().numpy()
     perm, sg = datagen.rpbh_params(d)
     cb = oracle.orbit_codebook(bits, d)
     packed, norms = oracle.orbit_quantize(w, bits, perm, sg, cb)
-    x = np.random.default_rng(bits).standard_normal((64, d)).astype(np.float32)
+    x = np.random.default_rng(bits + rows).standard_normal((rows, d)).astype(np.float32)
     bias = np.random.default_rng(9).standard_normal(w.shape[0]).astype(np.float32) * 0.1
     y = tq.orbit_forward(torch.from_numpy(x).to(DEV), torch.from_numpy(packed).to(DEV),
                          torch.from_numpy(norms).to(DEV), perm.to(DEV), sg.to(DEV), bits, cb,
