@@ -230,7 +230,8 @@ __global__ __launch_bounds__(64 * kSmallWaves) void orbit_linear_small_kernel(
 // each row padded by a dword so that the 16 rows a step reads start in
 // different banks, next to a per-row table of code pairs: entry (a, b) holds
 // the two fp32 products codebook[a] * norm and codebook[b] * norm, so one
-// 8-byte LDS read yields two operand values. x_rot (small, shared by every
+// 8-byte LDS read yields two operand values (4-bit codes use a table of
+// single products). x_rot (small, shared by every
 // block, L2-resident) goes straight into registers, four steps ahead. The K
 // order inside a step is permuted (the MFMA sums over it): in the step's e-th
 // MFMA, lane l supplies x_rot and W' at column 8 (l / 16) + e, so each lane
@@ -238,10 +239,14 @@ __global__ __launch_bounds__(64 * kSmallWaves) void orbit_linear_small_kernel(
 // codes of one W' row.
 constexpr size_t kFewLds = 64 * 1024;  // LDS ceiling of the one-tile kernel
 
-inline size_t few_lds(int64_t K, int bits) {  // codes, pair tables, partials
+// Tables: code pairs (two fp32 products, 8 bytes) for 2- and 3-bit codes;
+// single products for 4-bit codes, whose 256-pair tables (32 KB a block)
+// would leave room for fewer blocks.
+constexpr bool few_pairs(int bits) { return bits <= 3; }
+inline size_t few_lds(int64_t K, int bits) {  // codes, tables, partials
   const int64_t row_dw = K * bits / 32 + 1;
-  return (size_t)((16 * row_dw + 3) / 4 * 16) + (size_t)16 * (1 << (2 * bits)) * 8 +
-         (size_t)4 * 256 * 4;
+  const size_t table = few_pairs(bits) ? (size_t)(1 << (2 * bits)) * 8 : (size_t)(1 << bits) * 4;
+  return (size_t)((16 * row_dw + 3) / 4 * 16) + 16 * table + (size_t)4 * 256 * 4;
 }
 
 template <int BITS, bool LSB>
@@ -249,7 +254,9 @@ __global__ __launch_bounds__(256) void orbit_linear_few_kernel(
     const float* __restrict__ x, int64_t M, int64_t K, const uint8_t* __restrict__ packed,
     const float* __restrict__ norms, int64_t N, OrbitCodebook cb,
     const float* __restrict__ bias, float* __restrict__ y) {
-  constexpr int L = 1 << BITS, P = L * L;
+  constexpr int L = 1 << BITS;
+  constexpr bool PAIRS = few_pairs(BITS);
+  constexpr int P = PAIRS ? L * L : L;  // table entries per row
   constexpr int RING = 4;
   extern __shared__ __attribute__((aligned(16))) uint32_t lsm[];
   const int row_bytes = (int)(K * BITS / 8);
@@ -257,7 +264,8 @@ __global__ __launch_bounds__(256) void orbit_linear_few_kernel(
   const int code_words = (16 * row_dw + 3) / 4 * 4;
   uint32_t* codes = lsm;
   float2* ptab = reinterpret_cast<float2*>(lsm + code_words);
-  float* red = reinterpret_cast<float*>(ptab + 16 * P);
+  float* stab = reinterpret_cast<float*>(lsm + code_words);
+  float* red = PAIRS ? reinterpret_cast<float*>(ptab + 16 * P) : stab + 16 * P;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t n0 = (int64_t)blockIdx.x * 16;
@@ -281,16 +289,21 @@ __global__ __launch_bounds__(256) void orbit_linear_few_kernel(
   // (code a first), a | (b << BITS) for LSB-first.
   for (int e = tid; e < 16 * P; e += 256) {
     const int r = e / P, pr = e % P;
-    const int a = LSB ? pr % L : pr / L, b = LSB ? pr / L : pr % L;
     const int64_t n = n0 + r;
     const float nl = n < N ? norms[n] : 0.0f;
-    ptab[e] = make_float2(cb.cb[a] * nl, cb.cb[b] * nl);
+    if constexpr (PAIRS) {
+      const int a = LSB ? pr % L : pr / L, b = LSB ? pr / L : pr % L;
+      ptab[e] = make_float2(cb.cb[a] * nl, cb.cb[b] * nl);
+    } else {
+      stab[e] = cb.cb[pr] * nl;
+    }
   }
 
   const int j = lane >> 4;          // group of 8 columns inside a step
   const int nr = lane & 15;         // W' row inside the block, and x_rot row
   const uint8_t* crow = reinterpret_cast<const uint8_t*>(codes + nr * row_dw);
   const float2* tb = ptab + nr * P;
+  const float* ts = stab + nr * P;
   const float* xr = x + (nr < M ? nr : M - 1) * K + 8 * j;  // rows past M: never stored
   // This lane's group of 8 codes (group j of a step's four) from the staged
   // row: BITS = 3 takes the two dwords its 3 bytes straddle.
@@ -314,13 +327,19 @@ __global__ __launch_bounds__(256) void orbit_linear_few_kernel(
       else if constexpr (BITS == 3) w = (g >> 16) | (g & 0xff00u) | ((g & 0xffu) << 16);
       else w = ((g & 0xffu) << 8) | (g >> 8);
     }
+    if constexpr (PAIRS) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t idx = LSB ? (w >> (2 * BITS * p)) & (P - 1)
-                               : (w >> (BITS * (6 - 2 * p))) & (P - 1);
-      const float2 v = tb[idx];
-      b[2 * p] = v.x;
-      b[2 * p + 1] = v.y;
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t idx = LSB ? (w >> (2 * BITS * p)) & (P - 1)
+                                 : (w >> (BITS * (6 - 2 * p))) & (P - 1);
+        const float2 v = tb[idx];
+        b[2 * p] = v.x;
+        b[2 * p + 1] = v.y;
+      }
+    } else {
+      // 4-bit: code e of the group at nibble e (LSB-first) or 7 - e
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b[e] = ts[(w >> (4 * (LSB ? e : 7 - e))) & 15u];
     }
   };
 
