@@ -57,6 +57,9 @@ constexpr int kLpBM = 128, kLpBN = 128, kLpBK = 64;
 constexpr int kLpRow = 72;  // padded LDS row (elements)
 constexpr int kLpRing = 4;  // K steps whose global loads are in flight
 constexpr size_t kLpSmallLds = 64 * 1024;  // the few-rows kernel's LDS ceiling
+#ifndef TQ_LP_WIDE_MIN
+#define TQ_LP_WIDE_MIN 32  // above this many rows the few-rows blocks take 32 W' rows
+#endif
 
 // Many rows, square tiles (K = 32, or K of 2^22 and more). A 256-thread
 // block owns a 128 x 128 tile of y; its four waves sit
@@ -502,42 +505,47 @@ orbit_linear_lp_tall_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K
 // two rounded products for codes a then b as one packed dword, so one LDS
 // read yields two operand elements. A ring of four K steps keeps the next
 // four steps' loads in flight while one is multiplied.
-template <int DT, int BITS, bool LSB, int MT>
+template <int DT, int BITS, bool LSB, int MT, int NTL>
 __global__ __launch_bounds__(256) void orbit_linear_lp_small_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, const uint8_t* __restrict__ packed,
     const float* __restrict__ norms, int64_t N, OrbitCodebook cb,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y) {
   constexpr int L = 1 << BITS, P = L * L;
   constexpr int RING = 4;
+  constexpr int NR = 16 * NTL;  // W' rows of the block
   extern __shared__ __attribute__((aligned(16))) uint32_t lsm[];
   const int row_bytes = (int)(K * BITS / 8);
   const int row_dw = row_bytes / 4 + 1;       // padded LDS row, dwords
-  const int code_words = (16 * row_dw + 3) / 4 * 4;
+  const int code_words = (NR * row_dw + 3) / 4 * 4;
   uint32_t* codes = lsm;
   uint32_t* ptab = lsm + code_words;
-  float* red = reinterpret_cast<float*>(ptab + 16 * P);
+  // the partial tiles reuse the code rows once every wave is done with them
+  float* red = reinterpret_cast<float*>(lsm);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t n0 = (int64_t)blockIdx.x * NR;
 
   // the block's code rows -> LDS (rows past N are left unset: their table
   // entries are zero)
   {
-    const int nrows = N - n0 < 16 ? (int)(N - n0) : 16;
+    const int nrows = N - n0 < NR ? (int)(N - n0) : NR;
     const int rw = row_bytes / 4;  // dwords per row (a row is a multiple of 4 bytes)
     const uint32_t* src = reinterpret_cast<const uint32_t*>(packed + n0 * row_bytes);
     for (int c = tid; c < rw; c += 256) {
-      uint32_t v[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) v[r] = r < nrows ? src[r * rw + c] : 0u;
+      for (int h = 0; h < NTL; ++h) {
+        uint32_t v[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) codes[r * row_dw + c] = v[r];
+        for (int r = 0; r < 16; ++r) v[r] = 16 * h + r < nrows ? src[(16 * h + r) * rw + c] : 0u;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) codes[(16 * h + r) * row_dw + c] = v[r];
+      }
     }
   }
-  // Pair tables of the block's 16 rows (zeros past N). Entry index: the
-  // pair's bits as they sit in the stream -- (a << BITS) | b for MSB-first
-  // (code a first), a | (b << BITS) for LSB-first.
-  for (int e = tid; e < 16 * P; e += 256) {
+  // Pair tables of the block's rows (zeros past N). Entry index: the pair's
+  // bits as they sit in the stream -- (a << BITS) | b for MSB-first (code a
+  // first), a | (b << BITS) for LSB-first.
+  for (int e = tid; e < NR * P; e += 256) {
     const int r = e / P, pr = e % P;
     const int a = LSB ? pr % L : pr / L, b = LSB ? pr / L : pr % L;
     const int64_t n = n0 + r;
@@ -548,9 +556,14 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_small_kernel(
   }
 
   const int j = lane >> 4;          // K group of 8 inside a step
-  const int nr = lane & 15;         // W' row inside the block
-  const uint8_t* crow = reinterpret_cast<const uint8_t*>(codes + nr * row_dw);
-  const uint32_t* tb = ptab + nr * P;
+  const int nr = lane & 15;         // W' row inside each 16-row tile of the block
+  const uint8_t* crow[NTL];
+  const uint32_t* tb[NTL];
+#pragma unroll
+  for (int h = 0; h < NTL; ++h) {
+    crow[h] = reinterpret_cast<const uint8_t*>(codes + (16 * h + nr) * row_dw);
+    tb[h] = ptab + (16 * h + nr) * P;
+  }
   const uint16_t* xr[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
@@ -560,8 +573,8 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_small_kernel(
   // This lane's group (group j of a step's four) from the staged row: BITS = 3
   // takes the two dwords its 3 bytes straddle (inside the step's 12 bytes).
   const int glo = (3 * j) >> 2, ghi = glo + 1 < 3 ? glo + 1 : 2, gsh = 8 * ((3 * j) & 3);
-  auto group = [&](int s) -> uint32_t {
-    const uint8_t* g = crow + s * (4 * BITS);
+  auto group = [&](int h, int s) -> uint32_t {
+    const uint8_t* g = crow[h] + s * (4 * BITS);
     if constexpr (BITS == 4) {
       return reinterpret_cast<const uint32_t*>(g)[j];
     } else if constexpr (BITS == 2) {
@@ -572,7 +585,7 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_small_kernel(
     }
   };
   // the group's 4 code pairs in stream order -> 4 packed operand dwords
-  auto decode = [&](uint32_t g, u32x4v& b) {
+  auto decode = [&](int h, uint32_t g, u32x4v& b) {
     uint32_t w = g;
     if constexpr (!LSB) {
       if constexpr (BITS == 4) w = __builtin_bswap32(g);
@@ -583,13 +596,15 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_small_kernel(
     for (int p = 0; p < 4; ++p) {
       const uint32_t idx = LSB ? (w >> (2 * BITS * p)) & (P - 1)
                                : (w >> (BITS * (6 - 2 * p))) & (P - 1);
-      b[p] = tb[idx];
+      b[p] = tb[h][idx];
     }
   };
 
-  f32x4v acc[MT];
+  f32x4v acc[MT][NTL];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int h = 0; h < NTL; ++h) acc[t][h] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
   const int steps = (int)(K / 32);
   // Wave w takes steps w, w + 4, ... (nw of them, possibly none when K has
   // fewer than four steps); ring slot u holds the x_rot operands of its step
@@ -604,10 +619,13 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_small_kernel(
     for (int t = 0; t < MT; ++t) ar[u][t] = *reinterpret_cast<const u32x4v*>(xr[t] + 32 * s);
   };
   auto step = [&](int u, int i) {
-    u32x4v b;
-    decode(group(wave + 4 * i), b);
 #pragma unroll
-    for (int t = 0; t < MT; ++t) acc[t] = mfma_lp<DT>(ar[u][t], b, acc[t]);
+    for (int h = 0; h < NTL; ++h) {
+      u32x4v b;
+      decode(h, group(h, wave + 4 * i), b);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[t][h] = mfma_lp<DT>(ar[u][t], b, acc[t][h]);
+    }
   };
 #pragma unroll
   for (int u = 0; u < RING; ++u) fetch(u, u);
@@ -627,19 +645,26 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_small_kernel(
   for (int u = 0; u < RING - 1; ++u)
     if (i + u < nw) step(u, i + u);
 
-  // partial tiles -> LDS; wave-ordered sums; bias; one rounding
+  // partial tiles -> LDS (over the code rows, once every wave is done with
+  // them); wave-ordered sums; bias; one rounding
+  constexpr int TT = MT * NTL;  // output tiles
+  __syncthreads();
 #pragma unroll
   for (int t = 0; t < MT; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave * MT * 256 + (t * 4 + r) * 64 + lane] = acc[t][r];
+    for (int h = 0; h < NTL; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        red[wave * TT * 256 + ((t * NTL + h) * 4 + r) * 64 + lane] = acc[t][h][r];
   __syncthreads();
 #pragma unroll
-  for (int q = 0; q < MT; ++q) {
-    const int v = tid + 256 * q;  // (t * 4 + r) * 64 + lane'
-    const float sum = ((red[v] + red[MT * 256 + v]) + red[2 * MT * 256 + v]) + red[3 * MT * 256 + v];
-    const int ln = v & 63, r = (v >> 6) & 3, t = v >> 8;
+  for (int q = 0; q < TT; ++q) {
+    const int v = tid + 256 * q;  // ((t * NTL + h) * 4 + r) * 64 + lane'
+    const float sum = ((red[v] + red[TT * 256 + v]) + red[2 * TT * 256 + v]) + red[3 * TT * 256 + v];
+    const int ln = v & 63, r = (v >> 6) & 3, th = v >> 8;
+    const int t = th / NTL, h = th % NTL;
     const int64_t m = 16 * t + 4 * (ln >> 4) + r;
-    const int64_t nn = n0 + (ln & 15);
+    const int64_t nn = n0 + 16 * h + (ln & 15);
     if (m < M && nn < N) {
       const float bv = bias ? lp_float<DT>(bias[nn]) : 0.0f;
       y[m * N + nn] = (uint16_t)lp_bits<DT>(sum + bv);
@@ -648,10 +673,12 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_small_kernel(
 }
 
 // LDS bytes of the small kernel: the block's codes, pair tables, partials.
-inline size_t lp_small_lds(int64_t K, int bits, int mt) {
+inline size_t lp_small_lds(int64_t K, int bits, int mt, int ntl) {
   const int64_t row_dw = K * bits / 32 + 1;
-  return (size_t)((16 * row_dw + 3) / 4 * 16) + (size_t)16 * (1 << (2 * bits)) * 4 +
-         (size_t)4 * mt * 256 * 4;
+  const size_t code_bytes = (size_t)((16 * ntl * row_dw + 3) / 4 * 16);
+  const size_t red_bytes = (size_t)4 * mt * ntl * 256 * 4;
+  return (code_bytes > red_bytes ? code_bytes : red_bytes) +
+         (size_t)16 * ntl * (1 << (2 * bits)) * 4;
 }
 
 template <int DT, int BITS, bool LSB>
@@ -662,15 +689,20 @@ hipError_t launch_lp(const void* x, int64_t M, int64_t K, const uint8_t* packed,
   const uint16_t* bp = static_cast<const uint16_t*>(bias);
   uint16_t* yp = static_cast<uint16_t*>(y);
   const int mt = (int)((M + 15) / 16);
-  if (M <= 64 && lp_small_lds(K, BITS, mt) <= kLpSmallLds) {
-    const dim3 grid((unsigned)((N + 15) / 16));
-    const size_t shm = lp_small_lds(K, BITS, mt);
-#define TQ_SM(T) orbit_linear_lp_small_kernel<DT, BITS, LSB, T><<<grid, 256, shm, s>>>( \
+  // Above 32 rows a block takes two 16-row tiles of W' (when they fit in LDS):
+  // every block reads all of x_rot, and that read then serves twice the
+  // outputs.
+  const int ntl = M > TQ_LP_WIDE_MIN && lp_small_lds(K, BITS, mt, 2) <= kLpSmallLds ? 2 : 1;
+  if (M <= 64 && lp_small_lds(K, BITS, mt, ntl) <= kLpSmallLds) {
+    const dim3 grid((unsigned)((N + 16 * ntl - 1) / (16 * ntl)));
+    const size_t shm = lp_small_lds(K, BITS, mt, ntl);
+#define TQ_SM(T, H) orbit_linear_lp_small_kernel<DT, BITS, LSB, T, H><<<grid, 256, shm, s>>>( \
     xp, M, K, packed, norms, N, cb, bp, yp)
-    if (M <= 16) TQ_SM(1);
-    else if (M <= 32) TQ_SM(2);
-    else if (M <= 48) TQ_SM(3);
-    else TQ_SM(4);
+    if (M <= 16) TQ_SM(1, 1);
+    else if (M <= 32) TQ_SM(2, 1);
+    else if (ntl == 1) { if (M <= 48) TQ_SM(3, 1); else TQ_SM(4, 1); }
+    else if (M <= 48) TQ_SM(3, 2);
+    else TQ_SM(4, 2);
 #undef TQ_SM
     return hipGetLastError();
   }
