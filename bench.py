@@ -74,6 +74,10 @@ def parse():
     p.add_argument("--profile", action="store_true",
                    help="short run for counter collection: one 256 MiB device copy "
                         "(calibration), 1 warmup + 3 steps, nothing else")
+    p.add_argument("--profile-orbit", action="store_true",
+                   help="short run for counter collection on the OrbitQuant weight codec: "
+                        "one 256 MiB device copy (calibration), then for 2, 3 and 4 bits one "
+                        "warmup + 3 launches each of quantize, rotated and full dequantize")
     args = p.parse_args()
     if args.profile:
         args.steps, args.warmup = 3, 1
@@ -387,11 +391,49 @@ def secondary(tq, timer, dev, signs, mask):
     return out
 
 
+def profile_orbit(tq, dev):
+    """The 12288 x 3072 fp32 weight through the codec, a few launches per
+    kernel, for counters taken under a profiler."""
+    import ctypes
+    import datagen
+    a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    d = 3072
+    w = datagen.orbit_weight().to(dev)
+    rows = w.shape[0]
+    perm, sg = datagen.rpbh_params(d)
+    perm_d = perm.to(torch.int32).to(dev)
+    inv_d = torch.argsort(perm).to(torch.int32).to(dev)
+    sg_d = sg.to(dev)
+    norms = torch.empty(rows, dtype=torch.float32, device=dev)
+    wout = torch.empty_like(w)
+    L, sp = tq.lib, tq._stream(w)
+    for bits in (2, 3, 4):
+        cb = tq.orbit_make_codebook(bits, d)
+        cbh = (ctypes.c_float * len(cb))(*cb.tolist())
+        cbp = ctypes.cast(cbh, ctypes.c_void_p)
+        packed = torch.empty((rows, d * bits // 8), dtype=torch.uint8, device=dev)
+        for _ in range(4):
+            assert L.orbit_quantize_weight(tq._ptr(w), rows, d, bits, tq._ptr(perm_d),
+                                           tq._ptr(sg_d), cbp, tq.TQ_MSB_FIRST, tq._ptr(packed),
+                                           tq._ptr(norms), sp) == 0
+        for rot in (1, 0):
+            for _ in range(4):
+                assert L.orbit_dequantize(tq._ptr(packed), tq._ptr(norms), rows, d, bits,
+                                          tq._ptr(inv_d), tq._ptr(sg_d), cbp, tq.TQ_MSB_FIRST,
+                                          rot, tq._ptr(wout), tq.TQ_F32, sp) == 0
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_orbit": "done", "rows": rows, "d": d}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the codecs are "
-              "data-parallel per vector or row and this build measures one GPU's share",
+              "data-parallel per vector or row, and one GPU's share is what it measures",
               file=sys.stderr)
         sys.exit(2)
     import datagen
@@ -401,6 +443,9 @@ def main():
     torch.cuda.set_device(dev)
     signs = datagen.tq3_signs()
     mask = tq.sign_mask(signs)
+    if args.profile_orbit:
+        profile_orbit(tq, dev)
+        return
     if args.only_secondary:
         stream = torch.cuda.current_stream(dev)
         print(json.dumps({"secondary": secondary(tq, Timer(stream), dev, signs, mask)}), flush=True)
