@@ -403,13 +403,21 @@ __global__ __launch_bounds__(256) void tq3_attn_partial_kernel(
   }
 }
 
-// One 1024-thread block per query head. Slice sl (128 threads, one element
-// each) merges chunks sl, sl + 8, ... with the online rule (running maximum,
-// sum and accumulator, rescaled when the maximum grows); after one barrier
-// the first wave merges the eight slices, divides by the softmax sum, runs
-// the inverse rotation (S K H) on its 2 x 64 elements -- the stage on
-// element bit 6 in registers, bits 0..5 across lanes -- and stores.
-constexpr int kCombineSlices = 8;
+// One 1024-thread block per query head. Slice sl (1024 / S threads, 128 S /
+// 1024 elements each, for S slices) merges chunks sl, sl + S, ... with the
+// online rule (running maximum, sum and accumulators, rescaled when the
+// maximum grows); after one barrier the first wave merges the S slices,
+// divides by the softmax sum, runs the inverse rotation (S K H) on its
+// 2 x 64 elements -- the stage on element bit 6 in registers, bits 0..5
+// across lanes -- and stores.
+#ifndef ATTN_SLICES
+// 32 slices of 32 threads, four elements each: each slice's chain of merges
+// is a quarter as long as with 8 slices of one element per thread (-1 to
+// -2 us a call), and the first wave's merge of the slices stays short
+#define ATTN_SLICES 32
+#endif
+constexpr int kCombineSlices = ATTN_SLICES;
+constexpr int kSliceElems = 128 * kCombineSlices / 1024;  // elements per thread
 template <int ODT>
 __global__ __launch_bounds__(1024) void tq3_attn_combine_kernel(const float* __restrict__ ws,
                                                                int nchunk, SignMask mask,
@@ -417,21 +425,29 @@ __global__ __launch_bounds__(1024) void tq3_attn_combine_kernel(const float* __r
   __shared__ float sacc[kCombineSlices][128];
   __shared__ float smax[kCombineSlices], ssum[kCombineSlices];
   const int h = blockIdx.x;
-  const int j = threadIdx.x & 127, sl = threadIdx.x >> 7;
+  constexpr int kSliceThreads = 128 / kSliceElems;
+  const int j = threadIdx.x % kSliceThreads, sl = threadIdx.x / kSliceThreads;
   const float* part = ws + (int64_t)h * nchunk * kPartFloats;
-  float m = -__builtin_inff(), l = 0.0f, a = 0.0f;
+  float m = -__builtin_inff(), l = 0.0f, a[kSliceElems];
+#pragma unroll
+  for (int e = 0; e < kSliceElems; ++e) a[e] = 0.0f;
 #pragma unroll 8
   for (int c = sl; c < nchunk; c += kCombineSlices) {
     const float* pc = part + (int64_t)c * kPartFloats;
-    const float mc = pc[0], lc = pc[1], ac = pc[4 + j];
+    const float mc = pc[0], lc = pc[1];
+    float ac[kSliceElems];
+#pragma unroll
+    for (int e = 0; e < kSliceElems; ++e) ac[e] = pc[4 + j + kSliceThreads * e];
     const float mn = __builtin_fmaxf(m, mc);
     // a chunk never has m = -inf (it holds at least one token), so mn is finite
     const float fo = __builtin_amdgcn_exp2f(m - mn), fc = __builtin_amdgcn_exp2f(mc - mn);
     l = __builtin_fmaf(l, fo, lc * fc);
-    a = __builtin_fmaf(a, fo, ac * fc);
+#pragma unroll
+    for (int e = 0; e < kSliceElems; ++e) a[e] = __builtin_fmaf(a[e], fo, ac[e] * fc);
     m = mn;
   }
-  sacc[sl][j] = a;
+#pragma unroll
+  for (int e = 0; e < kSliceElems; ++e) sacc[sl][j + kSliceThreads * e] = a[e];
   if (j == 0) {
     smax[sl] = m;
     ssum[sl] = l;
