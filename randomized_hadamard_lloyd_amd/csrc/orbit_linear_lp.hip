@@ -510,7 +510,12 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_small_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, const uint8_t* __restrict__ packed,
     const float* __restrict__ norms, int64_t N, OrbitCodebook cb,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y) {
-  constexpr int L = 1 << BITS, P = L * L;
+  constexpr int L = 1 << BITS;
+  // Tables of code pairs (one dword holds both rounded products), except for
+  // 4-bit codes in two-tile blocks, whose pair tables would not fit beside
+  // the codes: those use 16-bit single values.
+  constexpr bool PAIRS = BITS <= 3 || NTL == 1;
+  constexpr int P = PAIRS ? L * L : L;  // entries per row
   constexpr int RING = 4;
   constexpr int NR = 16 * NTL;  // W' rows of the block
   extern __shared__ __attribute__((aligned(16))) uint32_t lsm[];
@@ -545,24 +550,31 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_small_kernel(
   // Pair tables of the block's rows (zeros past N). Entry index: the pair's
   // bits as they sit in the stream -- (a << BITS) | b for MSB-first (code a
   // first), a | (b << BITS) for LSB-first.
+  uint16_t* stab = reinterpret_cast<uint16_t*>(ptab);
   for (int e = tid; e < NR * P; e += 256) {
     const int r = e / P, pr = e % P;
-    const int a = LSB ? pr % L : pr / L, b = LSB ? pr / L : pr % L;
     const int64_t n = n0 + r;
     const float nl = n < N ? lp_float<DT>(lp_bits<DT>(norms[n])) : 0.0f;
-    const float wa = lp_float<DT>(lp_bits<DT>(cb.cb[a])) * nl;
-    const float wb = lp_float<DT>(lp_bits<DT>(cb.cb[b])) * nl;
-    ptab[e] = lp_bits<DT>(wa) | (lp_bits<DT>(wb) << 16);
+    if constexpr (PAIRS) {
+      const int a = LSB ? pr % L : pr / L, b = LSB ? pr / L : pr % L;
+      const float wa = lp_float<DT>(lp_bits<DT>(cb.cb[a])) * nl;
+      const float wb = lp_float<DT>(lp_bits<DT>(cb.cb[b])) * nl;
+      ptab[e] = lp_bits<DT>(wa) | (lp_bits<DT>(wb) << 16);
+    } else {
+      stab[e] = (uint16_t)lp_bits<DT>(lp_float<DT>(lp_bits<DT>(cb.cb[pr])) * nl);
+    }
   }
 
   const int j = lane >> 4;          // K group of 8 inside a step
   const int nr = lane & 15;         // W' row inside each 16-row tile of the block
   const uint8_t* crow[NTL];
   const uint32_t* tb[NTL];
+  const uint16_t* ts[NTL];
 #pragma unroll
   for (int h = 0; h < NTL; ++h) {
     crow[h] = reinterpret_cast<const uint8_t*>(codes + (16 * h + nr) * row_dw);
     tb[h] = ptab + (16 * h + nr) * P;
+    ts[h] = stab + (16 * h + nr) * P;
   }
   const uint16_t* xr[MT];
 #pragma unroll
@@ -592,11 +604,22 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_small_kernel(
       else if constexpr (BITS == 3) w = (g >> 16) | (g & 0xff00u) | ((g & 0xffu) << 16);
       else w = ((g & 0xffu) << 8) | (g >> 8);
     }
+    if constexpr (PAIRS) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t idx = LSB ? (w >> (2 * BITS * p)) & (P - 1)
-                               : (w >> (BITS * (6 - 2 * p))) & (P - 1);
-      b[p] = tb[h][idx];
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t idx = LSB ? (w >> (2 * BITS * p)) & (P - 1)
+                                 : (w >> (BITS * (6 - 2 * p))) & (P - 1);
+        b[p] = tb[h][idx];
+      }
+    } else {
+      // 4-bit codes: code e of the group at nibble e (LSB-first) or 7 - e
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int e0 = 2 * p, e1 = 2 * p + 1;
+        const uint32_t c0 = (w >> (4 * (LSB ? e0 : 7 - e0))) & 15u;
+        const uint32_t c1 = (w >> (4 * (LSB ? e1 : 7 - e1))) & 15u;
+        b[p] = (uint32_t)ts[h][c0] | ((uint32_t)ts[h][c1] << 16);
+      }
     }
   };
 
@@ -677,8 +700,8 @@ inline size_t lp_small_lds(int64_t K, int bits, int mt, int ntl) {
   const int64_t row_dw = K * bits / 32 + 1;
   const size_t code_bytes = (size_t)((16 * ntl * row_dw + 3) / 4 * 16);
   const size_t red_bytes = (size_t)4 * mt * ntl * 256 * 4;
-  return (code_bytes > red_bytes ? code_bytes : red_bytes) +
-         (size_t)16 * ntl * (1 << (2 * bits)) * 4;
+  const size_t table = bits <= 3 || ntl == 1 ? (size_t)(1 << (2 * bits)) * 4 : (size_t)(1 << bits) * 2;
+  return (code_bytes > red_bytes ? code_bytes : red_bytes) + (size_t)16 * ntl * table;
 }
 
 template <int DT, int BITS, bool LSB>
