@@ -111,6 +111,15 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _check_out(out, dtype, numel, device, what):
+    """A caller-given output buffer must be exactly what the kernels write: the
+    C entry points cannot see a buffer's size or type."""
+    if (not isinstance(out, torch.Tensor) or out.dtype != dtype or not out.is_contiguous()
+            or out.numel() != numel or out.device != device):
+        raise ValueError(f"{what}: out must be a contiguous {dtype} tensor of {numel} "
+                         f"elements on {device}")
+
+
 # ------------------------------------------------------------------- TQ3 ---
 
 def sign_mask(signs) -> bytes:
@@ -138,10 +147,12 @@ def tq3_quantize(x: torch.Tensor, signs, out: torch.Tensor = None) -> torch.Tens
         raise ValueError(f"last dim must be a positive multiple of 128, got {x.shape[-1]}")
     if x.dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {x.dtype}")
-    _need_gpu(x)
     nb = x.shape[-1] // TQ3_DIM
+    n = x.numel() // TQ3_DIM
+    if out is not None:
+        _check_out(out, torch.uint8, n * TQ3_RECORD_BYTES, x.device, "tq3_quantize")
+    _need_gpu(x)
     xv = x.reshape(-1, TQ3_DIM) if x.is_contiguous() else x.contiguous().reshape(-1, TQ3_DIM)
-    n = xv.shape[0]
     if out is None:
         out = torch.empty((*x.shape[:-1], nb, TQ3_RECORD_BYTES), dtype=torch.uint8,
                           device=x.device)
@@ -159,9 +170,11 @@ def tq3_dequantize(records: torch.Tensor, signs, dtype=torch.float32,
         raise ValueError("records must be uint8 [..., 56]")
     if dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {dtype}")
+    n = records.numel() // TQ3_RECORD_BYTES
+    if out is not None:
+        _check_out(out, dtype, n * TQ3_DIM, records.device, "tq3_dequantize")
     _need_gpu(records)
     rec = records.contiguous()
-    n = rec.numel() // TQ3_RECORD_BYTES
     lead = tuple(records.shape[:-2])
     nb = records.shape[-2] if records.ndim >= 2 else 1
     if out is None:
@@ -197,8 +210,8 @@ def tq3_quantize_split(x: torch.Tensor, signs, packed: torch.Tensor = None,
         scales = torch.empty(lead, dtype=torch.float32, device=x.device)
     for t, want, name in ((packed, torch.uint8, "packed"), (norms, torch.float32, "norms"),
                           (scales, torch.float32, "scales")):
-        if t.dtype != want or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous {want} tensor")
+        if t.dtype != want or not t.is_contiguous() or t.device != x.device:
+            raise ValueError(f"{name} must be a contiguous {want} tensor on {x.device}")
     if packed.numel() != n * 48 or norms.numel() != n or scales.numel() != n:
         raise ValueError("output sizes do not match the input's vector count")
     m = signs if isinstance(signs, (bytes, bytearray)) else sign_mask(signs)
@@ -219,9 +232,11 @@ def tq3_dequantize_split(packed: torch.Tensor, norms: torch.Tensor, scales: torc
         raise TypeError("TQ3 norms and scales must be float32")
     if dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {dtype}")
+    n = norms.numel()
+    if out is not None:
+        _check_out(out, dtype, n * TQ3_DIM, packed.device, "tq3_dequantize_split")
     _need_gpu(packed, norms, scales)
     pk, nr, sc = packed.contiguous(), norms.contiguous(), scales.contiguous()
-    n = nr.numel()
     lead = tuple(norms.shape[:-1])
     nb = norms.shape[-1] if norms.ndim >= 1 else 1
     if out is None:
@@ -272,8 +287,15 @@ def tq3_decode_attention(q: torch.Tensor, k_records: torch.Tensor, v_records: to
             raise ValueError("records must be uint8 [..., 56]")
     if k_records.numel() != v_records.numel():
         raise ValueError("K and V must hold the same number of records")
-    _need_gpu(q, k_records, v_records)
     hq, hkv = q.shape[0], int(n_kv_heads)
+    if out is not None:
+        _check_out(out, dtype, hq * TQ3_DIM, q.device, "tq3_decode_attention")
+    if workspace is not None and (not isinstance(workspace, torch.Tensor)
+                                  or not workspace.is_contiguous()
+                                  or workspace.device != q.device):
+        raise ValueError("tq3_decode_attention: workspace must be a contiguous tensor on "
+                         f"{q.device}")
+    _need_gpu(q, k_records, v_records)
     nrec = k_records.numel() // TQ3_RECORD_BYTES
     if hkv < 1 or nrec % hkv:
         raise ValueError("the records must split evenly over the KV heads")
@@ -436,17 +458,34 @@ def orbit_dequantize(packed: torch.Tensor, row_norms: torch.Tensor, d: int, bits
                      bit_order: int = TQ_MSB_FIRST, rotated_only: bool = False,
                      dtype=torch.float32, out: torch.Tensor = None) -> torch.Tensor:
     """-> [rows, d] of `dtype`: the rotated-basis W' (rotated_only) or W."""
-    _need_gpu(packed, row_norms)
     if dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {dtype}")
+    if bits not in (2, 3, 4):
+        raise ValueError("bits must be 2, 3 or 4")
+    rows = row_norms.numel()
+    if packed.dtype != torch.uint8 or packed.numel() != rows * d * bits // 8:
+        raise ValueError("packed must be uint8 holding rows * d * bits / 8 bytes")
+    cb = _host_f32(codebook)
+    if len(cb) != (1 << bits):
+        raise ValueError("codebook must hold 2**bits values")
+    for t, name in ((inv_perm, "inv_perm"), (signs, "signs")):
+        if t is None:
+            if not rotated_only:
+                raise ValueError(f"{name} is needed unless rotated_only")
+        elif t.numel() != d:
+            raise ValueError(f"{name} must hold d = {d} entries")
+    if out is not None:
+        _check_out(out, dtype, rows * d, packed.device, "orbit_dequantize")
+    _need_gpu(packed, row_norms)
     packed = packed.contiguous()
     row_norms = row_norms.to(torch.float32).contiguous()
-    rows = row_norms.numel()
     if out is None:
         out = torch.empty((rows, d), dtype=dtype, device=packed.device)
     ip = inv_perm.to(torch.int32).contiguous() if inv_perm is not None else None
     sg = signs.to(torch.int8).contiguous() if signs is not None else None
-    cb = _host_f32(codebook)
+    for t in (ip, sg):
+        if t is not None:
+            _need_gpu(t)
     _check(lib.orbit_dequantize(_ptr(packed), _ptr(row_norms), rows, d, bits,
                                 _ptr(ip) if ip is not None else None,
                                 _ptr(sg) if sg is not None else None,

@@ -98,5 +98,6 @@ def compare_reconstruction(gpu_out, orc_f32, norms, dtype=torch.float32):
     else:
         ref = torch.from_numpy(np.ascontiguousarray(orc_f32, dtype=np.float32)).to(dtype)
         exact = bool(torch.equal(gpu_out.cpu(), ref))
-    return {"max_abs_over_norm": float(np.max(err / np.asarray(norms)[:, None])) if err.size else 0.0,
+    scale = np.maximum(np.asarray(norms, dtype=np.float64), np.finfo(np.float64).tiny)
+    return {"max_abs_over_norm": float(np.max(err / scale[:, None])) if err.size else 0.0,
             "exact": exact}

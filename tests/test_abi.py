@@ -54,6 +54,17 @@ def test_codebook_matches_oracle(tq, bits):
     assert np.array_equal(lm.astype(np.float32), oracle.gaussian_lloyd_max(bits))
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_codebook_matches_oracle_every_width(tq, bits):
+    """The product's host codebook equals the oracle's at every input width the
+    GPU tests use: each multiple of 32 up to 16384 and a few wider ones."""
+    import oracle
+    widths = list(range(32, 16385, 32)) + [20480, 24576, 28672, 32768, 65536]
+    for d in widths:
+        assert np.array_equal(tq.orbit_make_codebook(bits, d).numpy(),
+                              oracle.orbit_codebook(bits, d)), d
+
+
 def test_sign_mask_matches_golden(tq):
     import json
     import datagen
@@ -113,3 +124,61 @@ def test_attention_arguments_without_gpu(tq):
     assert call(args(wsb=ws - 1)) == 8
     assert call(args(q=(1 << 20) + 4)) == 6
     assert call(args(k=(1 << 20) + 4)) == 6
+
+
+def test_caller_buffers_are_validated_before_any_call(tq):
+    """The C entry points cannot see the size or type of a buffer, so the binding
+    rejects a caller-given output that is not exactly what the kernels write
+    (these checks run before the GPU check, so CPU tensors exercise them)."""
+    import torch
+    x = torch.zeros(3, 256)
+    signs = torch.ones(128)
+    with pytest.raises(ValueError, match="out must be"):
+        tq.tq3_quantize(x, signs, out=torch.empty(6 * 56 - 1, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="out must be"):
+        tq.tq3_quantize(x, signs, out=torch.empty(6 * 56, dtype=torch.int8))
+    with pytest.raises(ValueError, match="out must be"):
+        tq.tq3_quantize(x, signs, out=torch.empty(6 * 112, dtype=torch.uint8)[::2])
+    rec = torch.zeros(5, 56, dtype=torch.uint8)
+    # an fp32 result into a bf16 buffer would write twice the buffer's bytes
+    with pytest.raises(ValueError, match="out must be"):
+        tq.tq3_dequantize(rec, signs, out=torch.empty(5 * 128, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="out must be"):
+        tq.tq3_dequantize(rec, signs, dtype=torch.bfloat16,
+                          out=torch.empty(5 * 128 - 8, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="out must be"):
+        tq.tq3_dequantize_split(torch.zeros(5, 48, dtype=torch.uint8), torch.zeros(5),
+                                torch.zeros(5), signs, out=torch.empty(5 * 128,
+                                                                       dtype=torch.float16))
+    with pytest.raises(ValueError, match="out must be"):
+        tq.tq3_decode_attention(torch.zeros(4, 128), torch.zeros(8, 56, dtype=torch.uint8),
+                                torch.zeros(8, 56, dtype=torch.uint8), 2, signs,
+                                out=torch.empty(4, 127))
+    with pytest.raises(ValueError, match="workspace"):
+        tq.tq3_decode_attention(torch.zeros(4, 128), torch.zeros(8, 56, dtype=torch.uint8),
+                                torch.zeros(8, 56, dtype=torch.uint8), 2, signs,
+                                workspace=torch.empty(4096, dtype=torch.uint8)[::2])
+
+
+def test_orbit_dequantize_arguments_are_validated(tq):
+    import torch
+    d, bits, rows = 256, 3, 4
+    packed = torch.zeros(rows, d * bits // 8, dtype=torch.uint8)
+    norms = torch.ones(rows)
+    inv, sg = torch.arange(d, dtype=torch.int32), torch.ones(d, dtype=torch.int8)
+    cb = [float(v) for v in range(8)]
+    with pytest.raises(ValueError, match="packed"):
+        tq.orbit_dequantize(packed[:, :-1], norms, d, bits, inv, sg, cb)
+    with pytest.raises(ValueError, match="codebook"):
+        tq.orbit_dequantize(packed, norms, d, bits, inv, sg, cb[:4])
+    with pytest.raises(ValueError, match="inv_perm"):
+        tq.orbit_dequantize(packed, norms, d, bits, inv[:-1], sg, cb)
+    with pytest.raises(ValueError, match="signs"):
+        tq.orbit_dequantize(packed, norms, d, bits, inv, sg[:10], cb)
+    with pytest.raises(ValueError, match="inv_perm"):
+        tq.orbit_dequantize(packed, norms, d, bits, None, sg, cb)
+    with pytest.raises(ValueError, match="out must be"):
+        tq.orbit_dequantize(packed, norms, d, bits, inv, sg, cb, dtype=torch.float16,
+                            out=torch.empty(rows, d))
+    with pytest.raises(ValueError, match="bits"):
+        tq.orbit_dequantize(packed, norms, d, 5, inv, sg, cb)

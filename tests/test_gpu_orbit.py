@@ -2,8 +2,9 @@
 
 Source: "zerogpu-sdxlTrainer: toolkit/util/orbit_quant.py" (_quantize_rows,
 _dequantize_rotated, dequantize). Weights ~ N(0, 0.02^2); rotations from the
-page's seed rule (datagen.rpbh_params); codebooks from orbit_make_codebook,
-which the CPU tests pin to the oracle's Lloyd-Max procedure.
+page's seed rule (datagen.rpbh_params). The library is handed its own codebook
+(orbit_make_codebook) and the oracle its own (oracle.orbit_codebook); the two
+are asserted equal for every (bits, d) used.
 """
 import numpy as np
 import pytest
@@ -31,16 +32,26 @@ def edges_of(cb):
     return ((c[:-1] + c[1:]) / np.float32(2)).astype(np.float64)
 
 
+def codebooks(tq, bits, d):
+    """(library codebook, oracle codebook), asserted identical."""
+    lib_cb = tq.orbit_make_codebook(bits, d)
+    o_cb = oracle.orbit_codebook(bits, d)
+    assert np.array_equal(lib_cb.numpy(), o_cb), (bits, d)
+    return lib_cb, o_cb
+
+
 def check(tq, w, d, bits, msb=True, dtype=torch.float32, full_check=True, cb=None):
     perm, sg = datagen.rpbh_params(d)
     inv = torch.argsort(perm)
     if cb is None:
-        cb = tq.orbit_make_codebook(bits, d)
+        cb, o_cb = codebooks(tq, bits, d)
+    else:
+        o_cb = np.asarray(cb, dtype=np.float32)   # an explicit input, given to both sides
     order = tq.TQ_MSB_FIRST if msb else tq.TQ_LSB_FIRST
     packed, norms = tq.orbit_quantize_weight(w.to(DEV), bits, perm.to(DEV), sg.to(DEV), cb,
                                              bit_order=order)
     torch.cuda.synchronize()
-    o_packed, o_norms = oracle.orbit_quantize(w.numpy(), bits, perm, sg, cb.numpy(),
+    o_packed, o_norms = oracle.orbit_quantize(w.numpy(), bits, perm, sg, o_cb,
                                               msb_first=msb)
     g_norms = norms.cpu().numpy()
     assert np.max(np.abs(g_norms - o_norms) / np.maximum(o_norms, 1e-30)) <= 1e-6
@@ -51,7 +62,7 @@ def check(tq, w, d, bits, msb=True, dtype=torch.float32, full_check=True, cb=Non
         oc = oracle.unpack(o_packed, rows * d, bits, msb_first=msb).reshape(rows, d)
         unit, _ = oracle.orbit_unit(w.numpy(), perm, sg)
         diff = gc != oc
-        dist = np.min(np.abs(unit[..., None].astype(np.float64) - edges_of(cb)), axis=-1)
+        dist = np.min(np.abs(unit[..., None].astype(np.float64) - edges_of(o_cb)), axis=-1)
         assert not (diff & (dist >= 1e-5 * np.abs(unit).max())).any(), "flips away from edges"
         assert diff.sum() <= 1e-6 * rows * d
         pytest.fail(f"codes not bit-identical: {int(diff.sum())} near-edge flips")
@@ -62,7 +73,7 @@ def check(tq, w, d, bits, msb=True, dtype=torch.float32, full_check=True, cb=Non
         out = tq.orbit_dequantize(packed, norms, d, bits, inv.to(DEV), sg.to(DEV), cb,
                                   bit_order=order, rotated_only=rotated, dtype=dtype)
         torch.cuda.synchronize()
-        ref = oracle.orbit_dequantize(o_packed, o_norms, d, bits, inv, sg, cb.numpy(),
+        ref = oracle.orbit_dequantize(o_packed, o_norms, d, bits, inv, sg, o_cb,
                                       msb_first=msb, rotated_only=rotated)
         st = compare_reconstruction(out, ref, o_norms, dtype)
         assert st["exact"], (rotated, st)
@@ -110,7 +121,7 @@ def test_orbit_asymmetric_codebook(tq, bits, msb):
     an uneven random ascending one."""
     d = 3072
     w = datagen.orbit_weight(rows=129, d=d, seed=20 + bits)
-    base = tq.orbit_make_codebook(bits, d)
+    base = torch.from_numpy(codebooks(tq, bits, d)[1])
     shifted = base + np.float32(0.37) * (base[1] - base[0])
     rng = np.random.default_rng(bits)
     rand = torch.from_numpy(np.sort(rng.normal(0.0, 1.5 / np.sqrt(d), 1 << bits))
@@ -159,15 +170,15 @@ def test_orbit_full_weight(tq):
     inv = torch.argsort(perm)
     rows = torch.from_numpy(np.random.default_rng(5).choice(w.shape[0], 512, replace=False))
     for bits in (2, 3, 4):
-        cb = tq.orbit_make_codebook(bits, d)
+        cb, o_cb = codebooks(tq, bits, d)
         packed, norms = tq.orbit_quantize_weight(w.to(DEV), bits, perm.to(DEV), sg.to(DEV), cb)
         full = tq.orbit_dequantize(packed, norms, d, bits, inv.to(DEV), sg.to(DEV), cb)
         torch.cuda.synchronize()
-        o_packed, o_norms = oracle.orbit_quantize(w.numpy(), bits, perm, sg, cb.numpy())
+        o_packed, o_norms = oracle.orbit_quantize(w.numpy(), bits, perm, sg, o_cb)
         assert np.array_equal(norms.cpu().numpy(), o_norms), bits
         assert np.array_equal(packed.cpu().numpy(), o_packed), bits
         ref = oracle.orbit_dequantize(o_packed[rows.numpy()], o_norms[rows.numpy()], d, bits,
-                                      inv, sg, cb.numpy())
+                                      inv, sg, o_cb)
         st = compare_reconstruction(full[rows.to(DEV)], ref, o_norms[rows.numpy()])
         assert st["exact"], (bits, st)
 
@@ -179,7 +190,7 @@ def test_orbit_requantize_in_place(tq):
     quantization of the new weight, and the buffers keep their identity."""
     d, bits, rows = 768, 3, 96
     perm, sg = datagen.rpbh_params(d)
-    cb = tq.orbit_make_codebook(bits, d)
+    cb, o_cb = codebooks(tq, bits, d)
     rng = np.random.default_rng(21)
     w1 = torch.from_numpy((rng.standard_normal((rows, d)) * 0.02).astype(np.float32))
     w2 = torch.from_numpy((rng.standard_normal((rows, d)) * 0.05).astype(np.float32))
@@ -190,7 +201,7 @@ def test_orbit_requantize_in_place(tq):
                                       packed=packed, row_norms=norms)
     torch.cuda.synchronize()
     assert (p2.data_ptr(), n2.data_ptr()) == ptrs
-    o_packed, o_norms = oracle.orbit_quantize(w2.numpy(), bits, perm, sg, cb.numpy())
+    o_packed, o_norms = oracle.orbit_quantize(w2.numpy(), bits, perm, sg, o_cb)
     assert np.array_equal(packed.cpu().numpy(), o_packed)
     assert np.array_equal(norms.cpu().numpy(), o_norms)
 

@@ -66,7 +66,8 @@ def test_rotate_bit_exact(tq, d, rows):
 
 @pytest.mark.parametrize("m", [1, 5, 16, 17, 32, 33, 130, 300])
 @pytest.mark.parametrize("d,n,bits,msb", [(96, 100, 2, True), (1024, 129, 3, True),
-                                          (3072, 384, 4, False), (512, 1, 3, False),
+                                          (3072, 384, 4, False), (3072, 384, 4, True),
+                                          (512, 1, 3, False),
                                           (2048, 256, 2, True)])
 def test_linear(tq, m, d, n, bits, msb):
     perm, sg, cb, packed, norms = quantized(n, d, bits, d + n + bits, msb)
@@ -196,7 +197,8 @@ def check_linear_lowp(tq, fmt, x_rot, packed, norms, d, bits, cb, bias=None, msb
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
 @pytest.mark.parametrize("m", [1, 5, 20, 40, 64, 130, 300])
 @pytest.mark.parametrize("d,n,bits,msb", [(96, 100, 2, True), (1024, 129, 3, True),
-                                          (3072, 384, 4, False), (512, 1, 3, False),
+                                          (3072, 384, 4, False), (3072, 384, 4, True),
+                                          (512, 1, 3, False),
                                           (2048, 256, 2, True)])
 def test_linear_lowp(tq, fmt, m, d, n, bits, msb):
     perm, sg, cb, packed, norms = quantized(n, d, bits, d + n + bits, msb)

@@ -14,6 +14,7 @@ import torch
 
 import datagen
 import oracle
+from oracle import attention as oatt
 
 pytestmark = pytest.mark.gpu
 
@@ -55,15 +56,31 @@ def test_orbit_and_attention_on_side_stream(tq):
     d, bits = 768, 3
     perm, sg = datagen.rpbh_params(d)
     cb = tq.orbit_make_codebook(bits, d)
+    o_cb = oracle.orbit_codebook(bits, d)
+    assert np.array_equal(cb.numpy(), o_cb)
     w = (torch.randn(64, d, generator=torch.Generator().manual_seed(3)) * 0.02)
+    signs = datagen.tq3_signs()
+    hkv, group, n_tok = 2, 4, 300
+    rng = np.random.default_rng(17)
+    k_rec = oracle.tq3_quantize(rng.standard_normal((n_tok * hkv, 128)).astype(np.float32),
+                                signs.numpy())
+    v_rec = oracle.tq3_quantize(rng.standard_normal((n_tok * hkv, 128)).astype(np.float32),
+                                signs.numpy())
+    q = rng.standard_normal((hkv * group, 128)).astype(np.float32)
     side = torch.cuda.Stream(device=DEV)
     with torch.cuda.stream(side):
         wd = w.to(DEV, non_blocking=False)
         packed, norms = tq.orbit_quantize_weight(wd, bits, perm.to(DEV), sg.to(DEV), cb)
         xr = tq.orbit_rotate(torch.ones(4, d, device=DEV), perm.to(DEV), sg.to(DEV))
+        att = tq.tq3_decode_attention(torch.from_numpy(q).to(DEV), torch.from_numpy(k_rec).to(DEV),
+                                      torch.from_numpy(v_rec).to(DEV), hkv, signs)
     side.synchronize()
-    o_packed, o_norms = oracle.orbit_quantize(w.numpy(), bits, perm, sg, cb.numpy())
+    o_packed, o_norms = oracle.orbit_quantize(w.numpy(), bits, perm, sg, o_cb)
     assert np.array_equal(packed.cpu().numpy(), o_packed)
     assert np.array_equal(norms.cpu().numpy(), o_norms)
     assert np.array_equal(xr.cpu().numpy(),
                           oracle.rpbh_forward(np.ones((4, d), np.float32), perm, sg))
+    ref = oatt.tq3_decode_attention(q, k_rec, v_rec, hkv, signs.numpy(), 128 ** -0.5)
+    vmax = np.abs(oatt.dequantized_cache(v_rec, hkv, signs.numpy())).max()
+    # fp32 rounding of scores and sums, far inside the attention tests' bound
+    assert np.abs(att.cpu().numpy().astype(np.float64) - ref).max() <= 1e-4 * vmax

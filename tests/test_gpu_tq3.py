@@ -238,7 +238,7 @@ def test_deterministic_across_grids(tq, signs):
 # ---------------------------------------------------------- full size ---
 
 def test_full_kv_layer(tq, signs):
-    """K and V of one layer: 2 x 524288 bf16 vectors, every record checked."""
+    """K and V of one layer: 2 x 262144 bf16 vectors, every record checked."""
     for which in ("K", "V"):
         x = datagen.kv_cache(which)
         g = run_quantize(tq, x, signs)

@@ -8,13 +8,18 @@ Independent references:
     optimal output levels and mean-squared errors of the Gaussian quantiser
     (the textbook table, to its printed precision);
   * the two Lloyd-Max conditions checked with numerical quadrature, which shares
-    nothing with the closed-form update the procedure uses.
+    nothing with the closed-form update the procedure uses;
+  * the page's fixed iteration count pinned by a second Lloyd iteration that
+    forms each conditional mean by adaptive quadrature (scipy.integrate.quad)
+    and starts from scipy's normal quantile function -- no closed-form
+    density ratio, no erf, no NormalDist -- and by the 4-bit codebook the
+    page's procedure yields after exactly 200 iterations, to six decimals.
 """
 import math
 
 import numpy as np
 import pytest
-from scipy import integrate
+from scipy import integrate, stats
 
 # Max (1960), Gaussian, positive output levels and distortion (unit variance)
 MAX_LEVELS = {
@@ -45,6 +50,57 @@ def test_four_bit_converges_to_max_table(oracle_mod):
         assert abs(got - want) < 0.6e-3
     c200 = oracle_mod.gaussian_lloyd_max(4)
     assert 1e-5 < np.max(np.abs(c200 - c)) < 1e-3   # the page's value differs
+
+
+# The page's procedure evaluated with torch in fp64 (erfinv start, torch.erf /
+# torch.exp updates, 200 iterations): the positive half of the 4-bit codebook,
+# rounded to six decimals. 199 or 201 iterations move it by about 1.9e-5.
+PAGE_4BIT_200 = [0.128324, 0.387841, 0.656431, 0.941915,
+                 1.255739, 1.617524, 2.068505, 2.732137]
+
+
+def _quadrature_lloyd(bits, iters):
+    """Lloyd's iteration with every centroid formed as the quadrature of
+    t * pdf over its cell divided by the quadrature of pdf."""
+    levels = 2 ** bits
+    c = [float(stats.norm.ppf((k + 0.5) / levels)) for k in range(levels)]
+    for _ in range(iters):
+        e = [-np.inf] + [(c[k] + c[k + 1]) / 2 for k in range(levels - 1)] + [np.inf]
+        nxt = []
+        for k in range(levels):
+            mass = integrate.quad(_pdf, e[k], e[k + 1], epsabs=1e-15, epsrel=1e-13)[0]
+            first = integrate.quad(lambda t: t * _pdf(t), e[k], e[k + 1],
+                                   epsabs=1e-15, epsrel=1e-13)[0]
+            nxt.append(first / mass)
+        c = nxt
+    return np.asarray(c)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_iteration_count_pinned_by_quadrature(oracle_mod, bits):
+    ref = _quadrature_lloyd(bits, 200)
+    got = np.asarray(oracle_mod.gaussian_lloyd_max_f64(bits, 200))
+    assert np.max(np.abs(got - ref)) < 1e-11
+    # the fp32 codebook is the rounding of that fp64 result
+    assert np.array_equal(oracle_mod.gaussian_lloyd_max(bits), ref.astype(np.float32))
+    if bits == 4:
+        # the pin separates the page's 200 iterations from 199 and 201
+        for n in (199, 201):
+            other = np.asarray(oracle_mod.gaussian_lloyd_max_f64(bits, n))
+            assert np.max(np.abs(other - ref)) > 1e-6, n
+
+
+def _six_decimals_match(c):
+    pos = np.asarray(c, dtype=np.float64)[8:]
+    return bool(np.all(np.abs(pos - np.asarray(PAGE_4BIT_200)) <= 0.5e-6 + 1e-7))
+
+
+def test_four_bit_200_iterations_to_six_decimals(oracle_mod):
+    c = oracle_mod.gaussian_lloyd_max(4)
+    assert _six_decimals_match(c)
+    assert np.array_equal(c[:8], -c[8:][::-1])        # mirror-symmetric in fp32
+    for n in (199, 201):
+        assert not _six_decimals_match(oracle_mod.gaussian_lloyd_max(4, n)), n
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
