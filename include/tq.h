@@ -45,7 +45,8 @@ enum {
     TQ_ERR_BLOCK = 5,   /* h = d & -d outside [32, 4096], or d > 4096       */
     TQ_ERR_ALIGN = 6,   /* pointer or stride breaks the stated alignment    */
     TQ_ERR_LAUNCH = 7,  /* the HIP runtime refused the launch               */
-    TQ_ERR_ARG = 8      /* other invalid argument (flag value, codebook)    */
+    TQ_ERR_ARG = 8,     /* other invalid argument (flag value, codebook)    */
+    TQ_ERR_SCRATCH = 9  /* sizes exceed the library-held scratch            */
 };
 
 /* ---- element types ----------------------------------------------------- */
@@ -267,6 +268,35 @@ int tq3_decode_attention(const void* q, int q_dtype, int n_q_heads,
 
 /* Workspace bytes tq3_decode_attention needs for these sizes (0 if invalid). */
 size_t tq3_attention_workspace_bytes(int64_t n_tokens, int n_q_heads, int n_kv_heads);
+
+/*
+ * tq3_decode_attention_noalloc -- tq3_decode_attention for callers that cannot
+ * allocate device memory or own a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation. Same arguments,
+ * arithmetic and results (bit for bit) as tq3_decode_attention, without the
+ * workspace: the per-chunk partial results go to a library-held array of
+ * tq3_attention_noalloc_max_bytes() = 16 MiB per GPU (a static device
+ * array, one copy on each GPU the library runs on, held until the process
+ * ends). The call allocates nothing.
+ *   Sizes whose partial results need more than that array
+ *   (tq3_attention_workspace_bytes(n_tokens, n_q_heads, n_kv_heads) > 16 MiB;
+ *   e.g. 32 query heads over about 250K tokens) return TQ_ERR_SCRATCH and
+ *   enqueue nothing.
+ *   Every call on a GPU shares that GPU's array: two calls that overlap in
+ *   time on one GPU (on different streams, or from different threads without
+ *   ordering) race and give undefined results. Calls ordered on one stream
+ *   are safe; each call writes every partial it later reads, so nothing has
+ *   to be cleared between calls.
+ *   The first call on a device looks up that device's copy of the array
+ *   (TQ_ERR_LAUNCH if the runtime cannot).
+ */
+int tq3_decode_attention_noalloc(const void* q, int q_dtype, int n_q_heads,
+                                 const uint8_t* k_records, const uint8_t* v_records,
+                                 int64_t n_tokens, int n_kv_heads, const uint8_t* sign_mask,
+                                 float softmax_scale, void* out, int out_dtype, void* stream);
+
+/* Bytes of the library-held scratch of tq3_decode_attention_noalloc (16 MiB). */
+size_t tq3_attention_noalloc_max_bytes(void);
 
 /* Bytes per TQ3 record: 48 + 4 + 4 = 56 ("tq3_core.py", tq3_memory_bytes). */
 size_t tq3_record_bytes(void);

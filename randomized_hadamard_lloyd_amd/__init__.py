@@ -41,7 +41,7 @@ TQ3_DIM, TQ3_RECORD_BYTES = 128, 56
 _DTYPES = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16, torch.float16: TQ_F16}
 _STATUS = {
     1: ValueError, 2: ValueError, 3: TypeError, 4: ValueError, 5: ValueError,
-    6: ValueError, 7: RuntimeError, 8: ValueError,
+    6: ValueError, 7: RuntimeError, 8: ValueError, 9: ValueError,
 }
 
 _vp, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
@@ -66,6 +66,8 @@ def _load():
         "orbit_linear": [_vp, _int, _i64, _i64, _vp, _vp, _i64, _int, _vp, _int, _vp, _vp, _vp],
         "tq3_decode_attention": [_vp, _int, _int, _vp, _vp, _i64, _int, _vp, ctypes.c_float,
                                  _vp, ctypes.c_size_t, _vp, _int, _vp],
+        "tq3_decode_attention_noalloc": [_vp, _int, _int, _vp, _vp, _i64, _int, _vp,
+                                         ctypes.c_float, _vp, _int, _vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -79,6 +81,8 @@ def _load():
     lib.tq_status_str.restype = ctypes.c_char_p
     lib.tq3_attention_workspace_bytes.argtypes = [_i64, _int, _int]
     lib.tq3_attention_workspace_bytes.restype = ctypes.c_size_t
+    lib.tq3_attention_noalloc_max_bytes.argtypes = []
+    lib.tq3_attention_noalloc_max_bytes.restype = ctypes.c_size_t
     return lib
 
 
@@ -88,7 +92,8 @@ lib = _load()
 EXPORTS = ("tq3_quantize", "tq3_dequantize", "tq3_quantize_split", "tq3_dequantize_split",
            "orbit_quantize_weight", "orbit_dequantize", "tq3_record_bytes", "orbit_block_size", "tq_gaussian_lloyd_max",
            "orbit_make_codebook", "tq_status_str", "tq3_decode_attention",
-           "tq3_attention_workspace_bytes", "orbit_rotate", "orbit_linear")
+           "tq3_attention_workspace_bytes", "orbit_rotate", "orbit_linear",
+           "tq3_decode_attention_noalloc", "tq3_attention_noalloc_max_bytes")
 
 
 def _check(status: int, what: str):
@@ -315,6 +320,50 @@ def tq3_decode_attention(q: torch.Tensor, k_records: torch.Tensor, v_records: to
                                     hkv, m, float(softmax_scale), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _ptr(out),
                                     _DTYPES[dtype], _stream(q)), "tq3_decode_attention")
+    return out
+
+
+def tq3_attention_noalloc_max_bytes() -> int:
+    return int(lib.tq3_attention_noalloc_max_bytes())
+
+
+def tq3_decode_attention_noalloc(q: torch.Tensor, k_records: torch.Tensor,
+                                 v_records: torch.Tensor, n_kv_heads: int, signs,
+                                 softmax_scale: float = None, dtype=torch.float32,
+                                 out: torch.Tensor = None) -> torch.Tensor:
+    """tq3_decode_attention with the library's own per-GPU scratch instead of a
+    workspace (the C call allocates nothing; with `out` given, neither does
+    this wrapper). Sizes needing more than tq3_attention_noalloc_max_bytes()
+    of partial results raise ValueError. Calls that overlap in time on one GPU
+    share the scratch and race."""
+    if q.dtype not in _DTYPES or dtype not in _DTYPES:
+        raise TypeError("unsupported dtype")
+    if q.ndim != 2 or q.shape[1] != TQ3_DIM:
+        raise ValueError("q must be [n_q_heads, 128]")
+    for r in (k_records, v_records):
+        if r.dtype != torch.uint8 or r.shape[-1] != TQ3_RECORD_BYTES:
+            raise ValueError("records must be uint8 [..., 56]")
+    if k_records.numel() != v_records.numel():
+        raise ValueError("K and V must hold the same number of records")
+    hq, hkv = q.shape[0], int(n_kv_heads)
+    if out is not None:
+        _check_out(out, dtype, hq * TQ3_DIM, q.device, "tq3_decode_attention_noalloc")
+    _need_gpu(q, k_records, v_records)
+    for t, name in ((q, "q"), (k_records, "k_records"), (v_records, "v_records")):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous (no copy is made)")
+    nrec = k_records.numel() // TQ3_RECORD_BYTES
+    if hkv < 1 or nrec % hkv:
+        raise ValueError("the records must split evenly over the KV heads")
+    if softmax_scale is None:
+        softmax_scale = TQ3_DIM ** -0.5
+    if out is None:
+        out = torch.empty((hq, TQ3_DIM), dtype=dtype, device=q.device)
+    m = signs if isinstance(signs, (bytes, bytearray)) else sign_mask(signs)
+    _check(lib.tq3_decode_attention_noalloc(_ptr(q), _DTYPES[q.dtype], hq, _ptr(k_records),
+                                            _ptr(v_records), nrec // hkv, hkv, m,
+                                            float(softmax_scale), _ptr(out), _DTYPES[dtype],
+                                            _stream(q)), "tq3_decode_attention_noalloc")
     return out
 
 

@@ -83,6 +83,8 @@ const char* tq_status_str(int status) {
     case TQ_ERR_ALIGN: return "misaligned pointer or stride";
     case TQ_ERR_LAUNCH: return "kernel launch failed";
     case TQ_ERR_ARG: return "invalid argument";
+    case TQ_ERR_SCRATCH:
+      return "sizes need more partial results than the library's 16 MiB attention scratch holds";
     default: return "unknown status";
   }
 }
@@ -299,6 +301,29 @@ int tq3_decode_attention(const void* q, int q_dtype, int n_q_heads, const uint8_
   return launched(tq::launch_tq3_attention(q, q_dtype, n_q_heads, k_records, v_records, n_tokens,
                                            n_kv_heads, m, softmax_scale,
                                            static_cast<float*>(workspace), out, out_dtype,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+size_t tq3_attention_noalloc_max_bytes(void) { return tq::kAttnScratchBytes; }
+
+int tq3_decode_attention_noalloc(const void* q, int q_dtype, int n_q_heads,
+                                 const uint8_t* k_records, const uint8_t* v_records,
+                                 int64_t n_tokens, int n_kv_heads, const uint8_t* sign_mask,
+                                 float softmax_scale, void* out, int out_dtype, void* stream) {
+  if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype)) return TQ_ERR_DTYPE;
+  if (!attn_shape_ok(n_tokens, n_q_heads, n_kv_heads)) return TQ_ERR_SHAPE;
+  if (!std::isfinite(softmax_scale)) return TQ_ERR_ARG;
+  if (!q || !k_records || !v_records || !sign_mask || !out) return TQ_ERR_NULL;
+  if (tq3_attention_workspace_bytes(n_tokens, n_q_heads, n_kv_heads) > tq::kAttnScratchBytes)
+    return TQ_ERR_SCRATCH;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_records, 8) || !aligned(v_records, 8))
+    return TQ_ERR_ALIGN;
+  float* ws = nullptr;
+  if (tq::attention_scratch(&ws) != hipSuccess || !ws) return TQ_ERR_LAUNCH;
+  tq::SignMask m;
+  std::memcpy(m.w, sign_mask, sizeof(m.w));
+  return launched(tq::launch_tq3_attention(q, q_dtype, n_q_heads, k_records, v_records, n_tokens,
+                                           n_kv_heads, m, softmax_scale, ws, out, out_dtype,
                                            static_cast<hipStream_t>(stream)));
 }
 

@@ -24,6 +24,14 @@
 #include "tq_common.h"
 #include "tq_kernels.h"
 
+#include <mutex>
+
+// Library-held partial results for tq3_decode_attention_noalloc: one copy per
+// GPU, alive until the process ends. Host code never passes this name to a
+// kernel (on the host it is a stand-in, not a device address); it uses the
+// per-device address hipGetSymbolAddress returns.
+static __device__ __align__(256) float scratch[tq::kAttnScratchBytes / sizeof(float)];
+
 namespace tq {
 
 namespace {
@@ -571,6 +579,29 @@ hipError_t launch_tq3_attention(const void* q, int qdt, int hq, const uint8_t* k
   else
     tq3_attn_combine_kernel<DT_F16><<<hq, 1024, 0, s>>>(ws, (int)p.nchunk, m, out);
   return hipGetLastError();
+}
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+float* g_scratch_ptr[kMaxScratchDevices];
+hipError_t g_scratch_err[kMaxScratchDevices];
+std::once_flag g_scratch_once[kMaxScratchDevices];
+}  // namespace
+
+hipError_t attention_scratch(float** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  // Once per device, with that device current (the caller's current device).
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? static_cast<float*>(p) : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace tq

@@ -79,6 +79,10 @@ hipError_t launch_tq3_attention(const void* q, int qdt, int hq, const uint8_t* k
                                 const uint8_t* v, int64_t n_tok, int hkv, const SignMask& m,
                                 float softmax_scale, float* ws, void* out, int odt,
                                 hipStream_t s);
+// Bytes of the library-held attention scratch (one array per GPU) and its
+// device address on the current device, looked up once per device.
+constexpr size_t kAttnScratchBytes = (size_t)16 << 20;
+hipError_t attention_scratch(float** ptr);
 
 // Blocks of `kernel` that one CU keeps resident with `block` threads and
 // `shm` bytes of dynamic LDS (at least 1).
