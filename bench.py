@@ -10,14 +10,22 @@ buffer sets whose total size exceeds the 256 MB last-level cache, so every
 launch streams from HBM. The timed region is bracketed by device
 synchronisation and measured with HIP events on the launch stream.
 
+Before the warmup steps, a pre-roll runs steps for a fixed stretch of device
+time (default 200 ms): the GPU idles at a low clock and needs some 20 ms of
+load to reach its sustained one, whatever --warmup asks for.
+
 Also reported, each timed with HIP events over repeated launches:
   * kernels: per-kernel average duration and effective bandwidth
     (algorithmic bytes read + written) of the headline step;
-  * roofline: the dominant kernel of the step against the vector-ALU peak
-    (it is issue-bound), with its HBM figures beside, and traffic from the
-    committed rocprofv3 counter summary when it matches the kernel source;
-  * valu: the same kernel's issued VALU lane-ops (from the committed
-    SQ_INSTS_VALU summary) against the same peak;
+  * roofline: the dominant kernel of the step against MI355X's 8 TB/s HBM
+    peak (algorithmic bytes per launch / average launch duration), with
+    traffic from the committed rocprofv3 counter summary when it matches the
+    kernel source;
+  * valu: the same kernel's arithmetic and issued VALU lane-ops (from the
+    committed SQ_INSTS_VALU summary) against the non-packed VALU issue peak;
+  * codec_kernels: each codec workload's own kernel line (KV-layer bf16
+    quantize and dequantize, 2^20 structured fp32 quantize and dequantize,
+    2^24 decode records to bf16) against the HBM peak;
   * secondary: the same layer with K and V as separate tensors (four
     launches per step); 2^20 structured fp32 vectors; 2^24 records
     dequantized to bf16; the 12288 x 3072 OrbitQuant weight at 2/3/4 bits;
@@ -66,7 +74,11 @@ def parse():
     p.add_argument("--steps", type=int, default=500)
     p.add_argument("--warmup", type=int, default=300)
     p.add_argument("--sets", type=int, default=4, help="rotating buffer sets")
-    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--preroll-ms", type=float, default=200.0,
+                   help="device time of untimed steps run before the warmup steps, so the "
+                        "clock has ramped up whatever --warmup is")
+    p.add_argument("--cpu-seconds", type=float, default=8.0,
+                   help="seconds of oracle work per thread count (1 thread, all threads)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--only-secondary", action="store_true",
@@ -80,7 +92,7 @@ def parse():
                         "warmup + 3 launches each of quantize, rotated and full dequantize")
     args = p.parse_args()
     if args.profile:
-        args.steps, args.warmup = 3, 1
+        args.steps, args.warmup, args.preroll_ms = 3, 1, 0.0
         args.no_secondary = args.no_cpu_baseline = True
     return args
 
@@ -149,24 +161,51 @@ def valu_per_vector():
     return t if t.get("source_hash") == source_hash() else None
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(k_cpu, signs, seconds):
     """The oracle, as it stands, on a bounded sample of the workload: the first
-    65536 K vectors, quantize + dequantize, repeated for about `seconds`."""
+    65536 K vectors, quantize + dequantize, repeated for about `seconds`, once
+    on one thread and once on every thread this process may use (OpenMP over
+    vectors). `value` is the all-threads rate."""
     import oracle
     sample = k_cpu.reshape(-1, 128)[:65536].to(torch.float32).numpy()
     s = signs.numpy()
-    threads = min(os.cpu_count() or 1, 16)
-    n_done, t0 = 0, time.perf_counter()
-    while True:
-        rec = oracle.tq3_quantize(sample, s, threads=threads)
-        oracle.tq3_dequantize(rec, s, threads=threads)
-        n_done += sample.shape[0]
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": n_done / el, "unit": "vectors/s", "cores": threads, "kind": "oracle",
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    threads_all = min(usable, int(env)) if env.isdigit() and int(env) > 0 else usable
+
+    def leg(threads):
+        n_done, t0 = 0, time.perf_counter()
+        while True:
+            rec = oracle.tq3_quantize(sample, s, threads=threads)
+            oracle.tq3_dequantize(rec, s, threads=threads)
+            n_done += sample.shape[0]
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return n_done / el, n_done // sample.shape[0], el
+
+    v1, p1, e1 = leg(1)
+    va, pa, ea = leg(threads_all)
+    return {"value": va, "unit": "vectors/s", "cores": threads_all, "kind": "oracle",
             "sample": f"first 65536 K vectors of the KV layer (bf16 widened to fp32), "
-                      f"quantize + dequantize, {n_done // 65536} passes in {el:.1f} s"}
+                      f"quantize + dequantize: {pa} passes in {ea:.1f} s on {threads_all} "
+                      f"threads, {p1} passes in {e1:.1f} s on 1 thread",
+            "single_thread_value": v1, "cpu_model": cpu_model(),
+            "host_cpus": os.cpu_count(), "usable_cpus": usable,
+            "omp_num_threads_env": env or None}
 
 
 def secondary(tq, timer, dev, signs, mask):
@@ -391,6 +430,67 @@ def secondary(tq, timer, dev, signs, mask):
     return out
 
 
+def codec_kernels(tq, dev, mask, sp, iters, kv_kernels):
+    """Each codec workload's kernel on its own, back-to-back launches over
+    rotating buffers (every launch streams from HBM), one event pair around
+    them: the KV layer's bf16 quantize and dequantize (from the headline run),
+    the 2^20 structured fp32 vectors (quantize, dequantize to fp32) and the
+    2^24 decode records to bf16."""
+    import datagen
+    L = tq.lib
+    stream = torch.cuda.current_stream(dev)
+
+    def avg_ms(calls, count):
+        for i in range(5):
+            calls[i % len(calls)]()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(count):
+            calls[i % len(calls)]()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / count
+
+    def line(kernel, ms, vectors, bpv):
+        gbs = rate(bpv * vectors, ms)
+        return {"kernel": kernel, "avg_ms": ms, "vectors": vectors, "bytes_per_vector": bpv,
+                "vectors_per_s": vectors / (ms * 1e-3), "GBps": gbs,
+                "frac_peak_hbm": gbs / PEAK_HBM_GBS}
+
+    out = {}
+    for name in ("quantize", "dequantize"):
+        k = kv_kernels[name]
+        out[f"{name}_kv_layer_bf16"] = line(k["kernel"], k["avg_ms"], k["vectors_per_launch"],
+                                            k["bytes_per_vector"])
+    # 2^20 structured fp32 vectors, two buffer sets (1.1 GB in all)
+    x = datagen.structured_blocks().to(dev)
+    n = x.shape[0]
+    xs = [x, x.clone()]
+    recs = [torch.empty((n, REC), dtype=torch.uint8, device=dev) for _ in xs]
+    ys = [torch.empty((n, 128), dtype=torch.float32, device=dev) for _ in xs]
+    qc = [lambda i=i: L.tq3_quantize(tq._ptr(xs[i]), tq.TQ_F32, n, 128, mask, tq._ptr(recs[i]),
+                                     sp) for i in range(2)]
+    dc = [lambda i=i: L.tq3_dequantize(tq._ptr(recs[i]), n, mask, tq._ptr(ys[i]), tq.TQ_F32,
+                                       128, sp) for i in range(2)]
+    its = max(20, min(iters, 200))
+    out["quantize_structured_2^20_f32"] = line("tq3_quantize_kernel<f32>", avg_ms(qc, its), n,
+                                               512 + REC)
+    out["dequantize_structured_2^20_f32"] = line("tq3_dequantize_kernel<f32>", avg_ms(dc, its),
+                                                 n, REC + 512)
+    del x, xs, recs, ys, qc, dc
+    # 2^24 decode records to bf16 (896 MiB in, 4 GiB out per launch)
+    rec = datagen.decode_records().to(dev)
+    n = rec.shape[0]
+    y = torch.empty((n, 128), dtype=torch.bfloat16, device=dev)
+    dd = [lambda: L.tq3_dequantize(tq._ptr(rec), n, mask, tq._ptr(y), tq.TQ_BF16, 128, sp)]
+    out["dequantize_decode_2^24_bf16"] = line("tq3_dequantize_kernel<bf16>",
+                                              avg_ms(dd, max(10, min(iters, 40))), n, REC + 256)
+    del rec, y, dd
+    return out
+
+
 def profile_orbit(tq, dev):
     """The 12288 x 3072 fp32 weight through the codec, a few launches per
     kernel, for counters taken under a profiler."""
@@ -486,6 +586,23 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    # Pre-roll: untimed steps for a fixed stretch of device time, so the clock
+    # has ramped up before the warmup and timed steps (the GPU idles at a low
+    # clock and needs about 20 ms of load to reach its sustained one).
+    preroll_steps, preroll_ms = 0, 0.0
+    if args.preroll_ms > 0:
+        p0 = torch.cuda.Event(enable_timing=True)
+        p1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        p0.record(stream)
+        chunk = 50
+        while preroll_ms < args.preroll_ms:
+            for i in range(chunk):
+                step(preroll_steps + i)
+            preroll_steps += chunk
+            p1.record(stream)
+            p1.synchronize()
+            preroll_ms = p0.elapsed_time(p1)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -552,26 +669,33 @@ def main():
     for name, k in kernels.items():
         k["alg_ops_per_vector"] = ALG_OPS_PER_VECTOR[name]
         k["alg_TOPs"] = ALG_OPS_PER_VECTOR[name] * n / (k["avg_ms"] * 1e-3) / 1e12
-    # The quantize kernel issues ~32 VALU lane-ops per element against 2.4
-    # bytes of HBM traffic: the vector ALU, not HBM, bounds it. Its roofline is
-    # the method's arithmetic against the chip's non-packed fp32 VALU peak.
+    # Roofline of the dominant kernel against HBM: the codec streams its input
+    # once and writes its output once, so its algorithmic bytes (256 B of bf16
+    # in + 56 B record out per vector) over its average launch duration,
+    # measured alone, against the 8 TB/s peak.
     traffic = measured_traffic(kernels[dom]["kernel"])
-    ach = kernels[dom]["alg_TOPs"]
-    peak = PEAK_VALU_LANE_OPS / 1e12
-    roofline = {"bound": "alu", "kernel": kernels[dom]["kernel"], "achieved": ach,
-                "peak": peak, "unit": "TOP/s", "frac": ach / peak, "traffic": traffic,
-                "alg_ops_per_launch": ALG_OPS_PER_VECTOR[dom] * n,
-                "alg_bytes_per_launch": bytes_per_vec[dom] * n,
-                "hbm": {"achieved": kernels[dom]["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": kernels[dom]["frac_peak_hbm"]}}
-    valu = None
+    alg_bytes = bytes_per_vec[dom] * n
+    ach = alg_bytes / (kernels[dom]["avg_ms"] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": kernels[dom]["kernel"], "achieved": ach,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+                "traffic": traffic, "alg_bytes_per_launch": alg_bytes,
+                "bytes_per_vector": bytes_per_vec[dom], "vectors_per_launch": n,
+                "avg_launch_ms": kernels[dom]["avg_ms"]}
+    # The same kernel's vector-ALU work: the method's arithmetic and (from the
+    # committed SQ_INSTS_VALU summary, when it matches the source) the issued
+    # lane-ops, both against the non-packed 32-bit VALU issue peak.
+    peak_valu = PEAK_VALU_LANE_OPS / 1e12
+    valu = {"kernel": kernels[dom]["kernel"], "alg_ops_per_vector": ALG_OPS_PER_VECTOR[dom],
+            "alg_achieved": kernels[dom]["alg_TOPs"], "peak": peak_valu, "unit": "TOP/s",
+            "alg_frac": kernels[dom]["alg_TOPs"] / peak_valu}
     vc = valu_per_vector()
     if vc is not None and kernels[dom]["kernel"] in vc.get("kernels", {}):
         ops = vc["kernels"][kernels[dom]["kernel"]]["valu_lane_ops_per_vector"]
         issued = ops * n / (kernels[dom]["avg_ms"] * 1e-3)
-        valu = {"kernel": kernels[dom]["kernel"], "issued_lane_ops_per_vector": ops,
-                "achieved": issued / 1e12, "peak": peak, "unit": "TOP/s",
-                "frac": issued / PEAK_VALU_LANE_OPS}
+        valu.update({"issued_lane_ops_per_vector": ops, "issued_achieved": issued / 1e12,
+                     "issued_frac": issued / PEAK_VALU_LANE_OPS})
+
+    codec = codec_kernels(tq, dev, mask, sp, args.steps, kernels)
 
     # correctness spot check of one set against the oracle (outside timing)
     import oracle
@@ -592,9 +716,11 @@ def main():
                                "dequantize launch back to bf16 per step",
                    "vectors_per_step": vec_per_step, "buffer_sets": args.sets},
         "effective_GBps": eff_gbs, "pct_of_peak_hbm": 100.0 * eff_gbs / PEAK_HBM_GBS,
+        "preroll": {"steps": preroll_steps, "device_ms": preroll_ms},
         "kernels": kernels,
         "roofline": roofline,
         "valu": valu,
+        "codec_kernels": codec,
         "parity_spot_check": ok,
     }
     if not args.no_secondary:
