@@ -157,6 +157,37 @@ def test_edge_vectors(tq, signs):
     check_dequantize(tq, g, signs, torch.bfloat16)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_edge_vectors_16bit(tq, signs, dtype):
+    """16-bit inputs: the kernels square them exactly (one fma per pair in the
+    sum of squares) except where a bf16 magnitude below 2^-63 has a square
+    that loses bits; vectors of tiny magnitudes (squares subnormal, halfway
+    cases included), tiny elements beside normal ones, zeros, huge values
+    and a wide spread must all match the oracle's separately rounded order."""
+    rng = np.random.default_rng(16)
+    rows = [np.zeros(128), np.full(128, 2.5), np.eye(128)[3] * 5.0]
+    if dtype == torch.bfloat16:
+        rows.append(np.full(128, 2.0 ** -75))               # squares 2^-150: halfway
+        rows.append(rng.choice([2.0 ** -75, 2.0 ** -74.5, 3 * 2.0 ** -76], 128))
+        t = rng.standard_normal(128)
+        t[::5] *= 2.0 ** -70                                  # tiny beside normal
+        rows.append(t)
+        rows.append(rng.standard_normal(128) * 2.0 ** -66)   # squares near 2^-132
+        rows.append(rng.standard_normal(128) * 2.0 ** 60)    # squares overflow
+        rows.append(rng.standard_normal(128) * np.exp2(rng.integers(-80, 60, 128)))
+        h = rng.standard_normal(128) * 2.0 ** -63
+        rows.append(h)
+    else:
+        rows.append(np.full(128, 2.0 ** -24))                # fp16's smallest subnormal
+        rows.append(rng.standard_normal(128) * 2.0 ** -14)
+        rows.append(rng.standard_normal(128) * 6e4 / 4)
+        rows.append(rng.standard_normal(128) * np.exp2(rng.integers(-20, 14, 128)))
+    x = torch.tensor(np.stack(rows), dtype=torch.float32).to(dtype)
+    x = torch.cat([x, datagen.gaussian_vectors(61, seed=17).to(dtype)])
+    g, _ = check_quantize(tq, x, signs)
+    check_dequantize(tq, g, signs, dtype)
+
+
 def near_boundary_vectors(n, signs, seed):
     """Vectors whose scaled coefficients land on or within a few ulps of the
     decision boundaries: target coefficients t (max |t| = 1) are chosen
