@@ -203,8 +203,8 @@ def block_size(d: int) -> int:
 
 def _check_orbit(d):
     h = d & (-d)
-    if h < 8 or h > 4096:
-        raise ValueError(f"oracle supports Hadamard blocks 8..4096, got {h}")
+    if h < 8 or h > 65536:
+        raise ValueError(f"oracle supports Hadamard blocks 8..65536, got {h}")
 
 
 def rpbh_forward(w, perm, signs, threads=0):

@@ -53,13 +53,17 @@ static float tq3_boundary(int k) {
     return (float)b[k];
 }
 
-/* Sum of squares by the canonical pairwise tree over a power-of-two run. */
+/* Sum of squares by the canonical pairwise tree over a power-of-two run
+ * (n <= 65536). */
 static float sumsq_pairwise(const float* v, int n) {
-    float s[4096];
+    float small[128] = {0.0f};
+    float* s = n <= 128 ? small : (float*)malloc((size_t)n * sizeof(float));
     for (int j = 0; j < n; ++j) s[j] = v[j] * v[j];
     for (int w = 1; w < n; w *= 2)
         for (int j = 0; j < n; j += 2 * w) s[j] = s[j] + s[j + w];
-    return s[0];
+    const float r = s[0];
+    if (s != small) free(s);
+    return r;
 }
 
 /* [TQ3] _fwht_inplace and [ORBIT] _fwht: butterfly stages with half-width

@@ -162,3 +162,74 @@ def test_quality_matches_gaussian_distortion(oracle_mod, bits):
                                        signs, cb)
     rel = np.linalg.norm(full - w) / np.linalg.norm(w)
     assert abs(rel - math.sqrt(mse)) < 0.03 * math.sqrt(mse)
+
+
+# ---- rows longer than 4096: Hadamard blocks of up to 16384 ---------------
+
+def sylvester_rotate_fp64(w, perm, signs):
+    """Rows of R w for R = blkdiag(H_h / sqrt(h)) . diag(signs) . P in fp64,
+    with the Sylvester matrix's closed form H[i, j] = (-1)^popcount(i & j)
+    evaluated directly (no staged transform), 1024 outputs at a time."""
+    w = np.asarray(w, dtype=np.float64)
+    d = w.shape[1]
+    h = d & -d
+    v = w[:, np.asarray(perm)] * np.asarray(signs, dtype=np.float64)[None, :]
+    out = np.empty_like(v)
+    j = np.arange(h, dtype=np.uint32)[None, :]
+    step = min(h, 1024)
+    for i0 in range(0, h, step):
+        i = np.arange(i0, i0 + step, dtype=np.uint32)[:, None]
+        sg = 1.0 - 2.0 * (np.bitwise_count(i & j) & 1)          # [step, h]
+        for b in range(d // h):
+            out[:, b * h + i0: b * h + i0 + step] = v[:, b * h:(b + 1) * h] @ sg.T
+    return out / math.sqrt(h)
+
+
+_LARGE_D = {}
+
+
+def _large_case(d):
+    """Two weight rows of width d and their fp64 rotation (cached per d)."""
+    if d not in _LARGE_D:
+        perm, signs = datagen.rpbh_params(d)
+        w = datagen.orbit_weight(rows=2, d=d, seed=d + 7).numpy()
+        _LARGE_D[d] = (perm, signs, w, sylvester_rotate_fp64(w, perm.numpy(), signs.numpy()))
+    return _LARGE_D[d]
+
+
+def test_sylvester_closed_form_is_the_dense_matrix():
+    # the closed form reproduces the recursive construction (so it can stand
+    # in for a dense matrix too large to build at d = 16384)
+    for n in (32, 256):
+        i = np.arange(n, dtype=np.uint32)
+        cf = 1 - 2 * (np.bitwise_count(i[:, None] & i[None, :]) & 1).astype(np.int64)
+        assert np.array_equal(cf, sylvester(n))
+
+
+@pytest.mark.parametrize("d", [5120, 8192, 12288, 16384])
+def test_rpbh_large_d_matches_closed_form(oracle_mod, d):
+    perm, signs, w, ref = _large_case(d)
+    assert oracle_mod.block_size(d) == (d & -d)
+    y = oracle_mod.rpbh_forward(w, perm, signs).astype(np.float64)
+    nrm = np.linalg.norm(w.astype(np.float64), axis=1)
+    assert np.max(np.abs(y - ref) / nrm[:, None]) < 2e-6
+    assert np.allclose(np.linalg.norm(y, axis=1), nrm, rtol=1e-6)
+    back = oracle_mod.rpbh_inverse(y.astype(np.float32), np.argsort(perm.numpy()), signs)
+    assert np.max(np.abs(back - w) / nrm[:, None]) < 2e-6
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("d", [12288, 16384])
+def test_quantize_large_d_matches_fp64(oracle_mod, bits, d):
+    perm, signs, w, y = _large_case(d)
+    cb = oracle_mod.orbit_codebook(bits, d)
+    edges = oracle_mod.orbit_edges(cb).astype(np.float64)
+    packed, norms = oracle_mod.orbit_quantize(w, bits, perm, signs, cb)
+    n64 = np.linalg.norm(y, axis=1)
+    assert np.max(np.abs(norms - n64) / n64) < 1e-6
+    unit = y / n64[:, None]
+    want = np.searchsorted(edges, unit, side="left")
+    got = unpack_msb(packed, 2 * d, bits).reshape(2, d)
+    near = np.min(np.abs(unit[..., None] - edges), axis=-1) < 1e-6 * np.abs(unit).max()
+    assert np.array_equal(got[~near], want[~near])
+    assert near.mean() < 1e-3
