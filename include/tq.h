@@ -42,7 +42,7 @@ enum {
     TQ_ERR_SHAPE = 2,   /* negative count, bad stride, d not a multiple of h */
     TQ_ERR_DTYPE = 3,   /* unknown dtype code                               */
     TQ_ERR_BITS = 4,    /* bits not in {2, 3, 4}                            */
-    TQ_ERR_BLOCK = 5,   /* h = d & -d outside [32, 4096], or d > 4096       */
+    TQ_ERR_BLOCK = 5,   /* h = d & -d below 32, or d above 16384            */
     TQ_ERR_ALIGN = 6,   /* pointer or stride breaks the stated alignment    */
     TQ_ERR_LAUNCH = 7,  /* the HIP runtime refused the launch               */
     TQ_ERR_ARG = 8,     /* other invalid argument (flag value, codebook)    */
@@ -149,9 +149,9 @@ int tq3_dequantize_split(const uint8_t* packed, const float* norms, const float*
  * Codes are packed in `bit_order` into rows of d*bits/8 bytes.
  *
  *   W            device, rows x d fp32, row-major, 16-byte aligned.
- *   d            input features; h = d & -d must lie in [32, 4096] (the page
- *                skips layers with h < 32) and d <= 4096 (one row is held
- *                on chip by one wave).
+ *   d            input features, at most 16384 (one row is held on chip by
+ *                one block of up to 16 waves); h = d & -d must be at least
+ *                32 (the page skips layers with h < 32).
  *   bits         2, 3 or 4.
  *   perm         device, d int32, a permutation of 0..d-1; 16-byte aligned.
  *   signs        device, d int8, each +1 or -1; 16-byte aligned.

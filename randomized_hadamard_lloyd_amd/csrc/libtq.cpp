@@ -38,6 +38,8 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int launched(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH; }
 
 constexpr int64_t kMaxVectors = (int64_t)1 << 40;
+// Longest OrbitQuant row: one 1024-thread block holds it on chip.
+constexpr int64_t kMaxOrbitD = 16384;
 
 // ---- Gaussian Lloyd-Max (fp64), the procedure of the OrbitQuant page ----
 
@@ -79,7 +81,7 @@ const char* tq_status_str(int status) {
     case TQ_ERR_SHAPE: return "invalid shape or stride";
     case TQ_ERR_DTYPE: return "invalid dtype";
     case TQ_ERR_BITS: return "bits must be 2, 3 or 4";
-    case TQ_ERR_BLOCK: return "Hadamard block d & -d outside [32, 4096] or d > 4096";
+    case TQ_ERR_BLOCK: return "Hadamard block d & -d below 32, or d above 16384";
     case TQ_ERR_ALIGN: return "misaligned pointer or stride";
     case TQ_ERR_LAUNCH: return "kernel launch failed";
     case TQ_ERR_ARG: return "invalid argument";
@@ -161,7 +163,7 @@ static int orbit_check(int64_t rows, int64_t d, int bits, const float* codebook,
   if (bits < 2 || bits > 4) return TQ_ERR_BITS;
   if (rows < 0 || rows > kMaxVectors || d <= 0) return TQ_ERR_SHAPE;
   const int64_t h = d & -d;
-  if (h < 32 || h > 4096 || d > 4096) return TQ_ERR_BLOCK;
+  if (h < 32 || d > kMaxOrbitD) return TQ_ERR_BLOCK;
   if (bit_order != TQ_MSB_FIRST && bit_order != TQ_LSB_FIRST) return TQ_ERR_ARG;
   if (!codebook) return TQ_ERR_NULL;
   const int levels = 1 << bits;
@@ -230,7 +232,7 @@ int orbit_rotate(const void* x, int dtype, int64_t rows, int64_t d, const int32_
   if (!valid_dtype(dtype)) return TQ_ERR_DTYPE;
   if (rows < 0 || rows > kMaxVectors || d <= 0) return TQ_ERR_SHAPE;
   const int64_t h = d & -d;
-  if (h < 32 || h > 4096 || d > 4096) return TQ_ERR_BLOCK;
+  if (h < 32 || d > kMaxOrbitD) return TQ_ERR_BLOCK;
   if (rows == 0) return TQ_OK;
   if (!x || !perm || !signs || !x_rot) return TQ_ERR_NULL;
   if (!aligned(x, 16) || !aligned(x_rot, 16) || !aligned(perm, 16) || !aligned(signs, 16))

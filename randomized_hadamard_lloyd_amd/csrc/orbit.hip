@@ -6,12 +6,20 @@
 // at a time; wave w holds the row's elements [1024 w, 1024 w + 1024) as 64
 // chunks of 16, one chunk per lane (see lane_chunk for which lane holds
 // which). Element j = 16 c + i of chunk c: index bits 0-3 are register bits,
-// bits 4-9 chunk bits inside the wave, bits 10-11 the wave. FWHT stages run
-// in the order 1, 2, 4, ..., h/2: in registers for bits 0-3; across lanes
-// without LDS for bits 4-9 (DPP fmac with the lazy lane sign described in
-// tq3.hip for bits 4-7, permlane16/32 swaps for bits 8 and 9); across waves
-// through LDS for bits 10-11. The row norm's sum of squares follows the same
-// bit order inside each h-block; block sums are then added left to right.
+// bits 4-9 chunk bits inside the wave, bits 10-13 the wave (d <= 16384:
+// up to 16 waves, a 1024-thread block). FWHT stages run in the order 1, 2,
+// 4, ..., h/2: in registers for bits 0-3; across lanes without LDS for bits
+// 4-9 (DPP fmac with the lazy lane sign described in tq3.hip for bits 4-7,
+// permlane16/32 swaps for bits 8 and 9); across waves through LDS for bits
+// 10-13. The row norm's sum of squares follows the same bit order inside
+// each h-block (1024-element tile sums meet in LDS and go through the rest
+// of the pairwise tree); block sums are then added left to right.
+//
+// NT = 1..4 are compiled for their exact wave count (256-thread launch
+// bounds); NT = 0 takes the wave count from the block size at run time, for
+// rows of 4097..16384 elements.
+#include <atomic>
+
 #include "orbit_codes.h"
 #include "tq_common.h"
 #include "tq_kernels.h"
@@ -20,7 +28,41 @@ namespace tq {
 
 namespace {
 
-constexpr int kMaxBlocks = 128; // d / h <= 4096 / 32
+constexpr int kMaxD = 16384;     // longest row: 16 waves of 1024 elements
+constexpr int kMaxBlocks = 512;  // d / h <= 16384 / 32
+
+// Waves of a block: NT, or for NT = 0 the block's own size.
+template <int NT>
+__device__ __forceinline__ int block_waves() {
+  if constexpr (NT > 0) return NT;
+  else return (int)(blockDim.x >> 6);
+}
+
+// Sum of squares of a row from its partial sums in LDS: for h <= 1024 one
+// value per h-block, added left to right; for h > 1024 one value per
+// 1024-element tile, combined by the pairwise tree inside each block (tiles
+// 2k and 2k + 1 first) before the block sums are added left to right.
+__device__ __forceinline__ float row_sumsq(const float* bsum, int log2h, int nblk) {
+  float total = 0.0f;
+  if (log2h <= 10) {
+    total = bsum[0];
+    for (int bi = 1; bi < nblk; ++bi) total = total + bsum[bi];
+    return total;
+  }
+  const int tpb = 1 << (log2h - 10);  // tiles per block, <= 16
+  for (int bi = 0; bi < nblk; ++bi) {
+    float t[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) t[k] = k < tpb ? bsum[bi * tpb + k] : 0.0f;
+#pragma unroll
+    for (int w = 1; w < 16; w *= 2)
+#pragma unroll
+      for (int k = 0; k < 16; k += 2 * w)
+        if (k + w < tpb) t[k] = t[k] + t[k + w];
+    total = bi == 0 ? t[0] : total + t[0];
+  }
+  return total;
+}
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // Chunk position (within its wave's 64 chunks) held by physical lane l.
@@ -275,7 +317,7 @@ __device__ __forceinline__ uint32_t sign_of(uint32_t w, int k) {
 // the rows read and, with ROT, of xrot; for bf16 / fp16 every stage rounds
 // to that format as the page's forward does on such activations.
 template <int BITS, bool LSB, int NT, bool FULL, bool ROT = false, int DT = DT_F32>
-__global__ __launch_bounds__(256) void orbit_quantize_kernel(
+__global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
     const void* __restrict__ W, int64_t rows, int d, int log2h, float kh,
     const int32_t* __restrict__ perm, const int8_t* __restrict__ signs, OrbitCodebook cb,
     uint8_t* __restrict__ packed, float* __restrict__ norms, void* __restrict__ xrot) {
@@ -283,7 +325,8 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
   extern __shared__ float lds[];
   float* rowbuf = lds;     // the row; later the cross-wave butterfly exchange
   float* bsum = lds + d;   // block (or, for h > 1024, tile) sums of squares
-  constexpr int NTHR = 64 * NT;
+  const int nwaves = block_waves<NT>();
+  const int NTHR = 64 * nwaves;
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -389,9 +432,10 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
     fwht_rows<FULL, RD>(y, log2h, cx);
     if (log2h > 10) {
       float4* mine = reinterpret_cast<float4*>(rowbuf + 16 * c);
+      // wave bit b (index bit 10 + b) pairs wave w with w ^ ht, ht = 2^b
 #pragma unroll
-      for (int ht = 1; ht < NT; ht *= 2) {
-        if (log2h <= 9 + ht) break;
+      for (int ht = 1, bit = 10; ht < (NT > 0 ? NT : 16); ht *= 2, ++bit) {
+        if (ht >= nwaves || log2h <= bit) break;
         __syncthreads();  // everyone is done reading the row buffer
 #pragma unroll
         for (int k = 0; k < 4; ++k)
@@ -471,16 +515,7 @@ __global__ __launch_bounds__(256) void orbit_quantize_kernel(
     if (lb > 5) part = lane_sum<5>(part);
     if (act && (c & ((1 << lb) - 1)) == 0) bsum[c >> lb] = part;  // one writer per block/tile
     __syncthreads();
-    float total;
-    if (log2h <= 10) {
-      total = bsum[0];
-      for (int bi = 1; bi < nblk; ++bi) total = total + bsum[bi];
-    } else if (log2h == 11) {
-      total = bsum[0] + bsum[1];
-    } else {
-      total = (bsum[0] + bsum[1]) + (bsum[2] + bsum[3]);
-    }
-    const float norm = __builtin_sqrtf(total);
+    const float norm = __builtin_sqrtf(row_sumsq(bsum, log2h, nblk));
     const float denom = norm + eps;
 
     // u = y / denom, correctly rounded: shared reciprocal while every nonzero
@@ -537,7 +572,7 @@ __device__ __forceinline__ void store_group(void* out, int64_t j0, const float* 
 // the rotation is undone. The next row's codes and norm are loaded while the
 // current row is processed.
 template <int BITS, bool LSB, int DT, int NT, bool FULL>
-__global__ __launch_bounds__(256) void orbit_dequantize_kernel(
+__global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_dequantize_kernel(
     const uint8_t* __restrict__ packed, const float* __restrict__ norms, int64_t rows, int d,
     int log2h, float kh, const int32_t* __restrict__ inv_perm,
     const int8_t* __restrict__ signs, OrbitCodebook cb, int rotated_only,
@@ -631,9 +666,10 @@ __global__ __launch_bounds__(256) void orbit_dequantize_kernel(
     fwht_rows<FULL>(w, log2h, cx);
     if (log2h > 10) {
       f32x4_t* mine = reinterpret_cast<f32x4_t*>(rowbuf + 16 * c);
+      const int nwaves = block_waves<NT>();
 #pragma unroll
-      for (int ht = 1; ht < NT; ht *= 2) {
-        if (log2h <= 9 + ht) break;
+      for (int ht = 1, bit = 10; ht < (NT > 0 ? NT : 16); ht *= 2, ++bit) {
+        if (ht >= nwaves || log2h <= bit) break;
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < 4; ++k)
@@ -677,21 +713,39 @@ __global__ __launch_bounds__(256) void orbit_dequantize_kernel(
   }
 }
 
-// LDS of a block: the row (d <= 1024 NT floats) and the block sums. The
-// resident-block count is taken once per kernel instantiation at its largest
-// LDS size (at most 17 KB: it never limits below the other resources).
+// LDS of a block: the row (d <= 1024 NT floats) and the block sums (or the
+// dequantizer's per-wave tables). The resident-block count is taken once per
+// kernel instantiation at its largest LDS size (18 KB for NT <= 4: it never
+// limits below the other resources; 66 KB for the rows of up to 16384).
 constexpr size_t orbit_lds(int d) { return (size_t)(d + kMaxBlocks) * sizeof(float); }
+constexpr int max_d_of(int nt) { return nt == 0 ? kMaxD : 1024 * nt; }
+inline int block_threads(int nt_tmpl, int nt) { return 64 * (nt_tmpl == 0 ? nt : nt_tmpl); }
+
+// Resident blocks per CU of one kernel instantiation, queried once per block
+// size (one size for NT = 1..4; one per wave count 5..16 for NT = 0). Racing
+// first calls store the same value.
+template <int NT, typename K>
+int resident_cached(std::atomic<int> (&cache)[17], K kernel, int nt) {
+  const int slot = NT == 0 ? nt : 0;
+  int v = cache[slot].load(std::memory_order_relaxed);
+  if (v == 0) {
+    v = resident_blocks_per_cu(kernel, block_threads(NT, nt), orbit_lds(max_d_of(NT)));
+    cache[slot].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
 
 template <int BITS, bool LSB, int NT, bool FULL>
 hipError_t launch_q(const float* W, int64_t rows, int d, int log2h, float kh,
                     const int32_t* perm, const int8_t* signs, const OrbitCodebook& cb,
                     uint8_t* packed, float* norms, int cus, hipStream_t s) {
   const size_t shm = orbit_lds(d);
-  static const int per_cu = resident_blocks_per_cu(orbit_quantize_kernel<BITS, LSB, NT, FULL>,
-                                                   64 * NT, orbit_lds(1024 * NT));
+  const int nt = (d + 1023) >> 10;
+  static std::atomic<int> cache[17];
+  const int per_cu = resident_cached<NT>(cache, orbit_quantize_kernel<BITS, LSB, NT, FULL>, nt);
   const int grid = grid_size(rows, cus, per_cu);
-  orbit_quantize_kernel<BITS, LSB, NT, FULL><<<grid, 64 * NT, shm, s>>>(W, rows, d, log2h, kh, perm,
-                                                                 signs, cb, packed, norms, nullptr);
+  orbit_quantize_kernel<BITS, LSB, NT, FULL><<<grid, block_threads(NT, nt), shm, s>>>(
+      W, rows, d, log2h, kh, perm, signs, cb, packed, norms, nullptr);
   return hipGetLastError();
 }
 
@@ -706,7 +760,8 @@ hipError_t launch_q_nt(int nt, const float* W, int64_t rows, int d, int log2h, f
     case 1: return full ? TQ_QN(1, true) : TQ_QN(1, false);
     case 2: return full ? TQ_QN(2, true) : TQ_QN(2, false);
     case 3: return full ? TQ_QN(3, true) : TQ_QN(3, false);
-    default: return full ? TQ_QN(4, true) : TQ_QN(4, false);
+    case 4: return full ? TQ_QN(4, true) : TQ_QN(4, false);
+    default: return full ? TQ_QN(0, true) : TQ_QN(0, false);
   }
 #undef TQ_QN
 }
@@ -717,10 +772,12 @@ hipError_t launch_dq(const uint8_t* packed, const float* norms, int64_t rows, in
                      const OrbitCodebook& cb, int rotated_only, void* out, int cus,
                      hipStream_t s) {
   const size_t shm = orbit_lds(d);
-  static const int per_cu = resident_blocks_per_cu(
-      orbit_dequantize_kernel<BITS, LSB, DT, NT, FULL>, 64 * NT, orbit_lds(1024 * NT));
+  const int nt = (d + 1023) >> 10;
+  static std::atomic<int> cache[17];
+  const int per_cu =
+      resident_cached<NT>(cache, orbit_dequantize_kernel<BITS, LSB, DT, NT, FULL>, nt);
   const int grid = grid_size(rows, cus, per_cu);
-  orbit_dequantize_kernel<BITS, LSB, DT, NT, FULL><<<grid, 64 * NT, shm, s>>>(
+  orbit_dequantize_kernel<BITS, LSB, DT, NT, FULL><<<grid, block_threads(NT, nt), shm, s>>>(
       packed, norms, rows, d, log2h, kh, inv_perm, signs, cb, rotated_only, out);
   return hipGetLastError();
 }
@@ -737,7 +794,8 @@ hipError_t launch_dq_nt(int nt, const uint8_t* packed, const float* norms, int64
     case 1: return full ? TQ_DQN(1, true) : TQ_DQN(1, false);
     case 2: return full ? TQ_DQN(2, true) : TQ_DQN(2, false);
     case 3: return full ? TQ_DQN(3, true) : TQ_DQN(3, false);
-    default: return full ? TQ_DQN(4, true) : TQ_DQN(4, false);
+    case 4: return full ? TQ_DQN(4, true) : TQ_DQN(4, false);
+    default: return full ? TQ_DQN(0, true) : TQ_DQN(0, false);
   }
 #undef TQ_DQN
 }
@@ -764,11 +822,13 @@ template <int NT, bool FULL, int DT>
 hipError_t launch_rot(const void* x, int64_t rows, int d, int log2h, float kh,
                       const int32_t* perm, const int8_t* signs, void* xrot, int cus, hipStream_t s) {
   const size_t shm = orbit_lds(d);
-  static const int per_cu = resident_blocks_per_cu(
-      orbit_quantize_kernel<2, false, NT, FULL, true, DT>, 64 * NT, orbit_lds(1024 * NT));
+  const int nt = (d + 1023) >> 10;
+  static std::atomic<int> cache[17];
+  const int per_cu =
+      resident_cached<NT>(cache, orbit_quantize_kernel<2, false, NT, FULL, true, DT>, nt);
   const int grid = grid_size(rows, cus, per_cu);
   OrbitCodebook cb{};
-  orbit_quantize_kernel<2, false, NT, FULL, true, DT><<<grid, 64 * NT, shm, s>>>(
+  orbit_quantize_kernel<2, false, NT, FULL, true, DT><<<grid, block_threads(NT, nt), shm, s>>>(
       x, rows, d, log2h, kh, perm, signs, cb, nullptr, nullptr, xrot);
   return hipGetLastError();
 }
@@ -813,7 +873,8 @@ hipError_t launch_rot_dt(const void* x, int64_t rows, int di, int log2h, float k
     case 1: return full ? TQ_R(1, true) : TQ_R(1, false);
     case 2: return full ? TQ_R(2, true) : TQ_R(2, false);
     case 3: return full ? TQ_R(3, true) : TQ_R(3, false);
-    default: return full ? TQ_R(4, true) : TQ_R(4, false);
+    case 4: return full ? TQ_R(4, true) : TQ_R(4, false);
+    default: return full ? TQ_R(0, true) : TQ_R(0, false);
   }
 #undef TQ_R
 }

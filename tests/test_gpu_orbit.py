@@ -94,6 +94,34 @@ def test_orbit_dims(tq, d):
     check(tq, w, d, 3)
 
 
+@pytest.mark.parametrize("msb", [True, False])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("d", [5120, 8192, 12288, 14336, 16384])
+def test_orbit_large_d(tq, d, bits, msb):
+    """Rows longer than 4096 ("orbit_quant.py", hadamard_block_size: the block
+    is d & -d, here 1024, 8192, 4096, 2048 and 16384): blocks of up to 16
+    waves, Hadamard stages across waves up to index bit 13, tile sums of
+    squares combined by the pairwise tree inside each block."""
+    w = datagen.orbit_weight(rows=37, d=d, seed=d + bits)
+    check(tq, w, d, bits, msb)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_orbit_large_d_narrow_outputs(tq, dtype):
+    w = datagen.orbit_weight(rows=20, d=12288, seed=12)
+    check(tq, w, 12288, 3, True, dtype)
+
+
+def test_orbit_large_d_limits(tq):
+    d = 16384 + 32                       # h = 32, one row longer than a block holds
+    perm, sg = datagen.rpbh_params(d)
+    cb = tq.orbit_make_codebook(3, d)
+    with pytest.raises(ValueError):
+        tq.orbit_quantize_weight(torch.zeros((2, d), device=DEV), 3, perm.to(DEV), sg.to(DEV), cb)
+    with pytest.raises(ValueError):
+        tq.orbit_rotate(torch.zeros((2, d), device=DEV), perm.to(DEV), sg.to(DEV))
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
 def test_orbit_narrow_outputs(tq, dtype):
     w = datagen.orbit_weight(rows=64, d=3072, seed=7)

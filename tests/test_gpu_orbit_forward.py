@@ -54,7 +54,7 @@ def check_linear(tq, x_rot, packed, norms, d, bits, cb, bias=None, msb=True):
     return float((err / (bound + 1e-30)).max())
 
 
-@pytest.mark.parametrize("d", [96, 256, 1024, 1536, 3072, 4096])
+@pytest.mark.parametrize("d", [96, 256, 1024, 1536, 3072, 4096, 5120, 8192, 12288, 16384])
 @pytest.mark.parametrize("rows", [1, 7, 65, 300])
 def test_rotate_bit_exact(tq, d, rows):
     x = np.random.default_rng(d + rows).standard_normal((rows, d)).astype(np.float32)
@@ -100,6 +100,26 @@ def test_forward_config5(tq, bits, rows):
     print(f"bits {bits}: max error / bound = {(err / bound).max():.3e}")
 
 
+@pytest.mark.parametrize("fmt", ["fp32", "bf16"])
+def test_forward_large_d(tq, fmt):
+    """The whole forward on a down-projection shape: in_features 12288 (the
+    transposed config-5 weight, h = 4096), 768 outputs, 3 bits, 40 rows."""
+    d, n, bits = 12288, 768, 3
+    perm, sg, cb, packed, norms = quantized(n, d, bits, 99)
+    x = np.random.default_rng(4).standard_normal((40, d)).astype(np.float32)
+    if fmt == "fp32":
+        xr = tq.orbit_rotate(torch.from_numpy(x).to(DEV), perm.to(DEV), sg.to(DEV))
+        x_rot = oracle.rpbh_forward(x, perm, sg)
+        assert np.array_equal(xr.cpu().numpy().view(np.uint32), x_rot.view(np.uint32))
+        check_linear(tq, x_rot, packed, norms, d, bits, cb)
+    else:
+        x = of.round_to(x, fmt)
+        xr = tq.orbit_rotate(lp_tensor(x, fmt).to(DEV), perm.to(DEV), sg.to(DEV))
+        x_rot = of.rpbh_forward_lowp(x, perm.numpy(), sg.numpy(), fmt)
+        assert np.array_equal(xr.float().cpu().numpy().view(np.uint32), x_rot.view(np.uint32))
+        check_linear_lowp(tq, fmt, x_rot, packed, norms, d, bits, cb)
+
+
 def test_argument_errors(tq):
     L = tq.lib
     cb = tq._host_f32([-1.0, -0.5, 0.5, 1.0])
@@ -135,7 +155,7 @@ def lp_tensor(a, fmt):
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
-@pytest.mark.parametrize("d", [96, 256, 1024, 1536, 2048, 3072, 4096])
+@pytest.mark.parametrize("d", [96, 256, 1024, 1536, 2048, 3072, 4096, 6144, 14336, 16384])
 @pytest.mark.parametrize("rows", [1, 7, 300])
 def test_rotate_lowp_bit_exact(tq, fmt, d, rows):
     x = of.round_to(np.random.default_rng(d + rows).standard_normal((rows, d)).astype(np.float32)
