@@ -695,7 +695,7 @@ def main():
         valu.update({"issued_lane_ops_per_vector": ops, "issued_achieved": issued / 1e12,
                      "issued_frac": issued / PEAK_VALU_LANE_OPS})
 
-    codec = codec_kernels(tq, dev, mask, sp, args.steps, kernels)
+    codec = None if args.profile else codec_kernels(tq, dev, mask, sp, args.steps, kernels)
 
     # correctness spot check of one set against the oracle (outside timing)
     import oracle
