@@ -430,6 +430,51 @@ def secondary(tq, timer, dev, signs, mask):
     return out
 
 
+def stream_ceiling(dev, sp, kv_kernels):
+    """What HBM gives the TQ3 kernels' own access patterns with no arithmetic:
+    the probe kernels of libtqprobe.so (quantize pattern: 256-byte bf16 rows
+    in, 56-byte records out; dequantize pattern: records in, rows out) over
+    four rotating buffer sets of the KV layer's size, at the kernels' grid and
+    at one block per 64 vectors, and the best probe's time as a fraction of
+    each kernel's."""
+    import ctypes
+    path = os.path.join(ROOT, "randomized_hadamard_lloyd_amd", "libtqprobe.so")
+    P = ctypes.CDLL(path)
+    P.tqprobe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                 ctypes.c_int, ctypes.c_void_p]
+    n = kv_kernels["quantize"]["vectors_per_launch"]
+    rows = [torch.empty((n, 128), dtype=torch.bfloat16, device=dev) for _ in range(4)]
+    recs = [torch.zeros((n, REC), dtype=torch.uint8, device=dev) for _ in range(4)]
+    for r in rows:
+        r.zero_()
+    stream = torch.cuda.current_stream(dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    res = {}
+    for kind, name, src, dst, kgrid in ((0, "quantize", rows, recs, 4 * 5 * cus),
+                                        (1, "dequantize", recs, rows, 4 * cus)):
+        best = None
+        for label, grid in (("kernel_grid", kgrid), ("one_block_per_64_vectors", n // 64)):
+            calls = [lambda i=i: P.tqprobe_stream(kind, src[i].data_ptr(), dst[i].data_ptr(), n, grid,
+                                                  sp) for i in range(4)]
+            for c in calls:
+                assert c() == 0
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(200):
+                calls[i % 4]()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 200
+            gbs = rate(312 * n, ms)
+            res[f"{name}_pattern_{label}"] = {"grid": grid, "avg_ms": ms, "GBps": gbs,
+                                              "frac_peak_hbm": gbs / PEAK_HBM_GBS}
+            best = ms if best is None else min(best, ms)
+        res[f"{name}_kernel_over_probe"] = best / kv_kernels[name]["avg_ms"]
+    return res
+
+
 def codec_kernels(tq, dev, mask, sp, iters, kv_kernels):
     """Each codec workload's kernel on its own, back-to-back launches over
     rotating buffers (every launch streams from HBM), one event pair around
@@ -464,6 +509,7 @@ def codec_kernels(tq, dev, mask, sp, iters, kv_kernels):
         k = kv_kernels[name]
         out[f"{name}_kv_layer_bf16"] = line(k["kernel"], k["avg_ms"], k["vectors_per_launch"],
                                             k["bytes_per_vector"])
+    out["stream_ceiling_kv_layer"] = stream_ceiling(dev, sp, kv_kernels)
     # 2^20 structured fp32 vectors, two buffer sets (1.1 GB in all)
     x = datagen.structured_blocks().to(dev)
     n = x.shape[0]

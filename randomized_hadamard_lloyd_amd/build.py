@@ -13,6 +13,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtq.so")
 SOURCES = ["tq3.hip", "tq3_attn.hip", "orbit.hip", "orbit_linear.hip", "orbit_linear_lp.hip", "libtq.cpp"]
+# Measurement probes timed by bench.py (the TQ3 kernels' memory traffic with
+# no arithmetic); a library of their own, not part of the codec's ABI.
+PROBE_LIB = os.path.join(HERE, "libtqprobe.so")
+PROBE_SOURCES = ["stream_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -42,19 +46,21 @@ def _finish(proc, what):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source to an object in parallel, then link libtq.so."""
+    """Compile every source to an object in parallel, then link libtq.so and
+    the probe library."""
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs, procs = [], []
-    for src in sources():
+    objs, pobjs, procs = [], [], []
+    for src in sources() + [os.path.join(CSRC, s) for s in PROBE_SOURCES]:
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
-        objs.append(obj)
+        (pobjs if os.path.basename(src) in PROBE_SOURCES else objs).append(obj)
         procs.append((_run([HIPCC, *FLAGS, "-c", src, "-o", obj], verbose), src))
     for proc, src in procs:
         _finish(proc, os.path.basename(src))
-    tmp = LIB + ".tmp"
-    _finish(_run([HIPCC, *FLAGS, "-shared", *objs, "-o", tmp], verbose), "link")
-    os.replace(tmp, LIB)
+    for out, o in ((LIB, objs), (PROBE_LIB, pobjs)):
+        tmp = out + ".tmp"
+        _finish(_run([HIPCC, *FLAGS, "-shared", *o, "-o", tmp], verbose), "link")
+        os.replace(tmp, out)
     return LIB
 
 

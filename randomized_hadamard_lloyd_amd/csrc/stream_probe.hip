@@ -1,0 +1,85 @@
+// Measurement probes (not part of the codec library): the memory traffic of
+// the TQ3 kernels with no arithmetic, to measure what HBM gives each access
+// pattern on this part. Built into libtqprobe.so and timed by bench.py.
+//
+//   kind 0 (quantize pattern): each 4-lane quad reads one 256-byte bf16 row
+//     with four 16-byte loads per lane and writes one 56-byte record (lanes
+//     0-2: one dword per 12-byte group; lane 3: 8 bytes), as
+//     tq3_quantize_kernel does.
+//   kind 1 (dequantize pattern): each quad reads one record with the
+//     dequantize kernel's loads (two 8-byte words per lane, plus the 8-byte
+//     norm and scale) and each wave writes its 16 consecutive 256-byte rows
+//     as four 1 KB stores.
+// The values written are a cheap function of the values read, so no load can
+// be dropped. Every access stays inside n_vec rows / records.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void probe_quantize_pattern(const uint16_t* __restrict__ x,
+                                                              uint8_t* __restrict__ rec,
+                                                              int64_t n) {
+  const int q = threadIdx.x & 3;
+  const int64_t step = (int64_t)gridDim.x * 64;
+  for (int64_t v = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2); v < n; v += step) {
+    const uint16_t* r = x + v * 128 + 8 * q;
+    uint32_t s = 0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(r + 32 * g);
+      s ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    uint8_t* out = rec + v * 56;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      if (q < 3) *reinterpret_cast<uint32_t*>(out + 12 * g + 4 * q) = s + g;
+    if (q == 3) *reinterpret_cast<uint2*>(out + 48) = make_uint2(s, s + 1);
+  }
+}
+
+__global__ __launch_bounds__(256) void probe_dequantize_pattern(const uint8_t* __restrict__ rec,
+                                                                u32x4* __restrict__ y,
+                                                                int64_t n) {
+  const int q = threadIdx.x & 3;
+  const int l = threadIdx.x & 63;
+  const int64_t step = (int64_t)gridDim.x * 64;
+  for (int64_t v = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2); v < n; v += step) {
+    const uint2* r = reinterpret_cast<const uint2*>(rec + v * 56);
+    const uint2 a = r[q], b = r[q + 3], c = r[6];
+    const uint32_t s = a.x ^ a.y ^ b.x ^ b.y ^ c.x ^ c.y;
+    const int64_t v0 = v - ((threadIdx.x >> 2) & 15);  // the wave's first row
+    if (v0 + 16 <= n) {
+      u32x4* dst = y + v0 * 16;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dst[l + 64 * k] = u32x4{s, s + 1, s + 2, s + 3};
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+// Enqueue one probe launch of `grid` 256-thread blocks on `stream`.
+// kind 0: `in` = n_vec bf16 rows of 128 (16-byte aligned), `out` = n_vec
+// records of 56 bytes (8-byte aligned). kind 1: `in` = n_vec records, `out`
+// = n_vec rows of 128 bf16 (16-byte aligned); n_vec a multiple of 16.
+// Returns 0, or 1 for bad arguments, 2 if the launch failed.
+int tqprobe_stream(int kind, const void* in, void* out, int64_t n_vec, int grid,
+                   void* stream) {
+  if (!in || !out || n_vec <= 0 || grid <= 0 || (kind != 0 && kind != 1)) return 1;
+  if (kind == 1 && n_vec % 16 != 0) return 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kind == 0)
+    probe_quantize_pattern<<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(in),
+                                                static_cast<uint8_t*>(out), n_vec);
+  else
+    probe_dequantize_pattern<<<grid, 256, 0, s>>>(static_cast<const uint8_t*>(in),
+                                                  static_cast<u32x4*>(out), n_vec);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+}  // extern "C"
