@@ -38,13 +38,20 @@ __device__ __forceinline__ int block_waves() {
   else return (int)(blockDim.x >> 6);
 }
 
+// Blocks longer than 1024 (h = d & -d > 1024) need d to be a multiple of
+// 2048, so with an exact wave count they occur only for an even one: odd
+// counts compile without the cross-wave paths.
+template <int NT>
+constexpr bool may_span_waves() { return NT == 0 || NT % 2 == 0; }
+
 // Sum of squares of a row from its partial sums in LDS: for h <= 1024 one
 // value per h-block, added left to right; for h > 1024 one value per
 // 1024-element tile, combined by the pairwise tree inside each block (tiles
 // 2k and 2k + 1 first) before the block sums are added left to right.
+template <bool SPAN>
 __device__ __forceinline__ float row_sumsq(const float* bsum, int log2h, int nblk) {
   float total = 0.0f;
-  if (log2h <= 10) {
+  if (!SPAN || log2h <= 10) {
     total = bsum[0];
     for (int bi = 1; bi < nblk; ++bi) total = total + bsum[bi];
     return total;
@@ -316,7 +323,8 @@ __device__ __forceinline__ uint32_t sign_of(uint32_t w, int k) {
 // the forward's first step) to xrot instead of quantizing. DT: the format of
 // the rows read and, with ROT, of xrot; for bf16 / fp16 every stage rounds
 // to that format as the page's forward does on such activations.
-template <int BITS, bool LSB, int NT, bool FULL, bool ROT = false, int DT = DT_F32>
+template <int BITS, bool LSB, int NT, bool FULL, bool ROT = false, int DT = DT_F32,
+          bool SYM = true>
 __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
     const void* __restrict__ W, int64_t rows, int d, int log2h, float kh,
     const int32_t* __restrict__ perm, const int8_t* __restrict__ signs, OrbitCodebook cb,
@@ -416,21 +424,23 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
       for (int k = 0; k < KL; ++k) pre[k] = src[fidx[k]];
     }
 
-    // y_j = W[perm_j] * signs_j.
+    // y_j = W[perm_j] * signs_j. Lanes past the row (d not a multiple of
+    // 1024) gather chunk 0 too: their chunks form whole h-blocks of their
+    // own, so no butterfly or block sum mixes them with the row, and nothing
+    // of theirs is stored. Unconditional reads are all in flight at once.
     float y[16];
     const char* rb = reinterpret_cast<const char*>(rowbuf);
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      y[i] = act ? as_f(*reinterpret_cast<const uint32_t*>(rb + poff[i]) ^
-                        ((sbits << (31 - i)) & 0x80000000u))
-                 : 0.0f;
+      y[i] = as_f(*reinterpret_cast<const uint32_t*>(rb + poff[i]) ^
+                  ((sbits << (31 - i)) & 0x80000000u));
 
     // Butterflies inside the wave (index bits 0..9), then across waves
     // through LDS for blocks longer than 1024 (bits 10, 11): the lower tile
     // takes a + b, the upper b' - a' = a - b with the same lazy lane sign.
     constexpr int RD = ROT ? DT : DT_F32;
     fwht_rows<FULL, RD>(y, log2h, cx);
-    if (log2h > 10) {
+    if (may_span_waves<NT>() && log2h > 10) {
       float4* mine = reinterpret_cast<float4*>(rowbuf + 16 * c);
       // wave bit b (index bit 10 + b) pairs wave w with w ^ ht, ht = 2^b
 #pragma unroll
@@ -515,7 +525,7 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
     if (lb > 5) part = lane_sum<5>(part);
     if (act && (c & ((1 << lb) - 1)) == 0) bsum[c >> lb] = part;  // one writer per block/tile
     __syncthreads();
-    const float norm = __builtin_sqrtf(row_sumsq(bsum, log2h, nblk));
+    const float norm = __builtin_sqrtf(row_sumsq<may_span_waves<NT>()>(bsum, log2h, nblk));
     const float denom = norm + eps;
 
     // u = y / denom, correctly rounded: shared reciprocal while every nonzero
@@ -529,9 +539,8 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
       for (int i = 0; i < 16; ++i) y[i] = y[i] / denom;
     }
 
-    // Codes and packing (the codebook test is uniform).
-    const uint64_t bytes =
-        cb.sym ? pack16<BITS, LSB, true>(y, cb) : pack16<BITS, LSB, false>(y, cb);
+    // Codes and packing (SYM: the codebook is mirror-symmetric).
+    const uint64_t bytes = pack16<BITS, LSB, SYM>(y, cb);
     if (act) store_codes<BITS>(packed + r * row_bytes + 2 * BITS * c, bytes);
     if (tid == 0) norms[r] = norm;
   }
@@ -664,7 +673,7 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_dequantize_kernel(
     // Inverse rotation: FWHT per block (across waves through LDS beyond
     // 1024), times h^-1/2 and the lazy lane sign, times signs_j.
     fwht_rows<FULL>(w, log2h, cx);
-    if (log2h > 10) {
+    if (may_span_waves<NT>() && log2h > 10) {
       f32x4_t* mine = reinterpret_cast<f32x4_t*>(rowbuf + 16 * c);
       const int nwaves = block_waves<NT>();
 #pragma unroll
@@ -735,21 +744,35 @@ int resident_cached(std::atomic<int> (&cache)[17], K kernel, int nt) {
   return v;
 }
 
-template <int BITS, bool LSB, int NT, bool FULL>
-hipError_t launch_q(const float* W, int64_t rows, int d, int log2h, float kh,
-                    const int32_t* perm, const int8_t* signs, const OrbitCodebook& cb,
-                    uint8_t* packed, float* norms, int cus, hipStream_t s) {
+template <int BITS, bool LSB, int NT, bool FULL, bool SYM>
+hipError_t launch_q_sym(const float* W, int64_t rows, int d, int log2h, float kh,
+                        const int32_t* perm, const int8_t* signs, const OrbitCodebook& cb,
+                        uint8_t* packed, float* norms, int cus, hipStream_t s) {
+  auto kernel = orbit_quantize_kernel<BITS, LSB, NT, FULL, false, DT_F32, SYM>;
   const size_t shm = orbit_lds(d);
   const int nt = (d + 1023) >> 10;
   static std::atomic<int> cache[17];
-  const int per_cu = resident_cached<NT>(cache, orbit_quantize_kernel<BITS, LSB, NT, FULL>, nt);
+  const int per_cu = resident_cached<NT>(cache, kernel, nt);
   // Twice the resident blocks: blocks that start later fall out of step with
   // the first ones, so loads and arithmetic of different blocks overlap
   // (2-4% on the 12288 x 3072 weight against a resident-sized grid).
   const int grid = grid_size(rows, cus, per_cu * 2);
-  orbit_quantize_kernel<BITS, LSB, NT, FULL><<<grid, block_threads(NT, nt), shm, s>>>(
-      W, rows, d, log2h, kh, perm, signs, cb, packed, norms, nullptr);
+  kernel<<<grid, block_threads(NT, nt), shm, s>>>(W, rows, d, log2h, kh, perm, signs, cb, packed,
+                                                  norms, nullptr);
   return hipGetLastError();
+}
+
+// One packing path per instantiation: with both in one kernel the loop ran
+// out of scalar registers and spilled them to VGPR lanes.
+template <int BITS, bool LSB, int NT, bool FULL>
+hipError_t launch_q(const float* W, int64_t rows, int d, int log2h, float kh,
+                    const int32_t* perm, const int8_t* signs, const OrbitCodebook& cb,
+                    uint8_t* packed, float* norms, int cus, hipStream_t s) {
+  if (cb.sym)
+    return launch_q_sym<BITS, LSB, NT, FULL, true>(W, rows, d, log2h, kh, perm, signs, cb, packed,
+                                                   norms, cus, s);
+  return launch_q_sym<BITS, LSB, NT, FULL, false>(W, rows, d, log2h, kh, perm, signs, cb, packed,
+                                                  norms, cus, s);
 }
 
 template <int BITS, bool LSB>

@@ -141,14 +141,15 @@ def test_orbit_edge_rows(tq):
     check(tq, w, d, 2, msb=False)
 
 
+@pytest.mark.parametrize("d", [96, 1056, 3072, 4096, 12288])
 @pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("msb", [True, False])
-def test_orbit_asymmetric_codebook(tq, bits, msb):
+def test_orbit_asymmetric_codebook(tq, d, bits, msb):
     """Codebooks that are not mirror-symmetric take the general edge count (the
-    Gaussian ones take the symmetric compare): a shifted Gaussian codebook and
-    an uneven random ascending one."""
-    d = 3072
-    w = datagen.orbit_weight(rows=129, d=d, seed=20 + bits)
+    Gaussian ones take the symmetric compare), in kernels of their own for
+    every wave count: a shifted Gaussian codebook and an uneven random
+    ascending one. d = 96 and 1056 leave lanes past the row's end."""
+    w = datagen.orbit_weight(rows=129 if d <= 4096 else 33, d=d, seed=20 + bits)
     base = torch.from_numpy(codebooks(tq, bits, d)[1])
     shifted = base + np.float32(0.37) * (base[1] - base[0])
     rng = np.random.default_rng(bits)
