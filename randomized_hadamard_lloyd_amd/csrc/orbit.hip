@@ -29,7 +29,7 @@ namespace tq {
 namespace {
 
 constexpr int kMaxD = 16384;     // longest row: 16 waves of 1024 elements
-constexpr int kMaxBlocks = 512;  // d / h <= 16384 / 32
+constexpr int kMaxBlocks = kMaxD / 32;  // d / h with h >= 32
 
 // Waves of a block: NT, or for NT = 0 the block's own size.
 template <int NT>
@@ -38,11 +38,11 @@ __device__ __forceinline__ int block_waves() {
   else return (int)(blockDim.x >> 6);
 }
 
-// Blocks longer than 1024 (h = d & -d > 1024) need d to be a multiple of
-// 2048, so with an exact wave count they occur only for an even one: odd
-// counts compile without the cross-wave paths.
-template <int NT>
-constexpr bool may_span_waves() { return NT == 0 || NT % 2 == 0; }
+// Stage class of a kernel instantiation, from h = d & -d: 0 for h < 1024,
+// 1 for h = 1024 (every in-wave stage runs, known at compile time), 2 for
+// h > 1024 (also stages across waves, with a second LDS buffer). Class 2
+// needs d to be a multiple of 2048: an even wave count (or the run-time one).
+inline int stage_class(int log2h) { return log2h < 10 ? 0 : log2h == 10 ? 1 : 2; }
 
 // Sum of squares of a row from its partial sums in LDS: for h <= 1024 one
 // value per h-block, added left to right; for h > 1024 one value per
@@ -203,6 +203,73 @@ __device__ __forceinline__ void fwht_rows(float (&y)[16], int log2h, const LaneC
   if (lb > 5) swap_stage<5, RD>(y);
 }
 
+// FWHT stages on the wave bits of a block longer than 1024 (index bits 10 ..
+// log2h - 1, up to 4 of them), through LDS. Two bits at a time where two
+// remain: each wave writes its values once, and after one barrier reads the
+// three waves that differ from it in those bits and forms the two stages
+// itself, in their order (bit 10 + b first), with the roundings of the staged
+// form: with x0, x1 this wave's two bits and v[x1', x0'] the four waves'
+// values, s[x1'] = v[x1', 0] +- v[x1', 1] (- where x0 = 1), then
+// s[0] +- s[1] (- where x1 = 1). A lone last bit takes one partner. Every
+// sum and difference is an fma with an exact +-1 factor, so it rounds as the
+// plain add or subtract does (the operands commute). The lazy lane sign is
+// the same in every wave at a given lane, so it passes through unchanged.
+// The first exchange uses xa, which nobody reads outside these stages; a
+// second one (5 or more wave bits in all: 8192 and 16384) uses xb, the
+// staged row, which the first exchange's barrier has made free. The caller
+// keeps the barrier that orders its next use of xb after these reads.
+// NT: the block's wave count (0: 5..16), which bounds the wave bits.
+template <int NT, int RD = DT_F32>
+__device__ __forceinline__ void span_stages(float (&y)[16], float* xa, float* xb, int c, int wave,
+                                            int log2h) {
+  constexpr int kMaxBits = NT == 0 ? 4 : NT == 4 ? 2 : 1;
+  const int nb = log2h - 10;
+  float* buf = xa;
+  for (int b = 0; b < nb; buf = xb) {
+    f32x4_t* mine = reinterpret_cast<f32x4_t*>(buf + 16 * c);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) mine[k] = f32x4_t{y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3]};
+    __syncthreads();
+    const int h0 = 64 << b;  // chunk distance of wave bit b
+    const float c0 = ((wave >> b) & 1) ? -1.0f : 1.0f;
+    const f32x4_t* p1 = reinterpret_cast<const f32x4_t*>(buf + 16 * (c ^ h0));
+    if (kMaxBits >= 2 && nb - b >= 2) {
+      const float c1 = ((wave >> (b + 1)) & 1) ? -1.0f : 1.0f;
+      const f32x4_t* p2 = reinterpret_cast<const f32x4_t*>(buf + 16 * (c ^ (2 * h0)));
+      const f32x4_t* p3 = reinterpret_cast<const f32x4_t*>(buf + 16 * (c ^ (3 * h0)));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const f32x4_t o1 = p1[k], o2 = p2[k], o3 = p3[k];
+        float so[4], sx[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          so[e] = __builtin_fmaf(y[4 * k + e], c0, o1[e]);  // s[x1]
+          sx[e] = __builtin_fmaf(o2[e], c0, o3[e]);         // s[1 - x1]
+        }
+        round_pair<RD>(so[0], so[1]);
+        round_pair<RD>(so[2], so[3]);
+        round_pair<RD>(sx[0], sx[1]);
+        round_pair<RD>(sx[2], sx[3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[4 * k + e] = __builtin_fmaf(so[e], c1, sx[e]);
+        // one group's three partner reads in flight at a time: hoisting all
+        // twelve costs 40 VGPRs (a lost wave per SIMD, or spills)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      b += 2;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const f32x4_t o1 = p1[k];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[4 * k + e] = __builtin_fmaf(y[4 * k + e], c0, o1[e]);
+      }
+      b += 1;
+    }
+    round16<RD>(y);
+  }
+}
+
 // --------------------------------------------------------------- packing ---
 
 // Code of u = number of codebook edges strictly below u, as BITS wave masks,
@@ -323,7 +390,7 @@ __device__ __forceinline__ uint32_t sign_of(uint32_t w, int k) {
 // the forward's first step) to xrot instead of quantizing. DT: the format of
 // the rows read and, with ROT, of xrot; for bf16 / fp16 every stage rounds
 // to that format as the page's forward does on such activations.
-template <int BITS, bool LSB, int NT, bool FULL, bool ROT = false, int DT = DT_F32,
+template <int BITS, bool LSB, int NT, int HC, bool ROT = false, int DT = DT_F32,
           bool SYM = true>
 __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
     const void* __restrict__ W, int64_t rows, int d, int log2h, float kh,
@@ -333,6 +400,7 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
   extern __shared__ float lds[];
   float* rowbuf = lds;     // the row; later the cross-wave butterfly exchange
   float* bsum = lds + d;   // block (or, for h > 1024, tile) sums of squares
+  float* xbuf = lds + d + kMaxBlocks;  // h > 1024: the wave-bit stages' exchange
   const int nwaves = block_waves<NT>();
   const int NTHR = 64 * nwaves;
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -343,6 +411,8 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
   const int c = lc + 64 * wave;  // this lane's chunk of 16 elements
   const bool act = c < (d >> 4);
   const int nblk = d >> log2h;
+  constexpr bool FULL = HC > 0, SPAN = HC == 2;
+  static_assert(!SPAN || NT == 0 || NT % 2 == 0, "h > 1024 needs an even wave count");
   const int lb = FULL ? 6 : (log2h - 4 < 6 ? log2h - 4 : 6);
   const LaneCx cx = lane_cx(lc, log2h);
   const float ksig = kh * cx.sigma;
@@ -440,32 +510,7 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
     // takes a + b, the upper b' - a' = a - b with the same lazy lane sign.
     constexpr int RD = ROT ? DT : DT_F32;
     fwht_rows<FULL, RD>(y, log2h, cx);
-    if (may_span_waves<NT>() && log2h > 10) {
-      float4* mine = reinterpret_cast<float4*>(rowbuf + 16 * c);
-      // wave bit b (index bit 10 + b) pairs wave w with w ^ ht, ht = 2^b
-#pragma unroll
-      for (int ht = 1, bit = 10; ht < (NT > 0 ? NT : 16); ht *= 2, ++bit) {
-        if (ht >= nwaves || log2h <= bit) break;
-        __syncthreads();  // everyone is done reading the row buffer
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          mine[k] = make_float4(y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3]);
-        __syncthreads();
-        const float4* other = reinterpret_cast<const float4*>(rowbuf + 16 * (c ^ (64 * ht)));
-        const bool upper = (wave & ht) != 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float4 o = other[k];
-          const float ov[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float a = y[4 * k + e];
-            y[4 * k + e] = upper ? ov[e] - a : a + ov[e];
-          }
-        }
-        round16<RD>(y);
-      }
-    }
+    if (SPAN) span_stages<NT, RD>(y, xbuf, rowbuf, c, wave, log2h);
 #pragma unroll
     for (int i = 0; i < 16; ++i) y[i] = y[i] * ksig;
     round16<RD>(y);
@@ -525,7 +570,7 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
     if (lb > 5) part = lane_sum<5>(part);
     if (act && (c & ((1 << lb) - 1)) == 0) bsum[c >> lb] = part;  // one writer per block/tile
     __syncthreads();
-    const float norm = __builtin_sqrtf(row_sumsq<may_span_waves<NT>()>(bsum, log2h, nblk));
+    const float norm = __builtin_sqrtf(row_sumsq<SPAN>(bsum, log2h, nblk));
     const float denom = norm + eps;
 
     // u = y / denom, correctly rounded: shared reciprocal while every nonzero
@@ -580,7 +625,7 @@ __device__ __forceinline__ void store_group(void* out, int64_t j0, const float* 
 // re-read from LDS in that order -- through the inverse permutation when
 // the rotation is undone. The next row's codes and norm are loaded while the
 // current row is processed.
-template <int BITS, bool LSB, int DT, int NT, bool FULL>
+template <int BITS, bool LSB, int DT, int NT, int HC>
 __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_dequantize_kernel(
     const uint8_t* __restrict__ packed, const float* __restrict__ norms, int64_t rows, int d,
     int log2h, float kh, const int32_t* __restrict__ inv_perm,
@@ -672,31 +717,8 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_dequantize_kernel(
 
     // Inverse rotation: FWHT per block (across waves through LDS beyond
     // 1024), times h^-1/2 and the lazy lane sign, times signs_j.
-    fwht_rows<FULL>(w, log2h, cx);
-    if (may_span_waves<NT>() && log2h > 10) {
-      f32x4_t* mine = reinterpret_cast<f32x4_t*>(rowbuf + 16 * c);
-      const int nwaves = block_waves<NT>();
-#pragma unroll
-      for (int ht = 1, bit = 10; ht < (NT > 0 ? NT : 16); ht *= 2, ++bit) {
-        if (ht >= nwaves || log2h <= bit) break;
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          mine[k] = f32x4_t{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
-        __syncthreads();
-        const f32x4_t* other = reinterpret_cast<const f32x4_t*>(rowbuf + 16 * (c ^ (64 * ht)));
-        const bool upper = (wave & ht) != 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const f32x4_t o = other[k];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float a = w[4 * k + e];
-            w[4 * k + e] = upper ? o[e] - a : a + o[e];
-          }
-        }
-      }
-    }
+    fwht_rows<(HC > 0)>(w, log2h, cx);
+    if (HC == 2) span_stages<NT>(w, lds + d + kMaxBlocks, rowbuf, c, wave, log2h);
     __syncthreads();  // the row buffer is free
     if (act) {
       f32x4_t* mine = reinterpret_cast<f32x4_t*>(rowbuf + 16 * c);
@@ -722,37 +744,40 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_dequantize_kernel(
   }
 }
 
-// LDS of a block: the row (d <= 1024 NT floats) and the block sums (or the
-// dequantizer's per-wave tables). The resident-block count is taken once per
-// kernel instantiation at its largest LDS size (18 KB for NT <= 4: it never
-// limits below the other resources; 66 KB for the rows of up to 16384).
-constexpr size_t orbit_lds(int d) { return (size_t)(d + kMaxBlocks) * sizeof(float); }
-constexpr int max_d_of(int nt) { return nt == 0 ? kMaxD : 1024 * nt; }
+// LDS of a block: the row (d <= 1024 NT floats), the block sums (or the
+// dequantizer's per-wave tables) and, for h > 1024, a second row-sized buffer
+// for the wave-bit stages. The resident-block count is taken once per block
+// size at the largest LDS that size can need (35 KB for 4 waves: it then
+// matches the register limit of four blocks per CU).
+constexpr size_t orbit_lds(int d, bool span) {
+  return (size_t)(d + kMaxBlocks + (span ? d : 0)) * sizeof(float);
+}
 inline int block_threads(int nt_tmpl, int nt) { return 64 * (nt_tmpl == 0 ? nt : nt_tmpl); }
 
 // Resident blocks per CU of one kernel instantiation, queried once per block
-// size (one size for NT = 1..4; one per wave count 5..16 for NT = 0). Racing
-// first calls store the same value.
+// size (one size for NT = 1..4; one per wave count 5..16 for NT = 0) at the
+// largest LDS it takes (d = 1024 x waves). Racing first calls store the same
+// value.
 template <int NT, typename K>
-int resident_cached(std::atomic<int> (&cache)[17], K kernel, int nt) {
+int resident_cached(std::atomic<int> (&cache)[17], K kernel, int nt, bool span) {
   const int slot = NT == 0 ? nt : 0;
   int v = cache[slot].load(std::memory_order_relaxed);
   if (v == 0) {
-    v = resident_blocks_per_cu(kernel, block_threads(NT, nt), orbit_lds(max_d_of(NT)));
+    v = resident_blocks_per_cu(kernel, block_threads(NT, nt), orbit_lds(1024 * nt, span));
     cache[slot].store(v, std::memory_order_relaxed);
   }
   return v;
 }
 
-template <int BITS, bool LSB, int NT, bool FULL, bool SYM>
+template <int BITS, bool LSB, int NT, int HC, bool SYM>
 hipError_t launch_q_sym(const float* W, int64_t rows, int d, int log2h, float kh,
                         const int32_t* perm, const int8_t* signs, const OrbitCodebook& cb,
                         uint8_t* packed, float* norms, int cus, hipStream_t s) {
-  auto kernel = orbit_quantize_kernel<BITS, LSB, NT, FULL, false, DT_F32, SYM>;
-  const size_t shm = orbit_lds(d);
+  auto kernel = orbit_quantize_kernel<BITS, LSB, NT, HC, false, DT_F32, SYM>;
+  const size_t shm = orbit_lds(d, HC == 2);
   const int nt = (d + 1023) >> 10;
   static std::atomic<int> cache[17];
-  const int per_cu = resident_cached<NT>(cache, kernel, nt);
+  const int per_cu = resident_cached<NT>(cache, kernel, nt, HC == 2);
   // Twice the resident blocks: blocks that start later fall out of step with
   // the first ones, so loads and arithmetic of different blocks overlap
   // (2-4% on the 12288 x 3072 weight against a resident-sized grid).
@@ -764,46 +789,51 @@ hipError_t launch_q_sym(const float* W, int64_t rows, int d, int log2h, float kh
 
 // One packing path per instantiation: with both in one kernel the loop ran
 // out of scalar registers and spilled them to VGPR lanes.
-template <int BITS, bool LSB, int NT, bool FULL>
+template <int BITS, bool LSB, int NT, int HC>
 hipError_t launch_q(const float* W, int64_t rows, int d, int log2h, float kh,
                     const int32_t* perm, const int8_t* signs, const OrbitCodebook& cb,
                     uint8_t* packed, float* norms, int cus, hipStream_t s) {
   if (cb.sym)
-    return launch_q_sym<BITS, LSB, NT, FULL, true>(W, rows, d, log2h, kh, perm, signs, cb, packed,
+    return launch_q_sym<BITS, LSB, NT, HC, true>(W, rows, d, log2h, kh, perm, signs, cb, packed,
                                                    norms, cus, s);
-  return launch_q_sym<BITS, LSB, NT, FULL, false>(W, rows, d, log2h, kh, perm, signs, cb, packed,
+  return launch_q_sym<BITS, LSB, NT, HC, false>(W, rows, d, log2h, kh, perm, signs, cb, packed,
                                                   norms, cus, s);
 }
+
+// Launch M(NT, HC) for the wave count nt and stage class hc (class 2 only
+// for the even and run-time wave counts).
+#define TQ_BY_NT_HC(M)                                               \
+  switch (nt) {                                                      \
+    case 1: return hc == 0 ? M(1, 0) : M(1, 1);                      \
+    case 2: return hc == 0 ? M(2, 0) : hc == 1 ? M(2, 1) : M(2, 2);  \
+    case 3: return hc == 0 ? M(3, 0) : M(3, 1);                      \
+    case 4: return hc == 0 ? M(4, 0) : hc == 1 ? M(4, 1) : M(4, 2);  \
+    default: return hc == 0 ? M(0, 0) : hc == 1 ? M(0, 1) : M(0, 2); \
+  }
 
 template <int BITS, bool LSB>
 hipError_t launch_q_nt(int nt, const float* W, int64_t rows, int d, int log2h, float kh,
                        const int32_t* perm, const int8_t* signs, const OrbitCodebook& cb,
                        uint8_t* packed, float* norms, int cus, hipStream_t s) {
-#define TQ_QN(N, F) \
-  launch_q<BITS, LSB, N, F>(W, rows, d, log2h, kh, perm, signs, cb, packed, norms, cus, s)
-  const bool full = log2h >= 10;
-  switch (nt) {
-    case 1: return full ? TQ_QN(1, true) : TQ_QN(1, false);
-    case 2: return full ? TQ_QN(2, true) : TQ_QN(2, false);
-    case 3: return full ? TQ_QN(3, true) : TQ_QN(3, false);
-    case 4: return full ? TQ_QN(4, true) : TQ_QN(4, false);
-    default: return full ? TQ_QN(0, true) : TQ_QN(0, false);
-  }
+#define TQ_QN(N, C) \
+  launch_q<BITS, LSB, N, C>(W, rows, d, log2h, kh, perm, signs, cb, packed, norms, cus, s)
+  const int hc = stage_class(log2h);
+  TQ_BY_NT_HC(TQ_QN)
 #undef TQ_QN
 }
 
-template <int BITS, bool LSB, int DT, int NT, bool FULL>
+template <int BITS, bool LSB, int DT, int NT, int HC>
 hipError_t launch_dq(const uint8_t* packed, const float* norms, int64_t rows, int d, int log2h,
                      float kh, const int32_t* inv_perm, const int8_t* signs,
                      const OrbitCodebook& cb, int rotated_only, void* out, int cus,
                      hipStream_t s) {
-  const size_t shm = orbit_lds(d);
+  const size_t shm = orbit_lds(d, HC == 2);
   const int nt = (d + 1023) >> 10;
   static std::atomic<int> cache[17];
   const int per_cu =
-      resident_cached<NT>(cache, orbit_dequantize_kernel<BITS, LSB, DT, NT, FULL>, nt);
+      resident_cached<NT>(cache, orbit_dequantize_kernel<BITS, LSB, DT, NT, HC>, nt, HC == 2);
   const int grid = grid_size(rows, cus, per_cu);
-  orbit_dequantize_kernel<BITS, LSB, DT, NT, FULL><<<grid, block_threads(NT, nt), shm, s>>>(
+  orbit_dequantize_kernel<BITS, LSB, DT, NT, HC><<<grid, block_threads(NT, nt), shm, s>>>(
       packed, norms, rows, d, log2h, kh, inv_perm, signs, cb, rotated_only, out);
   return hipGetLastError();
 }
@@ -813,16 +843,10 @@ hipError_t launch_dq_nt(int nt, const uint8_t* packed, const float* norms, int64
                         int log2h, float kh, const int32_t* inv_perm, const int8_t* signs,
                         const OrbitCodebook& cb, int rotated_only, void* out, int cus,
                         hipStream_t s) {
-#define TQ_DQN(N, F) launch_dq<BITS, LSB, DT, N, F>(packed, norms, rows, d, log2h, kh, inv_perm, \
+#define TQ_DQN(N, C) launch_dq<BITS, LSB, DT, N, C>(packed, norms, rows, d, log2h, kh, inv_perm, \
                                                  signs, cb, rotated_only, out, cus, s)
-  const bool full = log2h >= 10;
-  switch (nt) {
-    case 1: return full ? TQ_DQN(1, true) : TQ_DQN(1, false);
-    case 2: return full ? TQ_DQN(2, true) : TQ_DQN(2, false);
-    case 3: return full ? TQ_DQN(3, true) : TQ_DQN(3, false);
-    case 4: return full ? TQ_DQN(4, true) : TQ_DQN(4, false);
-    default: return full ? TQ_DQN(0, true) : TQ_DQN(0, false);
-  }
+  const int hc = stage_class(log2h);
+  TQ_BY_NT_HC(TQ_DQN)
 #undef TQ_DQN
 }
 
@@ -844,17 +868,17 @@ hipError_t launch_dq_dt(int dt, int nt, const uint8_t* packed, const float* norm
   }
 }
 
-template <int NT, bool FULL, int DT>
+template <int NT, int HC, int DT>
 hipError_t launch_rot(const void* x, int64_t rows, int d, int log2h, float kh,
                       const int32_t* perm, const int8_t* signs, void* xrot, int cus, hipStream_t s) {
-  const size_t shm = orbit_lds(d);
+  const size_t shm = orbit_lds(d, HC == 2);
   const int nt = (d + 1023) >> 10;
   static std::atomic<int> cache[17];
   const int per_cu =
-      resident_cached<NT>(cache, orbit_quantize_kernel<2, false, NT, FULL, true, DT>, nt);
+      resident_cached<NT>(cache, orbit_quantize_kernel<2, false, NT, HC, true, DT>, nt, HC == 2);
   const int grid = grid_size(rows, cus, per_cu);
   OrbitCodebook cb{};
-  orbit_quantize_kernel<2, false, NT, FULL, true, DT><<<grid, block_threads(NT, nt), shm, s>>>(
+  orbit_quantize_kernel<2, false, NT, HC, true, DT><<<grid, block_threads(NT, nt), shm, s>>>(
       x, rows, d, log2h, kh, perm, signs, cb, nullptr, nullptr, xrot);
   return hipGetLastError();
 }
@@ -893,17 +917,13 @@ hipError_t launch_rot_dt(const void* x, int64_t rows, int di, int log2h, float k
                          const int32_t* perm, const int8_t* signs, void* xrot, int cus,
                          hipStream_t s) {
   const int nt = (di + 1023) >> 10;
-  const bool full = log2h >= 10;
-#define TQ_R(N, F) launch_rot<N, F, DT>(x, rows, di, log2h, kh, perm, signs, xrot, cus, s)
-  switch (nt) {
-    case 1: return full ? TQ_R(1, true) : TQ_R(1, false);
-    case 2: return full ? TQ_R(2, true) : TQ_R(2, false);
-    case 3: return full ? TQ_R(3, true) : TQ_R(3, false);
-    case 4: return full ? TQ_R(4, true) : TQ_R(4, false);
-    default: return full ? TQ_R(0, true) : TQ_R(0, false);
-  }
+  const int hc = stage_class(log2h);
+#define TQ_R(N, C) launch_rot<N, C, DT>(x, rows, di, log2h, kh, perm, signs, xrot, cus, s)
+  TQ_BY_NT_HC(TQ_R)
 #undef TQ_R
 }
+
+#undef TQ_BY_NT_HC
 
 hipError_t launch_orbit_rotate(const void* x, int dt, int64_t rows, int64_t d,
                                const int32_t* perm, const int8_t* signs, void* xrot, int cus,
