@@ -420,11 +420,25 @@ def secondary(tq, timer, dev, signs, mask):
                                                    tq.TQ_MSB_FIRST, None, tq._ptr(yo), sp), 20)
         ms_t, _ = timer.run(lambda: torch.matmul(xr, wrt16), 20)
         flop = 2.0 * m * rows * d
-        fwd16[f"m{m}"] = {"rotate_ms": ms_r, "linear_ms": ms_l,
-                          "linear_TFLOPs": flop / (ms_l * 1e-3) / 1e12,
-                          "linear_frac_bf16_mfma_peak": flop / (ms_l * 1e-3) / 2.5e15,
-                          "codes_GBps": rate(packed.numel() + 2 * m * d + 2 * m * rows, ms_l),
-                          "torch_bf16_matmul_on_dequantized_ms": ms_t}
+        entry = {"path": "row-major", "rotate_ms": ms_r, "linear_ms": ms_l}
+        if m > 64:
+            # orbit_forward's path above 64 rows: the rotation written in the
+            # matrix-core operand layout, read straight into registers
+            xt = torch.empty(tq.orbit_tiled_bytes(m, d) // 2, dtype=torch.bfloat16, device=dev)
+            ms_rt, _ = timer.run(lambda: L.orbit_rotate_tiled(
+                tq._ptr(xa), tq.TQ_BF16, m, d, tq._ptr(perm_d), tq._ptr(sg_d), tq._ptr(xt), sp), 20)
+            ms_lt, _ = timer.run(lambda: L.orbit_linear_tiled(
+                tq._ptr(xt), tq.TQ_BF16, m, d, tq._ptr(packed), tq._ptr(norms), rows, bits, cbp,
+                tq.TQ_MSB_FIRST, None, tq._ptr(yo), sp), 20)
+            entry = {"path": "tiled", "rotate_ms": ms_rt, "linear_ms": ms_lt,
+                     "row_major_rotate_ms": ms_r, "row_major_linear_ms": ms_l}
+            ms_l = ms_lt
+        entry.update({"linear_TFLOPs": flop / (ms_l * 1e-3) / 1e12,
+                      "linear_frac_bf16_mfma_peak": flop / (ms_l * 1e-3) / 2.5e15,
+                      "codes_GBps": rate(packed.numel() + 2 * m * d + 2 * m * rows, ms_l),
+                      "torch_bf16_matmul_on_dequantized_ms": ms_t,
+                      "linear_vs_torch": ms_l / ms_t})
+        fwd16[f"m{m}"] = entry
     out["orbit_forward_12288x3072_3bit_bf16"] = fwd16
     del wrt16
     return out

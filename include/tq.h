@@ -234,6 +234,40 @@ int orbit_linear(const void* x_rot, int dtype, int64_t m, int64_t d_in, const ui
                  int bit_order, const void* bias, void* y, void* stream);
 
 /*
+ * The same two steps of the forward ("orbit_quant.py", OrbitQuantizer.forward:
+ * rpbh_forward, then F.linear with W') with the rotated activations passed in
+ * the operand layout of the library's bf16 / fp16 matrix-core tiles, so the
+ * linear layer loads them straight into registers (a layout of this library,
+ * not of the page). The values are those of orbit_rotate, and
+ * orbit_linear_tiled(orbit_rotate_tiled(x)) equals orbit_linear(orbit_rotate(x))
+ * bit for bit.
+ *
+ * Tiled layout of an m x d matrix (d a multiple of 32): rows padded to
+ * mp = 16 * ceil(m / 16); the 16 x 32 block of row tile t (rows 16 t ..) and
+ * column chunk kc (columns 32 kc ..) is 1024 bytes at byte offset
+ * (t * (d / 32) + kc) * 1024; inside it, the 16 bytes at l * 16 (l = 0..63)
+ * hold row 16 t + l % 16, columns 32 kc + 8 (l / 16) .. + 7, in column order.
+ * orbit_tiled_bytes(m, d) = mp * d * 2 (0 for d not a positive multiple of
+ * 32, d > 16384 or m out of range).
+ *
+ * orbit_rotate_tiled -- orbit_rotate into that layout; the pad rows are
+ *   written as zeros. dtype TQ_BF16 or TQ_F16 (TQ_ERR_DTYPE otherwise); x as
+ *   for orbit_rotate; x_tiled device, orbit_tiled_bytes(rows, d) bytes,
+ *   16-byte aligned. Same limits on d as orbit_rotate.
+ * orbit_linear_tiled -- orbit_linear with x_rot in that layout (its m rows;
+ *   the pad rows are read, their outputs not written). dtype TQ_BF16 or
+ *   TQ_F16; 64 <= d_in < 2^22, a multiple of 32 (TQ_ERR_SHAPE otherwise);
+ *   the other arguments as for orbit_linear.
+ */
+size_t orbit_tiled_bytes(int64_t m, int64_t d);
+int orbit_rotate_tiled(const void* x, int dtype, int64_t rows, int64_t d, const int32_t* perm,
+                       const int8_t* signs, void* x_tiled, void* stream);
+int orbit_linear_tiled(const void* x_tiled, int dtype, int64_t m, int64_t d_in,
+                       const uint8_t* packed, const float* row_norms, int64_t d_out, int bits,
+                       const float* codebook, int bit_order, const void* bias, void* y,
+                       void* stream);
+
+/*
  * tq3_decode_attention -- one decode step of attention over a KV cache whose
  * K and V vectors are TQ3 records ("ComfyUI-TurboQuant: tq3_core.py": TQ3 is
  * a KV-cache codec; attention reads the vectors tq3_dequantize reconstructs).

@@ -20,6 +20,9 @@ Entry points (same names as the C ABI in include/tq.h):
   orbit_rotate(x, perm, signs)     -> rpbh_forward of activation rows (fp32/bf16/fp16)
   orbit_linear(x_rot, packed, norms, bits, codebook, bias)
                                    -> x_rot @ W'^T + bias (W' decoded on the fly)
+  orbit_rotate_tiled, orbit_linear_tiled
+                                   -> the same two steps through the matrix-core
+                                      operand layout (bf16 / fp16)
   orbit_forward(x, packed, norms, perm, signs, bits, codebook, bias)
                                    -> the two above: the quantized layer's output
 plus host helpers tq3_record_bytes, orbit_block_size, tq_gaussian_lloyd_max,
@@ -64,6 +67,9 @@ def _load():
         "orbit_make_codebook": [_int, _i64, _vp],
         "orbit_rotate": [_vp, _int, _i64, _i64, _vp, _vp, _vp, _vp],
         "orbit_linear": [_vp, _int, _i64, _i64, _vp, _vp, _i64, _int, _vp, _int, _vp, _vp, _vp],
+        "orbit_rotate_tiled": [_vp, _int, _i64, _i64, _vp, _vp, _vp, _vp],
+        "orbit_linear_tiled": [_vp, _int, _i64, _i64, _vp, _vp, _i64, _int, _vp, _int, _vp, _vp,
+                               _vp],
         "tq3_decode_attention": [_vp, _int, _int, _vp, _vp, _i64, _int, _vp, ctypes.c_float,
                                  _vp, ctypes.c_size_t, _vp, _int, _vp],
         "tq3_decode_attention_noalloc": [_vp, _int, _int, _vp, _vp, _i64, _int, _vp,
@@ -83,6 +89,8 @@ def _load():
     lib.tq3_attention_workspace_bytes.restype = ctypes.c_size_t
     lib.tq3_attention_noalloc_max_bytes.argtypes = []
     lib.tq3_attention_noalloc_max_bytes.restype = ctypes.c_size_t
+    lib.orbit_tiled_bytes.argtypes = [_i64, _i64]
+    lib.orbit_tiled_bytes.restype = ctypes.c_size_t
     return lib
 
 
@@ -93,6 +101,7 @@ EXPORTS = ("tq3_quantize", "tq3_dequantize", "tq3_quantize_split", "tq3_dequanti
            "orbit_quantize_weight", "orbit_dequantize", "tq3_record_bytes", "orbit_block_size", "tq_gaussian_lloyd_max",
            "orbit_make_codebook", "tq_status_str", "tq3_decode_attention",
            "tq3_attention_workspace_bytes", "orbit_rotate", "orbit_linear",
+           "orbit_tiled_bytes", "orbit_rotate_tiled", "orbit_linear_tiled",
            "tq3_decode_attention_noalloc", "tq3_attention_noalloc_max_bytes")
 
 
@@ -457,6 +466,33 @@ def orbit_rotate(x: torch.Tensor, perm: torch.Tensor, signs: torch.Tensor,
     return out
 
 
+def _linear_weight_args(x, m, d_in, packed, row_norms, bits, codebook, bias, out, lead):
+    """Checks shared by orbit_linear and orbit_linear_tiled -> (packed,
+    norms, bias pointer, host codebook, out)."""
+    d_out = row_norms.numel()
+    if packed.numel() != d_out * d_in * bits // 8:
+        raise ValueError("packed does not match d_out x d_in at this bit width")
+    nr = row_norms.to(torch.float32).contiguous()
+    pk = packed.contiguous()
+    bp = None
+    if bias is not None:
+        if bias.dtype != x.dtype or bias.numel() != d_out:
+            raise ValueError("bias must hold d_out values of the activations' dtype")
+        bias = bias.contiguous()
+        _need_gpu(bias)
+        bp = _ptr(bias)
+    cb = _host_f32(codebook)
+    if len(cb) != (1 << bits):
+        raise ValueError("codebook must hold 2**bits values")
+    if out is None:
+        out = torch.empty((*lead, d_out), dtype=x.dtype, device=x.device)
+    if (out.dtype != x.dtype or not out.is_contiguous() or out.numel() != m * d_out
+            or out.device != x.device):
+        raise ValueError("out must be a contiguous [..., d_out] tensor of the activations' "
+                         "dtype on their device")
+    return pk, nr, bp, cb, out
+
+
 def orbit_linear(x_rot: torch.Tensor, packed: torch.Tensor, row_norms: torch.Tensor, bits: int,
                  codebook, bias: torch.Tensor = None, bit_order: int = TQ_MSB_FIRST,
                  out: torch.Tensor = None) -> torch.Tensor:
@@ -467,37 +503,84 @@ def orbit_linear(x_rot: torch.Tensor, packed: torch.Tensor, row_norms: torch.Ten
         raise ValueError("x_rot must be fp32, bf16 or fp16")
     _need_gpu(x_rot, packed, row_norms)
     d_in = x_rot.shape[-1]
-    d_out = row_norms.numel()
-    if packed.numel() != d_out * d_in * bits // 8:
-        raise ValueError("packed does not match d_out x d_in at this bit width")
     xv = x_rot.contiguous().reshape(-1, d_in)
-    nr = row_norms.to(torch.float32).contiguous()
-    pk = packed.contiguous()
-    bp = None
-    if bias is not None:
-        if bias.dtype != x_rot.dtype or bias.numel() != d_out:
-            raise ValueError("bias must hold d_out values of x_rot's dtype")
-        bias = bias.contiguous()
-        _need_gpu(bias)
-        bp = _ptr(bias)
-    cb = _host_f32(codebook)
-    if len(cb) != (1 << bits):
-        raise ValueError("codebook must hold 2**bits values")
-    if out is None:
-        out = torch.empty((*x_rot.shape[:-1], d_out), dtype=x_rot.dtype, device=x_rot.device)
-    if out.dtype != x_rot.dtype or not out.is_contiguous() or out.numel() != xv.shape[0] * d_out:
-        raise ValueError("out must be a contiguous [..., d_out] tensor of x_rot's dtype")
+    pk, nr, bp, cb, out = _linear_weight_args(x_rot, xv.shape[0], d_in, packed, row_norms, bits,
+                                              codebook, bias, out, x_rot.shape[:-1])
     _check(lib.orbit_linear(_ptr(xv), _DTYPES[x_rot.dtype], xv.shape[0], d_in, _ptr(pk),
-                            _ptr(nr), d_out, bits,
+                            _ptr(nr), row_norms.numel(), bits,
                             ctypes.cast(cb, _vp), bit_order, bp, _ptr(out), _stream(x_rot)),
            "orbit_linear")
     return out
 
 
+def orbit_tiled_bytes(m: int, d: int) -> int:
+    return int(lib.orbit_tiled_bytes(m, d))
+
+
+def orbit_rotate_tiled(x: torch.Tensor, perm: torch.Tensor, signs: torch.Tensor,
+                       out: torch.Tensor = None) -> torch.Tensor:
+    """orbit_rotate of bf16 / fp16 rows x [m, d] into the matrix-core operand
+    layout orbit_linear_tiled reads (rows padded to a multiple of 16 with
+    zeros) -> a flat tensor of x's dtype, orbit_tiled_bytes(m, d) bytes."""
+    if x.dtype not in (torch.bfloat16, torch.float16) or x.ndim != 2:
+        raise ValueError("x must be a 2-D bf16 or fp16 tensor")
+    m, d = x.shape
+    nbytes = orbit_tiled_bytes(m, d)
+    if nbytes == 0 and m > 0:
+        raise ValueError("d must be a positive multiple of 32, at most 16384")
+    if out is None:
+        out = torch.empty(nbytes // 2, dtype=x.dtype, device=x.device)
+    _check_out(out, x.dtype, nbytes // 2, x.device, "orbit_rotate_tiled")
+    _need_gpu(x, perm, signs)
+    xv = x.contiguous()
+    perm = perm.to(torch.int32).contiguous()
+    signs = signs.to(torch.int8).contiguous()
+    _check(lib.orbit_rotate_tiled(_ptr(xv), _DTYPES[x.dtype], m, d, _ptr(perm), _ptr(signs),
+                                  _ptr(out), _stream(x)), "orbit_rotate_tiled")
+    return out
+
+
+def orbit_linear_tiled(x_tiled: torch.Tensor, m: int, packed: torch.Tensor,
+                       row_norms: torch.Tensor, bits: int, codebook, bias: torch.Tensor = None,
+                       bit_order: int = TQ_MSB_FIRST, out: torch.Tensor = None) -> torch.Tensor:
+    """orbit_linear of m rows held in the tiled layout (orbit_rotate_tiled's
+    output; d_in from packed and row_norms) -> [m, d_out] of x_tiled's dtype."""
+    if x_tiled.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("x_tiled must be bf16 or fp16")
+    d_out = row_norms.numel()
+    if d_out < 1 or (packed.numel() * 8) % (bits * d_out):
+        raise ValueError("packed does not hold d_out rows at this bit width")
+    d_in = packed.numel() * 8 // (bits * d_out)
+    if not x_tiled.is_contiguous() or x_tiled.numel() * 2 != orbit_tiled_bytes(m, d_in):
+        raise ValueError("x_tiled must be a contiguous tiled [m, d_in] buffer")
+    _need_gpu(x_tiled, packed, row_norms)
+    pk, nr, bp, cb, out = _linear_weight_args(x_tiled, m, d_in, packed, row_norms, bits,
+                                              codebook, bias, out, (m,))
+    _check(lib.orbit_linear_tiled(_ptr(x_tiled), _DTYPES[x_tiled.dtype], m, d_in, _ptr(pk),
+                                  _ptr(nr), d_out, bits, ctypes.cast(cb, _vp), bit_order, bp,
+                                  _ptr(out), _stream(x_tiled)), "orbit_linear_tiled")
+    return out
+
+
+# the forward takes the tiled path above this many bf16 / fp16 rows (the
+# few-rows kernels below read x_rot through LDS anyway)
+_TILED_MIN_ROWS = 64
+
+
 def orbit_forward(x: torch.Tensor, packed: torch.Tensor, row_norms: torch.Tensor,
                   perm: torch.Tensor, signs: torch.Tensor, bits: int, codebook,
                   bias: torch.Tensor = None, bit_order: int = TQ_MSB_FIRST) -> torch.Tensor:
-    """The quantized layer's forward: orbit_linear(orbit_rotate(x), ...)."""
+    """The quantized layer's forward: orbit_linear(orbit_rotate(x), ...). For
+    more than 64 bf16 / fp16 rows (and 64 <= d_in < 2^22) the rotation goes
+    into the tiled layout and orbit_linear_tiled reads it: the same values."""
+    d_in = x.shape[-1]
+    rows = x.numel() // d_in if d_in else 0
+    if (x.dtype in (torch.bfloat16, torch.float16) and rows > _TILED_MIN_ROWS
+            and 64 <= d_in < (1 << 22) and d_in % 32 == 0):
+        xv = x.reshape(rows, d_in)
+        y = orbit_linear_tiled(orbit_rotate_tiled(xv, perm, signs), rows, packed, row_norms,
+                               bits, codebook, bias, bit_order)
+        return y.reshape(*x.shape[:-1], row_norms.numel())
     return orbit_linear(orbit_rotate(x, perm, signs), packed, row_norms, bits, codebook, bias,
                         bit_order)
 

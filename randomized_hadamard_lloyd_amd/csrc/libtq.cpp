@@ -237,7 +237,26 @@ int orbit_rotate(const void* x, int dtype, int64_t rows, int64_t d, const int32_
   if (!x || !perm || !signs || !x_rot) return TQ_ERR_NULL;
   if (!aligned(x, 16) || !aligned(x_rot, 16) || !aligned(perm, 16) || !aligned(signs, 16))
     return TQ_ERR_ALIGN;
-  return launched(tq::launch_orbit_rotate(x, dtype, rows, d, perm, signs, x_rot, cu_count(),
+  return launched(tq::launch_orbit_rotate(x, dtype, rows, d, perm, signs, x_rot, 0, cu_count(),
+                                          static_cast<hipStream_t>(stream)));
+}
+
+size_t orbit_tiled_bytes(int64_t rows, int64_t d) {
+  if (rows < 0 || rows > kMaxVectors || d < 32 || d % 32 != 0 || d > kMaxOrbitD) return 0;
+  return (size_t)((rows + 15) / 16 * 16) * (size_t)d * 2;
+}
+
+int orbit_rotate_tiled(const void* x, int dtype, int64_t rows, int64_t d, const int32_t* perm,
+                       const int8_t* signs, void* x_tiled, void* stream) {
+  if (dtype != TQ_BF16 && dtype != TQ_F16) return TQ_ERR_DTYPE;
+  if (rows < 0 || rows > kMaxVectors || d <= 0) return TQ_ERR_SHAPE;
+  const int64_t h = d & -d;
+  if (h < 32 || d > kMaxOrbitD) return TQ_ERR_BLOCK;
+  if (rows == 0) return TQ_OK;
+  if (!x || !perm || !signs || !x_tiled) return TQ_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(x_tiled, 16) || !aligned(perm, 16) || !aligned(signs, 16))
+    return TQ_ERR_ALIGN;
+  return launched(tq::launch_orbit_rotate(x, dtype, rows, d, perm, signs, x_tiled, 1, cu_count(),
                                           static_cast<hipStream_t>(stream)));
 }
 
@@ -265,12 +284,36 @@ int orbit_linear(const void* x_rot, int dtype, int64_t m, int64_t d_in, const ui
     return TQ_ERR_ALIGN;
   if (dtype != TQ_F32)
     return launched(tq::launch_orbit_linear_lp(x_rot, dtype, m, d_in, packed, row_norms, d_out,
-                                               bits, cb, bit_order == TQ_LSB_FIRST, bias, y,
+                                               bits, cb, bit_order == TQ_LSB_FIRST, bias, y, 0,
                                                static_cast<hipStream_t>(stream)));
   return launched(tq::launch_orbit_linear(static_cast<const float*>(x_rot), m, d_in, packed,
                                           row_norms, d_out, bits, cb, bit_order == TQ_LSB_FIRST,
                                           static_cast<const float*>(bias), static_cast<float*>(y),
                                           static_cast<hipStream_t>(stream)));
+}
+
+int orbit_linear_tiled(const void* x_tiled, int dtype, int64_t m, int64_t d_in,
+                       const uint8_t* packed, const float* row_norms, int64_t d_out, int bits,
+                       const float* codebook, int bit_order, const void* bias, void* y,
+                       void* stream) {
+  if (dtype != TQ_BF16 && dtype != TQ_F16) return TQ_ERR_DTYPE;
+  if (bits < 2 || bits > 4) return TQ_ERR_BITS;
+  // the tall tiles: 64 <= d_in < 2^22 (32-bit fragment offsets inside a block)
+  if (m < 0 || m > kMaxVectors || d_in < 64 || d_in % 32 != 0 || d_in >= ((int64_t)1 << 22) ||
+      d_out < 1 || d_out > ((int64_t)1 << 31))
+    return TQ_ERR_SHAPE;
+  if ((m + 255) / 256 * ((d_out + 63) / 64) > ((int64_t)1 << 30)) return TQ_ERR_SHAPE;
+  tq::OrbitCodebook cb;
+  const int st = orbit_check(1, 32, bits, codebook, bit_order, &cb);
+  if (st != TQ_OK) return st;
+  if (m == 0) return TQ_OK;
+  if (!x_tiled || !packed || !row_norms || !y) return TQ_ERR_NULL;
+  if (!aligned(x_tiled, 16) || !aligned(packed, 16) || !aligned(row_norms, 4) || !aligned(y, 2) ||
+      (bias && !aligned(bias, 2)))
+    return TQ_ERR_ALIGN;
+  return launched(tq::launch_orbit_linear_lp(x_tiled, dtype, m, d_in, packed, row_norms, d_out,
+                                             bits, cb, bit_order == TQ_LSB_FIRST, bias, y, 1,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 static bool attn_shape_ok(int64_t n_tok, int hq, int hkv) {

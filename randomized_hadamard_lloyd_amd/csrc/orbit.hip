@@ -390,13 +390,19 @@ __device__ __forceinline__ uint32_t sign_of(uint32_t w, int k) {
 // the forward's first step) to xrot instead of quantizing. DT: the format of
 // the rows read and, with ROT, of xrot; for bf16 / fp16 every stage rounds
 // to that format as the page's forward does on such activations.
+// TOUT (ROT, bf16 / fp16): xrot in the MFMA fragment layout of the tiled
+// linear layer: rows padded to a multiple of 16 (the pad rows zero); the
+// 16 x 32 block of row tile t and column chunk kc is 1 KB at
+// (t * d / 32 + kc) * 1024, lane l's 16 bytes at l * 16 holding row
+// 16 t + l % 16, columns 32 kc + 8 (l / 16) .. + 7.
 template <int BITS, bool LSB, int NT, int HC, bool ROT = false, int DT = DT_F32,
-          bool SYM = true>
+          bool SYM = true, bool TOUT = false>
 __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
     const void* __restrict__ W, int64_t rows, int d, int log2h, float kh,
     const int32_t* __restrict__ perm, const int8_t* __restrict__ signs, OrbitCodebook cb,
     uint8_t* __restrict__ packed, float* __restrict__ norms, void* __restrict__ xrot) {
   static_assert(ROT || DT == DT_F32, "the weight codec reads fp32 rows");
+  static_assert(!TOUT || (ROT && DT != DT_F32), "the tiled form holds bf16 / fp16 rotations");
   extern __shared__ float lds[];
   float* rowbuf = lds;     // the row; later the cross-wave butterfly exchange
   float* bsum = lds + d;   // block (or, for h > 1024, tile) sums of squares
@@ -457,7 +463,9 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
 #pragma unroll
     for (int k = 0; k < KL; ++k) pre[k] = src[fidx[k]];
   }
-  for (; r < rows; r += gridDim.x) {
+  // TOUT also covers the pad rows (their loads re-read row 0)
+  const int64_t rows_loop = TOUT ? (rows + 15) / 16 * 16 : rows;
+  for (; r < rows_loop; r += gridDim.x) {
 #pragma unroll
     for (int k = 0; k < KL; ++k) {
       const int f = tid + NTHR * k;
@@ -488,7 +496,7 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
     }
     __syncthreads();
     {
-      const int64_t rn = r + gridDim.x < rows ? r + gridDim.x : r;
+      const int64_t rn = r + gridDim.x < rows ? r + gridDim.x : 0;
       const u32x4* src = reinterpret_cast<const u32x4*>(Wb + rn * row_in);
 #pragma unroll
       for (int k = 0; k < KL; ++k) pre[k] = src[fidx[k]];
@@ -539,9 +547,20 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
                      ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y[2 * k + 1]) << 16);
             }
           }
-          u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(xrot) + r * d + 16 * c);
-          dst[0] = u32x4{w[0], w[1], w[2], w[3]};
-          dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+          if constexpr (TOUT) {
+            // columns 16 c .. 16 c + 15: chunk c / 2, lane groups 2 (c % 2) and + 1
+            const bool pad = r >= rows;
+            char* frag = static_cast<char*>(xrot) + ((r >> 4) * (d >> 5) + (c >> 1)) * 1024;
+            const int l0 = (int)(r & 15) + 32 * (c & 1);
+            *reinterpret_cast<u32x4*>(frag + 16 * l0) =
+                pad ? u32x4{0u, 0u, 0u, 0u} : u32x4{w[0], w[1], w[2], w[3]};
+            *reinterpret_cast<u32x4*>(frag + 16 * (l0 + 16)) =
+                pad ? u32x4{0u, 0u, 0u, 0u} : u32x4{w[4], w[5], w[6], w[7]};
+          } else {
+            u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(xrot) + r * d + 16 * c);
+            dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+            dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+          }
         }
       }
       __syncthreads();  // the row buffer is free for the next row
@@ -868,18 +887,18 @@ hipError_t launch_dq_dt(int dt, int nt, const uint8_t* packed, const float* norm
   }
 }
 
-template <int NT, int HC, int DT>
+template <int NT, int HC, int DT, bool TOUT>
 hipError_t launch_rot(const void* x, int64_t rows, int d, int log2h, float kh,
                       const int32_t* perm, const int8_t* signs, void* xrot, int cus, hipStream_t s) {
+  auto kernel = orbit_quantize_kernel<2, false, NT, HC, true, DT, true, TOUT>;
   const size_t shm = orbit_lds(d, HC == 2);
   const int nt = (d + 1023) >> 10;
   static std::atomic<int> cache[17];
-  const int per_cu =
-      resident_cached<NT>(cache, orbit_quantize_kernel<2, false, NT, HC, true, DT>, nt, HC == 2);
-  const int grid = grid_size(rows, cus, per_cu);
+  const int per_cu = resident_cached<NT>(cache, kernel, nt, HC == 2);
+  const int grid = grid_size(TOUT ? (rows + 15) / 16 * 16 : rows, cus, per_cu);
   OrbitCodebook cb{};
-  orbit_quantize_kernel<2, false, NT, HC, true, DT><<<grid, block_threads(NT, nt), shm, s>>>(
-      x, rows, d, log2h, kh, perm, signs, cb, nullptr, nullptr, xrot);
+  kernel<<<grid, block_threads(NT, nt), shm, s>>>(x, rows, d, log2h, kh, perm, signs, cb, nullptr,
+                                                  nullptr, xrot);
   return hipGetLastError();
 }
 
@@ -912,13 +931,13 @@ hipError_t launch_orbit_quantize(const float* W, int64_t rows, int64_t d, int bi
 #undef TQ_Q
 }
 
-template <int DT>
+template <int DT, bool TOUT>
 hipError_t launch_rot_dt(const void* x, int64_t rows, int di, int log2h, float kh,
                          const int32_t* perm, const int8_t* signs, void* xrot, int cus,
                          hipStream_t s) {
   const int nt = (di + 1023) >> 10;
   const int hc = stage_class(log2h);
-#define TQ_R(N, C) launch_rot<N, C, DT>(x, rows, di, log2h, kh, perm, signs, xrot, cus, s)
+#define TQ_R(N, C) launch_rot<N, C, DT, TOUT>(x, rows, di, log2h, kh, perm, signs, xrot, cus, s)
   TQ_BY_NT_HC(TQ_R)
 #undef TQ_R
 }
@@ -926,17 +945,19 @@ hipError_t launch_rot_dt(const void* x, int64_t rows, int di, int log2h, float k
 #undef TQ_BY_NT_HC
 
 hipError_t launch_orbit_rotate(const void* x, int dt, int64_t rows, int64_t d,
-                               const int32_t* perm, const int8_t* signs, void* xrot, int cus,
-                               hipStream_t s) {
+                               const int32_t* perm, const int8_t* signs, void* xrot, int tiled,
+                               int cus, hipStream_t s) {
   const int64_t h = d & -d;
   const int log2h = ilog2(h);
   const float kh = (float)pow((double)h, -0.5);
   const int di = (int)d;
+#define TQ_RD(T, O) launch_rot_dt<T, O>(x, rows, di, log2h, kh, perm, signs, xrot, cus, s)
   switch (dt) {
-    case DT_F32: return launch_rot_dt<DT_F32>(x, rows, di, log2h, kh, perm, signs, xrot, cus, s);
-    case DT_BF16: return launch_rot_dt<DT_BF16>(x, rows, di, log2h, kh, perm, signs, xrot, cus, s);
-    default: return launch_rot_dt<DT_F16>(x, rows, di, log2h, kh, perm, signs, xrot, cus, s);
+    case DT_F32: return TQ_RD(DT_F32, false);
+    case DT_BF16: return tiled ? TQ_RD(DT_BF16, true) : TQ_RD(DT_BF16, false);
+    default: return tiled ? TQ_RD(DT_F16, true) : TQ_RD(DT_F16, false);
   }
+#undef TQ_RD
 }
 
 hipError_t launch_orbit_dequantize(const uint8_t* packed, const float* norms, int64_t rows,

@@ -272,6 +272,14 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
 // Tile layout: row r holds 64 elements as eight 16-byte chunks; chunk c sits
 // in slot c ^ ((r / 2) % 8). The MFMA operand reads (16 consecutive rows, one
 // chunk) then cover all 64 banks once per 16 lanes.
+//
+// TILED: x_rot comes in the MFMA fragment layout orbit_rotate_tiled writes
+// (1 KB per 16 rows x 32 columns, lane l's 16 bytes at l * 16: row l % 16,
+// columns 8 (l / 16) .. + 7), so each wave loads its operands straight into
+// registers, whole cache lines per load, and x_rot never passes through LDS.
+// Each step's two halves load half a step apart (the next step's first half
+// at the start of a step, its second half into the registers of the first
+// half once those are consumed): 164 VGPRs, three waves per SIMD.
 constexpr int kTallBM = 256, kTallBN = 64;
 
 // One v_bfe_u32 per 3-bit field (left to itself the compiler shifts and
@@ -286,7 +294,7 @@ __device__ __forceinline__ int tall_off(int r, int c) {  // byte offset of (row,
   return r * 128 + ((c ^ (r >> 1)) & 7) * 16;
 }
 
-template <int DT, int BITS, bool LSB>
+template <int DT, int BITS, bool LSB, bool TILED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void
 orbit_linear_lp_tall_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                             const uint8_t* __restrict__ packed, const float* __restrict__ norms,
@@ -296,7 +304,7 @@ orbit_linear_lp_tall_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K
   constexpr bool PAIRS = BITS == 2;
   // dwords per row's table, padded by one so that rows start in different banks
   constexpr int TW = (PAIRS ? L * L : L / 2) + 1;
-  __shared__ __attribute__((aligned(16))) char As[4][64 * 128];
+  __shared__ __attribute__((aligned(16))) char As[TILED ? 1 : 4][TILED ? 16 : 64 * 128];
   __shared__ __attribute__((aligned(16))) char Bs[2][kTallBN * 128];
   __shared__ uint32_t tbw[kTallBN * TW];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -331,12 +339,20 @@ orbit_linear_lp_tall_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K
   // x_rot: piece p of this lane is row 8 p + lane / 8 of the wave's 64, chunk
   // lane % 8 of the step (byte offsets from the block's first row at the
   // step's column; rows past M re-read row m0 and are never stored).
+  // TILED: piece p = 2 i + h is the fragment of row tile 4 wave + i (tiles
+  // past the last one re-read it), half h of the step.
   const char* xblk = reinterpret_cast<const char*>(x + m0 * K);
   uint32_t xoff[8];
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
-    const int64_t r = 64 * wave + 8 * p + (lane >> 3);
-    xoff[p] = (uint32_t)(((m0 + r < M ? r : 0) * K + 8 * (lane & 7)) * 2);
+    if constexpr (TILED) {
+      const int64_t last_t = (M + 15) / 16 - 1 - m0 / 16;
+      const int64_t t = 4 * wave + (p >> 1) < last_t ? 4 * wave + (p >> 1) : last_t;
+      xoff[p] = (uint32_t)(((t * (K / 32) + (p & 1)) * 64 + lane) * 16);
+    } else {
+      const int64_t r = 64 * wave + 8 * p + (lane >> 3);
+      xoff[p] = (uint32_t)(((m0 + r < M ? r : 0) * K + 8 * (lane & 7)) * 2);
+    }
   }
   const int64_t steps = (K + 63) / 64;
   // K is a multiple of 32 (and at least 64): when it is an odd one, the last
@@ -346,14 +362,21 @@ orbit_linear_lp_tall_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K
   const int64_t last = steps - 1;
   auto kbase = [&](int64_t st) { return st * 64 - (half_last && st == last ? 32 : 0); };
   auto fetch_x = [&](u32x4v (&xv)[8], int64_t st) {
-    const char* b = xblk + kbase(st) * 2;
+    const char* b = TILED ? xblk + (kbase(st) / 32) * 1024 : xblk + kbase(st) * 2;
 #pragma unroll
     for (int p = 0; p < 8; ++p) xv[p] = *reinterpret_cast<const u32x4v*>(b + xoff[p]);
+  };
+  // TILED: the four fragments of one half step
+  auto fetch_half = [&](u32x4v (&xv)[4], int64_t st, int h) {
+    const char* b = xblk + (kbase(st) / 32) * 1024;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xv[i] = *reinterpret_cast<const u32x4v*>(b + xoff[2 * i + h]);
   };
   auto stage_x = [&](const u32x4v (&xv)[8]) {
 #pragma unroll
     for (int p = 0; p < 8; ++p)
-      *reinterpret_cast<u32x4v*>(&As[wave][tall_off(8 * p + (lane >> 3), lane & 7)]) = xv[p];
+      *reinterpret_cast<u32x4v*>(&As[TILED ? 0 : wave][tall_off(8 * p + (lane >> 3), lane & 7)]) =
+          xv[p];
   };
   auto fetch_c = [&](int64_t st) -> uint64_t {
     return load_codes<BITS>(prow + (kbase(st) / 16 + bq) * (2 * BITS));
@@ -411,7 +434,10 @@ orbit_linear_lp_tall_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
 
-  {
+  u32x4v xa[8];  // TILED: the current step's fragments
+  if constexpr (TILED) {
+    fetch_x(xa, 0);
+  } else {
     u32x4v xv[8];
     fetch_x(xv, 0);
     stage_x(xv);
@@ -426,7 +452,7 @@ orbit_linear_lp_tall_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K
   // One step: multiply the tile of step st (both halves, or only the second
   // on a half step) while the next step's x_rot and the codes two steps ahead
   // load and the next step's tile is decoded into the other buffer.
-  auto step = [&](int64_t st, bool first_half, bool more) {
+  auto step_staged = [&](int64_t st, bool first_half, bool more) {
     u32x4v xv[8];
     uint64_t cn = 0;
     if (more) {
@@ -469,8 +495,54 @@ orbit_linear_lp_tall_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma_lp<DT>(a[i], b[j], acc[i][j]);
     if (more) __syncthreads();
   };
-  for (int64_t st = 0; st < last; ++st) step(st, true, true);
-  step(last, !half_last, false);
+  // The same with the fragments in registers: the same MFMAs on the same
+  // operands, in the same order.
+  auto step_tiled = [&](int64_t st, bool first_half, bool more) {
+    u32x4v xn[4], xh[4];
+    uint64_t cn = 0;
+    if (more) {
+      fetch_half(xn, st + 1, 0);
+      cn = fetch_c(st + 2 < steps ? st + 2 : last);
+    }
+    asm volatile("" ::: "memory");
+    const char* bt = Bs[st & 1];
+    u32x4v b[4];
+    if (first_half) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b[j] = *reinterpret_cast<const u32x4v*>(&bt[tall_off(16 * j + orow, ochk)]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_lp<DT>(xa[2 * i], b[j], acc[i][j]);
+    }
+    if (more) {
+      fetch_half(xh, st + 1, 1);
+      decode(cr, (int)((st + 1) & 1));
+      cr = cn;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      b[j] = *reinterpret_cast<const u32x4v*>(&bt[tall_off(16 * j + orow, 4 + ochk)]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_lp<DT>(xa[2 * i + 1], b[j], acc[i][j]);
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xa[2 * i] = xn[i];
+        xa[2 * i + 1] = xh[i];
+      }
+      __syncthreads();
+    }
+  };
+  for (int64_t st = 0; st < last; ++st) {
+    if constexpr (TILED) step_tiled(st, true, true);
+    else step_staged(st, true, true);
+  }
+  if constexpr (TILED) step_tiled(last, !half_last, false);
+  else step_staged(last, !half_last, false);
 
   // y = round(acc + bias)
 #pragma unroll
@@ -707,10 +779,16 @@ inline size_t lp_small_lds(int64_t K, int bits, int mt, int ntl) {
 template <int DT, int BITS, bool LSB>
 hipError_t launch_lp(const void* x, int64_t M, int64_t K, const uint8_t* packed,
                      const float* norms, int64_t N, const OrbitCodebook& cb, const void* bias,
-                     void* y, hipStream_t s) {
+                     void* y, bool tiled, hipStream_t s) {
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const uint16_t* bp = static_cast<const uint16_t*>(bias);
   uint16_t* yp = static_cast<uint16_t*>(y);
+  if (tiled) {  // x_rot in the fragment layout: the tall tiles at every M (64 <= K < 2^22)
+    const unsigned grid = xcd_grid((N + kTallBN - 1) / kTallBN, (M + kTallBM - 1) / kTallBM);
+    orbit_linear_lp_tall_kernel<DT, BITS, LSB, true><<<grid, 256, 0, s>>>(xp, M, K, packed, norms,
+                                                                          N, cb, bp, yp);
+    return hipGetLastError();
+  }
   const int mt = (int)((M + 15) / 16);
   // Above 32 rows a block takes two 16-row tiles of W' (when they fit in LDS):
   // every block reads all of x_rot, and that read then serves twice the
@@ -735,7 +813,7 @@ hipError_t launch_lp(const void* x, int64_t M, int64_t K, const uint8_t* packed,
   // lanes' 32-bit x_rot offsets could overflow.
   if (K >= 64 && K < ((int64_t)1 << 22)) {
     const unsigned grid = xcd_grid((N + kTallBN - 1) / kTallBN, (M + kTallBM - 1) / kTallBM);
-    orbit_linear_lp_tall_kernel<DT, BITS, LSB><<<grid, 256, 0, s>>>(xp, M, K, packed, norms, N,
+    orbit_linear_lp_tall_kernel<DT, BITS, LSB, false><<<grid, 256, 0, s>>>(xp, M, K, packed, norms, N,
                                                                     cb, bp, yp);
     return hipGetLastError();
   }
@@ -748,8 +826,8 @@ hipError_t launch_lp(const void* x, int64_t M, int64_t K, const uint8_t* packed,
 template <int DT>
 hipError_t launch_lp_bits(const void* x, int64_t M, int64_t K, const uint8_t* packed,
                           const float* norms, int64_t N, int bits, const OrbitCodebook& cb,
-                          int lsb_first, const void* bias, void* y, hipStream_t s) {
-#define TQ_LP(B, O) launch_lp<DT, B, O>(x, M, K, packed, norms, N, cb, bias, y, s)
+                          int lsb_first, const void* bias, void* y, bool tiled, hipStream_t s) {
+#define TQ_LP(B, O) launch_lp<DT, B, O>(x, M, K, packed, norms, N, cb, bias, y, tiled, s)
   if (lsb_first) {
     if (bits == 2) return TQ_LP(2, true);
     if (bits == 3) return TQ_LP(3, true);
@@ -766,10 +844,12 @@ hipError_t launch_lp_bits(const void* x, int64_t M, int64_t K, const uint8_t* pa
 hipError_t launch_orbit_linear_lp(const void* x, int dt, int64_t M, int64_t K,
                                   const uint8_t* packed, const float* norms, int64_t N, int bits,
                                   const OrbitCodebook& cb, int lsb_first, const void* bias,
-                                  void* y, hipStream_t s) {
+                                  void* y, int tiled, hipStream_t s) {
   if (dt == DT_BF16)
-    return launch_lp_bits<DT_BF16>(x, M, K, packed, norms, N, bits, cb, lsb_first, bias, y, s);
-  return launch_lp_bits<DT_F16>(x, M, K, packed, norms, N, bits, cb, lsb_first, bias, y, s);
+    return launch_lp_bits<DT_BF16>(x, M, K, packed, norms, N, bits, cb, lsb_first, bias, y,
+                                   tiled != 0, s);
+  return launch_lp_bits<DT_F16>(x, M, K, packed, norms, N, bits, cb, lsb_first, bias, y,
+                                tiled != 0, s);
 }
 
 }  // namespace tq

@@ -55,13 +55,16 @@ hipError_t launch_orbit_linear(const float* x, int64_t M, int64_t K, const uint8
                                int lsb_first, const float* bias, float* y, hipStream_t s);
 // The same on bf16 / fp16 activations (dt = DT_BF16 or DT_F16): x, bias and y
 // of that format, W' products rounded to it, bf16 / fp16 matrix cores.
+// tiled: x is in the fragment layout of launch_orbit_rotate's tiled form
+// (64 <= K < 2^22).
 hipError_t launch_orbit_linear_lp(const void* x, int dt, int64_t M, int64_t K,
                                   const uint8_t* packed, const float* norms, int64_t N, int bits,
                                   const OrbitCodebook& cb, int lsb_first, const void* bias,
-                                  void* y, hipStream_t s);
+                                  void* y, int tiled, hipStream_t s);
+// tiled (bf16 / fp16): xrot in the fragment layout of the tiled linear layer
 hipError_t launch_orbit_rotate(const void* x, int dt, int64_t rows, int64_t d,
-                               const int32_t* perm, const int8_t* signs, void* xrot, int cus,
-                               hipStream_t s);
+                               const int32_t* perm, const int8_t* signs, void* xrot, int tiled,
+                               int cus, hipStream_t s);
 hipError_t launch_orbit_dequantize(const uint8_t* packed, const float* norms, int64_t rows,
                                    int64_t d, int bits, const int32_t* inv_perm,
                                    const int8_t* signs, const OrbitCodebook& cb,

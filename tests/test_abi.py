@@ -182,3 +182,33 @@ def test_orbit_dequantize_arguments_are_validated(tq):
                             out=torch.empty(rows, d))
     with pytest.raises(ValueError, match="bits"):
         tq.orbit_dequantize(packed, norms, d, 5, inv, sg, cb)
+
+
+def test_tiled_forward_arguments_are_validated(tq):
+    """orbit_rotate_tiled / orbit_linear_tiled reject bad arguments before any
+    GPU call, and orbit_tiled_bytes follows the layout's padding rule."""
+    import torch
+    d = 96
+    assert tq.orbit_tiled_bytes(1, d) == 16 * d * 2
+    assert tq.orbit_tiled_bytes(16, d) == 16 * d * 2
+    assert tq.orbit_tiled_bytes(17, d) == 32 * d * 2
+    assert tq.orbit_tiled_bytes(4, 48) == 0 and tq.orbit_tiled_bytes(4, 32768) == 0
+    assert tq.orbit_tiled_bytes(-1, d) == 0
+    perm, sg = torch.arange(d, dtype=torch.int32), torch.ones(d, dtype=torch.int8)
+    with pytest.raises(ValueError, match="bf16 or fp16"):
+        tq.orbit_rotate_tiled(torch.zeros(4, d), perm, sg)
+    with pytest.raises(ValueError, match="multiple of 32"):
+        tq.orbit_rotate_tiled(torch.zeros(4, 48, dtype=torch.bfloat16), perm[:48], sg[:48])
+    with pytest.raises(ValueError, match="out must be"):
+        tq.orbit_rotate_tiled(torch.zeros(4, d, dtype=torch.bfloat16), perm, sg,
+                              out=torch.empty(4 * d, dtype=torch.bfloat16))
+    pk = torch.zeros(8 * d * 2 // 8, dtype=torch.uint8)
+    nr = torch.ones(8)
+    xt = torch.zeros(tq.orbit_tiled_bytes(4, d) // 2, dtype=torch.bfloat16)
+    cb = [-1.0, -0.5, 0.5, 1.0]
+    with pytest.raises(ValueError, match="bf16 or fp16"):
+        tq.orbit_linear_tiled(xt.float(), 4, pk, nr, 2, cb)
+    with pytest.raises(ValueError, match="tiled"):
+        tq.orbit_linear_tiled(xt, 17, pk, nr, 2, cb)
+    with pytest.raises(ValueError, match="packed"):
+        tq.orbit_linear_tiled(xt, 4, pk[:-1], nr, 2, cb)

@@ -136,3 +136,21 @@ def test_attention_outputs(tq, n_tok, hkv, group):
         out2 = Guarded((hq, 128), odt)
         tq.tq3_decode_attention_noalloc(q, k, v, hkv, signs, dtype=odt, out=out2.t)
         out2.check("tq3_decode_attention_noalloc out")
+
+
+@pytest.mark.parametrize("m,d,n", [(1, 64, 40), (17, 96, 65), (300, 3072, 130), (33, 4096, 64)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_orbit_tiled_outputs(tq, m, d, n, dtype):
+    perm, sg = datagen.rpbh_params(d)
+    x = torch.randn(m, d, generator=torch.Generator().manual_seed(m + d)).to(dtype).to(DEV)
+    xt = Guarded((tq.orbit_tiled_bytes(m, d) // 2,), dtype)
+    tq.orbit_rotate_tiled(x, perm.to(DEV), sg.to(DEV), out=xt.t)
+    xt.check("orbit_rotate_tiled")
+    bits = 3
+    g = torch.Generator().manual_seed(n)
+    packed = torch.randint(0, 256, (n, d * bits // 8), generator=g, dtype=torch.uint8).to(DEV)
+    norms = (torch.rand(n, generator=g) + 0.5).to(DEV)
+    y = Guarded((m, n), dtype)
+    tq.orbit_linear_tiled(xt.t, m, packed, norms, bits, tq.orbit_make_codebook(bits, d),
+                          out=y.t)
+    y.check("orbit_linear_tiled")
