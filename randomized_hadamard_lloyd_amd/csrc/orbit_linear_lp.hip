@@ -278,8 +278,11 @@ __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
 // columns 8 (l / 16) .. + 7), so each wave loads its operands straight into
 // registers, whole cache lines per load, and x_rot never passes through LDS.
 // Each step's two halves load half a step apart (the next step's first half
-// at the start of a step, its second half into the registers of the first
-// half once those are consumed): 164 VGPRs, three waves per SIMD.
+// at the start of a step, its second half once the first half's MFMAs are
+// issued): 159-166 VGPRs, three waves per SIMD. The LDS left free also holds
+// pair tables for 3-bit codes (one table read per two codes; 68.7 -> 58.1 us
+// at 512 rows of the 12288 x 3072 layer). Unrolling three steps to rotate the
+// fragment registers instead of copying them spilled and ran 2.5x slower.
 constexpr int kTallBM = 256, kTallBN = 64;
 
 // One v_bfe_u32 per 3-bit field (left to itself the compiler shifts and
@@ -301,7 +304,9 @@ orbit_linear_lp_tall_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K
                             int64_t N, OrbitCodebook cb, const uint16_t* __restrict__ bias,
                             uint16_t* __restrict__ y) {
   constexpr int L = 1 << BITS;
-  constexpr bool PAIRS = BITS == 2;
+  // pair tables for 2-bit codes, and for 3-bit ones when x_rot does not take
+  // LDS (TILED): one read per two codes, already the packed dword
+  constexpr bool PAIRS = BITS == 2 || (TILED && BITS == 3);
   // dwords per row's table, padded by one so that rows start in different banks
   constexpr int TW = (PAIRS ? L * L : L / 2) + 1;
   __shared__ __attribute__((aligned(16))) char As[TILED ? 1 : 4][TILED ? 16 : 64 * 128];
