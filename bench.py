@@ -129,9 +129,16 @@ def rate(bytes_, ms):
     return bytes_ / (ms * 1e-3) / 1e9
 
 
-def source_hash():
+# the sources the TQ3 kernels are compiled from (the dominant kernel's
+# counters stay valid while these are unchanged)
+TQ3_SOURCES = ("tq3.hip", "tq_common.h", "tq_kernels.h")
+ALL_SOURCES = ("tq3.hip", "tq3_attn.hip", "orbit.hip", "orbit_linear.hip", "orbit_linear_lp.hip",
+               "orbit_codes.h", "tq_common.h", "tq_kernels.h", "libtq.cpp")
+
+
+def source_hash(files=TQ3_SOURCES):
     h = hashlib.sha256()
-    for f in ("tq3.hip", "orbit.hip", "tq_common.h", "tq_kernels.h", "libtq.cpp"):
+    for f in files:
         with open(os.path.join(ROOT, "randomized_hadamard_lloyd_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

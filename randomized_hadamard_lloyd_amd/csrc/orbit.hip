@@ -17,7 +17,8 @@
 //
 // NT = 1..4 are compiled for their exact wave count (256-thread launch
 // bounds); NT = 0 takes the wave count from the block size at run time, for
-// rows of 4097..16384 elements.
+// rows of 4097..16384 elements. Rows of up to 512 elements share a wave in
+// the quantize and rotation kernels: 64 / (d / 16) rows side by side.
 #include <atomic>
 
 #include "orbit_codes.h"
@@ -396,7 +397,7 @@ __device__ __forceinline__ uint32_t sign_of(uint32_t w, int k) {
 // (t * d / 32 + kc) * 1024, lane l's 16 bytes at l * 16 holding row
 // 16 t + l % 16, columns 32 kc + 8 (l / 16) .. + 7.
 template <int BITS, bool LSB, int NT, int HC, bool ROT = false, int DT = DT_F32,
-          bool SYM = true, bool TOUT = false>
+          bool SYM = true, bool TOUT = false, bool MR = false>
 __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
     const void* __restrict__ W, int64_t rows, int d, int log2h, float kh,
     const int32_t* __restrict__ perm, const int8_t* __restrict__ signs, OrbitCodebook cb,
@@ -404,9 +405,16 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
   static_assert(ROT || DT == DT_F32, "the weight codec reads fp32 rows");
   static_assert(!TOUT || (ROT && DT != DT_F32), "the tiled form holds bf16 / fp16 rotations");
   extern __shared__ float lds[];
-  float* rowbuf = lds;     // the row; later the cross-wave butterfly exchange
-  float* bsum = lds + d;   // block (or, for h > 1024, tile) sums of squares
-  float* xbuf = lds + d + kMaxBlocks;  // h > 1024: the wave-bit stages' exchange
+  // MR (one-wave blocks, rows of up to 512 elements): the wave takes
+  // R = 64 / (d / 16) rows at a time, side by side (lane chunk lc -> row
+  // lc / C, chunk lc % C, C = d / 16). A row's chunk count is a multiple of
+  // its h-block's, so every butterfly and block sum stays inside its row.
+  static_assert(!MR || (NT == 1 && HC == 0), "several rows per wave only for short rows");
+  const int C = d >> 4;
+  const int R = MR ? 64 / C : 1;
+  float* rowbuf = lds;              // the staged rows; later the cross-wave exchange
+  float* bsum = lds + R * d;        // block (or, for h > 1024, tile) sums of squares
+  float* xbuf = lds + d + kMaxBlocks;  // h > 1024 (R = 1): the wave-bit stages' exchange
   const int nwaves = block_waves<NT>();
   const int NTHR = 64 * nwaves;
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -414,8 +422,10 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int lc = lane_chunk(lane);
-  const int c = lc + 64 * wave;  // this lane's chunk of 16 elements
-  const bool act = c < (d >> 4);
+  const int grow = MR ? lc / C : 0;                 // row within the block's group
+  const int c = MR ? lc - grow * C : lc + 64 * wave;  // chunk of 16 elements in the row
+  const bool lane_ok = grow < R && c < C;
+  const int cw = MR ? lc : c;                       // chunk within the staged rows
   const int nblk = d >> log2h;
   constexpr bool FULL = HC > 0, SPAN = HC == 2;
   static_assert(!SPAN || NT == 0 || NT % 2 == 0, "h > 1024 needs an even wave count");
@@ -427,11 +437,14 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
   constexpr int ES = DT == DT_F32 ? 4 : 2;  // bytes per element of a row
   constexpr int KL = ES;                     // 16-byte loads per thread (d <= 1024 NT)
   const int nl = d * ES / 16;               // 16-byte pieces per row
+  const int nlg = R * nl;                   // ... per group of rows
 
   // Byte offsets into the staged row and sign masks of this lane's elements.
   uint32_t poff[16], sbits = 0;  // sbits: bit i set when signs_j = -1 for element i
   {
-    const int cc = act ? c : 0;  // inactive lanes read chunk 0 and never use it
+    // lanes past the rows read row 0's chunk 0 and never use it
+    const int cc = lane_ok ? c : 0;
+    const uint32_t roff = lane_ok ? 4u * (uint32_t)(grow * d) : 0u;
     const u32x4* pp = reinterpret_cast<const u32x4*>(perm + 16 * cc);
     const u32x4 sv = *reinterpret_cast<const u32x4*>(signs + 16 * cc);
 #pragma unroll
@@ -439,7 +452,7 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
       const u32x4 p = pp[k];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        poff[4 * k + e] = 4u * p[e];
+        poff[4 * k + e] = roff + 4u * p[e];
         sbits |= (sign_of(sv[k], e) >> 31) << (4 * k + e);
       }
     }
@@ -451,25 +464,40 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
   const char* Wb = static_cast<const char*>(W);
   const int64_t row_in = (int64_t)d * ES;
   u32x4 pre[KL];
-  int fidx[KL];
+  int frow[KL], fcol[KL];  // piece k of this thread: row of the group, piece in the row
 #pragma unroll
   for (int k = 0; k < KL; ++k) {
-    const int f = tid + NTHR * k;
-    fidx[k] = f < nl ? f : nl - 1;
+    const int f = tid + NTHR * k < nlg ? tid + NTHR * k : nlg - 1;
+    frow[k] = MR ? f / nl : 0;
+    fcol[k] = MR ? f - frow[k] * nl : f;
   }
-  int64_t r = blockIdx.x;
-  {
-    const u32x4* src = reinterpret_cast<const u32x4*>(Wb + (r < rows ? r : 0) * row_in);
-#pragma unroll
-    for (int k = 0; k < KL; ++k) pre[k] = src[fidx[k]];
-  }
-  // TOUT also covers the pad rows (their loads re-read row 0)
+  // TOUT also covers the pad rows (their loads re-read valid rows)
   const int64_t rows_loop = TOUT ? (rows + 15) / 16 * 16 : rows;
-  for (; r < rows_loop; r += gridDim.x) {
+  const int64_t ngroups = (rows_loop + R - 1) / R;
+  auto load_group = [&](int64_t gg) {
+    if constexpr (MR) {
+#pragma unroll
+      for (int k = 0; k < KL; ++k) {
+        int64_t rr = gg * R + frow[k];
+        rr = rr < rows ? rr : rows - 1;
+        pre[k] = reinterpret_cast<const u32x4*>(Wb + rr * row_in)[fcol[k]];
+      }
+    } else {  // gg < rows: one row, pieces past its end re-read its last one
+      const u32x4* src = reinterpret_cast<const u32x4*>(Wb + (gg < rows ? gg : rows - 1) * row_in);
+#pragma unroll
+      for (int k = 0; k < KL; ++k) pre[k] = src[fcol[k]];
+    }
+  };
+  int64_t g = blockIdx.x;
+  load_group(g < ngroups ? g : 0);
+  for (; g < ngroups; g += gridDim.x) {
+    const int64_t r = g * R + grow;  // this lane's row
+    // (one row per block: every iteration's row is in range)
+    const bool act = MR ? lane_ok && r < rows_loop : lane_ok;
 #pragma unroll
     for (int k = 0; k < KL; ++k) {
       const int f = tid + NTHR * k;
-      if (f < nl) {
+      if (f < nlg) {
         if constexpr (DT == DT_F32) {
           reinterpret_cast<u32x4*>(rowbuf)[f] = pre[k];
         } else {
@@ -495,12 +523,7 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
       }
     }
     __syncthreads();
-    {
-      const int64_t rn = r + gridDim.x < rows ? r + gridDim.x : 0;
-      const u32x4* src = reinterpret_cast<const u32x4*>(Wb + rn * row_in);
-#pragma unroll
-      for (int k = 0; k < KL; ++k) pre[k] = src[fidx[k]];
-    }
+    load_group(g + gridDim.x < ngroups ? g + gridDim.x : 0);
 
     // y_j = W[perm_j] * signs_j. Lanes past the row (d not a multiple of
     // 1024) gather chunk 0 too: their chunks form whole h-blocks of their
@@ -587,9 +610,10 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
     if (lb > 3) part = lane_sum<3>(part);
     if (lb > 4) part = lane_sum<4>(part);
     if (lb > 5) part = lane_sum<5>(part);
-    if (act && (c & ((1 << lb) - 1)) == 0) bsum[c >> lb] = part;  // one writer per block/tile
+    if (act && (cw & ((1 << lb) - 1)) == 0) bsum[cw >> lb] = part;  // one writer per block/tile
     __syncthreads();
-    const float norm = __builtin_sqrtf(row_sumsq<SPAN>(bsum, log2h, nblk));
+    const float norm =
+        __builtin_sqrtf(row_sumsq<SPAN>(MR ? bsum + (lane_ok ? grow : 0) * nblk : bsum, log2h, nblk));
     const float denom = norm + eps;
 
     // u = y / denom, correctly rounded: shared reciprocal while every nonzero
@@ -606,7 +630,7 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
     // Codes and packing (SYM: the codebook is mirror-symmetric).
     const uint64_t bytes = pack16<BITS, LSB, SYM>(y, cb);
     if (act) store_codes<BITS>(packed + r * row_bytes + 2 * BITS * c, bytes);
-    if (tid == 0) norms[r] = norm;
+    if (MR ? act && c == 0 : tid == 0) norms[r] = norm;
   }
 }
 
@@ -772,6 +796,9 @@ constexpr size_t orbit_lds(int d, bool span) {
   return (size_t)(d + kMaxBlocks + (span ? d : 0)) * sizeof(float);
 }
 inline int block_threads(int nt_tmpl, int nt) { return 64 * (nt_tmpl == 0 ? nt : nt_tmpl); }
+// Rows a one-wave block of the rotation / quantize kernel takes at a time
+// when rows are short (up to 512 elements): as many as fit the 64 lanes.
+inline int rows_per_group(int d) { return 64 / (d >> 4); }
 
 // Resident blocks per CU of one kernel instantiation, queried once per block
 // size (one size for NT = 1..4; one per wave count 5..16 for NT = 0) at the
@@ -788,19 +815,25 @@ int resident_cached(std::atomic<int> (&cache)[17], K kernel, int nt, bool span) 
   return v;
 }
 
-template <int BITS, bool LSB, int NT, int HC, bool SYM>
+template <int BITS, bool LSB, int NT, int HC, bool SYM, bool MR = false>
 hipError_t launch_q_sym(const float* W, int64_t rows, int d, int log2h, float kh,
                         const int32_t* perm, const int8_t* signs, const OrbitCodebook& cb,
                         uint8_t* packed, float* norms, int cus, hipStream_t s) {
-  auto kernel = orbit_quantize_kernel<BITS, LSB, NT, HC, false, DT_F32, SYM>;
-  const size_t shm = orbit_lds(d, HC == 2);
+  if constexpr (NT == 1 && HC == 0 && !MR) {
+    if (d <= 512)
+      return launch_q_sym<BITS, LSB, NT, HC, SYM, true>(W, rows, d, log2h, kh, perm, signs, cb,
+                                                        packed, norms, cus, s);
+  }
+  auto kernel = orbit_quantize_kernel<BITS, LSB, NT, HC, false, DT_F32, SYM, false, MR>;
   const int nt = (d + 1023) >> 10;
+  const int R = MR ? rows_per_group(d) : 1;
+  const size_t shm = orbit_lds(R * d, HC == 2);
   static std::atomic<int> cache[17];
   const int per_cu = resident_cached<NT>(cache, kernel, nt, HC == 2);
   // Twice the resident blocks: blocks that start later fall out of step with
   // the first ones, so loads and arithmetic of different blocks overlap
   // (2-4% on the 12288 x 3072 weight against a resident-sized grid).
-  const int grid = grid_size(rows, cus, per_cu * 2);
+  const int grid = grid_size((rows + R - 1) / R, cus, per_cu * 2);
   kernel<<<grid, block_threads(NT, nt), shm, s>>>(W, rows, d, log2h, kh, perm, signs, cb, packed,
                                                   norms, nullptr);
   return hipGetLastError();
@@ -887,15 +920,21 @@ hipError_t launch_dq_dt(int dt, int nt, const uint8_t* packed, const float* norm
   }
 }
 
-template <int NT, int HC, int DT, bool TOUT>
+template <int NT, int HC, int DT, bool TOUT, bool MR = false>
 hipError_t launch_rot(const void* x, int64_t rows, int d, int log2h, float kh,
                       const int32_t* perm, const int8_t* signs, void* xrot, int cus, hipStream_t s) {
-  auto kernel = orbit_quantize_kernel<2, false, NT, HC, true, DT, true, TOUT>;
-  const size_t shm = orbit_lds(d, HC == 2);
+  if constexpr (NT == 1 && HC == 0 && !MR) {
+    if (d <= 512)
+      return launch_rot<NT, HC, DT, TOUT, true>(x, rows, d, log2h, kh, perm, signs, xrot, cus, s);
+  }
+  auto kernel = orbit_quantize_kernel<2, false, NT, HC, true, DT, true, TOUT, MR>;
   const int nt = (d + 1023) >> 10;
+  const int R = MR ? rows_per_group(d) : 1;
+  const size_t shm = orbit_lds(R * d, HC == 2);
   static std::atomic<int> cache[17];
   const int per_cu = resident_cached<NT>(cache, kernel, nt, HC == 2);
-  const int grid = grid_size(TOUT ? (rows + 15) / 16 * 16 : rows, cus, per_cu);
+  const int64_t rows_loop = TOUT ? (rows + 15) / 16 * 16 : rows;
+  const int grid = grid_size((rows_loop + R - 1) / R, cus, per_cu);
   OrbitCodebook cb{};
   kernel<<<grid, block_threads(NT, nt), shm, s>>>(x, rows, d, log2h, kh, perm, signs, cb, nullptr,
                                                   nullptr, xrot);
