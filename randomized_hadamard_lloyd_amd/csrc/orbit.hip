@@ -18,7 +18,7 @@
 // NT = 1..4 are compiled for their exact wave count (256-thread launch
 // bounds); NT = 0 takes the wave count from the block size at run time, for
 // rows of 4097..16384 elements. Rows of up to 512 elements share a wave in
-// the quantize and rotation kernels: 64 / (d / 16) rows side by side.
+// all three kernels: 64 / (d / 16) rows side by side.
 #include <atomic>
 
 #include "orbit_codes.h"
@@ -668,51 +668,62 @@ __device__ __forceinline__ void store_group(void* out, int64_t j0, const float* 
 // re-read from LDS in that order -- through the inverse permutation when
 // the rotation is undone. The next row's codes and norm are loaded while the
 // current row is processed.
-template <int BITS, bool LSB, int DT, int NT, int HC>
+template <int BITS, bool LSB, int DT, int NT, int HC, bool MR = false>
 __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_dequantize_kernel(
     const uint8_t* __restrict__ packed, const float* __restrict__ norms, int64_t rows, int d,
     int log2h, float kh, const int32_t* __restrict__ inv_perm,
     const int8_t* __restrict__ signs, OrbitCodebook cb, int rotated_only,
     void* __restrict__ out) {
   extern __shared__ float lds[];
-  float* rowbuf = lds;  // d floats
+  // MR: as in the quantize kernel, a one-wave block takes R = 64 / (d / 16)
+  // short rows side by side (lane chunk lc -> row lc / C, chunk lc % C). The
+  // R rows are consecutive in memory, so the staged tile is stored as one
+  // flat run of R d elements; each row has its own norm, so the lanes
+  // multiply the codebook value by it (the same single rounding as a table
+  // of products).
+  static_assert(!MR || (NT == 1 && HC == 0), "several rows per wave only for short rows");
+  const int C = d >> 4;
+  const int R = MR ? 64 / C : 1;
+  float* rowbuf = lds;  // R d floats
   constexpr int EPS = DT == DT_F32 ? 4 : 8;
   constexpr int NG = 16 / EPS;  // 16-byte output groups per lane per tile
   constexpr int L = 1 << BITS;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  float* tab = lds + d + 16 * wave;  // this wave's codebook x row norm
+  float* tab = lds + R * d + 16 * wave;  // this wave's codebook x row norm (MR: codebook)
   const int lc = lane_chunk(lane);
-  const int c = lc + 64 * wave;
-  const bool act = c < (d >> 4);
+  const int grow = MR ? lc / C : 0;
+  const int c = MR ? lc - grow * C : lc + 64 * wave;
+  const bool lane_ok = grow < R && c < C;
+  const int cw = MR ? lc : c;  // chunk within the staged rows
   const LaneCx cx = lane_cx(lc, log2h);
   const float ksig = kh * cx.sigma;
   const int64_t row_bytes = (int64_t)d * BITS / 8;
 
   // Output groups of this lane and, when the rotation is undone, the byte
-  // offsets of their sources in the staged row and the signs of its chunk.
+  // offsets of their sources in the staged row(s) and the signs of its chunk.
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   int j0[NG];
-  bool gact[NG];
 #pragma unroll
-  for (int k = 0; k < NG; ++k) {
-    j0[k] = 1024 * wave + EPS * lane + 64 * EPS * k;
-    gact[k] = j0[k] < d;
-  }
+  for (int k = 0; k < NG; ++k) j0[k] = 1024 * wave + EPS * lane + 64 * EPS * k;
   uint32_t ioff[16], smask[16];
   if (!rotated_only) {
 #pragma unroll
     for (int k = 0; k < NG; ++k) {
-      const u32x4* ip = reinterpret_cast<const u32x4*>(inv_perm + (gact[k] ? j0[k] : 0));
+      // flat position j0 -> row j0 / d, column j0 % d (a group never straddles rows)
+      const int jr = MR ? j0[k] / d : 0;
+      const int jc = j0[k] - jr * d;
+      const bool ok = MR ? jr < R : jc < d;
+      const u32x4* ip = reinterpret_cast<const u32x4*>(inv_perm + (ok ? jc : 0));
 #pragma unroll
       for (int e4 = 0; e4 < EPS / 4; ++e4) {
         const u32x4 p = ip[e4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ioff[EPS * k + 4 * e4 + e] = 4u * p[e];
+        for (int e = 0; e < 4; ++e) ioff[EPS * k + 4 * e4 + e] = 4u * ((ok ? jr * d : 0) + p[e]);
       }
     }
-    const u32x4 sv = *reinterpret_cast<const u32x4*>(signs + 16 * (act ? c : 0));
+    const u32x4 sv = *reinterpret_cast<const u32x4*>(signs + 16 * (lane_ok ? c : 0));
 #pragma unroll
     for (int k = 0; k < 4; ++k)
 #pragma unroll
@@ -722,30 +733,39 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_dequantize_kernel(
     for (int i = 0; i < 16; ++i) ioff[i] = smask[i] = 0;
   }
 
-  int64_t r = blockIdx.x;
-  const int cc = act ? c : 0;
-  uint64_t ncodes = load_codes<BITS>(packed + (r < rows ? r : 0) * row_bytes + 2 * BITS * cc);
-  float nnorm = norms[r < rows ? r : 0];
-  for (; r < rows; r += gridDim.x) {
+  const int64_t ngroups = (rows + R - 1) / R;
+  int64_t g = blockIdx.x;
+  const int cc = lane_ok ? c : 0;
+  auto row_of = [&](int64_t gg) {
+    const int64_t rr = gg * R + (lane_ok ? grow : 0);
+    return rr < rows ? rr : rows - 1;
+  };
+  uint64_t ncodes = load_codes<BITS>(packed + row_of(g < ngroups ? g : 0) * row_bytes + 2 * BITS * cc);
+  float nnorm = norms[row_of(g < ngroups ? g : 0)];
+  if (MR && lane < L) tab[lane] = cb.cb[lane];
+  for (; g < ngroups; g += gridDim.x) {
+    const int64_t r = g * R;  // the group's first row
+    const int64_t nflat = (rows - r < R ? rows - r : R) * d;  // its elements
+    const bool act = lane_ok && r + grow < rows;
     const uint64_t codes = ncodes;
     const float norm = nnorm;
     {
-      const int64_t rn = r + gridDim.x < rows ? r + gridDim.x : r;
-      ncodes = load_codes<BITS>(packed + rn * row_bytes + 2 * BITS * cc);
-      nnorm = norms[rn];
+      const int64_t gn = g + gridDim.x < ngroups ? g + gridDim.x : g;
+      ncodes = load_codes<BITS>(packed + row_of(gn) * row_bytes + 2 * BITS * cc);
+      nnorm = norms[row_of(gn)];
     }
-    if (lane < L) tab[lane] = cb.cb[lane] * norm;
+    if (!MR && lane < L) tab[lane] = cb.cb[lane] * norm;
     __builtin_amdgcn_wave_barrier();
     uint32_t code[16];
     unpack16<BITS, LSB>(codes, code);
     float w[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) w[i] = tab[code[i]];
+    for (int i = 0; i < 16; ++i) w[i] = MR ? tab[code[i]] * norm : tab[code[i]];
 
     if (rotated_only) {
       // Stage this wave's tile in element order, re-read it in store order.
       if (act) {
-        f32x4_t* mine = reinterpret_cast<f32x4_t*>(rowbuf + 16 * c);
+        f32x4_t* mine = reinterpret_cast<f32x4_t*>(rowbuf + 16 * cw);
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           mine[k] = f32x4_t{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
@@ -753,7 +773,7 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_dequantize_kernel(
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int k = 0; k < NG; ++k)
-        if (gact[k]) store_group<DT>(out, r * d + j0[k], rowbuf + j0[k]);
+        if (j0[k] < nflat) store_group<DT>(out, r * d + j0[k], rowbuf + j0[k]);
       __builtin_amdgcn_wave_barrier();
       continue;
     }
@@ -764,7 +784,7 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_dequantize_kernel(
     if (HC == 2) span_stages<NT>(w, lds + d + kMaxBlocks, rowbuf, c, wave, log2h);
     __syncthreads();  // the row buffer is free
     if (act) {
-      f32x4_t* mine = reinterpret_cast<f32x4_t*>(rowbuf + 16 * c);
+      f32x4_t* mine = reinterpret_cast<f32x4_t*>(rowbuf + 16 * cw);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         float z[4];
@@ -778,7 +798,7 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_dequantize_kernel(
     const char* rb = reinterpret_cast<const char*>(rowbuf);
 #pragma unroll
     for (int k = 0; k < NG; ++k) {
-      if (!gact[k]) continue;
+      if (j0[k] >= nflat) continue;
       float o[EPS];
 #pragma unroll
       for (int e = 0; e < EPS; ++e) o[e] = *reinterpret_cast<const float*>(rb + ioff[EPS * k + e]);
@@ -874,19 +894,25 @@ hipError_t launch_q_nt(int nt, const float* W, int64_t rows, int d, int log2h, f
 #undef TQ_QN
 }
 
-template <int BITS, bool LSB, int DT, int NT, int HC>
+template <int BITS, bool LSB, int DT, int NT, int HC, bool MR = false>
 hipError_t launch_dq(const uint8_t* packed, const float* norms, int64_t rows, int d, int log2h,
                      float kh, const int32_t* inv_perm, const int8_t* signs,
                      const OrbitCodebook& cb, int rotated_only, void* out, int cus,
                      hipStream_t s) {
-  const size_t shm = orbit_lds(d, HC == 2);
+  if constexpr (NT == 1 && HC == 0 && !MR) {
+    if (d <= 512)
+      return launch_dq<BITS, LSB, DT, NT, HC, true>(packed, norms, rows, d, log2h, kh, inv_perm,
+                                                    signs, cb, rotated_only, out, cus, s);
+  }
+  auto kernel = orbit_dequantize_kernel<BITS, LSB, DT, NT, HC, MR>;
+  const int R = MR ? rows_per_group(d) : 1;
+  const size_t shm = orbit_lds(R * d, HC == 2);
   const int nt = (d + 1023) >> 10;
   static std::atomic<int> cache[17];
-  const int per_cu =
-      resident_cached<NT>(cache, orbit_dequantize_kernel<BITS, LSB, DT, NT, HC>, nt, HC == 2);
-  const int grid = grid_size(rows, cus, per_cu);
-  orbit_dequantize_kernel<BITS, LSB, DT, NT, HC><<<grid, block_threads(NT, nt), shm, s>>>(
-      packed, norms, rows, d, log2h, kh, inv_perm, signs, cb, rotated_only, out);
+  const int per_cu = resident_cached<NT>(cache, kernel, nt, HC == 2);
+  const int grid = grid_size((rows + R - 1) / R, cus, per_cu);
+  kernel<<<grid, block_threads(NT, nt), shm, s>>>(packed, norms, rows, d, log2h, kh, inv_perm,
+                                                  signs, cb, rotated_only, out);
   return hipGetLastError();
 }
 
