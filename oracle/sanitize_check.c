@@ -1,5 +1,5 @@
 /*
- * A driver that exercises every function of tq_oracle.c on small inputs held
+ * A test program that exercises every function of tq_oracle.c on small inputs held
  * in exactly sized heap buffers, for a build under AddressSanitizer and
  * UndefinedBehaviorSanitizer (tests/test_oracle_sanitizers.py builds and runs
  * it; any out-of-bounds access, leak or undefined operation ends the run with
