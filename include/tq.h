@@ -283,8 +283,8 @@ int orbit_linear_tiled(const void* x_tiled, int dtype, int64_t m, int64_t d_in,
  *   k_records,   device, n_tokens x n_kv_heads records of 56 bytes, token
  *   v_records    major (record t * n_kv_heads + j is token t of KV head j),
  *                8-byte aligned.
- *   n_tokens     >= 1, <= 2^31.
- *   n_q_heads / n_kv_heads must be 1, 2, 4 or 8 (n_kv_heads >= 1).
+ *   n_tokens     >= 1, <= 2^31, and n_tokens x n_kv_heads <= 2^31.
+ *   n_q_heads / n_kv_heads must be 1, 2, 4 or 8 (1 <= n_kv_heads <= 65535).
  *   sign_mask    host, 16 bytes, the mask the records were written with.
  *   workspace    device, at least tq3_attention_workspace_bytes(n_tokens,
  *                n_q_heads, n_kv_heads) bytes, 16-byte aligned; scratch for
@@ -314,7 +314,8 @@ size_t tq3_attention_workspace_bytes(int64_t n_tokens, int n_q_heads, int n_kv_h
  * ends). The call allocates nothing.
  *   Sizes whose partial results need more than that array
  *   (tq3_attention_workspace_bytes(n_tokens, n_q_heads, n_kv_heads) > 16 MiB;
- *   e.g. 32 query heads over about 250K tokens) return TQ_ERR_SCRATCH and
+ *   at most about 4 MiB up to 8192 query heads, whatever the token count, so
+ *   only sizes beyond about 31,000 query heads) return TQ_ERR_SCRATCH and
  *   enqueue nothing.
  *   Every call on a GPU shares that GPU's array: two calls that overlap in
  *   time on one GPU (on different streams, or from different threads without

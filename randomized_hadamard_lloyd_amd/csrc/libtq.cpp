@@ -317,7 +317,10 @@ int orbit_linear_tiled(const void* x_tiled, int dtype, int64_t m, int64_t d_in,
 }
 
 static bool attn_shape_ok(int64_t n_tok, int hq, int hkv) {
-  if (n_tok < 1 || n_tok > ((int64_t)1 << 31) || hkv < 1 || hq < hkv || hq % hkv != 0)
+  // hkv <= 65535: a lane's byte offset within a piece of 256 tokens' records
+  // is 32-bit; n_tok * hkv <= 2^31: the (chunk, KV head) blocks fit a 1D grid
+  if (n_tok < 1 || n_tok > ((int64_t)1 << 31) || hkv < 1 || hkv > 65535 || hq < hkv ||
+      hq % hkv != 0 || n_tok * hkv > ((int64_t)1 << 31))
     return false;
   const int g = hq / hkv;
   return g == 1 || g == 2 || g == 4 || g == 8;

@@ -18,13 +18,16 @@
 // elements 8r .. 8r+7, i.e. its 24 bits of each record's indices. A
 // 256-thread block (16 groups) handles one KV head over one chunk of tokens
 // for the G query heads that share that KV head, each group keeping a running
-// (max, sum, accumulator) per head (the online softmax). The block merges its
-// groups and writes one partial per head; a second kernel merges the chunks,
-// normalises, rotates back and stores.
+// (max, sum, accumulator) per head (the online softmax). A group's partial
+// scores are reduce-scattered over its lanes, so that each lane finishes one
+// score and its softmax step. The block merges its groups and writes one
+// partial per head; a second kernel merges the chunks, normalises, rotates
+// back and stores.
 #include "tq_common.h"
 #include "tq_kernels.h"
 
 #include <mutex>
+#include <utility>
 
 // Library-held partial results for tq3_decode_attention_noalloc: one copy per
 // GPU, alive until the process ends. Host code never passes this name to a
@@ -42,26 +45,6 @@ __device__ __forceinline__ float tq3_centroid_a(int k) {
   constexpr float c[8] = {(float)-0.9816, (float)-0.6168, (float)-0.3479, (float)-0.1129,
                           (float)0.1129,  (float)0.3479,  (float)0.6168,  (float)0.9816};
   return c[k];
-}
-
-// Sums over the 16-lane group, all in registers: DPP partners r ^ 1, r ^ 2
-// (quad sums), then r ^ 7 (row_half_mirror: the other quad of the 8-lane
-// half) and r ^ 15 (row_mirror: the other half). Every lane ends with the
-// same bits, because each pairwise sum is commutative. Four values at once,
-// one v_add_f32_dpp per step and value.
-// gfx9 needs two wait states between a VALU write of a register and a DPP
-// read of it (five after a VALU write of EXEC): the leading s_nop 4 covers
-// whatever precedes the block, and inside it each value is read again only
-// three instructions after its last write.
-#define TQ_DPP_STEP4(CTRL)                                                          \
-  "v_add_f32_dpp %0, %0, %0 " CTRL " row_mask:0xf bank_mask:0xf\n"                 \
-  "v_add_f32_dpp %1, %1, %1 " CTRL " row_mask:0xf bank_mask:0xf\n"                 \
-  "v_add_f32_dpp %2, %2, %2 " CTRL " row_mask:0xf bank_mask:0xf\n"                 \
-  "v_add_f32_dpp %3, %3, %3 " CTRL " row_mask:0xf bank_mask:0xf\n"
-__device__ __forceinline__ void group_allreduce4(float& a, float& b, float& c, float& d) {
-  asm volatile("s_nop 4\n" TQ_DPP_STEP4("quad_perm:[1,0,3,2]") TQ_DPP_STEP4("quad_perm:[2,3,0,1]")
-                   TQ_DPP_STEP4("row_half_mirror") TQ_DPP_STEP4("row_mirror")
-               : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
 }
 
 // Butterfly with the partner lane r ^ (1 << S): lower lane a + b, upper lane
@@ -100,6 +83,73 @@ __device__ __forceinline__ void group_fwht(float (&x)[8], int r) {
   for (int i = 0; i < 8; ++i) x[i] = lane_butterfly<2>(x[i], c2);
 #pragma unroll
   for (int i = 0; i < 8; ++i) x[i] = lane_butterfly<3>(x[i], c3);
+}
+
+// Cross-lane reads inside a 16-lane group. The reduction partners of lane r
+// are r ^ 1, r ^ 2 (quad_perm), r ^ 7 (row_half_mirror) and r ^ 15
+// (row_mirror). In the basis (1, 2, 7, 15) of the lane index, step k's
+// partner flips coordinate k alone; that coordinate vector is the lane's
+// label: c3 = r3, c2 = r2 ^ r3, c1 = r1 ^ r2, c0 = r0 ^ r2.
+template <int K>
+__device__ __forceinline__ float group_partner(float v) {
+  constexpr int ctrl = K == 0 ? 0xB1 : K == 1 ? 0x4E : K == 2 ? 0x141 : 0x140;
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               ctrl, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ int group_label(int r) {
+  const int r0 = r & 1, r1 = (r >> 1) & 1, r2 = (r >> 2) & 1, r3 = (r >> 3) & 1;
+  return (r0 ^ r2) | ((r1 ^ r2) << 1) | ((r2 ^ r3) << 2) | (r3 << 3);
+}
+
+// The lane whose label is l: l0 * 1 ^ l1 * 2 ^ l2 * 7 ^ l3 * 15.
+constexpr int group_lane_of_label(int l) {
+  return ((l & 1) ? 1 : 0) ^ ((l & 2) ? 2 : 0) ^ ((l & 4) ? 7 : 0) ^ ((l & 8) ? 15 : 0);
+}
+
+// Value v of lane LANE of this lane's 16-lane group (row_newbcast).
+template <int LANE>
+__device__ __forceinline__ float group_bcast(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               0x150 + LANE, 0xF, 0xF, true));
+}
+
+// Group sums of S partial values (S = 4, 8, 16), scattered by label: a lane
+// with label c enters value f at position f ^ (c % S) and returns the group
+// sum of value c % S. Step k (k < log2 S) pairs positions 2i and 2i + 1: the
+// even one holds a value whose index bit k is the lane's own label bit k,
+// and the partner (label bit k flipped) holds that same value at the odd
+// position, so one DPP add per pair keeps it and halves the array, which
+// then again holds value f at position (f >> (k + 1)) ^ (c % S >> (k + 1)).
+// For S < 16 the remaining steps are plain sums with partners that hold the
+// same value, so the 16 / S copies of each sum are identical.
+template <int S>
+__device__ __forceinline__ float group_reduce_scatter(float (&v)[S]) {
+  static_assert(S == 4 || S == 8 || S == 16, "4, 8 or 16 values");
+#pragma unroll
+  for (int j = 0; j < S / 2; ++j) v[j] = v[2 * j] + group_partner<0>(v[2 * j + 1]);
+#pragma unroll
+  for (int j = 0; j < S / 4; ++j) v[j] = v[2 * j] + group_partner<1>(v[2 * j + 1]);
+  if constexpr (S >= 8) {
+#pragma unroll
+    for (int j = 0; j < S / 8; ++j) v[j] = v[2 * j] + group_partner<2>(v[2 * j + 1]);
+  } else {
+    v[0] = v[0] + group_partner<2>(v[0]);
+  }
+  if constexpr (S == 16) v[0] = v[0] + group_partner<3>(v[1]);
+  else v[0] = v[0] + group_partner<3>(v[0]);
+  return v[0];
+}
+
+// f(integral_constant<0>), ..., f(integral_constant<N-1>): unrolled with the
+// index usable as a template argument.
+template <class F, int... I>
+__device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void unroll(F&& f) {
+  unroll_seq(f, std::make_integer_sequence<int, N>{});
 }
 
 // Sign of element j = 8r + i from the 128-bit mask (the word is selected
@@ -148,8 +198,8 @@ constexpr int kPartFloats = 132;
 constexpr int kAttnGroups = 16;        // 16-lane groups per 256-thread block
 constexpr int kAttnTokPerGroup = 16;   // token slots per group: pieces of up to 256 tokens
 #ifndef ATTN_TB
-// tokens per iteration sharing one max update (4 heads: 34.6 -> 32.1 us over
-// 2 tokens on the 32768-token layer, at 168 VGPRs, still three waves a SIMD)
+// tokens per iteration sharing one max update: G TB = 4, 8 or 16 scores,
+// reduce-scattered over a group's 16 lanes
 #define ATTN_TB(G) ((G) <= 4 ? 4 : 2)
 #endif
 #ifndef ATTN_WIN
@@ -158,39 +208,42 @@ constexpr int kAttnTokPerGroup = 16;   // token slots per group: pieces of up to
 #define ATTN_WIN(G) ((G) <= 2 ? 8 : 4)
 #endif
 
-template <int QDT, int G>
+// MULTI: chunks of more than one piece (256 tokens); the single-piece
+// instantiation keeps fewer registers live.
+template <int QDT, int G, bool MULTI>
 __global__ __launch_bounds__(256) void tq3_attn_partial_kernel(
     const void* __restrict__ q, const uint8_t* __restrict__ krec,
     const uint8_t* __restrict__ vrec, int64_t n_tok, int hkv, SignMask mask, float qscale,
-    int chunk, float* __restrict__ ws) {
+    int chunk, int nchunk, float* __restrict__ ws) {
   __shared__ float2 ctab[64];  // (C[p & 7], C[p >> 3]): two consecutive elements' values
   __shared__ __attribute__((aligned(16))) float red_m[G][16];
   __shared__ __attribute__((aligned(16))) float red_l[G][16];
   // Per wave, its groups' records: [token k][K, V][group in wave][16 dwords]
-  // (14 used). Reused by the final merge of the groups' accumulators.
+  // (14 used). Also holds the rotated queries before the loop and the
+  // groups' weighted accumulators in the final merge.
   __shared__ __attribute__((aligned(16))) uint32_t stage[4][kAttnTokPerGroup][2][4][16];
-  static_assert(sizeof(stage) >= 16 * 132 * sizeof(float), "merge buffer fits the staging area");
-  float (*red_acc)[132] = reinterpret_cast<float (*)[132]>(&stage[0][0][0][0][0]);
-  const int kv = blockIdx.y;
-  const int nchunk = gridDim.x;
+  // (chunk, KV head) pairs in row-major runs per XCD: the blocks that read
+  // the same cache lines of the token-major records (the KV heads of one
+  // token) share an L2.
+  int kv, ch;
+  if (!xcd_tile(hkv, nchunk, kv, ch)) return;
   const int grp = threadIdx.x >> 4, r = threadIdx.x & 15;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (threadIdx.x < 64)
     ctab[threadIdx.x] = make_float2(tq3_centroid_a(threadIdx.x & 7), tq3_centroid_a(threadIdx.x >> 3));
   __syncthreads();  // ctab
 
-  // The G heads' query elements 8r .. 8r+7 of lane r, loaded before the
-  // records so that waiting for them never waits for the record copies.
-  uint4 qraw[G][2];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const int64_t off = (int64_t)(kv * G + h) * 128 + 8 * r;
+  // Group g < G rotates query head g: lane r loads its elements 8r .. 8r+7
+  // before the records, so that waiting for them never waits for the record
+  // copies.
+  uint4 qraw[2] = {};
+  if (grp < G) {
+    const int64_t off = (int64_t)(kv * G + grp) * 128 + 8 * r;
     if constexpr (QDT == DT_F32) {
-      qraw[h][0] = *reinterpret_cast<const uint4*>(static_cast<const float*>(q) + off);
-      qraw[h][1] = *reinterpret_cast<const uint4*>(static_cast<const float*>(q) + off + 4);
+      qraw[0] = *reinterpret_cast<const uint4*>(static_cast<const float*>(q) + off);
+      qraw[1] = *reinterpret_cast<const uint4*>(static_cast<const float*>(q) + off + 4);
     } else {
-      qraw[h][0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + off);
-      qraw[h][1] = qraw[h][0];
+      qraw[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + off);
     }
   }
 
@@ -204,70 +257,112 @@ __global__ __launch_bounds__(256) void tq3_attn_partial_kernel(
   // slots it reaches while the next ones stay in flight. (Copies straight
   // into LDS would not overlap: the compiler waits for every such copy
   // before any later LDS read.)
-  const int64_t c0 = (int64_t)blockIdx.x * chunk;
+  const int64_t c0 = (int64_t)ch * chunk;
   const int64_t c1 = c0 + chunk < n_tok ? c0 + chunk : n_tok;
   constexpr int kPiece = kAttnGroups * kAttnTokPerGroup;
   int64_t t0 = c0, t1 = c0 + kPiece < c1 ? c0 + kPiece : c1;
   constexpr int kAttnWin = ATTN_WIN(G);
   uint32_t kraw[kAttnWin], vraw[kAttnWin];
   const int rd = (lane & 15) < 14 ? (lane & 15) : 13;
+  // Record addresses: a base at the piece's first token (uniform) plus a
+  // 32-bit byte offset per lane (at most 255 tokens x 65535 KV heads x 56
+  // bytes). Slots past the lane's last token of the piece re-read that
+  // token's record (token t0's, if it has none); such slots are never used.
+  const uint32_t rstride = (uint32_t)hkv * 56u;  // bytes from a token's record to the next
+  const uint32_t lane_tok = 4 * wave + (lane >> 4);  // this lane's token within a slot
+  const uint8_t* kb;
+  const uint8_t* vb;
+  uint32_t soff0, omax;
+  auto set_piece = [&]() {
+    kb = krec + (t0 * hkv + kv) * 56;
+    vb = vrec + (t0 * hkv + kv) * 56;
+    const uint32_t ntk = (uint32_t)(t1 - t0);  // 1 .. 256
+    const uint32_t nval = lane_tok < ntk ? (ntk - lane_tok + 15) / 16 : 0;
+    soff0 = lane_tok * rstride + 4 * rd;
+    omax = nval > 0 ? soff0 + (nval - 1) * 16u * rstride : 4u * rd;
+  };
   auto load_slot = [&](int k) {
-    const int64_t t = t0 + 4 * wave + (lane >> 4) + (int64_t)kAttnGroups * k;
-    const int64_t rec = (t < t1 ? t : t0) * hkv + kv;
-    kraw[k % kAttnWin] = *reinterpret_cast<const uint32_t*>(krec + rec * 56 + 4 * rd);
-    vraw[k % kAttnWin] = *reinterpret_cast<const uint32_t*>(vrec + rec * 56 + 4 * rd);
+    uint32_t o = soff0 + (uint32_t)k * 16u * rstride;
+    o = o < omax ? o : omax;
+    kraw[k % kAttnWin] = *reinterpret_cast<const uint32_t*>(kb + o);
+    vraw[k % kAttnWin] = *reinterpret_cast<const uint32_t*>(vb + o);
     // keeps the loads in slot order, as the loop's waits assume
     asm volatile("" ::: "memory");
   };
+  set_piece();
 #pragma unroll
   for (int k = 0; k < kAttnWin; ++k) load_slot(k);
 
-  // Rotated queries: lane r keeps elements 8r .. 8r+7.
-  float qr[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
+  // Rotated query head grp (groups below G): lane r's elements 8r .. 8r+7.
+  float* qs = reinterpret_cast<float*>(&stage[0][0][0][0][0]);  // [G][128] rotated queries
+  if (grp < G) {
+    float x[8];
     if constexpr (QDT == DT_F32) {
-      const uint4 a = qraw[h][0], b = qraw[h][1];
-      qr[h][0] = as_f(a.x); qr[h][1] = as_f(a.y); qr[h][2] = as_f(a.z); qr[h][3] = as_f(a.w);
-      qr[h][4] = as_f(b.x); qr[h][5] = as_f(b.y); qr[h][6] = as_f(b.z); qr[h][7] = as_f(b.w);
+      const uint4 a = qraw[0], b = qraw[1];
+      x[0] = as_f(a.x); x[1] = as_f(a.y); x[2] = as_f(a.z); x[3] = as_f(a.w);
+      x[4] = as_f(b.x); x[5] = as_f(b.y); x[6] = as_f(b.z); x[7] = as_f(b.w);
     } else {
-      const uint4 a = qraw[h][0];
+      const uint4 a = qraw[0];
       const uint32_t w[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         if constexpr (QDT == DT_BF16) {
-          qr[h][2 * p] = as_f(w[p] << 16);
-          qr[h][2 * p + 1] = as_f(w[p] & 0xffff0000u);
+          x[2 * p] = as_f(w[p] << 16);
+          x[2 * p + 1] = as_f(w[p] & 0xffff0000u);
         } else {
-          qr[h][2 * p] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[p] & 0xffffu));
-          qr[h][2 * p + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[p] >> 16));
+          x[2 * p] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[p] & 0xffffu));
+          x[2 * p + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[p] >> 16));
         }
       }
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (mask_bit(mask, r, i)) qr[h][i] = -qr[h][i];
-    group_fwht(qr[h], r);
+      if (mask_bit(mask, r, i)) x[i] = -x[i];
+    group_fwht(x, r);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) qr[h][i] = qr[h][i] * qscale;
+    for (int i = 0; i < 8; i += 4)
+      *reinterpret_cast<float4*>(qs + grp * 128 + 8 * r + i) =
+          make_float4(x[i] * qscale, x[i + 1] * qscale, x[i + 2] * qscale, x[i + 3] * qscale);
   }
+
+  // Token slots k = 0, 1, ... of this group (token t0 + grp + 16 k), TB per
+  // iteration. The S = G TB scores of an iteration (index h TB + u) are
+  // reduce-scattered over the group by lane label c: the lane finishes score
+  // c % S (head hl, token ul) and scales, masks and exponentiates it alone;
+  // a head's maximum and sum are over the TB lanes whose labels differ in
+  // the low bits, and each weight reaches the value FMAs of every lane by a
+  // broadcast from the lane that holds it. For S < 16 the merge reads the
+  // lanes with labels below S (the other copies are identical).
+  constexpr int TB = ATTN_TB(G);
+  constexpr int S = G * TB;
+  static_assert(TB == 2 || TB == 4, "a head's tokens are neighbours in the label");
+  const int lab = group_label(r) & (S - 1);
+  const int hl = lab / TB, ul = lab % TB;
+  const bool first_copy = group_label(r) < S;
+
+  // The rotated queries in this lane's order: position h' holds head
+  // h' ^ hl, so that partial score h' TB + u' is value (h' TB + u') ^ lab
+  // (the tokens are permuted the same way when read from LDS).
+  float qr[G][8];
+  __syncthreads();  // qs
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int i = 0; i < 8; i += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(qs + (h ^ hl) * 128 + 8 * r + i);
+      qr[h][i] = a.x; qr[h][i + 1] = a.y; qr[h][i + 2] = a.z; qr[h][i + 3] = a.w;
+    }
+  __syncthreads();  // before the loop's first slot writes
 
   const int dsel = (3 * r) >> 2;
   const uint32_t shift = (24u * r) & 31u;
-  float m[G], l[G], acc[G][8];
+  float m_own = -__builtin_inff(), l_own = 0.0f, acc[G][8];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -__builtin_inff();
-    l[h] = 0.0f;
+  for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[h][i] = 0.0f;
-  }
   const char* tb = reinterpret_cast<const char*>(ctab);
   const uint32_t* my = &stage[wave][0][0][grp & 3][0];
-  // Token slots k = 0, 1, ... of this group (token t0 + grp + 16 k), TB per
-  // iteration; the TB scores of each head share one max update. TB shrinks
-  // with G to keep the registers of G heads in budget.
-  constexpr int TB = ATTN_TB(G);
   for (;;) {
     const int nk = (int)((t1 - t0 + kAttnGroups - 1) / kAttnGroups);  // token slots per group
     // this group's tokens: the first nkg slots (groups differ by at most one)
@@ -285,129 +380,144 @@ __global__ __launch_bounds__(256) void tq3_attn_partial_kernel(
         if (k0 + u + kAttnWin < kAttnTokPerGroup) load_slot(k0 + u + kAttnWin);
       }
       const int64_t tb0 = t0 + grp + (int64_t)kAttnGroups * k0;
-      RecPart kp[TB], vp[TB];
-#pragma unroll
-      for (int u = 0; u < TB; ++u) {
-        const int ku = k0 + u < nk ? k0 + u : nk - 1;  // a loaded slot (finite values)
-        kp[u] = lds_part(my + ku * 128, dsel);
-        vp[u] = lds_part(my + ku * 128 + 64, dsel);
-      }
-      // scores (base-2 logits); -inf for the tokens past the end
-      float sc[G][TB];
+      // a loaded slot for token u of the iteration (finite values)
+      auto slot = [&](int u) { return k0 + u < nk ? k0 + u : nk - 1; };
+      // partial scores of this lane's 8 elements, in its order, then its
+      // own score in base-2 logits (-inf past the end)
+      float s;
       {
-        float ck[TB][8];
-#pragma unroll
-        for (int u = 0; u < TB; ++u) decode8(kp[u], shift, tb, ck[u]);
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-          for (int u = 0; u < TB; ++u) {
-            float dot = qr[h][0] * ck[u][0];
-#pragma unroll
-            for (int i = 1; i < 8; ++i) dot = __builtin_fmaf(qr[h][i], ck[u][i], dot);
-            sc[h][u] = dot;
-          }
-        static_assert((G * TB) % 4 == 0, "scores reduce four at a time");
-        float* flat = &sc[0][0];
-#pragma unroll
-        for (int k = 0; k < G * TB; k += 4) group_allreduce4(flat[k], flat[k + 1], flat[k + 2], flat[k + 3]);
+        float sc[S];
 #pragma unroll
         for (int u = 0; u < TB; ++u) {
-          const bool valid = tb0 + kAttnGroups * u < t1;
-          const float wk = as_f(kp[u].ns.x) * as_f(kp[u].ns.y);
+          float ck[8];
+          decode8(lds_part(my + slot(u ^ ul) * 128, dsel), shift, tb, ck);
 #pragma unroll
-          for (int h = 0; h < G; ++h) sc[h][u] = valid ? sc[h][u] * wk : -__builtin_inff();
+          for (int h = 0; h < G; ++h) {
+            float dot = qr[h][0] * ck[0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) dot = __builtin_fmaf(qr[h][i], ck[i], dot);
+            sc[h * TB + u] = dot;
+          }
         }
+        s = group_reduce_scatter<S>(sc);
+        const uint2 kns = *reinterpret_cast<const uint2*>(my + slot(ul) * 128 + 12);
+        const bool valid = tb0 + kAttnGroups * ul < t1;
+        s = valid ? s * (as_f(kns.x) * as_f(kns.y)) : -__builtin_inff();
       }
-      // online softmax: one max update per head for the four tokens
+      // online softmax: the head's maximum over its TB tokens; one update
+      float bm = __builtin_amdgcn_fmed3f(s, group_partner<0>(s), __builtin_inff());
+      if constexpr (TB == 4) bm = __builtin_amdgcn_fmed3f(bm, group_partner<1>(bm), __builtin_inff());
+      if (__builtin_amdgcn_ballot_w64(bm > m_own)) {
+        // some group of the wave has a new maximum: rescale (corr = 1 elsewhere)
+        const float mn = __builtin_amdgcn_fmed3f(m_own, bm, __builtin_inff());
+        const float corr = __builtin_amdgcn_exp2f(m_own - mn);
+        l_own = l_own * corr;
+        m_own = mn;
+        unroll<G>([&](auto hc) {
+          constexpr int h = decltype(hc)::value;
+          const float c = group_bcast<group_lane_of_label(h * TB)>(corr);
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float bm = sc[h][0];
-#pragma unroll
-        for (int u = 1; u < TB; ++u) bm = __builtin_fmaxf(bm, sc[h][u]);
-        if (__builtin_amdgcn_ballot_w64(bm > m[h])) {
-          // some group of the wave has a new maximum: rescale (corr = 1 elsewhere)
-          const float mn = __builtin_fmaxf(m[h], bm);
-          const float corr = __builtin_amdgcn_exp2f(m[h] - mn);
-          l[h] = l[h] * corr;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[h][i] = acc[h][i] * corr;
-          m[h] = mn;
-        }
-#pragma unroll
-        for (int u = 0; u < TB; ++u) sc[h][u] = __builtin_amdgcn_exp2f(sc[h][u] - m[h]);  // p (0 past the end)
+          for (int i = 0; i < 8; ++i) acc[h][i] = acc[h][i] * c;
+        });
       }
-      // values
-#pragma unroll
-      for (int u = 0; u < TB; ++u) {
+      const float p = __builtin_amdgcn_exp2f(s - m_own);  // 0 past the end
+      l_own = l_own + p;
+      const uint2 vns = *reinterpret_cast<const uint2*>(my + slot(ul) * 128 + 64 + 12);
+      const float pw = p * (as_f(vns.x) * as_f(vns.y));
+      // values: every lane's 8 elements of each token, weights from their lanes
+      unroll<TB>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
         float cv[8];
-        decode8(vp[u], shift, tb, cv);
-        const float wv = as_f(vp[u].ns.x) * as_f(vp[u].ns.y);
+        decode8(lds_part(my + slot(u) * 128 + 64, dsel), shift, tb, cv);
+        unroll<G>([&](auto hc) {
+          constexpr int h = decltype(hc)::value;
+          const float w = group_bcast<group_lane_of_label(h * TB + u)>(pw);
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          l[h] = l[h] + sc[h][u];
-          const float pw = sc[h][u] * wv;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[h][i] = __builtin_fmaf(pw, cv[i], acc[h][i]);
-        }
-      }
+          for (int i = 0; i < 8; ++i) acc[h][i] = __builtin_fmaf(w, cv[i], acc[h][i]);
+        });
+      });
       // keeps the next iteration's slot writes (and so the waits for their
       // loads) from moving up into this one
       asm volatile("" ::: "memory");
     }
     // the next piece of the chunk (its slots reuse this wave's LDS rows, which
-    // its own reads above have finished with); chunks of up to 4 heads per KV
-    // head are a single piece
-    if constexpr (G <= 4) break;
+    // its own reads above have finished with)
+    if constexpr (!MULTI) break;
     t0 = t1;
     if (t0 >= c1) break;
     t1 = t0 + kPiece < c1 ? t0 + kPiece : c1;
+    set_piece();
 #pragma unroll
     for (int k = 0; k < kAttnWin; ++k) load_slot(k);
   }
 
-  // Merge the 16 groups: weights 2^(m_g - M); groups that saw no token have
-  // m = -inf and weigh 0.
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    if (r == 0) {
-      red_m[h][grp] = m[h];
-      red_l[h][grp] = l[h];
-    }
+  // Merge the 16 groups: weights 2^(m_g - M), zero for groups that saw no
+  // token (m = -inf). Up to four heads per pass: the pass's weighted
+  // accumulators fill the staging area, then thread t sums outputs
+  // t, t + 256, ... over the groups in group order, and the 16 lanes of row
+  // hh sum head hh's softmax terms.
+  float lh = l_own + group_partner<0>(l_own);  // each head's softmax sum over its TB lanes
+  if constexpr (TB == 4) lh = lh + group_partner<1>(lh);
+  if (first_copy && ul == 0) {
+    red_m[hl][grp] = m_own;
+    red_l[hl][grp] = lh;
   }
   __syncthreads();
+  constexpr int HP = G < 4 ? G : 4;  // heads per pass
+  float* red = reinterpret_cast<float*>(&stage[0][0][0][0][0]);  // [HP][16 groups][128]
+  static_assert(sizeof(stage) >= HP * 16 * 128 * sizeof(float), "a pass fits the staging area");
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float mg[16], lg[16];
+  for (int h0 = 0; h0 < G; h0 += HP) {
+    if (h0 > 0) __syncthreads();  // the previous pass's reads of red
+    float mx[HP];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float4 a = reinterpret_cast<const float4*>(red_m[h])[k];
-      const float4 b = reinterpret_cast<const float4*>(red_l[h])[k];
-      mg[4 * k] = a.x; mg[4 * k + 1] = a.y; mg[4 * k + 2] = a.z; mg[4 * k + 3] = a.w;
-      lg[4 * k] = b.x; lg[4 * k + 1] = b.y; lg[4 * k + 2] = b.z; lg[4 * k + 3] = b.w;
-    }
-    float mx = mg[0];
+    for (int hh = 0; hh < HP; ++hh) {
+      const int h = h0 + hh;
+      float mg[16];
 #pragma unroll
-    for (int g = 1; g < 16; ++g) mx = __builtin_fmaxf(mx, mg[g]);
-    const float f = m[h] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m[h] - mx);
+      for (int k = 0; k < 4; ++k) {
+        const float4 v = reinterpret_cast<const float4*>(red_m[h])[k];
+        mg[4 * k] = v.x; mg[4 * k + 1] = v.y; mg[4 * k + 2] = v.z; mg[4 * k + 3] = v.w;
+      }
+      mx[hh] = mg[0];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) red_acc[grp][8 * r + i] = acc[h][i] * f;
-    __syncthreads();
-    float* part = ws + ((int64_t)(kv * G + h) * nchunk + blockIdx.x) * kPartFloats;
-    if (threadIdx.x < 128) {
-      float a = red_acc[0][threadIdx.x];
-#pragma unroll
-      for (int g = 1; g < 16; ++g) a = a + red_acc[g][threadIdx.x];
-      part[4 + threadIdx.x] = a;
-    } else if (threadIdx.x == 128) {
-      float sl = 0.0f;
-#pragma unroll
-      for (int g = 0; g < 16; ++g)
-        sl = sl + (mg[g] == -__builtin_inff() ? 0.0f : lg[g] * __builtin_amdgcn_exp2f(mg[g] - mx));
-      part[0] = mx;
-      part[1] = sl;
+      for (int g = 1; g < 16; ++g) mx[hh] = __builtin_fmaxf(mx[hh], mg[g]);
+      const float mh = red_m[h][grp];  // this group's maximum for head h
+      const float f = mh == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mh - mx[hh]);
+      float* dst = red + (hh * 16 + grp) * 128 + 8 * r;
+      *reinterpret_cast<float4*>(dst) =
+          make_float4(acc[h][0] * f, acc[h][1] * f, acc[h][2] * f, acc[h][3] * f);
+      *reinterpret_cast<float4*>(dst + 4) =
+          make_float4(acc[h][4] * f, acc[h][5] * f, acc[h][6] * f, acc[h][7] * f);
     }
     __syncthreads();
+#pragma unroll
+    for (int o = threadIdx.x; o < HP * 128; o += 256) {
+      const int hh = o >> 7, e = o & 127;
+      const float* src = red + hh * 16 * 128 + e;
+      float a = src[0];
+#pragma unroll
+      for (int g = 1; g < 16; ++g) a = a + src[g * 128];
+      ws[((int64_t)(kv * G + h0 + hh) * nchunk + ch) * kPartFloats + 4 + e] = a;
+    }
+    if (threadIdx.x < 16 * HP) {
+      const int hh = threadIdx.x >> 4;  // one 16-lane row per head; lane r: group r
+      float mxh = mx[0];
+#pragma unroll
+      for (int k = 1; k < HP; ++k)
+        if (hh == k) mxh = mx[k];
+      const float m = red_m[h0 + hh][r];
+      float t = m == -__builtin_inff() ? 0.0f : red_l[h0 + hh][r] * __builtin_amdgcn_exp2f(m - mxh);
+      t = t + group_partner<0>(t);
+      t = t + group_partner<1>(t);
+      t = t + group_partner<2>(t);
+      t = t + group_partner<3>(t);
+      if (r == 0) {
+        float* part = ws + ((int64_t)(kv * G + h0 + hh) * nchunk + ch) * kPartFloats;
+        part[0] = mxh;
+        part[1] = t;
+      }
+    }
   }
 }
 
@@ -510,8 +620,12 @@ template <int QDT, int G>
 hipError_t launch_partial(const void* q, const uint8_t* k, const uint8_t* v, int64_t n_tok,
                           int hkv, const SignMask& m, float qscale, int chunk, int nchunk,
                           float* ws, hipStream_t s) {
-  tq3_attn_partial_kernel<QDT, G><<<dim3(nchunk, hkv), 256, 0, s>>>(q, k, v, n_tok, hkv, m,
-                                                                     qscale, chunk, ws);
+  if (chunk <= kAttnGroups * kAttnTokPerGroup)
+    tq3_attn_partial_kernel<QDT, G, false><<<xcd_grid(hkv, nchunk), 256, 0, s>>>(
+        q, k, v, n_tok, hkv, m, qscale, chunk, nchunk, ws);
+  else
+    tq3_attn_partial_kernel<QDT, G, true><<<xcd_grid(hkv, nchunk), 256, 0, s>>>(
+        q, k, v, n_tok, hkv, m, qscale, chunk, nchunk, ws);
   return hipGetLastError();
 }
 
@@ -530,21 +644,23 @@ hipError_t launch_partial_g(int g, const void* q, const uint8_t* k, const uint8_
 }  // namespace
 
 AttnPlan tq3_attention_plan(int64_t n_tok, int hkv, int g) {
-  // About four blocks per CU of a 256-CU part up to 4 heads per KV head
-  // (with 2 or 4 heads only three fit at once, but chunks sized for three
-  // measured no faster), chunks of at most 256 tokens (one piece); two
-  // blocks per CU at 8 heads, where the registers allow two and one round of
-  // longer chunks beats two rounds; at least one token per group (16 per
-  // chunk); chunks are multiples of 16 tokens.
-  AttnPlan p;
-  const int64_t target = 256 * (g <= 4 ? 4 : 2);
-  int64_t nch = target / hkv;
+  // One round of blocks over a 256-CU part: about 1024 (four per CU, as LDS
+  // allows) up to 4 heads per KV head, when that gives chunks of at most one
+  // piece (256 tokens); longer caches take 768 (three per CU) with chunks of
+  // several pieces, so fewer blocks pay the query rotation and the merge.
+  // Two per CU (512) at 8 heads, where the registers allow two. At least one
+  // token per group (16 per chunk); chunks are multiples of 16 tokens.
   const int64_t max_ch = (n_tok + 15) / 16;
-  if (nch > max_ch) nch = max_ch;
-  if (nch < 1) nch = 1;
-  int64_t chunk = (n_tok + nch - 1) / nch;
-  chunk = (chunk + 15) / 16 * 16;
-  if (g <= 4 && chunk > kAttnGroups * kAttnTokPerGroup) chunk = kAttnGroups * kAttnTokPerGroup;
+  auto chunk_for = [&](int64_t target) {
+    int64_t nch = target / hkv;
+    if (nch > max_ch) nch = max_ch;
+    if (nch < 1) nch = 1;
+    const int64_t c = (n_tok + nch - 1) / nch;
+    return (c + 15) / 16 * 16;
+  };
+  int64_t chunk = chunk_for(g <= 4 ? 1024 : 512);
+  if (g <= 4 && chunk > kAttnGroups * kAttnTokPerGroup) chunk = chunk_for(768);
+  AttnPlan p;
   p.chunk = chunk;
   p.nchunk = (n_tok + chunk - 1) / chunk;
   return p;

@@ -106,6 +106,10 @@ def test_attention_arguments_without_gpu(tq):
     assert tq.tq3_attention_workspace_bytes(10, 12, 8) == 0   # 12 query heads over 8
     assert tq.tq3_attention_workspace_bytes(10, 24, 8) == 0   # group of 3
     assert tq.tq3_attention_workspace_bytes(10, 8, 0) == 0
+    assert tq.tq3_attention_workspace_bytes(10, 65536, 65536) == 0   # > 65535 KV heads
+    assert tq.tq3_attention_workspace_bytes(10, 65535, 65535) > 0
+    assert tq.tq3_attention_workspace_bytes((1 << 28) + 1, 8, 8) == 0   # tokens x heads > 2^31
+    assert tq.tq3_attention_workspace_bytes(1 << 28, 8, 8) > 0
     ws = tq.tq3_attention_workspace_bytes(32768, 32, 8)
     assert ws > 0 and ws % 16 == 0
     assert tq.tq3_attention_workspace_bytes(1, 8, 1) > 0

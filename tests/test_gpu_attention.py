@@ -111,6 +111,17 @@ def test_eight_heads_long_chunks(tq, signs, t, hkv):
     check(tq, q, k, v, hkv, signs, 128 ** -0.5)
 
 
+@pytest.mark.parametrize("t,hkv,group", [(5000, 64, 4), (40000, 8, 2), (33000, 8, 1)])
+def test_long_caches_in_pieces(tq, signs, t, hkv, group):
+    """Up to 4 query heads per KV head, caches long enough that 1024 chunks
+    would exceed 256 tokens take 768 chunks of several pieces: 432, 432 and
+    352 tokens here (two pieces each, a short last piece and last chunk)."""
+    q = np.random.default_rng(t + hkv).standard_normal((group * hkv, 128)).astype(np.float32)
+    k = gaussian_records(t * hkv, 500 + hkv, signs)
+    v = gaussian_records(t * hkv, 600 + hkv, signs)
+    check(tq, q, k, v, hkv, signs, 128 ** -0.5)
+
+
 def test_random_records_large(tq, signs):
     """Uniform random index bytes with norms and scales as in the decode
     workload, 4096 tokens x 4 KV heads, 8 query heads per KV head."""

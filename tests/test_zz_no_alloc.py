@@ -103,11 +103,14 @@ def test_noalloc_binding_and_size_limit(tq):
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     # sizes whose partial results exceed the array are refused before any launch
-    n_tok = 1 << 20
-    assert tq.tq3_attention_workspace_bytes(n_tok, 32, 8) > tq.tq3_attention_noalloc_max_bytes()
+    # (the buffers are never read): 32768 KV heads of one query head each, one
+    # chunk per head, 32768 partials of 528 bytes
+    n_tok, heads = 16, 32768
+    assert tq.tq3_attention_workspace_bytes(n_tok, heads, heads) > tq.tq3_attention_noalloc_max_bytes()
+    assert tq.tq3_attention_workspace_bytes(1 << 20, 32, 8) <= tq.tq3_attention_noalloc_max_bytes()
     out = torch.empty((32, 128), device=DEV)
     st = tq.lib.tq3_decode_attention_noalloc(
-        ctypes.c_void_p(out.data_ptr()), tq.TQ_F32, 32, ctypes.c_void_p(kd.data_ptr()),
-        ctypes.c_void_p(vd.data_ptr()), n_tok, 8, tq.sign_mask(signs), ctypes.c_float(0.1),
+        ctypes.c_void_p(out.data_ptr()), tq.TQ_F32, heads, ctypes.c_void_p(kd.data_ptr()),
+        ctypes.c_void_p(vd.data_ptr()), n_tok, heads, tq.sign_mask(signs), ctypes.c_float(0.1),
         ctypes.c_void_p(out.data_ptr()), tq.TQ_F32, None)
     assert st == 9
