@@ -219,28 +219,36 @@ __device__ __forceinline__ void fwht_rows(float (&y)[16], int log2h, const LaneC
 // second one (5 or more wave bits in all: 8192 and 16384) uses xb, the
 // staged row, which the first exchange's barrier has made free. The caller
 // keeps the barrier that orders its next use of xb after these reads.
+// The buffers hold quarter k of chunk c (4 values) at float (k nch + c) 4,
+// nch = d / 16 chunks in the row: a wave's 64 lanes write and read 1 KB
+// runs without bank conflicts (chunk-major, each lane's 64 bytes in a row,
+// put lanes 4 apart on the same banks).
 // NT: the block's wave count (0: 5..16), which bounds the wave bits.
 template <int NT, int RD = DT_F32>
 __device__ __forceinline__ void span_stages(float (&y)[16], float* xa, float* xb, int c, int wave,
-                                            int log2h) {
+                                            int log2h, int nch_rt) {
   constexpr int kMaxBits = NT == 0 ? 4 : NT == 4 ? 2 : 1;
+  // a row with blocks over 1024 fills its waves: 64 NT chunks (constant
+  // offsets for the exact wave counts)
+  const int nch = NT > 0 ? 64 * NT : nch_rt;
   const int nb = log2h - 10;
   float* buf = xa;
   for (int b = 0; b < nb; buf = xb) {
-    f32x4_t* mine = reinterpret_cast<f32x4_t*>(buf + 16 * c);
+    f32x4_t* q4 = reinterpret_cast<f32x4_t*>(buf);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) mine[k] = f32x4_t{y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3]};
+    for (int k = 0; k < 4; ++k)
+      q4[k * nch + c] = f32x4_t{y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3]};
     __syncthreads();
     const int h0 = 64 << b;  // chunk distance of wave bit b
     const float c0 = ((wave >> b) & 1) ? -1.0f : 1.0f;
-    const f32x4_t* p1 = reinterpret_cast<const f32x4_t*>(buf + 16 * (c ^ h0));
+    const f32x4_t* p1 = q4 + (c ^ h0);
     if (kMaxBits >= 2 && nb - b >= 2) {
       const float c1 = ((wave >> (b + 1)) & 1) ? -1.0f : 1.0f;
-      const f32x4_t* p2 = reinterpret_cast<const f32x4_t*>(buf + 16 * (c ^ (2 * h0)));
-      const f32x4_t* p3 = reinterpret_cast<const f32x4_t*>(buf + 16 * (c ^ (3 * h0)));
+      const f32x4_t* p2 = q4 + (c ^ (2 * h0));
+      const f32x4_t* p3 = q4 + (c ^ (3 * h0));
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const f32x4_t o1 = p1[k], o2 = p2[k], o3 = p3[k];
+        const f32x4_t o1 = p1[k * nch], o2 = p2[k * nch], o3 = p3[k * nch];
         float so[4], sx[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -261,7 +269,7 @@ __device__ __forceinline__ void span_stages(float (&y)[16], float* xa, float* xb
     } else {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const f32x4_t o1 = p1[k];
+        const f32x4_t o1 = p1[k * nch];
 #pragma unroll
         for (int e = 0; e < 4; ++e) y[4 * k + e] = __builtin_fmaf(y[4 * k + e], c0, o1[e]);
       }
@@ -541,7 +549,7 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
     // takes a + b, the upper b' - a' = a - b with the same lazy lane sign.
     constexpr int RD = ROT ? DT : DT_F32;
     fwht_rows<FULL, RD>(y, log2h, cx);
-    if (SPAN) span_stages<NT, RD>(y, xbuf, rowbuf, c, wave, log2h);
+    if (SPAN) span_stages<NT, RD>(y, xbuf, rowbuf, c, wave, log2h, C);
 #pragma unroll
     for (int i = 0; i < 16; ++i) y[i] = y[i] * ksig;
     round16<RD>(y);
@@ -781,7 +789,7 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_dequantize_kernel(
     // Inverse rotation: FWHT per block (across waves through LDS beyond
     // 1024), times h^-1/2 and the lazy lane sign, times signs_j.
     fwht_rows<(HC > 0)>(w, log2h, cx);
-    if (HC == 2) span_stages<NT>(w, lds + d + kMaxBlocks, rowbuf, c, wave, log2h);
+    if (HC == 2) span_stages<NT>(w, lds + d + kMaxBlocks, rowbuf, c, wave, log2h, d >> 4);
     __syncthreads();  // the row buffer is free
     if (act) {
       f32x4_t* mine = reinterpret_cast<f32x4_t*>(rowbuf + 16 * cw);
