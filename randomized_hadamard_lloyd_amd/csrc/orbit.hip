@@ -715,6 +715,14 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_dequantize_kernel(
   int j0[NG];
 #pragma unroll
   for (int k = 0; k < NG; ++k) j0[k] = 1024 * wave + EPS * lane + 64 * EPS * k;
+  // The full path stages the transformed tile quarter-major: quarter q of
+  // chunk cw (elements 16 cw + 4 q .. + 3) at float (q nch + cw) 4, nch =
+  // R C chunks, so that a wave's 16-byte writes are contiguous (chunk-major,
+  // lanes 4 apart would share banks); the gather offsets point there.
+  const int nch = R * C;
+  auto staged = [&](uint32_t pos) {  // float index of staged element pos
+    return ((((pos >> 2) & 3u) * (uint32_t)nch + (pos >> 4)) << 2) + (pos & 3u);
+  };
   uint32_t ioff[16], smask[16];
   if (!rotated_only) {
 #pragma unroll
@@ -728,7 +736,8 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_dequantize_kernel(
       for (int e4 = 0; e4 < EPS / 4; ++e4) {
         const u32x4 p = ip[e4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ioff[EPS * k + 4 * e4 + e] = 4u * ((ok ? jr * d : 0) + p[e]);
+        for (int e = 0; e < 4; ++e)
+          ioff[EPS * k + 4 * e4 + e] = 4u * staged((uint32_t)((ok ? jr * d : 0) + p[e]));
       }
     }
     const u32x4 sv = *reinterpret_cast<const u32x4*>(signs + 16 * (lane_ok ? c : 0));
@@ -792,13 +801,13 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_dequantize_kernel(
     if (HC == 2) span_stages<NT>(w, lds + d + kMaxBlocks, rowbuf, c, wave, log2h, d >> 4);
     __syncthreads();  // the row buffer is free
     if (act) {
-      f32x4_t* mine = reinterpret_cast<f32x4_t*>(rowbuf + 16 * cw);
+      f32x4_t* q4 = reinterpret_cast<f32x4_t*>(rowbuf);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         float z[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) z[e] = as_f(as_u(w[4 * k + e] * ksig) ^ smask[4 * k + e]);
-        mine[k] = f32x4_t{z[0], z[1], z[2], z[3]};
+        q4[k * nch + cw] = f32x4_t{z[0], z[1], z[2], z[3]};
       }
     }
     __syncthreads();
