@@ -406,8 +406,8 @@ __device__ __forceinline__ uint32_t sign_of(uint32_t w, int k) {
 // 16 t + l % 16, columns 32 kc + 8 (l / 16) .. + 7.
 // SB: rebuild the sign masks from their packed bits on every row (two
 // operations per element) instead of keeping 16 mask registers across rows:
-// 15 VGPRs fewer, which gives blocks of 5 waves a third block per CU and
-// keeps the kernels with blocks over 1024 free of spills.
+// 15 VGPRs fewer, which gives blocks of 5 and 6 waves a third block per CU
+// and keeps the kernels with blocks over 1024 free of spills.
 template <int BITS, bool LSB, int NT, int HC, bool ROT = false, int DT = DT_F32,
           bool SYM = true, bool TOUT = false, bool MR = false, bool SB = false>
 __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_quantize_kernel(
@@ -871,13 +871,14 @@ hipError_t launch_q_sym(const float* W, int64_t rows, int d, int log2h, float kh
   }
   const int nt = (d + 1023) >> 10;
   if constexpr (NT == 0 && !SB) {
-    // 5-wave blocks (a third block per CU) and blocks over 1024 (no spills):
-    // 3 bits, 37.7 M elements: 65 -> 53 us at d = 5120, 63 -> 59 at 8192,
-    // 74 -> 69 at 16384; blocks of 6-16 waves up to 1024 lose 2-6%
+    // 5- and 6-wave blocks (a third block per CU) and blocks over 1024 (no
+    // spills): 3 bits, 37.7 M elements: 65 -> 53 us at d = 5120, 75 -> 62
+    // at 5632, 63 -> 59 at 8192, 74 -> 69 at 16384; blocks of 7-16 waves up
+    // to 1024 lose 2-6%
     if constexpr (HC == 2)
       return launch_q_sym<BITS, LSB, NT, HC, SYM, MR, true>(W, rows, d, log2h, kh, perm, signs,
                                                             cb, packed, norms, cus, s);
-    else if (nt == 5)
+    else if (nt == 5 || nt == 6)
       return launch_q_sym<BITS, LSB, NT, HC, SYM, MR, true>(W, rows, d, log2h, kh, perm, signs,
                                                             cb, packed, norms, cus, s);
   }

@@ -96,11 +96,12 @@ def test_orbit_dims(tq, d):
 
 @pytest.mark.parametrize("msb", [True, False])
 @pytest.mark.parametrize("bits", [2, 3, 4])
-@pytest.mark.parametrize("d", [5120, 8192, 12288, 14336, 16384])
+@pytest.mark.parametrize("d", [4608, 5120, 5632, 6144, 8192, 12288, 14336, 16384])
 def test_orbit_large_d(tq, d, bits, msb):
     """Rows longer than 4096 ("orbit_quant.py", hadamard_block_size: the block
-    is d & -d, here 1024, 8192, 4096, 2048 and 16384): blocks of up to 16
-    waves, Hadamard stages across waves up to index bit 13, tile sums of
+    is d & -d, here 512, 1024, 512, 2048, 8192, 4096, 2048 and 16384):
+    blocks of up to 16 waves (5 and 6 waves with the sign masks rebuilt per
+    row), Hadamard stages across waves up to index bit 13, tile sums of
     squares combined by the pairwise tree inside each block."""
     w = datagen.orbit_weight(rows=37, d=d, seed=d + bits)
     check(tq, w, d, bits, msb)
