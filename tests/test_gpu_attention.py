@@ -100,11 +100,11 @@ def test_kv_layer_full_size(tq, signs, hq):
     print(f"max |o - o_ref| / max|V| = {worst:.3e}")
 
 
-@pytest.mark.parametrize("t,hkv", [(20000, 8), (40000, 4)])
+@pytest.mark.parametrize("t,hkv", [(20000, 8), (40000, 4), (4500, 32)])
 def test_eight_heads_long_chunks(tq, signs, t, hkv):
     """Eight query heads per KV head take chunks longer than 256 tokens,
     processed in pieces of 256: here 320-token chunks (a 64-token last piece)
-    and a shorter last chunk."""
+    and a shorter last chunk, and 288-token chunks over 32 KV heads."""
     q = np.random.default_rng(t).standard_normal((8 * hkv, 128)).astype(np.float32)
     k = gaussian_records(t * hkv, 300 + hkv, signs)
     v = gaussian_records(t * hkv, 400 + hkv, signs)

@@ -6,7 +6,7 @@ cannot allocate. Both entry points run the same kernels, so the results must
 be identical bit for bit; they are also held to the attention tests' bound
 against the oracle (fp64 softmax attention over the oracle's reconstructions,
 "ComfyUI-TurboQuant: tq3_core.py" tq3_dequantize). Two calls run back to back
-on the shared array, the second smaller than the first.
+on the shared array, each smaller than the one before.
 """
 import ctypes
 import math
@@ -72,9 +72,11 @@ def test_noalloc_matches_workspace_entry_point(tq, qdtype, odtype):
     mask = tq.sign_mask(signs)
     scale = 128 ** -0.5
     odt = tq.TQ_F32 if odtype == torch.float32 else tq.TQ_BF16
-    # two calls in a row on the shared array: 8192 tokens x 8 KV heads with 32
-    # query heads (128 chunks), then 1000 tokens x 2 KV heads with 8 (fewer)
-    for n_tok, hkv, group, seed in ((8192, 8, 4, 1), (1000, 2, 4, 2)):
+    # three calls in a row on the shared array, each smaller than the one
+    # before: 40000 tokens x 8 KV heads with 16 query heads (96 chunks of two
+    # pieces), 8192 tokens x 8 KV heads with 32 (128 chunks of one piece),
+    # then 1000 tokens x 2 KV heads with 8
+    for n_tok, hkv, group, seed in ((40000, 8, 2, 3), (8192, 8, 4, 1), (1000, 2, 4, 2)):
         q, k, v = case(n_tok, hkv, group, seed, signs)
         need = tq.tq3_attention_workspace_bytes(n_tok, hkv * group, hkv)
         assert 0 < need <= tq.tq3_attention_noalloc_max_bytes()
