@@ -49,27 +49,36 @@ inline int stage_class(int log2h) { return log2h < 10 ? 0 : log2h == 10 ? 1 : 2;
 // value per h-block, added left to right; for h > 1024 one value per
 // 1024-element tile, combined by the pairwise tree inside each block (tiles
 // 2k and 2k + 1 first) before the block sums are added left to right.
-template <bool SPAN>
-__device__ __forceinline__ float row_sumsq(const float* bsum, int log2h, int nblk) {
+template <int TPB>
+__device__ __forceinline__ float tiles_then_blocks(const float* bsum, int nblk) {
   float total = 0.0f;
-  if (!SPAN || log2h <= 10) {
-    total = bsum[0];
-    for (int bi = 1; bi < nblk; ++bi) total = total + bsum[bi];
-    return total;
-  }
-  const int tpb = 1 << (log2h - 10);  // tiles per block, <= 16
   for (int bi = 0; bi < nblk; ++bi) {
-    float t[16];
+    float t[TPB];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) t[k] = k < tpb ? bsum[bi * tpb + k] : 0.0f;
+    for (int k = 0; k < TPB; ++k) t[k] = bsum[bi * TPB + k];
 #pragma unroll
-    for (int w = 1; w < 16; w *= 2)
+    for (int w = 1; w < TPB; w *= 2)
 #pragma unroll
-      for (int k = 0; k < 16; k += 2 * w)
-        if (k + w < tpb) t[k] = t[k] + t[k + w];
+      for (int k = 0; k < TPB; k += 2 * w) t[k] = t[k] + t[k + w];
     total = bi == 0 ? t[0] : total + t[0];
   }
   return total;
+}
+template <bool SPAN>
+__device__ __forceinline__ float row_sumsq(const float* bsum, int log2h, int nblk) {
+  if (!SPAN || log2h <= 10) {
+    float total = bsum[0];
+    for (int bi = 1; bi < nblk; ++bi) total = total + bsum[bi];
+    return total;
+  }
+  // tiles per block (2..16) as a compile-time count: the tree is straight
+  // adds instead of sixteen guarded ones per block
+  switch (log2h - 10) {
+    case 1: return tiles_then_blocks<2>(bsum, nblk);
+    case 2: return tiles_then_blocks<4>(bsum, nblk);
+    case 3: return tiles_then_blocks<8>(bsum, nblk);
+    default: return tiles_then_blocks<16>(bsum, nblk);
+  }
 }
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
