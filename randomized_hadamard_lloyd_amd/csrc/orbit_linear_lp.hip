@@ -297,8 +297,14 @@ __device__ __forceinline__ int tall_off(int r, int c) {  // byte offset of (row,
   return r * 128 + ((c ^ (r >> 1)) & 7) * 16;
 }
 
-template <int DT, int BITS, bool LSB, bool TILED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void
+// KS = 2 (one row band of at most 256 rows and an even step count): eight
+// waves, waves 4 kh .. 4 kh + 3 taking the steps kh S/2 .. (kh + 1) S/2 - 1
+// of the same tile in lockstep, each half with its own tile buffers; the
+// second half's accumulators are then added to the first half's through LDS
+// (first half + second half: a fixed order). Half the dependent steps per
+// wave, where a lone row band leaves the CUs one block each.
+template <int DT, int BITS, bool LSB, bool TILED, int KS = 1>
+__global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS == 2 ? 2 : 3))) void
 orbit_linear_lp_tall_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                             const uint8_t* __restrict__ packed, const float* __restrict__ norms,
                             int64_t N, OrbitCodebook cb, const uint16_t* __restrict__ bias,
@@ -309,23 +315,30 @@ orbit_linear_lp_tall_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K
   constexpr bool PAIRS = BITS == 2 || (TILED && BITS == 3);
   // dwords per row's table, padded by one so that rows start in different banks
   constexpr int TW = (PAIRS ? L * L : L / 2) + 1;
-  __shared__ __attribute__((aligned(16))) char As[TILED ? 1 : 4][TILED ? 16 : 64 * 128];
-  __shared__ __attribute__((aligned(16))) char Bs[2][kTallBN * 128];
+  static_assert(KS == 1 || KS == 2, "one or two halves of the steps");
+  // x_rot staging (per wave) and, for KS = 2, the second half's accumulators
+  constexpr int AS_BYTES = TILED ? 16 : 4 * KS * 64 * 128;
+  constexpr int RED_BYTES = KS == 2 ? 16 * 4 * 256 * 4 : 0;
+  __shared__ __attribute__((aligned(16))) char As_[AS_BYTES > RED_BYTES ? AS_BYTES : RED_BYTES];
+  __shared__ __attribute__((aligned(16))) char Bs_[KS][2][kTallBN * 128];
   __shared__ uint32_t tbw[kTallBN * TW];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = wave & 3, kh = wave >> 2;  // the wave's 64 rows; its half of the steps
+  char (*Bs)[kTallBN * 128] = Bs_[kh];
   int tx, ty;
   if (!xcd_tile((int)((N + kTallBN - 1) / kTallBN), (int)((M + kTallBM - 1) / kTallBM), tx, ty))
     return;
   const int64_t m0 = (int64_t)ty * kTallBM, n0 = (int64_t)tx * kTallBN;
 
-  // This thread decodes codes 16 bq .. 16 bq + 15 of each step of W' row bn.
-  const int bn = tid >> 2, bq = tid & 3;
+  // This thread decodes codes 16 bq .. 16 bq + 15 of each step (of its
+  // half) of W' row bn.
+  const int bn = (tid & 255) >> 2, bq = tid & 3;
   const bool nvalid = n0 + bn < N;
   const int64_t row_bytes = K * BITS / 8;
   const uint8_t* prow = packed + (nvalid ? n0 + bn : 0) * row_bytes;
   uint16_t* t16 = reinterpret_cast<uint16_t*>(tbw) + bn * 2 * TW;
-  {
+  if (kh == 0) {  // one half builds the tables (KS = 2)
     // row bn's table of round(round(codebook[c]) * round(norm)) (zeros for
     // rows past N), split between the row's four threads
     const float nl = nvalid ? lp_float<DT>(lp_bits<DT>(norms[n0 + bn])) : 0.0f;
@@ -352,10 +365,10 @@ orbit_linear_lp_tall_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K
   for (int p = 0; p < 8; ++p) {
     if constexpr (TILED) {
       const int64_t last_t = (M + 15) / 16 - 1 - m0 / 16;
-      const int64_t t = 4 * wave + (p >> 1) < last_t ? 4 * wave + (p >> 1) : last_t;
+      const int64_t t = 4 * wv + (p >> 1) < last_t ? 4 * wv + (p >> 1) : last_t;
       xoff[p] = (uint32_t)(((t * (K / 32) + (p & 1)) * 64 + lane) * 16);
     } else {
-      const int64_t r = 64 * wave + 8 * p + (lane >> 3);
+      const int64_t r = 64 * wv + 8 * p + (lane >> 3);
       xoff[p] = (uint32_t)(((m0 + r < M ? r : 0) * K + 8 * (lane & 7)) * 2);
     }
   }
@@ -365,6 +378,10 @@ orbit_linear_lp_tall_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K
   // last 32 columns, and the MFMAs skip its first half.
   const bool half_last = (K & 63) != 0;
   const int64_t last = steps - 1;
+  // this wave's steps: s0 .. s0 + sh - 1 (KS = 2: half of them)
+  const int64_t sh = KS == 2 ? steps / 2 : steps;
+  const int64_t s0 = KS == 2 ? kh * sh : 0;
+  const int64_t s_end = s0 + sh - 1;
   auto kbase = [&](int64_t st) { return st * 64 - (half_last && st == last ? 32 : 0); };
   auto fetch_x = [&](u32x4v (&xv)[8], int64_t st) {
     const char* b = TILED ? xblk + (kbase(st) / 32) * 1024 : xblk + kbase(st) * 2;
@@ -380,7 +397,8 @@ orbit_linear_lp_tall_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K
   auto stage_x = [&](const u32x4v (&xv)[8]) {
 #pragma unroll
     for (int p = 0; p < 8; ++p)
-      *reinterpret_cast<u32x4v*>(&As[TILED ? 0 : wave][tall_off(8 * p + (lane >> 3), lane & 7)]) =
+      *reinterpret_cast<u32x4v*>(As_ + (TILED ? 0 : wave) * (64 * 128) +
+                                 tall_off(8 * p + (lane >> 3), lane & 7)) =
           xv[p];
   };
   auto fetch_c = [&](int64_t st) -> uint64_t {
@@ -441,14 +459,14 @@ orbit_linear_lp_tall_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K
 
   u32x4v xa[8];  // TILED: the current step's fragments
   if constexpr (TILED) {
-    fetch_x(xa, 0);
+    fetch_x(xa, s0);
   } else {
     u32x4v xv[8];
-    fetch_x(xv, 0);
+    fetch_x(xv, s0);
     stage_x(xv);
   }
-  const uint64_t craw0 = fetch_c(0);
-  uint64_t cr = fetch_c(steps > 1 ? 1 : 0);
+  const uint64_t craw0 = fetch_c(s0);
+  uint64_t cr = fetch_c(sh > 1 ? s0 + 1 : s0);
   __syncthreads();  // tables
   decode(craw0, 0);
   __syncthreads();  // the tile of step 0
@@ -462,12 +480,12 @@ orbit_linear_lp_tall_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K
     uint64_t cn = 0;
     if (more) {
       fetch_x(xv, st + 1);
-      cn = fetch_c(st + 2 < steps ? st + 2 : last);
+      cn = fetch_c(st + 2 <= s_end ? st + 2 : s_end);
     }
     // keeps those loads here, a whole step ahead of their use
     asm volatile("" ::: "memory");
-    const char* at = As[wave];
-    const char* bt = Bs[st & 1];
+    const char* at = As_ + wave * (64 * 128);
+    const char* bt = Bs[(st - s0) & 1];
     u32x4v a[4], b[4];
     if (first_half) {
 #pragma unroll
@@ -482,7 +500,7 @@ orbit_linear_lp_tall_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma_lp<DT>(a[i], b[j], acc[i][j]);
     }
     if (more) {
-      decode(cr, (int)((st + 1) & 1));
+      decode(cr, (int)((st + 1 - s0) & 1));
       cr = cn;
     }
 #pragma unroll
@@ -507,10 +525,10 @@ orbit_linear_lp_tall_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K
     uint64_t cn = 0;
     if (more) {
       fetch_half(xn, st + 1, 0);
-      cn = fetch_c(st + 2 < steps ? st + 2 : last);
+      cn = fetch_c(st + 2 <= s_end ? st + 2 : s_end);
     }
     asm volatile("" ::: "memory");
-    const char* bt = Bs[st & 1];
+    const char* bt = Bs[(st - s0) & 1];
     u32x4v b[4];
     if (first_half) {
 #pragma unroll
@@ -523,7 +541,7 @@ orbit_linear_lp_tall_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K
     }
     if (more) {
       fetch_half(xh, st + 1, 1);
-      decode(cr, (int)((st + 1) & 1));
+      decode(cr, (int)((st + 1 - s0) & 1));
       cr = cn;
     }
 #pragma unroll
@@ -542,12 +560,37 @@ orbit_linear_lp_tall_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K
       __syncthreads();
     }
   };
-  for (int64_t st = 0; st < last; ++st) {
+  for (int64_t st = s0; st < s_end; ++st) {
     if constexpr (TILED) step_tiled(st, true, true);
     else step_staged(st, true, true);
   }
-  if constexpr (TILED) step_tiled(last, !half_last, false);
-  else step_staged(last, !half_last, false);
+  const bool fh = !(half_last && s_end == last);
+  if constexpr (TILED) step_tiled(s_end, fh, false);
+  else step_staged(s_end, fh, false);
+
+  if constexpr (KS == 2) {
+    // the second half's tiles -> LDS (over the x_rot staging, which every
+    // wave is done with), then added to the first half's
+    float* red = reinterpret_cast<float*>(As_);  // [tile][reg][wave of the half][lane]
+    __syncthreads();
+    if (kh == 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) red[((i * 4 + j) * 4 + r) * 256 + wv * 64 + lane] = acc[i][j][r];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc[i][j][r] = acc[i][j][r] + red[((i * 4 + j) * 4 + r) * 256 + wv * 64 + lane];
+  }
 
   // y = round(acc + bias)
 #pragma unroll
@@ -559,7 +602,7 @@ orbit_linear_lp_tall_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t m = m0 + 64 * wave + 16 * i + 4 * (lane >> 4) + r;
+        const int64_t m = m0 + 64 * wv + 16 * i + 4 * (lane >> 4) + r;
         if (m < M) y[m * N + n] = (uint16_t)lp_bits<DT>(acc[i][j][r] + bv);
       }
   }
@@ -788,10 +831,19 @@ hipError_t launch_lp(const void* x, int64_t M, int64_t K, const uint8_t* packed,
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const uint16_t* bp = static_cast<const uint16_t*>(bias);
   uint16_t* yp = static_cast<uint16_t*>(y);
+  // One row band above the few-rows range (65..256 rows) with an even step
+  // count: the steps split between two halves of an 8-wave block (the grid
+  // then holds N / 64 blocks, fewer than the CUs).
+  const int64_t tsteps = (K + 63) / 64;
+  const bool split = M > 64 && M <= kTallBM && tsteps % 2 == 0;
   if (tiled) {  // x_rot in the fragment layout: the tall tiles at every M (64 <= K < 2^22)
     const unsigned grid = xcd_grid((N + kTallBN - 1) / kTallBN, (M + kTallBM - 1) / kTallBM);
-    orbit_linear_lp_tall_kernel<DT, BITS, LSB, true><<<grid, 256, 0, s>>>(xp, M, K, packed, norms,
-                                                                          N, cb, bp, yp);
+    if (split)
+      orbit_linear_lp_tall_kernel<DT, BITS, LSB, true, 2><<<grid, 512, 0, s>>>(
+          xp, M, K, packed, norms, N, cb, bp, yp);
+    else
+      orbit_linear_lp_tall_kernel<DT, BITS, LSB, true><<<grid, 256, 0, s>>>(
+          xp, M, K, packed, norms, N, cb, bp, yp);
     return hipGetLastError();
   }
   const int mt = (int)((M + 15) / 16);
@@ -818,8 +870,12 @@ hipError_t launch_lp(const void* x, int64_t M, int64_t K, const uint8_t* packed,
   // lanes' 32-bit x_rot offsets could overflow.
   if (K >= 64 && K < ((int64_t)1 << 22)) {
     const unsigned grid = xcd_grid((N + kTallBN - 1) / kTallBN, (M + kTallBM - 1) / kTallBM);
-    orbit_linear_lp_tall_kernel<DT, BITS, LSB, false><<<grid, 256, 0, s>>>(xp, M, K, packed, norms, N,
-                                                                    cb, bp, yp);
+    if (split)
+      orbit_linear_lp_tall_kernel<DT, BITS, LSB, false, 2><<<grid, 512, 0, s>>>(
+          xp, M, K, packed, norms, N, cb, bp, yp);
+    else
+      orbit_linear_lp_tall_kernel<DT, BITS, LSB, false><<<grid, 256, 0, s>>>(
+          xp, M, K, packed, norms, N, cb, bp, yp);
     return hipGetLastError();
   }
   const unsigned grid = xcd_grid((N + kLpBN - 1) / kLpBN, (M + kLpBM - 1) / kLpBM);
