@@ -124,6 +124,24 @@ class Timer:
         ms = [a.elapsed_time(b) for a, b in evs]
         return sum(ms) / len(ms), min(ms)
 
+    def run_batch(self, fn, iters, warmup=5):
+        """Average duration of iters back-to-back calls between one event pair
+        (queued behind the spin kernel like run's): for calls of several
+        kernels, where an event pair around each call adds its own gaps."""
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(self.stream):
+            torch.cuda._sleep(int(iters * 100_000))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for _ in range(iters):
+            fn()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
 
 def rate(bytes_, ms):
     return bytes_ / (ms * 1e-3) / 1e9
@@ -318,11 +336,15 @@ def secondary(tq, timer, dev, signs, mask):
         ws = torch.zeros(tq.tq3_attention_workspace_bytes(n_tok, hq, hkv), dtype=torch.uint8,
                          device=dev)
         o = torch.empty((hq, 128), dtype=torch.float32, device=dev)
-        ms_a, _ = timer.run(lambda: L.tq3_decode_attention(
+        call = lambda: L.tq3_decode_attention(
             tq._ptr(qh), tq.TQ_F32, hq, tq._ptr(kv_k), tq._ptr(kv_v), n_tok, hkv, mask,
-            ctypes.c_float(128 ** -0.5), tq._ptr(ws), ws.numel(), tq._ptr(o), tq.TQ_F32, sp), 50,
-            warmup=20)
+            ctypes.c_float(128 ** -0.5), tq._ptr(ws), ws.numel(), tq._ptr(o), tq.TQ_F32, sp)
+        # one call is two kernels (partial results, then their merge): timed
+        # back to back between one event pair, and with a pair around each call
+        ms_a = timer.run_batch(call, 200, warmup=20)
+        ms_p, _ = timer.run(call, 50, warmup=5)
         ent = {"query_heads": hq, "kv_heads": hkv, "tokens": n_tok, "avg_ms": ms_a,
+               "avg_ms_event_pair_per_call": ms_p,
                "records_GBps": rate(2 * n_tok * hkv * REC, ms_a)}
         if group == 4:
             # the unfused path: dequantize K and V to fp32, then bmm / softmax / bmm
@@ -416,7 +438,7 @@ def secondary(tq, timer, dev, signs, mask):
     wrt16 = tq.orbit_dequantize(packed, norms, d, bits, None, None, cb, rotated_only=True,
                                 dtype=torch.float32).to(torch.bfloat16).t().contiguous()
     fwd16 = {}
-    for m in (16, 1024):
+    for m in (16, 128, 1024):
         xa = torch.randn(m, d, generator=torch.Generator().manual_seed(m)).to(dev).to(torch.bfloat16)
         xr = torch.empty_like(xa)
         yo = torch.empty((m, rows), dtype=torch.bfloat16, device=dev)
