@@ -115,6 +115,8 @@ def test_rotate_tiled_bit_exact(tq, fmt, m, d):
     ("bf16", 520, 1024, 64, 3, False),   # three 256-row tiles, LSB-first 3-bit codes
     ("f16", 300, 2048, 256, 4, False),
     ("bf16", 1024, 3072, 384, 3, True),  # the forward workload's width, four row tiles
+    ("bf16", 100, 96, 65, 3, True),      # steps split in two halves, the second a half step
+    ("f16", 200, 224, 130, 2, False),    # four steps in two halves, the last a half step
 ])
 def test_linear_tiled(tq, fmt, m, d, n, bits, msb):
     perm, sg, cb, packed, norms = quantized(n, d, bits, d + n + bits + m, msb)
