@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256) void tq3_attn_partial_kernel(
   // tokens (16 slots per group). This wave's records, one dword per lane and
   // record (lane 16a + d holds dword min(d, 13) of group a's record), K and
   // V, through a window of kAttnWin token slots in registers: slots past the
-  // piece's end re-read token t0's record, which is never used. Each slot
+  // piece's end re-read a record of the piece (below), never used. Each slot
   // goes to LDS just before the loop reads it, and its registers then load
   // the slot kAttnWin later, so the loop waits only for the loads of the
   // slots it reaches while the next ones stay in flight. (Copies straight
