@@ -37,14 +37,23 @@ def signs():
     return datagen.tq3_signs().numpy()
 
 
-def check(tq, q, k_rec, v_rec, hkv, signs, scale, qdtype=torch.float32, odtype=torch.float32):
-    hq = q.shape[0]
+def run(tq, q, k_rec, v_rec, hkv, signs, scale, qdtype=torch.float32, odtype=torch.float32):
+    """Kernel output (fp64) and the query it saw, rounded to qdtype."""
     out = tq.tq3_decode_attention(torch.from_numpy(q).to(DEV, qdtype),
                                   torch.from_numpy(k_rec).to(DEV), torch.from_numpy(v_rec).to(DEV),
                                   hkv, signs, scale, dtype=odtype)
     torch.cuda.synchronize()
     got = out.float().cpu().numpy().astype(np.float64)
-    qq = torch.from_numpy(q).to(qdtype).float().numpy()  # the query the kernel saw
+    return got, torch.from_numpy(q).to(qdtype).float().numpy()
+
+
+def check(tq, q, k_rec, v_rec, hkv, signs, scale, qdtype=torch.float32, odtype=torch.float32):
+    got, qq = run(tq, q, k_rec, v_rec, hkv, signs, scale, qdtype, odtype)
+    return compare(got, qq, k_rec, v_rec, hkv, signs, scale, odtype)
+
+
+def compare(got, qq, k_rec, v_rec, hkv, signs, scale, odtype=torch.float32):
+    hq = qq.shape[0]
     ref = oatt.tq3_decode_attention(qq, k_rec, v_rec, hkv, signs, scale)
     kd = oatt.dequantized_cache(k_rec, hkv, signs).astype(np.float64)
     vd = oatt.dequantized_cache(v_rec, hkv, signs).astype(np.float64)
@@ -120,6 +129,25 @@ def test_long_caches_in_pieces(tq, signs, t, hkv, group):
     k = gaussian_records(t * hkv, 500 + hkv, signs)
     v = gaussian_records(t * hkv, 600 + hkv, signs)
     check(tq, q, k, v, hkv, signs, 128 ** -0.5)
+
+
+@pytest.mark.parametrize("t,group", [(20, 1), (33, 2)])
+def test_most_kv_heads(tq, signs, t, group):
+    """65535 KV heads, the most the library takes: the per-lane record
+    offsets within a piece reach 255 tokens' stride apart only through the
+    head count, and one chunk per head gives 65535 blocks. Sampled KV heads
+    (the first, the last and some between) are checked, each against the
+    oracle on its own records alone."""
+    hkv = 65535
+    rec = datagen.decode_records(2 * t * hkv, seed=40 + t).numpy()
+    k, v = rec[: t * hkv], rec[t * hkv:]
+    q = np.random.default_rng(t).standard_normal((group * hkv, 128)).astype(np.float32) * 0.05
+    got, qq = run(tq, q, k, v, hkv, signs, 128 ** -0.5)
+    kt, vt = k.reshape(t, hkv, 56), v.reshape(t, hkv, 56)
+    for j in (0, 1, 4097, 32768, 54321, hkv - 2, hkv - 1):
+        h = slice(j * group, (j + 1) * group)
+        compare(got[h], qq[h], np.ascontiguousarray(kt[:, j]), np.ascontiguousarray(vt[:, j]), 1,
+                signs, 128 ** -0.5)
 
 
 def test_random_records_large(tq, signs):
