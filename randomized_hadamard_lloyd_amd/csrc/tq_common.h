@@ -85,6 +85,17 @@ __device__ __forceinline__ float div_rn(float a, const Recip& r) {
   const float rem = __builtin_fmaf(-q0, r.d, a);
   return __builtin_fmaf(rem, r.rh, q0);
 }
+// The same quotient for a numerator with at most 16 significant bits (a bf16
+// or fp16 value widened to fp32): q0 = RN(a*rh) alone need not be faithful,
+// but the one correction from the exact remainder still rounds correctly.
+// Checked exhaustively against IEEE division for numerators of 8, 11, 12 and
+// 16 significant bits over every divisor mantissa and both quotient binades
+// (tests/division_check.c); the same normal-range condition applies.
+__device__ __forceinline__ float div_rn_short(float a, const Recip& r) {
+  const float q0 = a * r.rh;
+  const float rem = __builtin_fmaf(-q0, r.d, a);
+  return __builtin_fmaf(rem, r.rh, q0);
+}
 
 // Tile (tx, ty) of an nx x ny tiling for block blockIdx.x of a 1-D grid of
 // 8 * ceil(nx * ny / 8) blocks. Blocks go to the 8 XCDs round-robin, so block
