@@ -423,12 +423,15 @@ __global__ __launch_bounds__(256) void tq3_dequantize_kernel(const uint8_t* __re
                                                              int64_t n_vec, SignMask mask,
                                                              void* __restrict__ y,
                                                              int64_t stride) {
-  // The 8 centroids, shared by the block. Each element's value is the
-  // centroid times its record's scale, the same fp32 product a per-record
-  // table of scaled centroids would hold; every lane reading one of only 8
-  // words, in 8 different banks, keeps the reads free of bank conflicts.
-  __shared__ float ctab[8];
-  if (threadIdx.x < 8) ctab[threadIdx.x] = tq3_centroid(threadIdx.x);
+  // The 64 centroid pairs, shared by the block: entry a | (b << 3) holds
+  // (C[a], C[b]), the centroids of two consecutive elements with indices a
+  // then b, which is the pair's 6-bit field of the record as it stands. One
+  // 8-byte read serves two elements. Each element's value is the centroid
+  // times its record's scale, the same fp32 product a per-record table of
+  // scaled centroids would hold.
+  __shared__ __attribute__((aligned(8))) float2 ptab[64];
+  if (threadIdx.x < 64)
+    ptab[threadIdx.x] = make_float2(tq3_centroid(threadIdx.x & 7), tq3_centroid(threadIdx.x >> 3));
   __syncthreads();
   // Per-wave staging of 16-bit outputs: 16 rows, each padded from 256 to 320
   // bytes so that both the quad-ordered writes and the row-ordered reads are
@@ -494,16 +497,19 @@ __global__ __launch_bounds__(256) void tq3_dequantize_kernel(const uint8_t* __re
     const uint2 ns = cur.ns;
     const float norm = as_f(ns.x), scale = as_f(ns.y);
 
-    // Byte offset of centroid idx: 4 * idx.
+    // Byte offset of the pair entry of elements 2p, 2p + 1: 8 * (bits 6p ..
+    // 6p + 5 of the chunk).
     float w[4][8];
-    const char* tb = reinterpret_cast<const char*>(&ctab[0]);
+    const char* tb = reinterpret_cast<const char*>(&ptab[0]);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const uint32_t c4 = chunk[g] << 2;
+      const uint32_t c8 = chunk[g] << 3;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t off = (c4 >> (3 * i)) & 28u;
-        w[g][i] = *reinterpret_cast<const float*>(tb + off) * scale;
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t off = (c8 >> (6 * p)) & 0x1f8u;
+        const float2 c = *reinterpret_cast<const float2*>(tb + off);
+        w[g][2 * p] = c.x * scale;
+        w[g][2 * p + 1] = c.y * scale;
       }
     }
 
