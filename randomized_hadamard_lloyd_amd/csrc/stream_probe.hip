@@ -1,6 +1,7 @@
 // Measurement probes (not part of the codec library): the memory traffic of
 // the TQ3 kernels with no arithmetic, to measure what HBM gives each access
-// pattern on this part. Built into libtqprobe.so and timed by bench.py.
+// pattern on this part, built into libtqprobe.so and timed by bench.py; and
+// an exhaustive device check of the reciprocal the codec kernels use.
 //
 //   kind 0 (quantize pattern): each 4-lane quad reads one 256-byte bf16 row
 //     with four 16-byte loads per lane and writes one 56-byte record (lanes
@@ -14,6 +15,8 @@
 // be dropped. Every access stays inside n_vec rows / records.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "tq_common.h"
 
 namespace {
 
@@ -59,9 +62,43 @@ __global__ __launch_bounds__(256) void probe_dequantize_pattern(const uint8_t* _
   }
 }
 
+// Arithmetic check (not a stream probe): recip_rn against the IEEE quotient
+// 1.0f / d for every fp32 d with exponent field 1 .. 252 (every normal d
+// below 2^126, where 1/d stays normal) and every mantissa. One thread per
+// mantissa, one grid row per exponent; cnt[0] counts the cases, cnt[1] the
+// mismatches, cnt[2] the mismatches of the raw hardware reciprocal (which
+// shows that the check can see a wrong result).
+__global__ __launch_bounds__(256) void recip_rn_check(unsigned long long* __restrict__ cnt) {
+  const uint32_t m = blockIdx.x * 256u + threadIdx.x;  // < 2^23
+  const uint32_t e = 1u + blockIdx.y;                  // 1 .. 252
+  const float d = __builtin_bit_cast(float, (e << 23) | m);
+  const float r = tq::recip_rn(d);
+  const float r0 = __builtin_amdgcn_rcpf(d);
+  const float ref = 1.0f / d;
+  unsigned long long bad = __builtin_bit_cast(uint32_t, r) != __builtin_bit_cast(uint32_t, ref);
+  unsigned long long raw = __builtin_bit_cast(uint32_t, r0) != __builtin_bit_cast(uint32_t, ref);
+  for (int o = 32; o > 0; o >>= 1) {
+    bad += __shfl_xor(bad, o);
+    raw += __shfl_xor(raw, o);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    atomicAdd(&cnt[0], 64ull);
+    atomicAdd(&cnt[1], bad);
+    atomicAdd(&cnt[2], raw);
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+// Runs recip_rn_check on `stream`: cnt = 3 zeroed 64-bit device counters.
+// Returns 0, 1 for a null pointer, 2 if the launch failed.
+int tqprobe_recip_check(unsigned long long* cnt, void* stream) {
+  if (!cnt) return 1;
+  recip_rn_check<<<dim3((1u << 23) / 256, 252), 256, 0, static_cast<hipStream_t>(stream)>>>(cnt);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 // Enqueue one probe launch of `grid` 256-thread blocks on `stream`.
 // kind 0: `in` = n_vec bf16 rows of 128 (16-byte aligned), `out` = n_vec
