@@ -1,7 +1,8 @@
 // Measurement probes (not part of the codec library): the memory traffic of
 // the TQ3 kernels with no arithmetic, to measure what HBM gives each access
 // pattern on this part, built into libtqprobe.so and timed by bench.py; and
-// an exhaustive device check of the reciprocal the codec kernels use.
+// exhaustive device checks of the reciprocal and the division the codec
+// kernels use.
 //
 //   kind 0 (quantize pattern): each 4-lane quad reads one 256-byte bf16 row
 //     with four 16-byte loads per lane and writes one 56-byte record (lanes
@@ -88,9 +89,40 @@ __global__ __launch_bounds__(256) void recip_rn_check(unsigned long long* __rest
   }
 }
 
+// Arithmetic check: div_rn against the IEEE quotient a / d. One thread per
+// divisor mantissa (d in [1, 2), 2^23 threads); each runs over the numerator
+// bit patterns base .. base + span - 1 (inside [1, 4): exponent fields 127
+// and 128, so the quotient lies on both sides of 1). cnt[0] counts the
+// mismatches. With corrected = 0 the uncorrected product RN(a * rh) is
+// checked instead (which shows that the check can see a wrong quotient).
+__global__ __launch_bounds__(256) void div_rn_check(unsigned long long* __restrict__ cnt,
+                                                    uint32_t base, uint32_t span, int corrected) {
+  const uint32_t mn = blockIdx.x * 256u + threadIdx.x;  // < 2^23
+  const tq::Recip r = tq::make_recip(__builtin_bit_cast(float, (127u << 23) | mn));
+  unsigned long long bad = 0;
+  for (uint32_t j = 0; j < span; ++j) {
+    const float a = __builtin_bit_cast(float, base + j);
+    const float q = corrected ? tq::div_rn(a, r) : a * r.rh;
+    bad += __builtin_bit_cast(uint32_t, q) != __builtin_bit_cast(uint32_t, a / r.d);
+  }
+  for (int o = 32; o > 0; o >>= 1) bad += __shfl_xor(bad, o);
+  if ((threadIdx.x & 63) == 0 && bad) atomicAdd(&cnt[0], bad);
+}
+
 }  // namespace
 
 extern "C" {
+
+// Runs div_rn_check over numerators base .. base + span - 1 (bit patterns in
+// [1, 4)) for every divisor mantissa; cnt = one zeroed 64-bit device counter.
+// Returns 0, 1 for bad arguments, 2 if the launch failed.
+int tqprobe_div_check(unsigned long long* cnt, uint32_t base, uint32_t span, int corrected,
+                      void* stream) {
+  if (!cnt || span == 0 || base < (127u << 23) || span > (129u << 23) - base) return 1;
+  div_rn_check<<<(1u << 23) / 256, 256, 0, static_cast<hipStream_t>(stream)>>>(cnt, base, span,
+                                                                              corrected);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 // Runs recip_rn_check on `stream`: cnt = 3 zeroed 64-bit device counters.
 // Returns 0, 1 for a null pointer, 2 if the launch failed.

@@ -251,16 +251,14 @@ __global__ __launch_bounds__(256) void tq3_quantize_kernel(const void* __restric
 
     // u = x / norm, correctly rounded. The shared-reciprocal path is exact
     // while every nonzero |x_j| >= norm * 2^-60 and norm <= 2^100; otherwise
-    // the vector takes plain IEEE division. A bf16 / fp16 numerator needs
-    // only the correction step (div_rn_short).
+    // the vector takes plain IEEE division.
     float u[4][8];
     if (amin >= norm * 0x1p-60f && norm <= 0x1p100f) {
       const Recip rn = make_recip(norm);
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          u[g][i] = DT == DT_F32 ? div_rn(x_[g][i], rn) : div_rn_short(x_[g][i], rn);
+        for (int i = 0; i < 8; ++i) u[g][i] = div_rn(x_[g][i], rn);
     } else {
 #pragma unroll
       for (int g = 0; g < 4; ++g)

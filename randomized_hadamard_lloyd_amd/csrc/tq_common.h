@@ -60,47 +60,37 @@ __device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(fl
 __device__ __forceinline__ uint32_t as_u(float f) { return __builtin_bit_cast(uint32_t, f); }
 
 // Quotient a / d rounded to nearest, for a divisor shared by many numerators.
-// rh = RN(1/d), rl = RN(1 - d*rh) * rh carries the reciprocal's rounding error,
-// so q0 = RN(a*rh + RN(a*rl)) is within one ulp of a/d (faithful). The
-// remainder a - d*q0 is then exact and one correction step gives the correctly
-// rounded quotient (P. Markstein, "Computation of elementary functions on the
-// IBM RISC System/6000 processor", IBM J. Res. Dev. 1990; J.-M. Muller et al.,
-// Handbook of Floating-Point Arithmetic, the section on division with an FMA).
-// Valid while no step leaves the normal range: the callers only use it where
-// |a/d| >= 2^-60 (or a = 0) and 1e-8 <= d <= 2^100.
-struct Recip {
-  float d, rh, rl;
-};
-// RN(1/d) from the hardware reciprocal (within an ulp) and one correction
-// with the exact residual 1 - d*r0: the same bits as the IEEE quotient 1.0f/d
-// in three instructions instead of the division's ten. Checked on the device
-// for every normal d below 2^126 (recip_rn_check in stream_probe.hip, run by
-// tests/test_gpu_arith_checks.py); the callers keep 1e-10 <= d <= 2^100.
+// rh = RN(1/d) (recip_rn); q0 = RN(a*rh) is within 1.5 ulp of a/d; the
+// remainder a - d*q0 is exact (one fma), and one correction step
+// q = RN(q0 + rem*rh) gives the correctly rounded quotient. (Markstein's
+// theorem covers this step for a faithful q0 -- P. Markstein, "Computation of
+// elementary functions on the IBM RISC System/6000 processor", IBM J. Res.
+// Dev. 1990; Muller et al., Handbook of Floating-Point Arithmetic -- which
+// RN(a*rh) need not be.) Checked exhaustively on the device instead: every
+// numerator mantissa against every divisor mantissa, the quotient on both
+// sides of 1, 1.4e14 quotients, no mismatch (div_rn_check in
+// stream_probe.hip, run by tests/test_gpu_arith_checks.py). Exponent shifts
+// scale every step exactly while no step leaves the normal range: the callers
+// only use it where |a/d| >= 2^-60 (or a = 0) and 1e-10 <= d <= 2^100.
+//
+// rh itself: the hardware reciprocal (within an ulp) and one correction with
+// the exact residual 1 - d*r0, the same bits as the IEEE quotient 1.0f/d in
+// three instructions instead of the division's ten; checked on the device
+// for every normal d below 2^126 (recip_rn_check).
 __device__ __forceinline__ float recip_rn(float d) {
   const float r0 = __builtin_amdgcn_rcpf(d);
   return __builtin_fmaf(__builtin_fmaf(-d, r0, 1.0f), r0, r0);
 }
+struct Recip {
+  float d, rh;
+};
 __device__ __forceinline__ Recip make_recip(float d) {
   Recip r;
   r.d = d;
   r.rh = recip_rn(d);
-  const float e = __builtin_fmaf(-d, r.rh, 1.0f);
-  r.rl = e * r.rh;
   return r;
 }
 __device__ __forceinline__ float div_rn(float a, const Recip& r) {
-  const float t = a * r.rl;
-  const float q0 = __builtin_fmaf(a, r.rh, t);
-  const float rem = __builtin_fmaf(-q0, r.d, a);
-  return __builtin_fmaf(rem, r.rh, q0);
-}
-// The same quotient for a numerator with at most 16 significant bits (a bf16
-// or fp16 value widened to fp32): q0 = RN(a*rh) alone need not be faithful,
-// but the one correction from the exact remainder still rounds correctly.
-// Checked exhaustively against IEEE division for numerators of 8, 11, 12 and
-// 16 significant bits over every divisor mantissa and both quotient binades
-// (tests/division_check.c); the same normal-range condition applies.
-__device__ __forceinline__ float div_rn_short(float a, const Recip& r) {
   const float q0 = a * r.rh;
   const float rem = __builtin_fmaf(-q0, r.d, a);
   return __builtin_fmaf(rem, r.rh, q0);

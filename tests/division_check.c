@@ -1,6 +1,7 @@
-/* Exhaustive check of the shared-reciprocal division the TQ3 quantizer uses
- * for bf16 / fp16 inputs (host-side; the kernel runs the same IEEE fp32
- * operations): with rh = RN(1/n), q0 = RN(a*rh), rem = fma(-q0, n, a),
+/* Host-side exhaustive check of the shared-reciprocal division the codec
+ * kernels use, for numerators of up to 16 significant bits (bf16 / fp16
+ * inputs; a device check covers every fp32 numerator). The kernels run the
+ * same IEEE fp32 operations: with rh = RN(1/n), q0 = RN(a*rh), rem = fma(-q0, n, a),
  * q = fma(rem, rh, q0) must equal RN(a/n) for every numerator a with at most
  * BITS significant bits and every divisor mantissa n in [1, 2), with a in
  * [1, 2) and [2, 4) so that the quotient lies on both sides of 1. Exponent

@@ -1,9 +1,10 @@
-"""The TQ3 quantizer divides bf16 / fp16 inputs by the vector's norm with a
-shared reciprocal and one correction step (three fp32 operations instead of
-the four a 24-bit numerator needs). This checks, on the host with the same
-IEEE fp32 operations, that the sequence rounds exactly like IEEE division for
-every numerator of 8 (bf16) and 11 (fp16) significant bits and every divisor
-mantissa; and that the check sees the errors of the uncorrected product."""
+"""The codec kernels divide by a shared divisor with its correctly rounded
+reciprocal and one correction step from the exact remainder (three fp32
+operations). This checks, on the host with the same IEEE fp32 operations,
+that the sequence rounds exactly like IEEE division for every numerator of 8
+(bf16) and 11 (fp16) significant bits and every divisor mantissa, and that
+the check sees the errors of the uncorrected product. (The device check in
+test_gpu_arith_checks.py covers every fp32 numerator.)"""
 import os
 import shutil
 import subprocess
