@@ -1,8 +1,8 @@
 // Measurement probes (not part of the codec library): the memory traffic of
 // the TQ3 kernels with no arithmetic, to measure what HBM gives each access
 // pattern on this part, built into libtqprobe.so and timed by bench.py; and
-// exhaustive device checks of the reciprocal and the division the codec
-// kernels use.
+// exhaustive device checks of the reciprocal, division and square root the
+// codec kernels use.
 //
 //   kind 0 (quantize pattern): each 4-lane quad reads one 256-byte bf16 row
 //     with four 16-byte loads per lane and writes one 56-byte record (lanes
@@ -109,9 +109,43 @@ __global__ __launch_bounds__(256) void div_rn_check(unsigned long long* __restri
   if ((threadIdx.x & 63) == 0 && bad) atomicAdd(&cnt[0], bad);
 }
 
+// Arithmetic check: sqrt_rn_large against the IEEE square root for every x
+// with exponent field 31 .. 254 (x in [2^-96, 2^128)) and every mantissa,
+// plus +inf. cnt[0] counts the cases, cnt[1] the mismatches, cnt[2] the
+// mismatches of the raw hardware square root.
+__global__ __launch_bounds__(256) void sqrt_rn_check(unsigned long long* __restrict__ cnt) {
+  const uint32_t m = blockIdx.x * 256u + threadIdx.x;  // < 2^23
+  const uint32_t e = 31u + blockIdx.y;                 // 31 .. 254
+  const bool inf = blockIdx.y == 224;                  // one extra row: +inf
+  const float x = __builtin_bit_cast(float, inf ? 0x7f800000u : (e << 23) | m);
+  const float r = tq::sqrt_rn_large(x), ref = __builtin_sqrtf(x);
+  const float raw = __builtin_amdgcn_sqrtf(x);
+  const bool one = !inf || m == 0;  // the inf row counts one case
+  unsigned long long c = one;
+  unsigned long long bad = one && __builtin_bit_cast(uint32_t, r) != __builtin_bit_cast(uint32_t, ref);
+  unsigned long long rb = one && __builtin_bit_cast(uint32_t, raw) != __builtin_bit_cast(uint32_t, ref);
+  for (int o = 32; o > 0; o >>= 1) {
+    c += __shfl_xor(c, o);
+    bad += __shfl_xor(bad, o);
+    rb += __shfl_xor(rb, o);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    atomicAdd(&cnt[0], c);
+    atomicAdd(&cnt[1], bad);
+    atomicAdd(&cnt[2], rb);
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+// Runs sqrt_rn_check on `stream`: cnt = 3 zeroed 64-bit device counters.
+int tqprobe_sqrt_check(unsigned long long* cnt, void* stream) {
+  if (!cnt) return 1;
+  sqrt_rn_check<<<dim3((1u << 23) / 256, 225), 256, 0, static_cast<hipStream_t>(stream)>>>(cnt);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 // Runs div_rn_check over numerators base .. base + span - 1 (bit patterns in
 // [1, 4)) for every divisor mantissa; cnt = one zeroed 64-bit device counter.

@@ -247,7 +247,7 @@ __global__ __launch_bounds__(256) void tq3_quantize_kernel(const void* __restric
     for (int g = 0; g < 4; ++g) part[g] = part[g] + swz<QP_XOR2>(part[g]);
     const float ss = (part[0] + part[1]) + (part[2] + part[3]);
 
-    const float norm = __builtin_fmaxf(__builtin_sqrtf(ss), kFloor);
+    const float norm = __builtin_fmaxf(sqrt_rn_large(ss), kFloor);
 
     // u = x / norm, correctly rounded. The shared-reciprocal path is exact
     // while every nonzero |x_j| >= norm * 2^-60 and norm <= 2^100; otherwise

@@ -96,6 +96,21 @@ __device__ __forceinline__ float div_rn(float a, const Recip& r) {
   return __builtin_fmaf(rem, r.rh, q0);
 }
 
+// Square root rounded to nearest for x >= 2^-96 (and +inf): the hardware
+// square root s (within an ulp) moved to a neighbour when the exact residual
+// x - s'*s of that neighbour s' says so -- the correction of the IEEE
+// sequence without its rescaling of tiny inputs. A caller that clamps the
+// result to at least 1e-8 may pass any x >= 0: below 2^-96 every candidate is
+// below the clamp. Checked on the device against the IEEE square root for
+// every x in [2^-96, 2^128) (sqrt_rn_check in stream_probe.hip).
+__device__ __forceinline__ float sqrt_rn_large(float x) {
+  const float s = __builtin_amdgcn_sqrtf(x);
+  const float sm = as_f(as_u(s) - 1u), sp = as_f(as_u(s) + 1u);
+  float r = __builtin_fmaf(-sm, s, x) <= 0.0f ? sm : s;
+  r = __builtin_fmaf(-sp, s, x) > 0.0f ? sp : r;
+  return r;
+}
+
 // Tile (tx, ty) of an nx x ny tiling for block blockIdx.x of a 1-D grid of
 // 8 * ceil(nx * ny / 8) blocks. Blocks go to the 8 XCDs round-robin, so block
 // b runs on XCD b % 8; the tiles are dealt so that each XCD works through a

@@ -11,6 +11,10 @@ it replaces):
   TQ_FULL_DIVISION_CHECK=1 it runs over every numerator pattern in [1, 4):
   all 1.4e14 quotients, about a minute on one MI355X.
 
+* sqrt_rn_large, the hardware square root moved to a neighbour by the signs
+  of exact residuals, against the IEEE square root for every x in
+  [2^-96, 2^128) and +inf (the TQ3 norm clamps anything smaller to 1e-8).
+
 Each check also counts the errors of the uncorrected step, to show that it
 sees a wrong result."""
 import ctypes
@@ -31,6 +35,7 @@ SPAN_1_4 = 2 << 23       # patterns in [1, 4)
 def probe():
     lib = ctypes.CDLL(PROBE)
     lib.tqprobe_recip_check.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.tqprobe_sqrt_check.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     lib.tqprobe_div_check.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32,
                                       ctypes.c_int, ctypes.c_void_p]
     return lib
@@ -70,3 +75,13 @@ def test_div_rn_matches_ieee(probe):
 
 def test_div_check_sees_the_uncorrected_product(probe):
     assert _div_mismatches(probe, ONE, 1024, 0) > 0
+
+
+def test_sqrt_rn_large_matches_ieee(probe):
+    cnt = torch.zeros(3, dtype=torch.int64, device="cuda:0")
+    assert probe.tqprobe_sqrt_check(cnt.data_ptr(), _stream()) == 0
+    torch.cuda.synchronize()
+    total, bad, raw = cnt.cpu().tolist()
+    assert total == 224 * (1 << 23) + 1
+    assert bad == 0, f"{bad} square roots differ from the IEEE result"
+    assert raw > 0
