@@ -716,7 +716,15 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_dequantize_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  float* tab = lds + R * d + 16 * wave;  // this wave's codebook x row norm (MR: codebook)
+  // PT: the wave's table holds pairs -- entry e = the stream bits of two
+  // consecutive codes a, b (pairs16) holds (cb[a] * norm, cb[b] * norm), the
+  // same products as single entries -- so one 8-byte read decodes two
+  // elements. For 2-bit codes, and 3-bit ones in blocks of up to 4 waves
+  // (64 pairs: 128 floats a wave, inside the block-sum area).
+  constexpr bool PT = !MR && (BITS == 2 || (BITS == 3 && NT >= 1 && NT <= 4));
+  constexpr int TABF = PT ? 2 << (2 * BITS) : 16;  // floats of one wave's table
+  static_assert(TABF * (NT == 0 ? 16 : NT) <= kMaxBlocks, "tables inside the block-sum area");
+  float* tab = lds + R * d + TABF * wave;  // this wave's codebook x row norm (MR: codebook)
   const int lc = lane_chunk(lane);
   const int grow = MR ? lc / C : 0;
   const int c = MR ? lc - grow * C : lc + 64 * wave;
@@ -788,13 +796,29 @@ __global__ __launch_bounds__(NT == 0 ? 1024 : 256) void orbit_dequantize_kernel(
       ncodes = load_codes<BITS>(packed + row_of(gn) * row_bytes + 2 * BITS * cc);
       nnorm = norms[row_of(gn)];
     }
-    if (!MR && lane < L) tab[lane] = cb.cb[lane] * norm;
-    __builtin_amdgcn_wave_barrier();
-    uint32_t code[16];
-    unpack16<BITS, LSB>(codes, code);
     float w[16];
+    if constexpr (PT) {
+      for (int e = lane; e < L * L; e += 64) {
+        const int a = LSB ? e % L : e / L, b = LSB ? e / L : e % L;
+        reinterpret_cast<float2*>(tab)[e] = make_float2(cb.cb[a] * norm, cb.cb[b] * norm);
+      }
+      __builtin_amdgcn_wave_barrier();
+      uint32_t pi[8];
+      pairs16<BITS, LSB>(codes, pi);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) w[i] = MR ? tab[code[i]] * norm : tab[code[i]];
+      for (int p = 0; p < 8; ++p) {
+        const float2 v = reinterpret_cast<const float2*>(tab)[pi[p]];
+        w[2 * p] = v.x;
+        w[2 * p + 1] = v.y;
+      }
+    } else {
+      if (!MR && lane < L) tab[lane] = cb.cb[lane] * norm;
+      __builtin_amdgcn_wave_barrier();
+      uint32_t code[16];
+      unpack16<BITS, LSB>(codes, code);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) w[i] = MR ? tab[code[i]] * norm : tab[code[i]];
+    }
 
     if (rotated_only) {
       // Stage this wave's tile in element order, re-read it in store order.

@@ -69,30 +69,6 @@ constexpr size_t kLpSmallLds = 64 * 1024;  // the few-rows kernel's LDS ceiling
 // ring. LDS rows hold 64 elements padded to 72 (144 bytes), so the 16-byte
 // operand reads of eight consecutive lanes fall in distinct banks.
 
-// Code pairs of a 64-bit chunk of 16 codes (stream order), as table indices:
-// the pair's bits as they sit in the stream, (a << BITS) | b for MSB-first
-// and a | (b << BITS) for LSB-first (a = the earlier code).
-template <int BITS, bool LSB>
-__device__ __forceinline__ void pairs16(uint64_t acc, uint32_t (&pi)[8]) {
-  constexpr uint32_t mask = (1u << (2 * BITS)) - 1;
-  if constexpr (LSB) {
-#pragma unroll
-    for (int p = 0; p < 8; ++p) pi[p] = (uint32_t)(acc >> (2 * BITS * p)) & mask;
-  } else if constexpr (BITS == 3) {
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const uint32_t le = (uint32_t)(acc >> (24 * g)) & 0xffffffu;
-      const uint32_t w = (le >> 16) | (le & 0xff00u) | ((le & 0xffu) << 16);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) pi[4 * g + p] = (w >> (18 - 6 * p)) & mask;
-    }
-  } else {
-    // BITS = 2: each byte holds two pairs, the earlier in its high half
-#pragma unroll
-    for (int p = 0; p < 8; ++p) pi[p] = (uint32_t)(acc >> (8 * (p >> 1) + 4 - 4 * (p & 1))) & mask;
-  }
-}
-
 template <int DT, int BITS, bool LSB>
 __global__ __launch_bounds__(256) void orbit_linear_lp_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, const uint8_t* __restrict__ packed,
