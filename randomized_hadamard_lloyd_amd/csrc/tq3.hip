@@ -563,6 +563,9 @@ __global__ __launch_bounds__(256) void tq3_dequantize_kernel(const uint8_t* __re
 // Iterations per wave from which the software-pipelined dequantize kernel
 // pays off.
 constexpr int kTq3PipelineMinIters = 16;
+// Cap on the blocks per CU of a grid with one block per 64 vectors (so the
+// grid stays far inside the 2^31 limit; beyond it the blocks loop).
+constexpr int kTq3MaxBlocksPerCu = 1 << 16;
 
 // Quantize grids hold four times the blocks the CUs keep resident (when there
 // is that much work): the hardware then dispatches the remaining blocks as
@@ -591,15 +594,24 @@ hipError_t tq3_dq(const uint8_t* rec, const float* norms, const float* scales, i
   static const int per_cu =
       resident_blocks_per_cu(tq3_dequantize_kernel<DT, false, SPLIT>, 256, 0);
   static const int per_cu_pf =
-      resident_blocks_per_cu(tq3_dequantize_kernel<DT, true, SPLIT>, 256, 0);
+      DT == DT_F32 ? 0 : resident_blocks_per_cu(tq3_dequantize_kernel<DT, true, SPLIT>, 256, 0);
   const int64_t need = (n_vec + kTq3VecPerBlock - 1) / kTq3VecPerBlock;
   const int grid_pf = grid_size(need, cus, per_cu_pf);
-  if (need >= (int64_t)grid_pf * kTq3PipelineMinIters) {
-    tq3_dequantize_kernel<DT, true, SPLIT>
-        <<<grid_pf, 256, 0, s>>>(rec, norms, scales, n_vec, m, y, stride);
-  } else {
+  if constexpr (DT == DT_F32) {
+    // fp32 rows (512 bytes a vector): one block per 64 vectors, no
+    // grid-stride loop. Measured on 2^20 vectors against the pipelined loop:
+    // 117.5-118.3 against 121.8-122.5 us (for 16-bit rows the same grid is
+    // 10-16% slower than the loops below).
     tq3_dequantize_kernel<DT, false, SPLIT>
-        <<<grid_size(need, cus, per_cu), 256, 0, s>>>(rec, norms, scales, n_vec, m, y, stride);
+        <<<grid_size(need, cus, kTq3MaxBlocksPerCu), 256, 0, s>>>(rec, norms, scales, n_vec, m,
+                                                                  y, stride);
+  } else {
+    if (need >= (int64_t)grid_pf * kTq3PipelineMinIters)
+      tq3_dequantize_kernel<DT, true, SPLIT>
+          <<<grid_pf, 256, 0, s>>>(rec, norms, scales, n_vec, m, y, stride);
+    else
+      tq3_dequantize_kernel<DT, false, SPLIT>
+          <<<grid_size(need, cus, per_cu), 256, 0, s>>>(rec, norms, scales, n_vec, m, y, stride);
   }
   return hipGetLastError();
 }
